@@ -1,0 +1,163 @@
+"""Seeded synthetic decode-attention workloads.
+
+This module only draws inputs: shapes, lengths and 16-bit Q/K/V (or latent)
+values from a seeded torch CPU generator.  It holds none of the attention
+arithmetic.  Both the GPU path and the fp64 oracle consume exactly the bytes
+it returns.
+
+Recipe (the pages measure only end-to-end serving on trained models, so these
+stand in for the workload; no dataset or weights are involved):
+  * generator: torch.Generator('cpu').manual_seed(seed); seed defaults to the
+    configuration number;
+  * draw order: lengths (torch.randint(lo, hi + 1), inclusive), then Q, then
+    K, then V (MLA: lengths, Q, latent), each as float32 torch.randn, then
+    rounded once (round-to-nearest-even) to the 16-bit dtype;
+  * fixed length lists are used in their listed order;
+  * layout: Q [B, Hq, Dk]; K, V [T, Hkv, D] packed in sequence order;
+    latent [T, Dk]; cu_seqlens int32 [B+1] with cu[0] = 0.
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+import math
+from typing import Optional, Sequence, Tuple, Union
+
+import numpy as np
+import torch
+
+Lens = Union[Tuple[int, ...], Tuple[str, int, int]]
+
+
+@dataclasses.dataclass(frozen=True)
+class Spec:
+    name: str
+    kind: str            # "gqa" or "mla"
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int    # 1 for MLA (one shared latent)
+    head_dim_k: int
+    head_dim_v: int
+    lens: Lens           # explicit tuple, or ("uniform", lo, hi) inclusive
+    dtype: str           # "f16" or "bf16"
+    scale: float         # already rounded to float32
+    seed: int
+
+    @property
+    def torch_dtype(self):
+        return torch.float16 if self.dtype == "f16" else torch.bfloat16
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+
+def _f32(x: float) -> float:
+    return float(np.float32(x))
+
+
+CONFIGS = {
+    1: Spec("tiny-gqa-b4-h8kv2-d64", "gqa", 4, 8, 2, 64, 64, (17, 64, 100, 128), "f16",
+            _f32(1.0 / math.sqrt(64)), 1),
+    2: Spec("llama3-8b-decode-b32-h32kv8-d128", "gqa", 32, 32, 8, 128, 128, ("uniform", 512, 4096),
+            "f16", _f32(1.0 / math.sqrt(128)), 2),
+    3: Spec("70b-tp8-share-b64-h8kv1-d128", "gqa", 64, 8, 1, 128, 128, ("uniform", 1024, 8192),
+            "f16", _f32(1.0 / math.sqrt(128)), 3),
+    4: Spec("long-ctx-b8-h32kv8-d128-L32768", "gqa", 8, 32, 8, 128, 128, (32768,) * 8, "bf16",
+            _f32(1.0 / math.sqrt(128)), 4),
+    5: Spec("mla-absorbed-b32-h16-r512-rope64", "mla", 32, 16, 1, 576, 512, ("uniform", 1024, 8192),
+            "bf16", _f32(1.0 / math.sqrt(192)), 5),
+}
+
+
+@dataclasses.dataclass
+class Inputs:
+    spec: Spec
+    lens: np.ndarray                  # int64 [B]
+    cu_seqlens: torch.Tensor          # int32 [B+1] (CPU)
+    q: torch.Tensor                   # 16-bit [B, Hq, Dk] (CPU)
+    k: Optional[torch.Tensor] = None  # 16-bit [T, Hkv, D]
+    v: Optional[torch.Tensor] = None  # 16-bit [T, Hkv, D]
+    latent: Optional[torch.Tensor] = None  # 16-bit [T, Dk] (MLA)
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    @property
+    def max_seqlen(self) -> int:
+        return int(self.lens.max()) if len(self.lens) else 0
+
+    def kv_bytes(self) -> int:
+        """Bytes of K and V (or of the latent rows) that one decode step must read once."""
+        if self.latent is not None:
+            return self.latent.numel() * 2
+        return (self.k.numel() + self.v.numel()) * 2
+
+    def bits(self, name: str) -> np.ndarray:
+        """Raw uint16 patterns of a 16-bit tensor, as numpy (for the oracle)."""
+        t = getattr(self, name)
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    def sha256(self) -> str:
+        h = hashlib.sha256()
+        h.update(self.cu_seqlens.numpy().tobytes())
+        for name in ("q", "k", "v", "latent"):
+            t = getattr(self, name)
+            if t is not None:
+                h.update(t.contiguous().view(torch.int16).numpy().tobytes())
+        return h.hexdigest()
+
+
+def draw_lens(spec: Spec, gen: torch.Generator) -> np.ndarray:
+    if isinstance(spec.lens[0], str):
+        _, lo, hi = spec.lens
+        return torch.randint(lo, hi + 1, (spec.batch,), generator=gen).numpy().astype(np.int64)
+    if len(spec.lens) != spec.batch:
+        raise ValueError("explicit length list must have one entry per sequence")
+    return np.asarray(spec.lens, dtype=np.int64)
+
+
+def cu_from_lens(lens: Sequence[int]) -> torch.Tensor:
+    cu = np.zeros(len(lens) + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(np.asarray(lens, dtype=np.int64))
+    if cu[-1] > np.iinfo(np.int32).max:
+        raise ValueError("total tokens exceed int32")
+    return torch.from_numpy(cu.astype(np.int32))
+
+
+def make_inputs(spec: Spec, seed: Optional[int] = None, lens: Optional[Sequence[int]] = None,
+                q_mult: float = 1.0) -> Inputs:
+    """Draw one batch for `spec`.
+
+    seed   : overrides spec.seed.
+    lens   : overrides the length draw (edge cases: zeros, ragged tails ...);
+             the generator still draws nothing for lengths in that case.
+    q_mult : multiplies Q before rounding ("peaked" scores for stress tests).
+    """
+    gen = torch.Generator("cpu")
+    gen.manual_seed(spec.seed if seed is None else seed)
+    if lens is None:
+        lens_np = draw_lens(spec, gen)
+    else:
+        lens_np = np.asarray(lens, dtype=np.int64)
+        if len(lens_np) != spec.batch:
+            raise ValueError("lens must have batch entries")
+    cu = cu_from_lens(lens_np)
+    T = int(cu[-1])
+    dt = spec.torch_dtype
+    q = torch.randn(spec.batch, spec.num_q_heads, spec.head_dim_k, generator=gen)
+    if q_mult != 1.0:
+        q = q * q_mult
+    q = q.to(dt)
+    if spec.kind == "mla":
+        latent = torch.randn(T, spec.head_dim_k, generator=gen).to(dt)
+        return Inputs(spec, lens_np, cu, q, latent=latent)
+    k = torch.randn(T, spec.num_kv_heads, spec.head_dim_k, generator=gen).to(dt)
+    v = torch.randn(T, spec.num_kv_heads, spec.head_dim_v, generator=gen).to(dt)
+    return Inputs(spec, lens_np, cu, q, k=k, v=v)
+
+
+def with_shape(spec: Spec, **changes) -> Spec:
+    """A copy of `spec` with some fields replaced (for edge-case tests)."""
+    return dataclasses.replace(spec, **changes)
