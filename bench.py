@@ -1,0 +1,244 @@
+"""Decode-attention benchmark on one MI355X.
+
+One step = one call of the fused decode attention for the whole batch (the
+split-KV work and the log-sum-exp combine both run inside the one kernel
+launch), on synthetic inputs already resident in HBM.  Inputs are replicated
+R = max(2, ceil(1 GiB / bytes)) times and the steps cycle through the
+replicas, so the 256 MB Infinity Cache cannot serve a step from the previous
+one.
+
+Prints one JSON line:
+  value      KV GB/s = algorithmic bytes (every K and V element, or every
+             latent row, read once) / wall time per step
+  roofline   the decode kernel against the 8 TB/s HBM peak; achieved = the
+             same bytes / the kernel's own average duration, from HIP events
+             recorded around every launch on the launch stream
+  cpu_baseline  the fp64 oracle on the host cores, on a bounded sample
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["zl_device.h", "zl_split.h", "zl_tile.h", "zl_kernels.h", "decode_attn.hip",
+                  "decode_mla.hip"]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mla_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
+                    help="workload (default 2: batch 32, 32/8 heads, D 128, ragged 512..4096)")
+    ap.add_argument("--workers", type=int, default=0, help="decode workers (0 = library default)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target host time of the oracle sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="a few launches only (for rocprofv3 counter passes); no JSON")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU: the decode kernel is measured on "
+                                   "one GPU's share; multi-GPU scaling is not part of it",
+                          "n_gpus_requested": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mla_attention_amd as zl
+    import workloads
+
+    spec = workloads.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    x = workloads.make_inputs(spec)
+    kv_bytes = x.kv_bytes()
+    reps = max(2, math.ceil((1 << 30) / kv_bytes))
+    if args.profile_run:
+        reps = 1
+    cu = x.cu_seqlens.to(dev)
+    q = x.q.to(dev)
+    if spec.kind == "mla":
+        caches = [(x.latent.to(dev),) for _ in range(reps)]
+        ws_bytes = zl.zl_decode_attn_mla_workspace_size(spec.batch, spec.num_q_heads, 512, 64,
+                                                        x.max_seqlen, spec.torch_dtype, args.workers)
+    else:
+        caches = [(x.k.to(dev), x.v.to(dev)) for _ in range(reps)]
+        ws_bytes = zl.zl_decode_attn_workspace_size(spec.batch, spec.num_q_heads, spec.num_kv_heads,
+                                                    spec.head_dim_k, x.max_seqlen, spec.torch_dtype,
+                                                    args.workers)
+    ws = zl.new_workspace(ws_bytes, dev)
+    out = torch.empty(spec.batch, spec.num_q_heads, spec.head_dim_v, dtype=spec.torch_dtype, device=dev)
+    lse = torch.empty(spec.batch, spec.num_q_heads, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        c = caches[i % reps]
+        if spec.kind == "mla":
+            zl.zl_decode_attn_mla(q, c[0], cu, x.max_seqlen, spec.scale, out=out, lse=lse, workspace=ws,
+                                  num_workers=args.workers, stream=stream)
+        else:
+            zl.zl_decode_attn_gqa(q, c[0], c[1], cu, x.max_seqlen, spec.scale, out=out, lse=lse,
+                                  workspace=ws, num_workers=args.workers, stream=stream)
+
+    if args.profile_run:
+        for i in range(max(3, args.steps)):
+            step(i)
+        torch.cuda.synchronize()
+        print(f"profile run: {spec.name}, {max(3, args.steps)} launches", flush=True)
+        return
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        starts[i].record(stream)
+        step(args.warmup + i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    span_ms = starts[0].elapsed_time(ends[-1])
+    per_launch_ms = [starts[i].elapsed_time(ends[i]) for i in range(K)]
+    ms_per_step = span_ms / K
+    kern_ms = float(np.mean(per_launch_ms))
+    value_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved_gbs = kv_bytes / (kern_ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(x, spec, args.cpu_seconds)
+
+    workload = spec.name
+    rec = {
+        "metric": "decode-attn KV GB/s (algorithmic K+V bytes / step time) and us/step, % of MI355X HBM peak",
+        "value": round(value_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "hbm_peak_frac": round(value_gbs / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if spec.dtype == "f16" else "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V, ragged lengths; no dataset or weights)",
+        "config": {
+            "workload": workload,
+            "batch": spec.batch,
+            "num_q_heads": spec.num_q_heads,
+            "num_kv_heads": spec.num_kv_heads,
+            "head_dim_k": spec.head_dim_k,
+            "head_dim_v": spec.head_dim_v,
+            "ctx_lens": list(spec.lens) if not isinstance(spec.lens[0], str) else
+            f"uniform[{spec.lens[1]},{spec.lens[2]}] seed {spec.seed}",
+            "total_tokens": x.total_tokens,
+            "kv_bytes_per_step": kv_bytes,
+            "cold_cache_replicas": reps,
+            "workers": args.workers or "default",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "mla_decode_kernel" if spec.kind == "mla" else "decode_kernel",
+            "achieved": round(achieved_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profile(workload),
+            "avg_launch_us": round(kern_ms * 1e3, 2),
+        },
+        "cpu_baseline": cpu,
+        "wall_ms_timed_region": round(wall_ms, 2),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(x, spec, target_s: float):
+    """The fp64 oracle on all host cores over whole sequences of the same
+    batch, added until about target_s seconds of work; reported in the
+    metric's unit (KV GB/s of the sample)."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.max_threads()
+    cu = x.cu_seqlens.numpy()
+    dt = oracle.F16 if spec.dtype == "f16" else oracle.BF16
+    row_bytes = (spec.head_dim_k * 2 if spec.kind == "mla"
+                 else 2 * spec.num_kv_heads * spec.head_dim_k * 2)
+    q = x.bits("q")
+    done_bytes, elapsed, nseq, passes = 0, 0.0, 0, 0
+    order = list(range(spec.batch))
+    while elapsed < target_s and passes < 100:
+        for b in order:
+            a, e = int(cu[b]), int(cu[b + 1])
+            sub = np.array([0, e - a], dtype=np.int32)
+            t = time.perf_counter()
+            if spec.kind == "mla":
+                oracle.mla_decode(q[b:b + 1], x.bits("latent")[a:e], sub, spec.scale, dt, threads=threads)
+            else:
+                oracle.gqa_decode(q[b:b + 1], x.bits("k")[a:e], x.bits("v")[a:e], sub, spec.num_kv_heads,
+                                  spec.scale, dt, threads=threads)
+            elapsed += time.perf_counter() - t
+            done_bytes += (e - a) * row_bytes
+            nseq += 1
+            if elapsed >= target_s:
+                break
+        passes += 1
+    return {
+        "value": round(done_bytes / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{nseq} whole sequences of this batch (all {spec.num_q_heads} query heads each, "
+                  f"{done_bytes} KV bytes) through the fp64 C oracle, OpenMP over heads, {elapsed:.1f} s",
+        "us_per_step_equiv": round(x.kv_bytes() / (done_bytes / elapsed) * 1e6, 1),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,200 @@
+/*
+ * zl_attn.h -- C ABI of the MI355X (gfx950) fused batched decode attention
+ * library, libzl_attn.so.
+ *
+ * The operation.  In the decode stage of LLM serving every sequence of a
+ * dynamically assembled batch contributes one new query token per head; that
+ * query attends over the sequence's whole key/value cache.  The ZhiLight pages
+ * single this out as the engine's core difference from vLLM/SGLang ("ZhiLight：
+ * 知乎开源的高性能 LLM 推理加速引擎", section 4 "Tensor Core 上的 Flash
+ * Attention": decode runs a tensor-core Fused Batch Attention because one new
+ * token per step with small batches suits the matrix units; "ZhiLight: Zhihu's
+ * CUDA Inference Engine for Llama and DeepSeek on PCIe GPUs", section "Dual
+ * streams, host all-reduce and the memory model": fused batch attention for
+ * decoding with tensor core instructions).  Batches are built from requests of
+ * different lengths (first page, section "功能生态", dynamic batching), so the
+ * cache is ragged.  The pages give no formula; the library computes the plain
+ * scaled-dot-product attention for every (sequence b, query head h):
+ *
+ *     s_i = softmax_scale * <q[b,h,:], K[cu[b]+i, g(h), :]>,  0 <= i < L_b
+ *     out[b,h,:] = sum_i exp(s_i - m) V[cu[b]+i, g(h), :] / sum_i exp(s_i - m)
+ *     lse[b,h]   = m + ln(sum_i exp(s_i - m)),   m = max_i s_i
+ *     L_b = 0  ->  out = 0, lse = -inf
+ *
+ * with g(h) = h / (num_q_heads / num_kv_heads): consecutive query heads share
+ * one key/value head (grouped/multi-query attention; the third page, part 01
+ * section 1, names Multi-Query Attention as a variant of multi-head attention).
+ * No causal mask: the cache holds every token the new query may see.
+ *
+ * Conventions for every entry point.
+ *  - Pointers are DEVICE pointers unless marked "host".  The caller owns every
+ *    buffer; the library keeps no pointer after it returns.
+ *  - Work is enqueued on `stream` (NULL = the default stream) and is
+ *    asynchronous: nothing synchronises, nothing is allocated.
+ *  - Host-checkable arguments are validated before any HIP call; a bad argument
+ *    returns an error status and enqueues nothing.  Device contents (the values
+ *    in cu_seqlens) are preconditions: cu[0] = 0, non-decreasing, every length
+ *    at most max_seqlen_k, cu[batch] = total_tokens of the caches.
+ *  - 16-bit buffers (q, k, v, latent, out) must be 16-byte aligned.  Rows are
+ *    dense: the layouts below have no padding.
+ *  - Results are bitwise deterministic for identical inputs, arguments and
+ *    device (no floating-point atomics; fixed reduction order).
+ *  - Calls that share one workspace must not overlap in time (same stream, or
+ *    ordered by events).
+ *  - No status crosses the ABI as an exception; nothing aborts or prints.
+ */
+#ifndef ZL_ATTN_H
+#define ZL_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define ZL_API __attribute__((visibility("default")))
+#else
+#define ZL_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ZL_OK = 0,
+    ZL_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, misalignment, ...   */
+    ZL_ERR_UNSUPPORTED = 2,        /* valid but not implemented (head_dim, ...)   */
+    ZL_ERR_WORKSPACE_TOO_SMALL = 3,
+    ZL_ERR_HIP = 4                 /* a HIP runtime call or launch failed          */
+} zl_status_t;
+
+typedef enum {
+    ZL_DTYPE_F16 = 0,              /* IEEE binary16                                */
+    ZL_DTYPE_BF16 = 1              /* bfloat16                                     */
+} zl_dtype_t;
+
+/* Opaque HIP stream handle (hipStream_t); NULL means the default stream. */
+typedef struct ihipStream_t *zl_stream_t;
+
+/*
+ * Bytes of device workspace that zl_decode_attn_gqa needs for these sizes
+ * (host function, no HIP call).  Returns 0 for invalid sizes.
+ * The workspace holds per-worker partial results and one completion counter
+ * per (sequence, key/value head); it must be ZERO-FILLED before its first use
+ * (e.g. allocated with torch.zeros).  Every call leaves the counters at zero
+ * again, so a workspace is zeroed once and then reused.
+ */
+ZL_API size_t zl_decode_attn_workspace_size(int batch, int num_q_heads, int num_kv_heads,
+                                     int head_dim, int max_seqlen_k, zl_dtype_t dtype);
+
+/*
+ * Grouped-query decode attention over a packed ragged cache (the operation in
+ * the file header).
+ *   q          [batch, num_q_heads, head_dim]             dtype
+ *   k_cache    [total_tokens, num_kv_heads, head_dim]     dtype, sequence b
+ *              owns rows cu_seqlens[b] .. cu_seqlens[b+1]-1
+ *   v_cache    [total_tokens, num_kv_heads, head_dim]     dtype, same rows
+ *              (k_cache / v_cache may be NULL only if every sequence is empty)
+ *   cu_seqlens [batch + 1] int32 (device)
+ *   batch >= 0 (0 is a no-op), num_q_heads % num_kv_heads == 0,
+ *   num_q_heads / num_kv_heads <= 16 or a multiple of 16,
+ *   head_dim in {64, 128} (else ZL_ERR_UNSUPPORTED),
+ *   max_seqlen_k (host) >= every sequence length,
+ *   softmax_scale finite (0 allowed),
+ *   out        [batch, num_q_heads, head_dim] dtype, fully overwritten
+ *   lse        [batch, num_q_heads] float32, natural log; NULL = not written
+ *   workspace  zero-filled once, >= zl_decode_attn_workspace_size(...) bytes,
+ *              256-byte aligned
+ */
+ZL_API zl_status_t zl_decode_attn_gqa(const void *q, const void *k_cache, const void *v_cache,
+                               const int32_t *cu_seqlens, int batch, int num_q_heads,
+                               int num_kv_heads, int head_dim, int max_seqlen_k,
+                               float softmax_scale, zl_dtype_t dtype, void *out, float *lse,
+                               void *workspace, size_t workspace_bytes, zl_stream_t stream);
+
+/*
+ * Bytes of device workspace that zl_decode_attn_mla needs (host function,
+ * same zero-fill rule as above).  Returns 0 for invalid sizes.
+ */
+ZL_API size_t zl_decode_attn_mla_workspace_size(int batch, int num_q_heads, int kv_lora_rank,
+                                         int rope_dim, int max_seqlen_k, zl_dtype_t dtype);
+
+/*
+ * Absorbed multi-head latent attention decode (DeepSeek-V2 MLA, which the
+ * ZhiLight pages list as natively supported: first page, sections "技术架构"
+ * (flash_mla) and "功能生态"; second page, section "Dual streams, host
+ * all-reduce and the memory model").  Every query head attends over one shared
+ * latent row per token; the query is already multiplied into latent space
+ * (its first kv_lora_rank values) and carries its rotary part in the last
+ * rope_dim values; the value is the first kv_lora_rank columns of the same
+ * row, and the output stays in latent space (the up-projection is applied
+ * after this call).  It is the operation of the file header with one
+ * key/value head, K = row[0 : rank+rope], V = row[0 : rank].
+ *   q          [batch, num_q_heads, kv_lora_rank + rope_dim]  dtype
+ *   kv_cache   [total_tokens, kv_lora_rank + rope_dim]        dtype (NULL only if
+ *              every sequence is empty)
+ *   cu_seqlens [batch + 1] int32 (device)
+ *   kv_lora_rank == 512 and rope_dim == 64 (else ZL_ERR_UNSUPPORTED),
+ *   1 <= num_q_heads, num_q_heads <= 16 or a multiple of 16,
+ *   out        [batch, num_q_heads, kv_lora_rank] dtype
+ *   lse        [batch, num_q_heads] float32 or NULL
+ *   workspace  as for zl_decode_attn_gqa, sized by
+ *              zl_decode_attn_mla_workspace_size
+ */
+ZL_API zl_status_t zl_decode_attn_mla(const void *q, const void *kv_cache, const int32_t *cu_seqlens,
+                               int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
+                               int max_seqlen_k, float softmax_scale, zl_dtype_t dtype,
+                               void *out, float *lse, void *workspace, size_t workspace_bytes,
+                               zl_stream_t stream);
+
+/*
+ * Log-sum-exp combine of split partial results (the merge step that makes
+ * split-KV "flash decoding" exact; the first page names flash_decoding among
+ * the engine's third-party kernels, section "技术架构").  Each split s holds
+ * the attention result of a disjoint subset of one row's tokens:
+ *   partial_out [num_splits, rows, head_dim_v] float32, normalised (O_s / l_s)
+ *   partial_lse [num_splits, rows] float32, natural log; -inf = empty split
+ * with rows = batch * num_heads.  Writes
+ *   M = max_s lse_s,  w_s = exp(lse_s - M),
+ *   out[r,:] = sum_s w_s O_s / sum_s w_s    (out_dtype, [rows, head_dim_v])
+ *   lse[r]   = M + ln(sum_s w_s)           (float32 or NULL)
+ * All splits empty -> out = 0, lse = -inf.  1 <= num_splits <= 1024,
+ * head_dim_v % 4 == 0, partial buffers 16-byte aligned.
+ */
+ZL_API zl_status_t zl_attn_combine(const float *partial_out, const float *partial_lse, int num_splits,
+                            int batch, int num_heads, int head_dim_v, zl_dtype_t out_dtype,
+                            void *out, float *lse, zl_stream_t stream);
+
+/*
+ * The same two decode calls with an explicit number of workers (wavefronts
+ * that split the batch's (kv-head, token) rows evenly; a multiple of 8,
+ * 8 .. 65536; 0 = the default for the layout) and the matching workspace
+ * sizes.  The result is the same attention for any worker count, up to the
+ * fp32 rounding of how tokens are grouped; tests use this to vary the split,
+ * and it lets a caller trade split overhead against parallelism.
+ */
+ZL_API size_t zl_decode_attn_workspace_size_ex(int batch, int num_q_heads, int num_kv_heads,
+                                        int head_dim, int max_seqlen_k, zl_dtype_t dtype,
+                                        int num_workers);
+ZL_API zl_status_t zl_decode_attn_gqa_ex(const void *q, const void *k_cache, const void *v_cache,
+                                  const int32_t *cu_seqlens, int batch, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int max_seqlen_k,
+                                  float softmax_scale, zl_dtype_t dtype, void *out, float *lse,
+                                  int num_workers, void *workspace, size_t workspace_bytes,
+                                  zl_stream_t stream);
+ZL_API size_t zl_decode_attn_mla_workspace_size_ex(int batch, int num_q_heads, int kv_lora_rank,
+                                            int rope_dim, int max_seqlen_k, zl_dtype_t dtype,
+                                            int num_workers);
+ZL_API zl_status_t zl_decode_attn_mla_ex(const void *q, const void *kv_cache, const int32_t *cu_seqlens,
+                                  int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
+                                  int max_seqlen_k, float softmax_scale, zl_dtype_t dtype,
+                                  void *out, float *lse, int num_workers, void *workspace,
+                                  size_t workspace_bytes, zl_stream_t stream);
+
+/* Static, human-readable name of a status code (host). */
+ZL_API const char *zl_status_string(zl_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZL_ATTN_H */

@@ -1,0 +1,233 @@
+"""Python binding of libzl_attn.so, the MI355X fused batched decode attention.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/zl_attn.h.  PyTorch supplies
+device memory and streams.  There is no fallback: if the library is missing
+or no GPU is present, the calls raise.
+
+Entry points (same names as the C ABI):
+  zl_decode_attn_gqa      grouped-query decode attention over a packed ragged cache
+  zl_decode_attn_mla      absorbed multi-head latent attention decode
+  zl_attn_combine         log-sum-exp combine of split partial results
+  zl_decode_attn_workspace_size / zl_decode_attn_mla_workspace_size
+  zl_status_string
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch  # loads the HIP runtime first; the library reuses it (same soname)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzl_attn.so")
+_lib = None
+_lock = threading.Lock()
+
+ZL_OK = 0
+ZL_ERR_INVALID_ARGUMENT = 1
+ZL_ERR_UNSUPPORTED = 2
+ZL_ERR_WORKSPACE_TOO_SMALL = 3
+ZL_ERR_HIP = 4
+
+_DTYPE = {torch.float16: 0, torch.bfloat16: 1}
+
+# Every symbol include/zl_attn.h declares, with its ctypes signature.
+_c_int, _c_size, _c_float, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
+SIGNATURES = {
+    "zl_decode_attn_workspace_size": (_c_size, [_c_int] * 6),
+    "zl_decode_attn_workspace_size_ex": (_c_size, [_c_int] * 7),
+    "zl_decode_attn_gqa": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                    _c_float, _c_int, _vp, _vp, _vp, _c_size, _vp]),
+    "zl_decode_attn_gqa_ex": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                       _c_float, _c_int, _vp, _vp, _c_int, _vp, _c_size, _vp]),
+    "zl_decode_attn_mla_workspace_size": (_c_size, [_c_int] * 6),
+    "zl_decode_attn_mla_workspace_size_ex": (_c_size, [_c_int] * 7),
+    "zl_decode_attn_mla": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
+                                    _c_int, _vp, _vp, _vp, _c_size, _vp]),
+    "zl_decode_attn_mla_ex": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                       _c_float, _c_int, _vp, _vp, _c_int, _vp, _c_size, _vp]),
+    "zl_attn_combine": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
+    "zl_status_string": (ctypes.c_char_p, [_c_int]),
+}
+
+
+class ZlError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {zl_status_string(status)}")
+
+
+def library():
+    """Load libzl_attn.so (built in-tree by mla_attention_amd/build.py); raise if absent."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                                  "or python mla_attention_amd/build.py")
+            lib = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+        return _lib
+
+
+def zl_status_string(status: int) -> str:
+    return library().zl_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != ZL_OK:
+        raise ZlError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def zl_decode_attn_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_seqlen_k,
+                                  dtype: torch.dtype, num_workers: int = 0) -> int:
+    return int(library().zl_decode_attn_workspace_size_ex(batch, num_q_heads, num_kv_heads, head_dim,
+                                                           max_seqlen_k, _DTYPE[dtype], num_workers))
+
+
+def zl_decode_attn_mla_workspace_size(batch, num_q_heads, kv_lora_rank, rope_dim, max_seqlen_k,
+                                      dtype: torch.dtype, num_workers: int = 0) -> int:
+    return int(library().zl_decode_attn_mla_workspace_size_ex(batch, num_q_heads, kv_lora_rank,
+                                                               rope_dim, max_seqlen_k, _DTYPE[dtype],
+                                                               num_workers))
+
+
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-filled workspace (the counters must start at zero; calls keep them there)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def zl_decode_attn_gqa(q, k_cache, v_cache, cu_seqlens, max_seqlen_k: int, softmax_scale: float,
+                       out=None, lse=None, workspace=None, num_workers: int = 0, stream=None,
+                       return_lse: bool = False):
+    """out[b,h] = softmax(scale * q[b,h] . K[seq b, h // G]) V[seq b, h // G].
+
+    q [B, Hq, D], k_cache/v_cache [T, Hkv, D] (fp16 or bf16, packed ragged),
+    cu_seqlens int32 [B+1].  Returns out (and lse [B, Hq] fp32 if return_lse
+    or lse is given).  workspace: zero-filled uint8 tensor from new_workspace();
+    allocated here when omitted.
+    """
+    _need(q, "q", ndim=3)
+    dev = q.device
+    if q.dtype not in _DTYPE:
+        raise ValueError("q must be float16 or bfloat16")
+    _need(k_cache, "k_cache", q.dtype, 3, dev)
+    _need(v_cache, "v_cache", q.dtype, 3, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1, dev)
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    if k_cache.shape[2] != D or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache / v_cache must be [T, Hkv, head_dim] like q")
+    if cu_seqlens.numel() != B + 1:
+        raise ValueError("cu_seqlens must have batch + 1 entries")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, 3, dev)
+    if out.shape != q.shape:
+        raise ValueError("out must be [B, Hq, head_dim]")
+    if lse is None and return_lse:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2, dev)
+    nbytes = zl_decode_attn_workspace_size(B, Hq, Hkv, D, max_seqlen_k, q.dtype, num_workers)
+    if workspace is None:
+        workspace = new_workspace(nbytes, dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    st = library().zl_decode_attn_gqa_ex(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens), B, Hq, Hkv, D, int(max_seqlen_k),
+        float(softmax_scale), _DTYPE[q.dtype], _ptr(out), _ptr(lse), int(num_workers),
+        _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    _check(st, "zl_decode_attn_gqa")
+    return (out, lse) if lse is not None else out
+
+
+def zl_decode_attn_mla(q, kv_cache, cu_seqlens, max_seqlen_k: int, softmax_scale: float,
+                       kv_lora_rank: int = 512, rope_dim: int = 64, out=None, lse=None,
+                       workspace=None, num_workers: int = 0, stream=None, return_lse: bool = False):
+    """Absorbed MLA decode: q [B, H, rank+rope], kv_cache [T, rank+rope];
+    K = whole latent row, V = its first kv_lora_rank columns.  Returns out [B, H, rank]."""
+    _need(q, "q", ndim=3)
+    dev = q.device
+    if q.dtype not in _DTYPE:
+        raise ValueError("q must be float16 or bfloat16")
+    _need(kv_cache, "kv_cache", q.dtype, 2, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1, dev)
+    B, H, Dk = q.shape
+    if Dk != kv_lora_rank + rope_dim or kv_cache.shape[1] != Dk:
+        raise ValueError("q and kv_cache rows must be kv_lora_rank + rope_dim wide")
+    if cu_seqlens.numel() != B + 1:
+        raise ValueError("cu_seqlens must have batch + 1 entries")
+    if out is None:
+        out = torch.empty(B, H, kv_lora_rank, dtype=q.dtype, device=dev)
+    _need(out, "out", q.dtype, 3, dev)
+    if tuple(out.shape) != (B, H, kv_lora_rank):
+        raise ValueError("out must be [B, H, kv_lora_rank]")
+    if lse is None and return_lse:
+        lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2, dev)
+    nbytes = zl_decode_attn_mla_workspace_size(B, H, kv_lora_rank, rope_dim, max_seqlen_k, q.dtype,
+                                               num_workers)
+    if workspace is None:
+        workspace = new_workspace(nbytes, dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    st = library().zl_decode_attn_mla_ex(
+        _ptr(q), _ptr(kv_cache), _ptr(cu_seqlens), B, H, kv_lora_rank, rope_dim, int(max_seqlen_k),
+        float(softmax_scale), _DTYPE[q.dtype], _ptr(out), _ptr(lse), int(num_workers),
+        _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    _check(st, "zl_decode_attn_mla")
+    return (out, lse) if lse is not None else out
+
+
+def zl_attn_combine(partial_out, partial_lse, out_dtype: torch.dtype = torch.bfloat16, out=None,
+                    lse=None, stream=None, return_lse: bool = False):
+    """Merge split results: partial_out [S, B, H, Dv] fp32 (normalised),
+    partial_lse [S, B, H] fp32 (natural log, -inf = empty) -> out [B, H, Dv]."""
+    _need(partial_out, "partial_out", torch.float32, 4)
+    dev = partial_out.device
+    _need(partial_lse, "partial_lse", torch.float32, 3, dev)
+    S, B, H, Dv = partial_out.shape
+    if tuple(partial_lse.shape) != (S, B, H):
+        raise ValueError("partial_lse must be [S, B, H]")
+    if out is None:
+        out = torch.empty(B, H, Dv, dtype=out_dtype, device=dev)
+    _need(out, "out", out_dtype, 3, dev)
+    if lse is None and return_lse:
+        lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2, dev)
+    st = library().zl_attn_combine(_ptr(partial_out), _ptr(partial_lse), S, B, H, Dv,
+                                   _DTYPE[out_dtype], _ptr(out), _ptr(lse), _stream(stream, dev))
+    _check(st, "zl_attn_combine")
+    return (out, lse) if lse is not None else out

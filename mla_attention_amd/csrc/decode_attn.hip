@@ -1,0 +1,313 @@
+// decode_attn.hip -- fused batched decode attention for gfx950 (MI355X),
+// grouped-query layout (K, V [T, Hkv, D], D = 64 or 128).  The absorbed-MLA
+// variant (576-wide latent, V inside the K row) is decode_mla.hip.
+//
+// One query token per (sequence, query head) attends over a packed ragged
+// cache: the decode-stage fused batch attention that the ZhiLight pages put on
+// the matrix units (first page, section 4 "Tensor Core 上的 Flash Attention").
+//
+// Kernel structure (one wavefront per workgroup, one worker per wavefront):
+//  * Work split: every worker streams the same number of (unit, token) rows,
+//    whatever the mix of sequence lengths; see zl_split.h.
+//  * Data path: 32-token tiles go HBM -> LDS with 16-byte global_load_lds
+//    (no VGPR round trip), each 16-lane group reading contiguous bytes of one
+//    row.  STAGES tiles form an LDS ring, STAGES-1 of them in flight while the
+//    oldest is consumed.  16-byte slots are XOR-swizzled per row so that the
+//    MFMA operand reads (16 rows, one slot) and the transposing V reads (4 rows,
+//    two slots) fall in distinct banks.
+//  * QK^T: v_mfma_f32_16x16x32 with the K tile as A (16 tokens x 32 dims) and
+//    the unit's query heads as B (32 dims x 16 heads, zero-padded when fewer).
+//    Result lane (g, n) = 16g + n: head n, tokens 4g..4g+3 (and +16).
+//  * Online softmax in fp32 per head; max and sum over the four lane groups by
+//    lane exchange; exp2 with log2(e) folded into the scale.
+//  * PV: O^T = V^T P^T.  V^T is the A operand, read from LDS with
+//    ds_read_b64_tr_b16; P^T is the B operand straight from the score
+//    registers (the tr read's token order equals the score layout, so no lane
+//    exchange is needed).  O^T keeps head n in lane n, so the per-head rescale
+//    is lane-local.
+#include "zl_device.h"
+#include "zl_kernels.h"
+#include "zl_split.h"
+#include "zl_tile.h"
+
+namespace zl {
+
+// Tile geometry per cache layout.
+template <int L>
+struct Geo;
+
+template <>
+struct Geo<kGqaD64> {
+  static constexpr int DK = 64, DV = 64;
+  static constexpr bool SHARED_KV = false;
+  static constexpr int STAGES = 3;
+  static constexpr int WAVES_PER_CU = 6;
+  static constexpr int MAX_WAVES_PER_SIMD = 2;
+  // 128-byte rows: two rows per 256-byte bank line.
+  __device__ static int slot(int c, int r) { return c ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1)); }
+};
+
+template <>
+struct Geo<kGqaD128> {
+  static constexpr int DK = 128, DV = 128;
+  static constexpr bool SHARED_KV = false;
+  static constexpr int STAGES = 3;
+  static constexpr int WAVES_PER_CU = 3;
+  static constexpr int MAX_WAVES_PER_SIMD = 1;
+  // 256-byte rows: XOR over all 16 slots.
+  __device__ static int slot(int c, int r) { return c ^ (((r << 1) & 15) | ((r >> 3) & 1)); }
+};
+
+template <int L>
+struct Tile {
+  using G = Geo<L>;
+  static constexpr int DK = G::DK, DV = G::DV;
+  static constexpr int KROWB = DK * 2;                 // bytes per K row in LDS
+  static constexpr int VROWB = G::SHARED_KV ? KROWB : DV * 2;
+  static constexpr int KCPR = DK / 8;                  // 16-byte chunks per K row
+  static constexpr int VCPR = DV / 8;
+  static constexpr int KBYTES = 32 * KROWB;            // one tile of K
+  static constexpr int VBYTES = G::SHARED_KV ? 0 : 32 * VROWB;
+  static constexpr int STAGE_BYTES = KBYTES + VBYTES;
+  static constexpr int NI_K = KBYTES / 1024;           // 1 KB DMA instructions per tile
+  static constexpr int NI_V = VBYTES / 1024;
+  static constexpr int PER_TILE = NI_K + NI_V;
+  static constexpr int KSTEPS = DK / 32;
+  static constexpr int VBLK = DV / 16;
+  static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "tile must be whole DMA blocks");
+};
+
+// DMA one tensor's 32-row tile: 1 KB instruction i covers the tile's 16-byte
+// slots 64i .. 64i+63 in row-major order; lane picks the global chunk that the
+// swizzle stores in its slot.  Rows past the segment are clamped to its last
+// row (finite data, masked out of the softmax).
+template <int L, int CPR, int NI>
+__device__ __forceinline__ void dma_tile(const uint16_t* base, long long row_elems, int tok0,
+                                         int nvalid, ZL_LDS char* dst, int lane) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int lin = 64 * i + lane;
+    const int r = lin / CPR;
+    const int s = lin - r * CPR;
+    const int c = Geo<L>::slot(s, r);  // the slot permutation is an involution
+    const int rr = r < nvalid ? r : nvalid - 1;
+    dma16(base + (long long)(tok0 + rr) * row_elems + c * 8, dst + i * 1024);
+  }
+}
+
+template <int PER_TILE, int STAGES>
+__device__ __forceinline__ void wait_tiles_after(int n_after) {
+  if constexpr (STAGES >= 3) {
+    if (n_after >= 2) {
+      wait_vmcnt<2 * PER_TILE>();
+      return;
+    }
+  }
+  if (n_after >= 1)
+    wait_vmcnt<PER_TILE>();
+  else
+    wait_vmcnt<0>();
+}
+
+template <int L, int DT>
+__global__ __attribute__((amdgpu_flat_work_group_size(64, 64),
+                          amdgpu_waves_per_eu(1, Geo<L>::MAX_WAVES_PER_SIMD))) void
+decode_kernel(DecodeArgs a) {
+  using TL = Tile<L>;
+  using GE = Geo<L>;
+  constexpr int STAGES = GE::STAGES;
+  constexpr int DK = TL::DK, DV = TL::DV;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[STAGES * TL::STAGE_BYTES];
+  ZL_LDS char* smem = (ZL_LDS char*)smem_raw;
+
+  const int lane = __lane_id();
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int w = worker_id(blockIdx.x, a.P);
+  const int B = a.B;
+  const int U = a.Hkv * a.HB;
+  const long long k_row = GE::SHARED_KV ? (long long)DK : (long long)a.Hkv * DK;
+  const long long v_row = GE::SHARED_KV ? (long long)DK : (long long)a.Hkv * DV;
+
+  // Empty sequences: out = 0, lse = -inf (no worker run covers them).
+  for (int idx = w; idx < B * U; idx += a.P) {
+    const int b = idx / U, u = idx - (idx / U) * U;
+    if (a.cu[b + 1] - a.cu[b] != 0) continue;
+    const int kvh = u / a.HB, hb = u - (u / a.HB) * a.HB;
+    const int h0 = kvh * a.G + hb * kHeadsPerUnit;
+    const int nh = min(kHeadsPerUnit, a.G - hb * kHeadsPerUnit);
+    for (int e = lane; e < nh * DV; e += 64) a.out[((long long)b * a.Hq + h0) * DV + e] = 0;
+    if (a.lse && lane < nh) a.lse[(long long)b * a.Hq + h0 + lane] = -INFINITY;
+  }
+
+  const int T = a.cu[B];
+  const long long N = (long long)U * T;
+  long long per = (N + a.P - 1) / a.P;
+  if (per < kMinPerWorker) per = kMinPerWorker;
+  long long p = (long long)w * per;
+  const long long p_end = N < p + per ? N : p + per;
+
+  while (p < p_end) {
+    // ---- segment: tokens [t0, t1) of sequence b, work unit u
+    const int u = (int)(p / T);
+    const int t0 = (int)(p - (long long)u * T);
+    const int b = seq_of_token(a.cu, B, t0);
+    const int cs = a.cu[b], ce = a.cu[b + 1];
+    const long long rem = p_end - p;
+    const int t1 = (long long)(ce - t0) < rem ? ce : (int)(t0 + rem);
+    const int len = t1 - t0;
+    const long long seq_p0 = (long long)u * T + cs;
+    const long long seq_p1 = (long long)u * T + ce;
+    const int w_first = (int)(seq_p0 / per);
+    const int w_last = (int)((seq_p1 - 1) / per);
+    const int kvh = u / a.HB, hb = u - (u / a.HB) * a.HB;
+    const int h0 = kvh * a.G + hb * kHeadsPerUnit;
+    const int nh = min(kHeadsPerUnit, a.G - hb * kHeadsPerUnit);
+    const uint16_t* kbase = a.k + (long long)kvh * DK;
+    const uint16_t* vbase = a.v + (long long)kvh * DV;
+
+    wait_vmcnt<0>();  // stores/atomics of the previous segment out of the DMA count
+
+    // Query heads h0 .. h0+nh-1 as the B operand: lane (g, n) = head n,
+    // dims 32kb + 8g .. +7 (zero for padding heads).
+    i16x8 qop[TL::KSTEPS];
+    {
+      const uint16_t* qrow = a.q + ((long long)b * a.Hq + h0 + n) * DK + 8 * g;
+#pragma unroll
+      for (int kb = 0; kb < TL::KSTEPS; ++kb) {
+        u32x4 v4 = {0u, 0u, 0u, 0u};
+        if (n < nh) v4 = *(const u32x4*)(qrow + 32 * kb);
+        qop[kb] = __builtin_bit_cast(i16x8, v4);
+      }
+    }
+
+    const int ntiles = (len + 31) >> 5;
+    // Prologue: always STAGES-1 tiles, so the number of loads in flight does
+    // not depend on the segment length (a segment shorter than the prologue
+    // re-reads its first tile into the unused stage).
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) {
+      ZL_LDS char* st = smem + s * TL::STAGE_BYTES;
+      const bool real = s < ntiles;
+      const int tok = real ? t0 + 32 * s : t0;
+      const int nv = real ? min(32, len - 32 * s) : min(32, len);
+      dma_tile<L, TL::KCPR, TL::NI_K>(kbase, k_row, tok, nv, st, lane);
+      if constexpr (!GE::SHARED_KV)
+        dma_tile<L, TL::VCPR, TL::NI_V>(vbase, v_row, tok, nv, st + TL::KBYTES, lane);
+    }
+    // The query loads were issued before the prologue DMA: waiting for them
+    // here leaves the prologue tiles in flight.
+#pragma unroll
+    for (int kb = 0; kb < TL::KSTEPS; ++kb) touch(qop[kb]);
+
+    f32x4 o[TL::VBLK];
+#pragma unroll
+    for (int i = 0; i < TL::VBLK; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    SoftmaxState sm{-INFINITY, 0.f};
+    const auto slot = [](int c, int r) { return GE::slot(c, r); };
+
+    for (int j = 0; j < ntiles; ++j) {
+      const int ahead = j + STAGES - 1;
+      if (ahead < ntiles) {
+        ZL_LDS char* st = smem + (ahead % STAGES) * TL::STAGE_BYTES;
+        const int nv = min(32, len - 32 * ahead);
+        dma_tile<L, TL::KCPR, TL::NI_K>(kbase, k_row, t0 + 32 * ahead, nv, st, lane);
+        if constexpr (!GE::SHARED_KV)
+          dma_tile<L, TL::VCPR, TL::NI_V>(vbase, v_row, t0 + 32 * ahead, nv, st + TL::KBYTES, lane);
+      }
+      wait_tiles_after<TL::PER_TILE, STAGES>(min(STAGES - 1, ntiles - 1 - j));
+
+      const ZL_LDS char* kt = smem + (j % STAGES) * TL::STAGE_BYTES;
+      const ZL_LDS char* vt = GE::SHARED_KV ? kt : kt + TL::KBYTES;
+
+      f32x4 s[2];
+      scores<DT, TL::KSTEPS, TL::KROWB>(kt, qop, n, g, slot, s);
+      float alpha;
+      const i16x8 pop = softmax_update<DT>(s, g, min(32, len - 32 * j), a.scale_log2, sm, alpha);
+#pragma unroll
+      for (int i = 0; i < TL::VBLK; ++i) o[i] *= alpha;
+      pv_blocks<DT, TL::VBLK, TL::VROWB>(vt, pop, n, g, 0, slot, o);
+    }
+
+    // ---- segment epilogue: lane (g, n) holds head n, dims 16blk + 4g .. +3
+    const float l_tot = sum_over_groups(sm.l);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse_v = l_tot > 0.f ? sm.m * kLn2 + __logf(l_tot) : -INFINITY;
+    if (w_first == w_last) {
+      if (n < nh) {
+        uint16_t* orow = a.out + ((long long)b * a.Hq + h0 + n) * DV + 4 * g;
+#pragma unroll
+        for (int blk = 0; blk < TL::VBLK; ++blk) store_out4<DT>(orow + 16 * blk, o[blk], inv);
+        if (a.lse && g == 0) a.lse[(long long)b * a.Hq + h0 + n] = lse_v;
+      }
+    } else {
+      const int slot = partial_slot(w, per, seq_p0);
+      float* po = a.part_o + ((long long)slot * kHeadsPerUnit + n) * DV + 4 * g;
+#pragma unroll
+      for (int blk = 0; blk < TL::VBLK; ++blk) *(f32x4*)(po + 16 * blk) = o[blk] * inv;
+      if (g == 0) a.part_lse[slot * kHeadsPerUnit + n] = lse_v;
+      __threadfence();  // release this partial before counting it
+      uint32_t* ctr = a.counters + (long long)u * B + b;
+      uint32_t old = 0;
+      if (lane == 0) old = atomicAdd(ctr, 1u);
+      old = (uint32_t)readfirstlane((int)old);
+      const uint32_t nparts = (uint32_t)(w_last - w_first + 1);
+      if (old == nparts - 1) {
+        __threadfence();  // acquire the other workers' partials
+        float M = -INFINITY;
+        for (int wi = w_first; wi <= w_last; ++wi)
+          M = fmaxf(M, a.part_lse[partial_slot(wi, per, seq_p0) * kHeadsPerUnit + n]);
+        f32x4 acc[TL::VBLK];
+#pragma unroll
+        for (int i = 0; i < TL::VBLK; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float wsum = 0.f;
+        for (int wi = w_first; wi <= w_last; ++wi) {
+          const int sl = partial_slot(wi, per, seq_p0);
+          const float ls = a.part_lse[sl * kHeadsPerUnit + n];
+          const float wt = (ls == -INFINITY) ? 0.f : exp2_fast((ls - M) * kLog2e);
+          wsum += wt;
+          const float* pi = a.part_o + ((long long)sl * kHeadsPerUnit + n) * DV + 4 * g;
+#pragma unroll
+          for (int blk = 0; blk < TL::VBLK; ++blk) acc[blk] += wt * *(const f32x4*)(pi + 16 * blk);
+        }
+        if (n < nh) {
+          const float winv = wsum > 0.f ? 1.f / wsum : 0.f;
+          uint16_t* orow = a.out + ((long long)b * a.Hq + h0 + n) * DV + 4 * g;
+#pragma unroll
+          for (int blk = 0; blk < TL::VBLK; ++blk) store_out4<DT>(orow + 16 * blk, acc[blk], winv);
+          if (a.lse && g == 0)
+            a.lse[(long long)b * a.Hq + h0 + n] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
+        }
+        if (lane == 0) *ctr = 0u;  // leave the counter at zero for the next call
+      }
+    }
+    p += len;
+  }
+}
+
+int default_workers(Layout layout) {
+  switch (layout) {
+    case kGqaD64: return 256 * Geo<kGqaD64>::WAVES_PER_CU;
+    case kGqaD128: return 256 * Geo<kGqaD128>::WAVES_PER_CU;
+    default: return mla_default_workers();
+  }
+}
+
+template <int L, int DT>
+static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_kernel<L, DT>), dim3(a.P), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, Layout layout, int dtype, hipStream_t stream) {
+  switch (layout) {
+    case kGqaD64:
+      return dtype == kF16 ? launch_t<kGqaD64, kF16>(a, stream) : launch_t<kGqaD64, kBF16>(a, stream);
+    case kGqaD128:
+      return dtype == kF16 ? launch_t<kGqaD128, kF16>(a, stream) : launch_t<kGqaD128, kBF16>(a, stream);
+    default:
+      return launch_mla(a, dtype, stream);
+  }
+}
+
+}  // namespace zl

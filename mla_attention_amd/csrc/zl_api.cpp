@@ -1,0 +1,254 @@
+// zl_api.cpp -- the C ABI of libzl_attn.so: argument validation, workspace
+// layout and kernel dispatch.  Validation runs before any HIP call, so a bad
+// argument never touches the device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "zl_attn.h"
+#include "zl_kernels.h"
+
+namespace {
+
+using zl::Layout;
+
+constexpr int kMaxBatch = 1 << 22;
+constexpr int kMaxHeads = 1 << 12;
+constexpr int kMaxWorkers = 1 << 16;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct WsLayout {
+  size_t counters_off, lse_off, out_off, total;
+};
+
+// Workspace: [counters U*B u32][part_lse 2P*16 f32][part_o 2P*16*Dv f32],
+// each region 256-byte aligned.
+WsLayout ws_layout(long long units_times_batch, int workers, int dv) {
+  WsLayout w;
+  w.counters_off = 0;
+  w.lse_off = round_up((size_t)units_times_batch * 4, 256);
+  w.out_off = w.lse_off + round_up((size_t)2 * workers * zl::kHeadsPerUnit * 4, 256);
+  w.total = w.out_off + (size_t)2 * workers * zl::kHeadsPerUnit * dv * 4;
+  return w;
+}
+
+int head_blocks(int group) { return group <= zl::kHeadsPerUnit ? 1 : group / zl::kHeadsPerUnit; }
+
+bool group_ok(int group) {
+  return group >= 1 && (group <= zl::kHeadsPerUnit || group % zl::kHeadsPerUnit == 0);
+}
+
+int pick_workers(int requested, Layout layout) {
+  return requested > 0 ? requested : zl::default_workers(layout);
+}
+
+bool workers_ok(int w) { return w >= 8 && w <= kMaxWorkers && w % 8 == 0; }
+
+// Shared shape checks; returns ZL_OK or the status to report.
+zl_status_t check_common(int batch, int num_q_heads, int num_kv_heads, int max_seqlen_k,
+                         zl_dtype_t dtype, int workers) {
+  if (batch < 0 || batch > kMaxBatch) return ZL_ERR_INVALID_ARGUMENT;
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads > kMaxHeads) return ZL_ERR_INVALID_ARGUMENT;
+  if (num_q_heads % num_kv_heads != 0) return ZL_ERR_INVALID_ARGUMENT;
+  if (max_seqlen_k < 0) return ZL_ERR_INVALID_ARGUMENT;
+  if (dtype != ZL_DTYPE_F16 && dtype != ZL_DTYPE_BF16) return ZL_ERR_INVALID_ARGUMENT;
+  if (!workers_ok(workers)) return ZL_ERR_INVALID_ARGUMENT;
+  if (!group_ok(num_q_heads / num_kv_heads)) return ZL_ERR_UNSUPPORTED;
+  return ZL_OK;
+}
+
+size_t gqa_ws_size(int batch, int num_q_heads, int num_kv_heads, int head_dim, int max_seqlen_k,
+                   zl_dtype_t dtype, int num_workers) {
+  if (head_dim != 64 && head_dim != 128) return 0;
+  const Layout layout = head_dim == 128 ? zl::kGqaD128 : zl::kGqaD64;
+  const int P = pick_workers(num_workers, layout);
+  if (check_common(batch, num_q_heads, num_kv_heads, max_seqlen_k, dtype, P) != ZL_OK) return 0;
+  const long long units = (long long)num_kv_heads * head_blocks(num_q_heads / num_kv_heads);
+  return ws_layout(units * batch, P, head_dim).total;
+}
+
+size_t mla_ws_size(int batch, int num_q_heads, int kv_lora_rank, int rope_dim, int max_seqlen_k,
+                   zl_dtype_t dtype, int num_workers) {
+  if (kv_lora_rank != 512 || rope_dim != 64) return 0;
+  const int P = pick_workers(num_workers, zl::kMla576);
+  if (check_common(batch, num_q_heads, 1, max_seqlen_k, dtype, P) != ZL_OK) return 0;
+  return ws_layout((long long)head_blocks(num_q_heads) * batch, P, kv_lora_rank).total;
+}
+
+zl_status_t run_decode(zl::DecodeArgs a, Layout layout, int dv, zl_dtype_t dtype, void* workspace,
+                       size_t workspace_bytes, zl_stream_t stream) {
+  const long long units = (long long)a.Hkv * a.HB;
+  const WsLayout wl = ws_layout(units * a.B, a.P, dv);
+  if (workspace == nullptr || !aligned(workspace, 256)) return ZL_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < wl.total) return ZL_ERR_WORKSPACE_TOO_SMALL;
+  char* ws = static_cast<char*>(workspace);
+  a.counters = reinterpret_cast<uint32_t*>(ws + wl.counters_off);
+  a.part_lse = reinterpret_cast<float*>(ws + wl.lse_off);
+  a.part_o = reinterpret_cast<float*>(ws + wl.out_off);
+  const hipError_t e = zl::launch_decode(a, layout, dtype, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ZL_OK : ZL_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t zl_decode_attn_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                     int max_seqlen_k, zl_dtype_t dtype) {
+  return gqa_ws_size(batch, num_q_heads, num_kv_heads, head_dim, max_seqlen_k, dtype, 0);
+}
+
+size_t zl_decode_attn_workspace_size_ex(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                        int max_seqlen_k, zl_dtype_t dtype, int num_workers) {
+  if (num_workers < 0) return 0;
+  return gqa_ws_size(batch, num_q_heads, num_kv_heads, head_dim, max_seqlen_k, dtype, num_workers);
+}
+
+zl_status_t zl_decode_attn_gqa_ex(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* cu_seqlens, int batch, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int max_seqlen_k,
+                                  float softmax_scale, zl_dtype_t dtype, void* out, float* lse,
+                                  int num_workers, void* workspace, size_t workspace_bytes,
+                                  zl_stream_t stream) {
+  if (num_workers < 0) return ZL_ERR_INVALID_ARGUMENT;
+  if (head_dim != 64 && head_dim != 128) {
+    if (head_dim <= 0) return ZL_ERR_INVALID_ARGUMENT;
+    return ZL_ERR_UNSUPPORTED;
+  }
+  const Layout layout = head_dim == 128 ? zl::kGqaD128 : zl::kGqaD64;
+  const int P = pick_workers(num_workers, layout);
+  const zl_status_t st = check_common(batch, num_q_heads, num_kv_heads, max_seqlen_k, dtype, P);
+  if (st != ZL_OK) return st;
+  if (!std::isfinite(softmax_scale)) return ZL_ERR_INVALID_ARGUMENT;
+  if (batch == 0) return ZL_OK;
+  // k_cache / v_cache may be NULL only when every sequence is empty (the
+  // kernel never reads a cache row then); the host cannot see the lengths.
+  if (!q || !cu_seqlens || !out) return ZL_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(cu_seqlens, 4) || !aligned(lse, 4))
+    return ZL_ERR_INVALID_ARGUMENT;
+  zl::DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_cache);
+  a.v = static_cast<const uint16_t*>(v_cache);
+  a.cu = cu_seqlens;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.B = batch;
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.G = num_q_heads / num_kv_heads;
+  a.HB = head_blocks(a.G);
+  a.P = P;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  return run_decode(a, layout, head_dim, dtype, workspace, workspace_bytes, stream);
+}
+
+zl_status_t zl_decode_attn_gqa(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* cu_seqlens, int batch, int num_q_heads,
+                               int num_kv_heads, int head_dim, int max_seqlen_k,
+                               float softmax_scale, zl_dtype_t dtype, void* out, float* lse,
+                               void* workspace, size_t workspace_bytes, zl_stream_t stream) {
+  return zl_decode_attn_gqa_ex(q, k_cache, v_cache, cu_seqlens, batch, num_q_heads, num_kv_heads,
+                               head_dim, max_seqlen_k, softmax_scale, dtype, out, lse, 0, workspace,
+                               workspace_bytes, stream);
+}
+
+size_t zl_decode_attn_mla_workspace_size(int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
+                                         int max_seqlen_k, zl_dtype_t dtype) {
+  return mla_ws_size(batch, num_q_heads, kv_lora_rank, rope_dim, max_seqlen_k, dtype, 0);
+}
+
+size_t zl_decode_attn_mla_workspace_size_ex(int batch, int num_q_heads, int kv_lora_rank,
+                                            int rope_dim, int max_seqlen_k, zl_dtype_t dtype,
+                                            int num_workers) {
+  if (num_workers < 0) return 0;
+  return mla_ws_size(batch, num_q_heads, kv_lora_rank, rope_dim, max_seqlen_k, dtype, num_workers);
+}
+
+zl_status_t zl_decode_attn_mla_ex(const void* q, const void* kv_cache, const int32_t* cu_seqlens,
+                                  int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
+                                  int max_seqlen_k, float softmax_scale, zl_dtype_t dtype,
+                                  void* out, float* lse, int num_workers, void* workspace,
+                                  size_t workspace_bytes, zl_stream_t stream) {
+  if (num_workers < 0) return ZL_ERR_INVALID_ARGUMENT;
+  if (kv_lora_rank <= 0 || rope_dim < 0) return ZL_ERR_INVALID_ARGUMENT;
+  if (kv_lora_rank != 512 || rope_dim != 64) return ZL_ERR_UNSUPPORTED;
+  const int P = pick_workers(num_workers, zl::kMla576);
+  const zl_status_t st = check_common(batch, num_q_heads, 1, max_seqlen_k, dtype, P);
+  if (st != ZL_OK) return st;
+  if (!std::isfinite(softmax_scale)) return ZL_ERR_INVALID_ARGUMENT;
+  if (batch == 0) return ZL_OK;
+  if (!q || !cu_seqlens || !out) return ZL_ERR_INVALID_ARGUMENT;  // kv_cache: see above
+  if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(cu_seqlens, 4) ||
+      !aligned(lse, 4))
+    return ZL_ERR_INVALID_ARGUMENT;
+  zl::DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(kv_cache);
+  a.v = static_cast<const uint16_t*>(kv_cache);
+  a.cu = cu_seqlens;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.B = batch;
+  a.Hq = num_q_heads;
+  a.Hkv = 1;
+  a.G = num_q_heads;
+  a.HB = head_blocks(num_q_heads);
+  a.P = P;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  return run_decode(a, zl::kMla576, kv_lora_rank, dtype, workspace, workspace_bytes, stream);
+}
+
+zl_status_t zl_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* cu_seqlens,
+                               int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
+                               int max_seqlen_k, float softmax_scale, zl_dtype_t dtype, void* out,
+                               float* lse, void* workspace, size_t workspace_bytes,
+                               zl_stream_t stream) {
+  return zl_decode_attn_mla_ex(q, kv_cache, cu_seqlens, batch, num_q_heads, kv_lora_rank, rope_dim,
+                               max_seqlen_k, softmax_scale, dtype, out, lse, 0, workspace,
+                               workspace_bytes, stream);
+}
+
+zl_status_t zl_attn_combine(const float* partial_out, const float* partial_lse, int num_splits,
+                            int batch, int num_heads, int head_dim_v, zl_dtype_t out_dtype,
+                            void* out, float* lse, zl_stream_t stream) {
+  if (num_splits < 1 || num_splits > 1024) return ZL_ERR_INVALID_ARGUMENT;
+  if (batch < 0 || batch > kMaxBatch || num_heads <= 0 || num_heads > kMaxHeads)
+    return ZL_ERR_INVALID_ARGUMENT;
+  if (head_dim_v < 4 || head_dim_v > 4096 || head_dim_v % 4 != 0) return ZL_ERR_INVALID_ARGUMENT;
+  if (out_dtype != ZL_DTYPE_F16 && out_dtype != ZL_DTYPE_BF16) return ZL_ERR_INVALID_ARGUMENT;
+  if (batch == 0) return ZL_OK;
+  if (!partial_out || !partial_lse || !out) return ZL_ERR_INVALID_ARGUMENT;
+  if (!aligned(partial_out, 16) || !aligned(partial_lse, 4) || !aligned(out, 8) || !aligned(lse, 4))
+    return ZL_ERR_INVALID_ARGUMENT;
+  const long long rows = (long long)batch * num_heads;
+  if (rows > (1LL << 30)) return ZL_ERR_INVALID_ARGUMENT;
+  zl::CombineArgs a{};
+  a.part_o = partial_out;
+  a.part_lse = partial_lse;
+  a.out = out;
+  a.lse = lse;
+  a.S = num_splits;
+  a.rows = (int)rows;
+  a.Dv = head_dim_v;
+  const hipError_t e = zl::launch_combine(a, out_dtype, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ZL_OK : ZL_ERR_HIP;
+}
+
+const char* zl_status_string(zl_status_t status) {
+  switch (status) {
+    case ZL_OK: return "ZL_OK";
+    case ZL_ERR_INVALID_ARGUMENT: return "ZL_ERR_INVALID_ARGUMENT";
+    case ZL_ERR_UNSUPPORTED: return "ZL_ERR_UNSUPPORTED";
+    case ZL_ERR_WORKSPACE_TOO_SMALL: return "ZL_ERR_WORKSPACE_TOO_SMALL";
+    case ZL_ERR_HIP: return "ZL_ERR_HIP";
+  }
+  return "unknown zl_status_t";
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// zl_kernels.h -- argument blocks and launchers of the decode kernels
+// (internal to libzl_attn.so; the public ABI is include/zl_attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace zl {
+
+// Sizes shared by host planning and the kernels.
+constexpr int kHeadsPerUnit = 16;  // query heads packed into one MFMA N dimension
+constexpr int kMinPerWorker = 64;  // fewest (unit, token) positions a worker is given
+
+enum Layout {
+  kGqaD64 = 0,   // K, V [T, Hkv, 64]
+  kGqaD128 = 1,  // K, V [T, Hkv, 128]
+  kMla576 = 2,   // latent [T, 576]; K = row[0:576], V = row[0:512]
+};
+
+// One decode call.  For MLA: Hkv = 1, G = Hq, v == k == latent.
+struct DecodeArgs {
+  const uint16_t* q;    // [B, Hq, Dk]
+  const uint16_t* k;    // K rows
+  const uint16_t* v;    // V rows
+  const int32_t* cu;    // [B + 1]
+  uint16_t* out;        // [B, Hq, Dv]
+  float* lse;           // [B, Hq] or nullptr
+  float* part_o;        // [2P, 16, Dv]
+  float* part_lse;      // [2P, 16]
+  uint32_t* counters;   // [U * B], zero between calls (U = Hkv * HB)
+  int B, Hq, Hkv, G, HB, P;
+  float scale_log2;     // softmax_scale * log2(e)
+};
+
+struct CombineArgs {
+  const float* part_o;   // [S, rows, Dv]
+  const float* part_lse; // [S, rows]
+  void* out;             // [rows, Dv] 16-bit
+  float* lse;            // [rows] or nullptr
+  int S, rows, Dv;
+};
+
+// Workers (one wavefront each, a multiple of 8) a decode call launches.
+int default_workers(Layout layout);
+int mla_default_workers();
+hipError_t launch_mla(const DecodeArgs& a, int dtype, hipStream_t stream);
+
+hipError_t launch_decode(const DecodeArgs& a, Layout layout, int dtype, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t stream);
+
+}  // namespace zl

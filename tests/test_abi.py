@@ -1,0 +1,119 @@
+"""The C ABI on the CPU: the library loads without a GPU, exports exactly what
+include/zl_attn.h declares, sizes workspaces, and rejects every bad argument
+with the documented status before making any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zl_attn.h")
+
+
+@pytest.fixture(scope="module")
+def zl():
+    import mla_attention_amd
+    if not os.path.exists(mla_attention_amd.LIB_PATH):
+        from mla_attention_amd import build
+        build.build()
+    mla_attention_amd.library()
+    return mla_attention_amd
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return set(re.findall(r"^ZL_API [^;(]*?\b(zl_\w+)\s*\(", text, flags=re.M))
+
+
+def test_header_declares_the_boundary():
+    names = declared_symbols()
+    for required in ("zl_decode_attn_gqa", "zl_decode_attn_mla", "zl_attn_combine",
+                     "zl_decode_attn_workspace_size", "zl_status_string"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(zl):
+    lib = zl.library()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert declared_symbols() == set(zl.SIGNATURES), "binding signatures out of step with the header"
+    nm = os.popen(f"nm -D --defined-only {zl.LIB_PATH}").read()
+    exported = set(re.findall(r" T (zl_\w+)", nm))
+    assert exported == declared_symbols()
+
+
+def test_status_strings(zl):
+    for code, name in [(0, "ZL_OK"), (1, "ZL_ERR_INVALID_ARGUMENT"), (2, "ZL_ERR_UNSUPPORTED"),
+                       (3, "ZL_ERR_WORKSPACE_TOO_SMALL"), (4, "ZL_ERR_HIP")]:
+        assert zl.zl_status_string(code) == name
+    assert "unknown" in zl.zl_status_string(99)
+
+
+def test_workspace_sizes(zl):
+    lib = zl.library()
+    s = lib.zl_decode_attn_workspace_size(32, 32, 8, 128, 4096, 0)
+    assert s > 0 and s % 4 == 0
+    # larger batch -> more counters; more workers -> more partial slots
+    assert lib.zl_decode_attn_workspace_size(64, 32, 8, 128, 4096, 0) > s
+    assert lib.zl_decode_attn_workspace_size_ex(32, 32, 8, 128, 4096, 0, 4096) > s
+    assert lib.zl_decode_attn_mla_workspace_size(32, 16, 512, 64, 8192, 1) > 0
+    # invalid shapes -> 0
+    for args in [(32, 32, 8, 96, 4096, 0), (32, 30, 8, 128, 4096, 0), (-1, 32, 8, 128, 4096, 0),
+                 (32, 32, 8, 128, -5, 0), (32, 32, 8, 128, 4096, 7), (32, 40, 2, 128, 64, 0)]:
+        assert lib.zl_decode_attn_workspace_size(*args) == 0, args
+    assert lib.zl_decode_attn_workspace_size_ex(32, 32, 8, 128, 4096, 0, 12) == 0   # not a multiple of 8
+    assert lib.zl_decode_attn_mla_workspace_size(32, 16, 256, 64, 8192, 1) == 0
+
+
+BIG = 1 << 20
+A = 0x100000  # a 256-byte aligned fake address: never dereferenced (validation fails first)
+
+
+def gqa(lib, **kw):
+    args = dict(q=A, k=A, v=A, cu=A, B=4, Hq=8, Hkv=2, D=128, maxL=128, scale=0.125, dt=0, out=A,
+                lse=None, workers=0, ws=A, wsb=BIG, stream=None)
+    args.update(kw)
+    return lib.zl_decode_attn_gqa_ex(args["q"], args["k"], args["v"], args["cu"], args["B"], args["Hq"],
+                                     args["Hkv"], args["D"], args["maxL"], args["scale"], args["dt"],
+                                     args["out"], args["lse"], args["workers"], args["ws"], args["wsb"],
+                                     args["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), 1), (dict(cu=None), 1), (dict(out=None), 1), (dict(ws=None), 1),
+    (dict(q=A + 2), 1), (dict(out=A + 8), 1), (dict(k=A + 4), 1), (dict(lse=A + 2), 1),
+    (dict(ws=A + 16), 1), (dict(cu=A + 2), 1),
+    (dict(B=-1), 1), (dict(Hq=0), 1), (dict(Hkv=0), 1), (dict(Hq=6, Hkv=4), 1),
+    (dict(maxL=-1), 1), (dict(scale=float("inf")), 1), (dict(scale=float("nan")), 1),
+    (dict(dt=2), 1), (dict(workers=12), 1), (dict(workers=-8), 1),
+    (dict(D=96), 2), (dict(D=256), 2), (dict(D=0), 1), (dict(Hq=40, Hkv=2), 2),
+    (dict(wsb=16), 3),
+    (dict(B=0, q=None, k=None, v=None, cu=None, out=None, ws=None), 0),   # empty batch: no-op
+])
+def test_gqa_rejects_bad_arguments_before_any_hip_call(zl, kw, expect):
+    assert gqa(zl.library(), **kw) == expect
+
+
+def test_mla_and_combine_reject_bad_arguments(zl):
+    lib = zl.library()
+
+    def mla(**kw):
+        a = dict(q=A, c=A, cu=A, B=2, H=16, r=512, rope=64, maxL=10, scale=0.07, dt=1, out=A, lse=None,
+                 workers=0, ws=A, wsb=BIG, stream=None)
+        a.update(kw)
+        return lib.zl_decode_attn_mla_ex(a["q"], a["c"], a["cu"], a["B"], a["H"], a["r"], a["rope"],
+                                         a["maxL"], a["scale"], a["dt"], a["out"], a["lse"], a["workers"],
+                                         a["ws"], a["wsb"], a["stream"])
+    assert mla(r=256) == 2 and mla(rope=32) == 2 and mla(r=0) == 1
+    assert mla(H=0) == 1 and mla(H=24) == 2 and mla(q=None) == 1 and mla(wsb=8) == 3
+    assert mla(B=0, q=None, c=None, cu=None, out=None, ws=None) == 0
+
+    def comb(**kw):
+        a = dict(po=A, pl=A, S=4, B=2, H=8, Dv=128, dt=0, out=A, lse=None, stream=None)
+        a.update(kw)
+        return lib.zl_attn_combine(a["po"], a["pl"], a["S"], a["B"], a["H"], a["Dv"], a["dt"], a["out"],
+                                   a["lse"], a["stream"])
+    assert comb(S=0) == 1 and comb(S=1025) == 1 and comb(Dv=6) == 1 and comb(H=0) == 1
+    assert comb(po=None) == 1 and comb(po=A + 4) == 1 and comb(dt=5) == 1
+    assert comb(B=0, po=None, pl=None, out=None) == 0

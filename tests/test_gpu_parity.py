@@ -1,0 +1,226 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle on
+identical seeded inputs.
+
+Small cases compare every output; the full-size workloads compare sampled
+(sequence, head) rows that the oracle computes one by one (every sequence,
+heads covering every key/value head), plus whole-output checks.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.parity import gate
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_attention_amd as zl
+    zl.library()
+    yield
+
+
+def zl():
+    import mla_attention_amd
+    return mla_attention_amd
+
+
+def odt(spec_or_dtype):
+    dt = spec_or_dtype.torch_dtype if hasattr(spec_or_dtype, "torch_dtype") else spec_or_dtype
+    return oracle.F16 if dt == torch.float16 else oracle.BF16
+
+
+def run_gpu(x: workloads.Inputs, num_workers=0, workspace=None):
+    s = x.spec
+    cu = x.cu_seqlens.to(DEV)
+    q = x.q.to(DEV)
+    if s.kind == "mla":
+        out, lse = zl().zl_decode_attn_mla(q, x.latent.to(DEV), cu, x.max_seqlen, s.scale,
+                                           num_workers=num_workers, workspace=workspace,
+                                           return_lse=True)
+    else:
+        out, lse = zl().zl_decode_attn_gqa(q, x.k.to(DEV), x.v.to(DEV), cu, x.max_seqlen, s.scale,
+                                           num_workers=num_workers, workspace=workspace,
+                                           return_lse=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def run_oracle(x: workloads.Inputs, pairs=None):
+    s = x.spec
+    cu = x.cu_seqlens.numpy()
+    if s.kind == "mla":
+        return oracle.mla_decode(x.bits("q"), x.bits("latent"), cu, s.scale, odt(s), pairs=pairs)
+    return oracle.gqa_decode(x.bits("q"), x.bits("k"), x.bits("v"), cu, s.num_kv_heads, s.scale,
+                             odt(s), pairs=pairs)
+
+
+def check_full(x, where, **kw):
+    out, lse = run_gpu(x, **kw)
+    ro, rl = run_oracle(x)
+    return gate(out, ro, x.spec.torch_dtype, lse, rl, where=where)
+
+
+def sample_pairs(spec):
+    heads = sorted({0, spec.num_q_heads - 1} |
+                   {kv * spec.group + (kv % spec.group) for kv in range(spec.num_kv_heads)} |
+                   {kv * spec.group + spec.group - 1 for kv in range(spec.num_kv_heads)})
+    return [(b, h) for b in range(spec.batch) for h in heads]
+
+
+# ------------------------------------------------------------ the five configs
+def test_config1_full():
+    x = workloads.make_inputs(workloads.CONFIGS[1])
+    st = check_full(x, "config 1")
+    print("config 1", st)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_size_config_sampled(cfg):
+    spec = workloads.CONFIGS[cfg]
+    print(f"config {cfg}: {spec.name}", flush=True)
+    x = workloads.make_inputs(spec)
+    out, lse = run_gpu(x)
+    pairs = sample_pairs(spec)
+    ro, rl = run_oracle(x, pairs=pairs)
+    idx_b = np.array([p[0] for p in pairs])
+    idx_h = np.array([p[1] for p in pairs])
+    tb, th = torch.from_numpy(idx_b).to(DEV), torch.from_numpy(idx_h).to(DEV)
+    st = gate(out[tb, th], ro[idx_b, idx_h], spec.torch_dtype, lse[tb, th], rl[idx_b, idx_h],
+              where=f"config {cfg}")
+    # whole output: finite, and every row was written (a row of exact zeros
+    # would mean a missed (sequence, head))
+    o = out.float()
+    assert torch.isfinite(o).all()
+    assert (o.abs().amax(dim=-1) > 0).all()
+    assert torch.isfinite(lse).all()
+    print(f"config {cfg}", st, flush=True)
+
+
+# ------------------------------------------------------------- edge cases
+GQA_EDGE = [
+    # (batch lens, Hq, Hkv, D, dtype)
+    ([1], 1, 1, 128, torch.float16),
+    ([33, 1, 31, 32, 64, 65, 7], 8, 2, 128, torch.float16),
+    ([5, 0, 130, 0, 2], 4, 4, 64, torch.bfloat16),
+    ([0, 0, 0], 8, 1, 128, torch.float16),
+    ([300, 17, 1000], 16, 1, 128, torch.bfloat16),
+    ([129, 2, 70], 32, 1, 64, torch.float16),      # G = 32: two 16-head blocks
+    ([96, 95, 97], 6, 2, 128, torch.bfloat16),     # G = 3 (padding heads)
+    ([2000], 2, 1, 64, torch.float16),
+]
+
+
+@pytest.mark.parametrize("lens,Hq,Hkv,D,dt", GQA_EDGE)
+def test_gqa_edge_shapes(lens, Hq, Hkv, D, dt):
+    spec = workloads.Spec("edge", "gqa", len(lens), Hq, Hkv, D, D, tuple(lens),
+                          "f16" if dt == torch.float16 else "bf16", float(np.float32(1 / math.sqrt(D))), 7)
+    x = workloads.make_inputs(spec)
+    check_full(x, f"edge {lens} {Hq}/{Hkv} D{D} {dt}")
+
+
+MLA_EDGE = [
+    ([1, 33, 64], 16, torch.bfloat16),
+    ([0, 257, 31], 16, torch.float16),
+    ([100, 3], 8, torch.bfloat16),
+    ([70, 0, 150], 32, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("lens,H,dt", MLA_EDGE)
+def test_mla_edge_shapes(lens, H, dt):
+    spec = workloads.Spec("mla-edge", "mla", len(lens), H, 1, 576, 512, tuple(lens),
+                          "f16" if dt == torch.float16 else "bf16", float(np.float32(1 / math.sqrt(192))), 9)
+    x = workloads.make_inputs(spec)
+    check_full(x, f"mla edge {lens} H{H} {dt}")
+
+
+@pytest.mark.parametrize("workers", [8, 16, 64, 256, 2048])
+def test_any_worker_count_gives_the_same_attention(workers):
+    """Invariance to how the batch is cut between workers (split-KV + combine)."""
+    spec = workloads.with_shape(workloads.CONFIGS[2], batch=6, lens=("uniform", 1, 3000))
+    x = workloads.make_inputs(spec, seed=21)
+    check_full(x, f"gqa workers={workers}", num_workers=workers)
+    mspec = workloads.with_shape(workloads.CONFIGS[5], batch=3, lens=("uniform", 1, 1500))
+    xm = workloads.make_inputs(mspec, seed=22)
+    check_full(xm, f"mla workers={workers}", num_workers=workers)
+
+
+def test_peaked_scores():
+    spec = workloads.with_shape(workloads.CONFIGS[1], dtype="bf16")
+    x = workloads.make_inputs(spec, q_mult=8.0)
+    check_full(x, "peaked gqa")
+    mspec = workloads.with_shape(workloads.CONFIGS[5], batch=2, lens=(40, 300))
+    xm = workloads.make_inputs(mspec, q_mult=4.0)
+    check_full(xm, "peaked mla")
+
+
+def test_repeated_calls_reuse_workspace_and_are_bitwise_deterministic():
+    spec = workloads.with_shape(workloads.CONFIGS[3], batch=8, lens=("uniform", 100, 3000))
+    x = workloads.make_inputs(spec, seed=31)
+    B, H, D = x.q.shape
+    ws = zl().new_workspace(zl().zl_decode_attn_workspace_size(B, H, 1, D, x.max_seqlen, x.q.dtype), DEV)
+    outs = [run_gpu(x, workspace=ws)[0].clone() for _ in range(5)]
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    # the counters are back at zero after every call
+    nctr = spec.batch * 1
+    assert int(ws[: 4 * nctr].view(torch.int32).abs().sum()) == 0
+    ro, rl = run_oracle(x)
+    gate(outs[0], ro, spec.torch_dtype, where="repeat")
+    # a different batch through the same workspace
+    x2 = workloads.make_inputs(workloads.with_shape(spec, batch=3, lens=(5, 4000, 77)), seed=32)
+    out2, lse2 = run_gpu(x2, workspace=ws)
+    ro2, rl2 = run_oracle(x2)
+    gate(out2, ro2, spec.torch_dtype, lse2, rl2, where="second batch")
+
+
+# ---------------------------------------------------------------- combine
+@pytest.mark.parametrize("S,Dv,dt", [(1, 128, torch.float16), (5, 128, torch.bfloat16), (13, 512, torch.bfloat16),
+                                     (64, 64, torch.float16)])
+def test_combine_entry_point(S, Dv, dt):
+    rng = np.random.default_rng(S + Dv)
+    B, H = 3, 4
+    part_o = rng.standard_normal((S, B, H, Dv)).astype(np.float32)
+    part_l = (rng.standard_normal((S, B, H)) * 3).astype(np.float32)
+    part_l[rng.random((S, B, H)) < 0.2] = -np.inf     # some empty splits
+    part_l[:, 0, 0] = -np.inf                          # one row with every split empty
+    ro, rl = oracle.combine(part_o.astype(np.float64), part_l.astype(np.float64))
+    out, lse = zl().zl_attn_combine(torch.from_numpy(part_o).to(DEV), torch.from_numpy(part_l).to(DEV),
+                                    out_dtype=dt, return_lse=True)
+    torch.cuda.synchronize()
+    gate(out, ro, dt, lse, rl, where=f"combine S={S}")
+    assert torch.all(out[0, 0] == 0)
+
+
+def test_combine_of_oracle_partials_equals_unsplit_attention():
+    spec = workloads.with_shape(workloads.CONFIGS[2], batch=4, lens=(100, 257, 64, 1))
+    x = workloads.make_inputs(spec, seed=41)
+    S = 3
+    B, Hq, D = x.q.shape
+    po = np.zeros((S, B, Hq, D))
+    pl = np.full((S, B, Hq), -np.inf)
+    cu = x.cu_seqlens.numpy()
+    for b in range(B):
+        edges = np.linspace(0, cu[b + 1] - cu[b], S + 1).astype(int)
+        for s in range(S):
+            a, e = cu[b] + edges[s], cu[b] + edges[s + 1]
+            sub = workloads.cu_from_lens([e - a]).numpy()
+            o, l = oracle.gqa_decode(x.bits("q")[b:b + 1], x.bits("k")[a:e], x.bits("v")[a:e], sub,
+                                     spec.num_kv_heads, spec.scale, oracle.F16)
+            po[s, b], pl[s, b] = o[0], l[0]
+    po32, pl32 = po.astype(np.float32), pl.astype(np.float32)
+    out, lse = zl().zl_attn_combine(torch.from_numpy(po32).to(DEV), torch.from_numpy(pl32).to(DEV),
+                                    out_dtype=torch.float16, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = run_oracle(x)
+    gate(out, ro, torch.float16, lse, rl, where="combine of partials")
