@@ -112,7 +112,7 @@ __device__ __forceinline__ void wait_tiles_after(int n_after) {
 template <int L, int DT>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, 64),
                           amdgpu_waves_per_eu(1, Geo<L>::MAX_WAVES_PER_SIMD))) void
-decode_kernel(DecodeArgs a) {
+decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
   using TL = Tile<L>;
   using GE = Geo<L>;
   constexpr int STAGES = GE::STAGES;
@@ -132,7 +132,7 @@ decode_kernel(DecodeArgs a) {
   // Empty sequences: out = 0, lse = -inf (no worker run covers them).
   for (int idx = w; idx < B * U; idx += a.P) {
     const int b = idx / U, u = idx - (idx / U) * U;
-    if (a.cu[b + 1] - a.cu[b] != 0) continue;
+    if (cu[b + 1] - cu[b] != 0) continue;
     const int kvh = u / a.HB, hb = u - (u / a.HB) * a.HB;
     const int h0 = kvh * a.G + hb * kHeadsPerUnit;
     const int nh = min(kHeadsPerUnit, a.G - hb * kHeadsPerUnit);
@@ -140,7 +140,7 @@ decode_kernel(DecodeArgs a) {
     if (a.lse && lane < nh) a.lse[(long long)b * a.Hq + h0 + lane] = -INFINITY;
   }
 
-  const int T = a.cu[B];
+  const int T = cu[B];
   const long long N = (long long)U * T;
   long long per = (N + a.P - 1) / a.P;
   if (per < kMinPerWorker) per = kMinPerWorker;
@@ -151,8 +151,8 @@ decode_kernel(DecodeArgs a) {
     // ---- segment: tokens [t0, t1) of sequence b, work unit u
     const int u = (int)(p / T);
     const int t0 = (int)(p - (long long)u * T);
-    const int b = seq_of_token(a.cu, B, t0);
-    const int cs = a.cu[b], ce = a.cu[b + 1];
+    const int b = seq_of_token(cu, B, t0);
+    const int cs = cu[b], ce = cu[b + 1];
     const long long rem = p_end - p;
     const int t1 = (long long)(ce - t0) < rem ? ce : (int)(t0 + rem);
     const int len = t1 - t0;
@@ -223,7 +223,7 @@ decode_kernel(DecodeArgs a) {
       f32x4 s[2];
       scores<DT, TL::KSTEPS, TL::KROWB>(kt, qop, n, g, slot, s);
       float alpha;
-      const i16x8 pop = softmax_update<DT>(s, g, min(32, len - 32 * j), a.scale_log2, sm, alpha);
+      const POperand pop = softmax_update<DT>(s, g, min(32, len - 32 * j), a.scale_log2, sm, alpha);
 #pragma unroll
       for (int i = 0; i < TL::VBLK; ++i) o[i] *= alpha;
       pv_blocks<DT, TL::VBLK, TL::VROWB>(vt, pop, n, g, 0, slot, o);
@@ -244,31 +244,30 @@ decode_kernel(DecodeArgs a) {
       const int slot = partial_slot(w, per, seq_p0);
       float* po = a.part_o + ((long long)slot * kHeadsPerUnit + n) * DV + 4 * g;
 #pragma unroll
-      for (int blk = 0; blk < TL::VBLK; ++blk) *(f32x4*)(po + 16 * blk) = o[blk] * inv;
-      if (g == 0) a.part_lse[slot * kHeadsPerUnit + n] = lse_v;
-      __threadfence();  // release this partial before counting it
+      for (int blk = 0; blk < TL::VBLK; ++blk) store_coherent(po + 16 * blk, o[blk] * inv);
+      if (g == 0) store_coherent(a.part_lse + slot * kHeadsPerUnit + n, lse_v);
+      stores_done();  // the partial is in memory before it is counted
       uint32_t* ctr = a.counters + (long long)u * B + b;
       uint32_t old = 0;
-      if (lane == 0) old = atomicAdd(ctr, 1u);
+      if (lane == 0) old = counter_add(ctr);
       old = (uint32_t)readfirstlane((int)old);
       const uint32_t nparts = (uint32_t)(w_last - w_first + 1);
       if (old == nparts - 1) {
-        __threadfence();  // acquire the other workers' partials
         float M = -INFINITY;
         for (int wi = w_first; wi <= w_last; ++wi)
-          M = fmaxf(M, a.part_lse[partial_slot(wi, per, seq_p0) * kHeadsPerUnit + n]);
+          M = fmaxf(M, load_coherent(a.part_lse + partial_slot(wi, per, seq_p0) * kHeadsPerUnit + n));
         f32x4 acc[TL::VBLK];
 #pragma unroll
         for (int i = 0; i < TL::VBLK; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         float wsum = 0.f;
         for (int wi = w_first; wi <= w_last; ++wi) {
           const int sl = partial_slot(wi, per, seq_p0);
-          const float ls = a.part_lse[sl * kHeadsPerUnit + n];
+          const float ls = load_coherent(a.part_lse + sl * kHeadsPerUnit + n);
           const float wt = (ls == -INFINITY) ? 0.f : exp2_fast((ls - M) * kLog2e);
           wsum += wt;
           const float* pi = a.part_o + ((long long)sl * kHeadsPerUnit + n) * DV + 4 * g;
 #pragma unroll
-          for (int blk = 0; blk < TL::VBLK; ++blk) acc[blk] += wt * *(const f32x4*)(pi + 16 * blk);
+          for (int blk = 0; blk < TL::VBLK; ++blk) acc[blk] += wt * load_coherent4(pi + 16 * blk);
         }
         if (n < nh) {
           const float winv = wsum > 0.f ? 1.f / wsum : 0.f;
@@ -278,7 +277,7 @@ decode_kernel(DecodeArgs a) {
           if (a.lse && g == 0)
             a.lse[(long long)b * a.Hq + h0 + n] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
         }
-        if (lane == 0) *ctr = 0u;  // leave the counter at zero for the next call
+        if (lane == 0) counter_reset(ctr);  // leave the counter at zero for the next call
       }
     }
     p += len;
@@ -295,7 +294,7 @@ int default_workers(Layout layout) {
 
 template <int L, int DT>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<L, DT>), dim3(a.P), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((decode_kernel<L, DT>), dim3(a.P), dim3(64), 0, stream, a, a.cu);
   return hipGetLastError();
 }
 

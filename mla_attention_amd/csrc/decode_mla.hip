@@ -67,7 +67,7 @@ __device__ __forceinline__ void dma_half(const uint16_t* c, int tok0, int nvalid
 
 template <int DT>
 __global__ __attribute__((amdgpu_flat_work_group_size(128, 128), amdgpu_waves_per_eu(1, 1))) void
-mla_decode_kernel(DecodeArgs a) {
+mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
   // One LDS object only: with a second __shared__ variable the compiler starts
   // tracking global->LDS DMA per object and makes every LDS read wait for all
   // in-flight DMA (vmcnt(0)), which would serialise the tile pipeline.
@@ -87,14 +87,14 @@ mla_decode_kernel(DecodeArgs a) {
   // Empty sequences: out = 0, lse = -inf (no worker run covers them).
   for (int idx = w; idx < B * U; idx += a.P) {
     const int b = idx / U, hb = idx - (idx / U) * U;
-    if (a.cu[b + 1] - a.cu[b] != 0) continue;
+    if (cu[b + 1] - cu[b] != 0) continue;
     const int h0 = hb * kHeadsPerUnit;
     const int nh = min(kHeadsPerUnit, a.G - h0);
     for (int e = tid; e < nh * kDV; e += 64 * kWaves) a.out[((long long)b * a.Hq + h0) * kDV + e] = 0;
     if (a.lse && tid < nh) a.lse[(long long)b * a.Hq + h0 + tid] = -INFINITY;
   }
 
-  const int T = a.cu[B];
+  const int T = cu[B];
   const long long N = (long long)U * T;
   long long per = (N + a.P - 1) / a.P;
   if (per < kMinPerWorker) per = kMinPerWorker;
@@ -104,8 +104,8 @@ mla_decode_kernel(DecodeArgs a) {
   while (p < p_end) {
     const int u = (int)(p / T);
     const int t0 = (int)(p - (long long)u * T);
-    const int b = seq_of_token(a.cu, B, t0);
-    const int cs = a.cu[b], ce = a.cu[b + 1];
+    const int b = seq_of_token(cu, B, t0);
+    const int cs = cu[b], ce = cu[b + 1];
     const long long rem = p_end - p;
     const int t1 = (long long)(ce - t0) < rem ? ce : (int)(t0 + rem);
     const int len = t1 - t0;
@@ -158,7 +158,7 @@ mla_decode_kernel(DecodeArgs a) {
       f32x4 s[2];
       scores<DT, kKSteps, kRowB>(kt, qop, n, g, slot_fn, s);
       float alpha;
-      const i16x8 pop = softmax_update<DT>(s, g, min(32, len - 32 * j), a.scale_log2, sm, alpha);
+      const POperand pop = softmax_update<DT>(s, g, min(32, len - 32 * j), a.scale_log2, sm, alpha);
 #pragma unroll
       for (int i = 0; i < kBlkPerWave; ++i) o[i] *= alpha;
       pv_blocks<DT, kBlkPerWave, kRowB>(kt, pop, n, g, wave * kBlkPerWave, slot_fn, o);
@@ -180,32 +180,31 @@ mla_decode_kernel(DecodeArgs a) {
       const int sl_own = partial_slot(w, per, seq_p0);
       float* po = a.part_o + ((long long)sl_own * kHeadsPerUnit + n) * kDV + dim0;
 #pragma unroll
-      for (int bb = 0; bb < kBlkPerWave; ++bb) *(f32x4*)(po + 16 * bb) = o[bb] * inv;
-      if (wave == 0 && g == 0) a.part_lse[sl_own * kHeadsPerUnit + n] = lse_v;
-      __threadfence();  // release this worker's partial
+      for (int bb = 0; bb < kBlkPerWave; ++bb) store_coherent(po + 16 * bb, o[bb] * inv);
+      if (wave == 0 && g == 0) store_coherent(a.part_lse + sl_own * kHeadsPerUnit + n, lse_v);
+      stores_done();  // this wave's half of the partial is in memory
       __syncthreads();
       uint32_t* ctr = a.counters + (long long)u * B + b;
-      if (tid == 0) sh_old = atomicAdd(ctr, 1u);
+      if (tid == 0) sh_old = counter_add(ctr);
       __syncthreads();
       const uint32_t old = sh_old;
       const uint32_t nparts = (uint32_t)(w_last - w_first + 1);
       if (old == nparts - 1) {
-        __threadfence();  // acquire the other workers' partials
         float M = -INFINITY;
         for (int wi = w_first; wi <= w_last; ++wi)
-          M = fmaxf(M, a.part_lse[partial_slot(wi, per, seq_p0) * kHeadsPerUnit + n]);
+          M = fmaxf(M, load_coherent(a.part_lse + partial_slot(wi, per, seq_p0) * kHeadsPerUnit + n));
         f32x4 acc[kBlkPerWave];
 #pragma unroll
         for (int i = 0; i < kBlkPerWave; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         float wsum = 0.f;
         for (int wi = w_first; wi <= w_last; ++wi) {
           const int sl = partial_slot(wi, per, seq_p0);
-          const float ls = a.part_lse[sl * kHeadsPerUnit + n];
+          const float ls = load_coherent(a.part_lse + sl * kHeadsPerUnit + n);
           const float wt = (ls == -INFINITY) ? 0.f : exp2_fast((ls - M) * kLog2e);
           wsum += wt;
           const float* pi = a.part_o + ((long long)sl * kHeadsPerUnit + n) * kDV + dim0;
 #pragma unroll
-          for (int bb = 0; bb < kBlkPerWave; ++bb) acc[bb] += wt * *(const f32x4*)(pi + 16 * bb);
+          for (int bb = 0; bb < kBlkPerWave; ++bb) acc[bb] += wt * load_coherent4(pi + 16 * bb);
         }
         if (n < nh) {
           const float winv = wsum > 0.f ? 1.f / wsum : 0.f;
@@ -215,7 +214,7 @@ mla_decode_kernel(DecodeArgs a) {
           if (a.lse && wave == 0 && g == 0)
             a.lse[(long long)b * a.Hq + h0 + n] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
         }
-        if (tid == 0) *ctr = 0u;  // leave the counter at zero for the next call
+        if (tid == 0) counter_reset(ctr);  // leave the counter at zero for the next call
       }
     }
     p += len;
@@ -226,9 +225,9 @@ int mla_default_workers() { return 256 * kWorkgroupsPerCU; }
 
 hipError_t launch_mla(const DecodeArgs& a, int dtype, hipStream_t stream) {
   if (dtype == kF16)
-    hipLaunchKernelGGL(mla_decode_kernel<kF16>, dim3(a.P), dim3(64 * kWaves), 0, stream, a);
+    hipLaunchKernelGGL(mla_decode_kernel<kF16>, dim3(a.P), dim3(64 * kWaves), 0, stream, a, a.cu);
   else
-    hipLaunchKernelGGL(mla_decode_kernel<kBF16>, dim3(a.P), dim3(64 * kWaves), 0, stream, a);
+    hipLaunchKernelGGL(mla_decode_kernel<kBF16>, dim3(a.P), dim3(64 * kWaves), 0, stream, a, a.cu);
   return hipGetLastError();
 }
 

@@ -38,12 +38,21 @@ __device__ __forceinline__ void scores(const ZL_LDS char* kt, const i16x8 (&qop)
   }
 }
 
+// P^T operand of the PV product.  For bf16 (8 significant bits) the
+// probabilities are split as P = hi + lo with both halves in bf16, and PV runs
+// twice (V hi + V lo): P keeps about 16 significant bits, so the PV result is
+// not limited by bf16 rounding of the weights.  fp16 (11 bits) uses hi only.
+struct POperand {
+  i16x8 hi;
+  i16x8 lo;
+};
+
 // Online-softmax update with the tile's scores.  Tokens at or past nvalid are
 // masked.  Returns the P^T operand (16-bit probabilities in PV k-slot order)
 // and the factor alpha by which the accumulators must be rescaled.
 template <int DT>
-__device__ __forceinline__ i16x8 softmax_update(const f32x4 (&s)[2], int g, int nvalid,
-                                                float scale_log2, SoftmaxState& st, float& alpha) {
+__device__ __forceinline__ POperand softmax_update(const f32x4 (&s)[2], int g, int nvalid,
+                                                   float scale_log2, SoftmaxState& st, float& alpha) {
   float x[8];
   float tmax = -INFINITY;
 #pragma unroll
@@ -68,12 +77,24 @@ __device__ __forceinline__ i16x8 softmax_update(const f32x4 (&s)[2], int g, int 
   }
   st.l = st.l * alpha + psum;
   st.m = m_new;
+  POperand p;
   u32x4 pw;
-  pw[0] = pack2<DT>(x[0], x[1]);
-  pw[1] = pack2<DT>(x[2], x[3]);
-  pw[2] = pack2<DT>(x[4], x[5]);
-  pw[3] = pack2<DT>(x[6], x[7]);
-  return __builtin_bit_cast(i16x8, pw);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pw[i] = pack2<DT>(x[2 * i], x[2 * i + 1]);
+  p.hi = __builtin_bit_cast(i16x8, pw);
+  if constexpr (DT == kBF16) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t h = (uint32_t)to16<DT>(x[i]) << 16;  // hi as fp32
+      x[i] -= __builtin_bit_cast(float, h);               // exact residual
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pw[i] = pack2<DT>(x[2 * i], x[2 * i + 1]);
+    p.lo = __builtin_bit_cast(i16x8, pw);
+  } else {
+    p.lo = p.hi;  // unused
+  }
+  return p;
 }
 
 // O^T[16 dims x 16 heads] += V^T P^T for NB consecutive 16-dim blocks starting
@@ -81,7 +102,7 @@ __device__ __forceinline__ i16x8 softmax_update(const f32x4 (&s)[2], int g, int 
 // points at token 4g + m/4 (and +16), dims 16blk + 4(m%4) .. +3.  Reads go out
 // in groups of 4 blocks (8 reads) with one group of lookahead.
 template <int DT, int NB, int ROWB, typename SlotFn>
-__device__ __forceinline__ void pv_blocks(const ZL_LDS char* vt, const i16x8& pop, int n, int g,
+__device__ __forceinline__ void pv_blocks(const ZL_LDS char* vt, const POperand& pop, int n, int g,
                                           int blk0, SlotFn slot, f32x4 (&o)[NB]) {
   static_assert(NB % 4 == 0, "blocks come in groups of 4");
   constexpr int NG = NB / 4;
@@ -117,7 +138,8 @@ __device__ __forceinline__ void pv_blocks(const ZL_LDS char* vt, const i16x8& po
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       i16x8 av = __builtin_shufflevector(lo[buf][k], hi[buf][k], 0, 1, 2, 3, 4, 5, 6, 7);
-      o[4 * grp + k] = mfma16x16x32<DT>(av, pop, o[4 * grp + k]);
+      o[4 * grp + k] = mfma16x16x32<DT>(av, pop.hi, o[4 * grp + k]);
+      if constexpr (DT == kBF16) o[4 * grp + k] = mfma16x16x32<DT>(av, pop.lo, o[4 * grp + k]);
     }
   }
 }
