@@ -32,7 +32,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["zl_device.h", "zl_split.h", "zl_tile.h", "zl_kernels.h", "decode_attn.hip",
-                  "decode_mla.hip"]
+                  "decode_mla.hip", "split_merge.hip"]
 
 
 def kernel_source_sha() -> str:
@@ -69,7 +69,22 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--profile-run", action="store_true",
                     help="a few launches only (for rocprofv3 counter passes); no JSON")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead: copy a MIB-sized buffer a few times with a plain device copy "
+                         "(the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int, launches: int):
+    import torch
+
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(launches):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copy calibration: {launches} copies of {n} bytes", flush=True)
 
 
 def main():
@@ -79,6 +94,10 @@ def main():
                                    "one GPU's share; multi-GPU scaling is not part of it",
                           "n_gpus_requested": args.gpus}))
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, max(3, args.steps))
+        return
 
     import numpy as np
     import torch
@@ -109,14 +128,14 @@ def main():
     lse = torch.empty(spec.batch, spec.num_q_heads, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(i):
+    def step(i, phases=3):
         c = caches[i % reps]
         if spec.kind == "mla":
             zl.zl_decode_attn_mla(q, c[0], cu, x.max_seqlen, spec.scale, out=out, lse=lse, workspace=ws,
-                                  num_workers=args.workers, stream=stream)
+                                  num_workers=args.workers, stream=stream, phases=phases)
         else:
             zl.zl_decode_attn_gqa(q, c[0], c[1], cu, x.max_seqlen, spec.scale, out=out, lse=lse,
-                                  workspace=ws, num_workers=args.workers, stream=stream)
+                                  workspace=ws, num_workers=args.workers, stream=stream, phases=phases)
 
     if args.profile_run:
         for i in range(max(3, args.steps)):
@@ -129,21 +148,24 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    # Each step is the decode kernel then the merge kernel (the two phases of
+    # one call, enqueued separately so that an event can sit between them).
     K = args.steps
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        starts[i].record(stream)
-        step(args.warmup + i)
-        ends[i].record(stream)
+        ev[i][0].record(stream)
+        step(args.warmup + i, phases=1)
+        ev[i][1].record(stream)
+        step(args.warmup + i, phases=2)
+        ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
-    span_ms = starts[0].elapsed_time(ends[-1])
-    per_launch_ms = [starts[i].elapsed_time(ends[i]) for i in range(K)]
+    span_ms = ev[0][0].elapsed_time(ev[-1][2])
+    kern_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]))
+    merge_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]))
     ms_per_step = span_ms / K
-    kern_ms = float(np.mean(per_launch_ms))
     value_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved_gbs = kv_bytes / (kern_ms * 1e-3) / 1e9
 
@@ -190,6 +212,7 @@ def main():
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic_from_profile(workload),
             "avg_launch_us": round(kern_ms * 1e3, 2),
+            "merge_launch_us": round(merge_ms * 1e3, 2),
         },
         "cpu_baseline": cpu,
         "wall_ms_timed_region": round(wall_ms, 2),

@@ -30,7 +30,10 @@
  *  - Pointers are DEVICE pointers unless marked "host".  The caller owns every
  *    buffer; the library keeps no pointer after it returns.
  *  - Work is enqueued on `stream` (NULL = the default stream) and is
- *    asynchronous: nothing synchronises, nothing is allocated.
+ *    asynchronous: nothing synchronises, nothing is allocated.  A decode call
+ *    enqueues two kernels: the decode kernel, which splits the batch evenly
+ *    over its workers and leaves fp32 partials for sequences that several
+ *    workers share, and the merge kernel, which combines those partials.
  *  - Host-checkable arguments are validated before any HIP call; a bad argument
  *    returns an error status and enqueues nothing.  Device contents (the values
  *    in cu_seqlens) are preconditions: cu[0] = 0, non-decreasing, every length
@@ -77,11 +80,9 @@ typedef struct ihipStream_t *zl_stream_t;
 
 /*
  * Bytes of device workspace that zl_decode_attn_gqa needs for these sizes
- * (host function, no HIP call).  Returns 0 for invalid sizes.
- * The workspace holds per-worker partial results and one completion counter
- * per (sequence, key/value head); it must be ZERO-FILLED before its first use
- * (e.g. allocated with torch.zeros).  Every call leaves the counters at zero
- * again, so a workspace is zeroed once and then reused.
+ * (host function, no HIP call).  Returns 0 for invalid sizes.  The workspace
+ * holds two fp32 partial results per worker; it needs no initialisation and
+ * its contents are meaningless between calls.
  */
 ZL_API size_t zl_decode_attn_workspace_size(int batch, int num_q_heads, int num_kv_heads,
                                      int head_dim, int max_seqlen_k, zl_dtype_t dtype);
@@ -102,8 +103,7 @@ ZL_API size_t zl_decode_attn_workspace_size(int batch, int num_q_heads, int num_
  *   softmax_scale finite (0 allowed),
  *   out        [batch, num_q_heads, head_dim] dtype, fully overwritten
  *   lse        [batch, num_q_heads] float32, natural log; NULL = not written
- *   workspace  zero-filled once, >= zl_decode_attn_workspace_size(...) bytes,
- *              256-byte aligned
+ *   workspace  >= zl_decode_attn_workspace_size(...) bytes, 256-byte aligned
  */
 ZL_API zl_status_t zl_decode_attn_gqa(const void *q, const void *k_cache, const void *v_cache,
                                const int32_t *cu_seqlens, int batch, int num_q_heads,
@@ -113,7 +113,7 @@ ZL_API zl_status_t zl_decode_attn_gqa(const void *q, const void *k_cache, const 
 
 /*
  * Bytes of device workspace that zl_decode_attn_mla needs (host function,
- * same zero-fill rule as above).  Returns 0 for invalid sizes.
+ * as above).  Returns 0 for invalid sizes.
  */
 ZL_API size_t zl_decode_attn_mla_workspace_size(int batch, int num_q_heads, int kv_lora_rank,
                                          int rope_dim, int max_seqlen_k, zl_dtype_t dtype);
@@ -165,12 +165,16 @@ ZL_API zl_status_t zl_attn_combine(const float *partial_out, const float *partia
                             void *out, float *lse, zl_stream_t stream);
 
 /*
- * The same two decode calls with an explicit number of workers (wavefronts
+ * The same two decode calls with an explicit number of workers (the units
  * that split the batch's (kv-head, token) rows evenly; a multiple of 8,
  * 8 .. 65536; 0 = the default for the layout) and the matching workspace
  * sizes.  The result is the same attention for any worker count, up to the
  * fp32 rounding of how tokens are grouped; tests use this to vary the split,
  * and it lets a caller trade split overhead against parallelism.
+ * `phases` selects the kernels to enqueue: 1 = the decode kernel only, 2 = the
+ * merge kernel only, 3 = both (what the plain entry points do).  Phase 2 must
+ * follow phase 1 of the same arguments on the same workspace, stream-ordered;
+ * splitting a call lets a caller time or place the two launches separately.
  */
 ZL_API size_t zl_decode_attn_workspace_size_ex(int batch, int num_q_heads, int num_kv_heads,
                                         int head_dim, int max_seqlen_k, zl_dtype_t dtype,
@@ -179,16 +183,16 @@ ZL_API zl_status_t zl_decode_attn_gqa_ex(const void *q, const void *k_cache, con
                                   const int32_t *cu_seqlens, int batch, int num_q_heads,
                                   int num_kv_heads, int head_dim, int max_seqlen_k,
                                   float softmax_scale, zl_dtype_t dtype, void *out, float *lse,
-                                  int num_workers, void *workspace, size_t workspace_bytes,
-                                  zl_stream_t stream);
+                                  int num_workers, int phases, void *workspace,
+                                  size_t workspace_bytes, zl_stream_t stream);
 ZL_API size_t zl_decode_attn_mla_workspace_size_ex(int batch, int num_q_heads, int kv_lora_rank,
                                             int rope_dim, int max_seqlen_k, zl_dtype_t dtype,
                                             int num_workers);
 ZL_API zl_status_t zl_decode_attn_mla_ex(const void *q, const void *kv_cache, const int32_t *cu_seqlens,
                                   int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
                                   int max_seqlen_k, float softmax_scale, zl_dtype_t dtype,
-                                  void *out, float *lse, int num_workers, void *workspace,
-                                  size_t workspace_bytes, zl_stream_t stream);
+                                  void *out, float *lse, int num_workers, int phases,
+                                  void *workspace, size_t workspace_bytes, zl_stream_t stream);
 
 /* Static, human-readable name of a status code (host). */
 ZL_API const char *zl_status_string(zl_status_t status);

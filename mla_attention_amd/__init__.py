@@ -42,13 +42,13 @@ SIGNATURES = {
     "zl_decode_attn_gqa": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     _c_float, _c_int, _vp, _vp, _vp, _c_size, _vp]),
     "zl_decode_attn_gqa_ex": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
-                                       _c_float, _c_int, _vp, _vp, _c_int, _vp, _c_size, _vp]),
+                                       _c_float, _c_int, _vp, _vp, _c_int, _c_int, _vp, _c_size, _vp]),
     "zl_decode_attn_mla_workspace_size": (_c_size, [_c_int] * 6),
     "zl_decode_attn_mla_workspace_size_ex": (_c_size, [_c_int] * 7),
     "zl_decode_attn_mla": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
                                     _c_int, _vp, _vp, _vp, _c_size, _vp]),
     "zl_decode_attn_mla_ex": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
-                                       _c_float, _c_int, _vp, _vp, _c_int, _vp, _c_size, _vp]),
+                                       _c_float, _c_int, _vp, _vp, _c_int, _c_int, _vp, _c_size, _vp]),
     "zl_attn_combine": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
     "zl_status_string": (ctypes.c_char_p, [_c_int]),
 }
@@ -124,19 +124,20 @@ def zl_decode_attn_mla_workspace_size(batch, num_q_heads, kv_lora_rank, rope_dim
 
 
 def new_workspace(nbytes: int, device) -> torch.Tensor:
-    """A zero-filled workspace (the counters must start at zero; calls keep them there)."""
-    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    """A workspace buffer (no initialisation needed)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 def zl_decode_attn_gqa(q, k_cache, v_cache, cu_seqlens, max_seqlen_k: int, softmax_scale: float,
                        out=None, lse=None, workspace=None, num_workers: int = 0, stream=None,
-                       return_lse: bool = False):
+                       return_lse: bool = False, phases: int = 3):
     """out[b,h] = softmax(scale * q[b,h] . K[seq b, h // G]) V[seq b, h // G].
 
     q [B, Hq, D], k_cache/v_cache [T, Hkv, D] (fp16 or bf16, packed ragged),
     cu_seqlens int32 [B+1].  Returns out (and lse [B, Hq] fp32 if return_lse
-    or lse is given).  workspace: zero-filled uint8 tensor from new_workspace();
-    allocated here when omitted.
+    or lse is given).  workspace: uint8 tensor of at least
+    zl_decode_attn_workspace_size() bytes, allocated here when omitted.
+    phases: 1 = decode kernel, 2 = merge kernel, 3 = both.
     """
     _need(q, "q", ndim=3)
     dev = q.device
@@ -166,7 +167,7 @@ def zl_decode_attn_gqa(q, k_cache, v_cache, cu_seqlens, max_seqlen_k: int, softm
     _need(workspace, "workspace", torch.uint8, 1, dev)
     st = library().zl_decode_attn_gqa_ex(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens), B, Hq, Hkv, D, int(max_seqlen_k),
-        float(softmax_scale), _DTYPE[q.dtype], _ptr(out), _ptr(lse), int(num_workers),
+        float(softmax_scale), _DTYPE[q.dtype], _ptr(out), _ptr(lse), int(num_workers), int(phases),
         _ptr(workspace), workspace.numel(), _stream(stream, dev))
     _check(st, "zl_decode_attn_gqa")
     return (out, lse) if lse is not None else out
@@ -174,7 +175,8 @@ def zl_decode_attn_gqa(q, k_cache, v_cache, cu_seqlens, max_seqlen_k: int, softm
 
 def zl_decode_attn_mla(q, kv_cache, cu_seqlens, max_seqlen_k: int, softmax_scale: float,
                        kv_lora_rank: int = 512, rope_dim: int = 64, out=None, lse=None,
-                       workspace=None, num_workers: int = 0, stream=None, return_lse: bool = False):
+                       workspace=None, num_workers: int = 0, stream=None, return_lse: bool = False,
+                       phases: int = 3):
     """Absorbed MLA decode: q [B, H, rank+rope], kv_cache [T, rank+rope];
     K = whole latent row, V = its first kv_lora_rank columns.  Returns out [B, H, rank]."""
     _need(q, "q", ndim=3)
@@ -204,7 +206,7 @@ def zl_decode_attn_mla(q, kv_cache, cu_seqlens, max_seqlen_k: int, softmax_scale
     _need(workspace, "workspace", torch.uint8, 1, dev)
     st = library().zl_decode_attn_mla_ex(
         _ptr(q), _ptr(kv_cache), _ptr(cu_seqlens), B, H, kv_lora_rank, rope_dim, int(max_seqlen_k),
-        float(softmax_scale), _DTYPE[q.dtype], _ptr(out), _ptr(lse), int(num_workers),
+        float(softmax_scale), _DTYPE[q.dtype], _ptr(out), _ptr(lse), int(num_workers), int(phases),
         _ptr(workspace), workspace.numel(), _stream(stream, dev))
     _check(st, "zl_decode_attn_mla")
     return (out, lse) if lse is not None else out

@@ -8,7 +8,8 @@
 //
 // Kernel structure (one wavefront per workgroup, one worker per wavefront):
 //  * Work split: every worker streams the same number of (unit, token) rows,
-//    whatever the mix of sequence lengths; see zl_split.h.
+//    whatever the mix of sequence lengths; see zl_split.h.  Sequences cut
+//    between workers are merged by split_merge.hip, launched right after.
 //  * Data path: 32-token tiles go HBM -> LDS with 16-byte global_load_lds
 //    (no VGPR round trip), each 16-lane group reading contiguous bytes of one
 //    row.  STAGES tiles form an LDS ring, STAGES-1 of them in flight while the
@@ -117,8 +118,14 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
   using GE = Geo<L>;
   constexpr int STAGES = GE::STAGES;
   constexpr int DK = TL::DK, DV = TL::DV;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[STAGES * TL::STAGE_BYTES];
+  constexpr int QBYTES = kHeadsPerUnit * DK * 2;  // the unit's query rows
+  static_assert(QBYTES % 1024 == 0, "query block must be whole DMA blocks");
+  // One LDS object: [STAGES K/V tiles][query rows].  (With a second
+  // __shared__ variable the compiler tracks DMA per object and makes every
+  // LDS read wait for all in-flight DMA.)
+  __shared__ __attribute__((aligned(1024))) char smem_raw[STAGES * TL::STAGE_BYTES + QBYTES];
   ZL_LDS char* smem = (ZL_LDS char*)smem_raw;
+  ZL_LDS char* qlds = smem + STAGES * TL::STAGE_BYTES;
 
   const int lane = __lane_id();
   const int n = lane & 15;
@@ -128,6 +135,7 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
   const int U = a.Hkv * a.HB;
   const long long k_row = GE::SHARED_KV ? (long long)DK : (long long)a.Hkv * DK;
   const long long v_row = GE::SHARED_KV ? (long long)DK : (long long)a.Hkv * DV;
+  const auto slot = [](int c, int r) { return GE::slot(c, r); };
 
   // Empty sequences: out = 0, lse = -inf (no worker run covers them).
   for (int idx = w; idx < B * U; idx += a.P) {
@@ -142,10 +150,10 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
 
   const int T = cu[B];
   const long long N = (long long)U * T;
-  long long per = (N + a.P - 1) / a.P;
-  if (per < kMinPerWorker) per = kMinPerWorker;
+  const long long per = positions_per_worker(N, a.P);
   long long p = (long long)w * per;
   const long long p_end = N < p + per ? N : p + per;
+
 
   while (p < p_end) {
     // ---- segment: tokens [t0, t1) of sequence b, work unit u
@@ -165,23 +173,22 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
     const int nh = min(kHeadsPerUnit, a.G - hb * kHeadsPerUnit);
     const uint16_t* kbase = a.k + (long long)kvh * DK;
     const uint16_t* vbase = a.v + (long long)kvh * DV;
+    const int ntiles = (len + 31) >> 5;
 
-    wait_vmcnt<0>();  // stores/atomics of the previous segment out of the DMA count
-
-    // Query heads h0 .. h0+nh-1 as the B operand: lane (g, n) = head n,
-    // dims 32kb + 8g .. +7 (zero for padding heads).
-    i16x8 qop[TL::KSTEPS];
+    // Query rows h0 .. h0+15 into LDS with the first tiles (padding heads
+    // repeat head h0; their results are never stored).  Slot-swizzled like a
+    // K row so the operand read below is conflict-free.
     {
-      const uint16_t* qrow = a.q + ((long long)b * a.Hq + h0 + n) * DK + 8 * g;
+      const uint16_t* qb = a.q + ((long long)b * a.Hq + h0) * DK;
+      constexpr int CPR = DK / 8;
 #pragma unroll
-      for (int kb = 0; kb < TL::KSTEPS; ++kb) {
-        u32x4 v4 = {0u, 0u, 0u, 0u};
-        if (n < nh) v4 = *(const u32x4*)(qrow + 32 * kb);
-        qop[kb] = __builtin_bit_cast(i16x8, v4);
+      for (int i = 0; i < QBYTES / 1024; ++i) {
+        const int lin = 64 * i + lane;
+        const int r = lin / CPR;
+        const int c = slot(lin - r * CPR, r);
+        dma16(qb + (long long)(r < nh ? r : 0) * DK + c * 8, qlds + i * 1024);
       }
     }
-
-    const int ntiles = (len + 31) >> 5;
     // Prologue: always STAGES-1 tiles, so the number of loads in flight does
     // not depend on the segment length (a segment shorter than the prologue
     // re-reads its first tile into the unused stage).
@@ -195,16 +202,12 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
       if constexpr (!GE::SHARED_KV)
         dma_tile<L, TL::VCPR, TL::NI_V>(vbase, v_row, tok, nv, st + TL::KBYTES, lane);
     }
-    // The query loads were issued before the prologue DMA: waiting for them
-    // here leaves the prologue tiles in flight.
-#pragma unroll
-    for (int kb = 0; kb < TL::KSTEPS; ++kb) touch(qop[kb]);
 
     f32x4 o[TL::VBLK];
 #pragma unroll
     for (int i = 0; i < TL::VBLK; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     SoftmaxState sm{-INFINITY, 0.f};
-    const auto slot = [](int c, int r) { return GE::slot(c, r); };
+    i16x8 qop[TL::KSTEPS];
 
     for (int j = 0; j < ntiles; ++j) {
       const int ahead = j + STAGES - 1;
@@ -216,10 +219,15 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
           dma_tile<L, TL::VCPR, TL::NI_V>(vbase, v_row, t0 + 32 * ahead, nv, st + TL::KBYTES, lane);
       }
       wait_tiles_after<TL::PER_TILE, STAGES>(min(STAGES - 1, ntiles - 1 - j));
+      if (j == 0) {
+        // B operand: lane (g, n) = head n, dims 32kb + 8g .. +7
+#pragma unroll
+        for (int kb = 0; kb < TL::KSTEPS; ++kb)
+          qop[kb] = __builtin_bit_cast(i16x8, lds_read_b128(qlds + n * TL::KROWB + (slot(4 * kb + g, n) << 4)));
+      }
 
       const ZL_LDS char* kt = smem + (j % STAGES) * TL::STAGE_BYTES;
       const ZL_LDS char* vt = GE::SHARED_KV ? kt : kt + TL::KBYTES;
-
       f32x4 s[2];
       scores<DT, TL::KSTEPS, TL::KROWB>(kt, qop, n, g, slot, s);
       float alpha;
@@ -229,55 +237,24 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
       pv_blocks<DT, TL::VBLK, TL::VROWB>(vt, pop, n, g, 0, slot, o);
     }
 
-    // ---- segment epilogue: lane (g, n) holds head n, dims 16blk + 4g .. +3
+    // ---- segment epilogue: lane (g, n) holds head n, dims 16blk + 4g .. +3.
+    // Stores only: nothing here waits, so the next segment starts at once.
+    // A split sequence leaves its partial for the merge launch.
     const float l_tot = sum_over_groups(sm.l);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse_v = l_tot > 0.f ? sm.m * kLn2 + __logf(l_tot) : -INFINITY;
-    if (w_first == w_last) {
-      if (n < nh) {
+    if (n < nh) {
+      if (w_first == w_last) {
         uint16_t* orow = a.out + ((long long)b * a.Hq + h0 + n) * DV + 4 * g;
 #pragma unroll
         for (int blk = 0; blk < TL::VBLK; ++blk) store_out4<DT>(orow + 16 * blk, o[blk], inv);
         if (a.lse && g == 0) a.lse[(long long)b * a.Hq + h0 + n] = lse_v;
-      }
-    } else {
-      const int slot = partial_slot(w, per, seq_p0);
-      float* po = a.part_o + ((long long)slot * kHeadsPerUnit + n) * DV + 4 * g;
+      } else {
+        const int sl = partial_slot(w, per, seq_p0);
+        float* po = a.part_o + ((long long)sl * kHeadsPerUnit + n) * DV + 4 * g;
 #pragma unroll
-      for (int blk = 0; blk < TL::VBLK; ++blk) store_coherent(po + 16 * blk, o[blk] * inv);
-      if (g == 0) store_coherent(a.part_lse + slot * kHeadsPerUnit + n, lse_v);
-      stores_done();  // the partial is in memory before it is counted
-      uint32_t* ctr = a.counters + (long long)u * B + b;
-      uint32_t old = 0;
-      if (lane == 0) old = counter_add(ctr);
-      old = (uint32_t)readfirstlane((int)old);
-      const uint32_t nparts = (uint32_t)(w_last - w_first + 1);
-      if (old == nparts - 1) {
-        float M = -INFINITY;
-        for (int wi = w_first; wi <= w_last; ++wi)
-          M = fmaxf(M, load_coherent(a.part_lse + partial_slot(wi, per, seq_p0) * kHeadsPerUnit + n));
-        f32x4 acc[TL::VBLK];
-#pragma unroll
-        for (int i = 0; i < TL::VBLK; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float wsum = 0.f;
-        for (int wi = w_first; wi <= w_last; ++wi) {
-          const int sl = partial_slot(wi, per, seq_p0);
-          const float ls = load_coherent(a.part_lse + sl * kHeadsPerUnit + n);
-          const float wt = (ls == -INFINITY) ? 0.f : exp2_fast((ls - M) * kLog2e);
-          wsum += wt;
-          const float* pi = a.part_o + ((long long)sl * kHeadsPerUnit + n) * DV + 4 * g;
-#pragma unroll
-          for (int blk = 0; blk < TL::VBLK; ++blk) acc[blk] += wt * load_coherent4(pi + 16 * blk);
-        }
-        if (n < nh) {
-          const float winv = wsum > 0.f ? 1.f / wsum : 0.f;
-          uint16_t* orow = a.out + ((long long)b * a.Hq + h0 + n) * DV + 4 * g;
-#pragma unroll
-          for (int blk = 0; blk < TL::VBLK; ++blk) store_out4<DT>(orow + 16 * blk, acc[blk], winv);
-          if (a.lse && g == 0)
-            a.lse[(long long)b * a.Hq + h0 + n] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
-        }
-        if (lane == 0) counter_reset(ctr);  // leave the counter at zero for the next call
+        for (int blk = 0; blk < TL::VBLK; ++blk) *(f32x4*)(po + 16 * blk) = o[blk] * inv;
+        if (g == 0) a.part_lse[sl * kLseSlot + n] = lse_v;
       }
     }
     p += len;

@@ -1,0 +1,103 @@
+// split_merge.hip -- the log-sum-exp merge of split sequences, as a second
+// launch after the decode kernel.
+//
+// The decode kernels cut the ragged batch into equal runs of (unit, token)
+// positions, so a sequence may be shared by several workers; each of them
+// leaves an fp32 partial (O / l and lse per head) in the workspace.  This
+// kernel merges them exactly (split-KV "flash decoding"; the first ZhiLight
+// page names flash_decoding among the engine's kernels, section "技术架构"):
+//   M = max_s lse_s,  w_s = exp(lse_s - M),
+//   out = sum_s w_s O_s / sum_s w_s,  lse = M + ln(sum_s w_s).
+// One thread per (unit, sequence, head, 4-float column): all split sequences
+// are merged at once across the whole GPU, in about one memory round trip per
+// four partials.  Sequences that one worker covered alone were already
+// written by the decode kernel; their threads return at once.  The partials
+// are visible here because kernels on one stream are ordered and caches are
+// written back / invalidated between launches.
+#include "zl_device.h"
+#include "zl_kernels.h"
+#include "zl_split.h"
+#include "zl_tile.h"
+
+namespace zl {
+
+template <int DT, int DV>
+__global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a, const int32_t* __restrict__ cu,
+                                                          int heads_per_unit) {
+  constexpr int C4 = DV / 4;  // float4 columns per output row
+  const int U = a.Hkv * a.HB;
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (long long)U * a.B * heads_per_unit * C4) return;
+  const int c4 = (int)(gid % C4);
+  long long r = gid / C4;
+  const int h = (int)(r % heads_per_unit);
+  r /= heads_per_unit;
+  const int b = (int)(r % a.B);
+  const int u = (int)(r / a.B);
+  const int kvh = u / a.HB, hb = u - (u / a.HB) * a.HB;
+  const int nh = min(kHeadsPerUnit, a.G - hb * kHeadsPerUnit);
+  if (h >= nh) return;
+  const int cs = cu[b], ce = cu[b + 1];
+  if (ce == cs) return;
+  const int T = cu[a.B];
+  const long long per = positions_per_worker((long long)U * T, a.P);
+  const long long seq_p0 = (long long)u * T + cs;
+  const int w_first = (int)(seq_p0 / per);
+  const int w_last = (int)(((long long)u * T + ce - 1) / per);
+  if (w_first == w_last) return;
+
+  const int nparts = w_last - w_first + 1;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float M = -INFINITY, wsum = 0.f;
+  constexpr int BATCH = 4;  // partials whose loads are in flight together
+  for (int i0 = 0; i0 < nparts; i0 += BATCH) {
+    float ls[BATCH];
+    f32x4 v[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int i = min(i0 + j, nparts - 1);  // tail of the batch re-reads the last one
+      const int sl = partial_slot(w_first + i, per, seq_p0);
+      ls[j] = i0 + j < nparts ? a.part_lse[sl * kLseSlot + h] : -INFINITY;
+      v[j] = *(const f32x4*)(a.part_o + ((long long)sl * kHeadsPerUnit + h) * DV + 4 * c4);
+    }
+    float bm = ls[0];
+#pragma unroll
+    for (int j = 1; j < BATCH; ++j) bm = fmaxf(bm, ls[j]);
+    const float m_new = fmaxf(M, bm);
+    if (m_new == -INFINITY) continue;
+    const float rs = exp2_fast((M - m_new) * kLog2e);  // 0 while M is -inf
+    wsum *= rs;
+    acc *= rs;
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const float wt = exp2_fast((ls[j] - m_new) * kLog2e);  // 0 for -inf
+      wsum += wt;
+      acc += wt * v[j];
+    }
+    M = m_new;
+  }
+  const int h0 = kvh * a.G + hb * kHeadsPerUnit;
+  const float winv = wsum > 0.f ? 1.f / wsum : 0.f;
+  store_out4<DT>(a.out + ((long long)b * a.Hq + h0 + h) * DV + 4 * c4, acc, winv);
+  if (a.lse && c4 == 0) a.lse[(long long)b * a.Hq + h0 + h] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
+}
+
+template <int DT, int DV>
+static hipError_t launch_merge_t(const DecodeArgs& a, hipStream_t stream) {
+  const int hpu = a.G < kHeadsPerUnit ? a.G : kHeadsPerUnit;
+  const long long threads = (long long)a.Hkv * a.HB * a.B * hpu * (DV / 4);
+  const long long blocks = (threads + 255) / 256;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((split_merge_kernel<DT, DV>), dim3((unsigned)blocks), dim3(256), 0, stream, a, a.cu, hpu);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const DecodeArgs& a, int dv, int dtype, hipStream_t stream) {
+  if (dv == 64)
+    return dtype == kF16 ? launch_merge_t<kF16, 64>(a, stream) : launch_merge_t<kBF16, 64>(a, stream);
+  if (dv == 128)
+    return dtype == kF16 ? launch_merge_t<kF16, 128>(a, stream) : launch_merge_t<kBF16, 128>(a, stream);
+  return dtype == kF16 ? launch_merge_t<kF16, 512>(a, stream) : launch_merge_t<kBF16, 512>(a, stream);
+}
+
+}  // namespace zl

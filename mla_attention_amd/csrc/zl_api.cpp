@@ -22,16 +22,15 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t counters_off, lse_off, out_off, total;
+  size_t lse_off, out_off, total;
 };
 
-// Workspace: [counters U*B u32][part_lse 2P*16 f32][part_o 2P*16*Dv f32],
-// each region 256-byte aligned.
-WsLayout ws_layout(long long units_times_batch, int workers, int dv) {
+// Workspace: [part_lse 2P*32 f32][part_o 2P*16*Dv f32], 256-byte aligned:
+// two fp32 partial slots per worker (see zl_split.h).
+WsLayout ws_layout(int workers, int dv) {
   WsLayout w;
-  w.counters_off = 0;
-  w.lse_off = round_up((size_t)units_times_batch * 4, 256);
-  w.out_off = w.lse_off + round_up((size_t)2 * workers * zl::kHeadsPerUnit * 4, 256);
+  w.lse_off = 0;
+  w.out_off = round_up((size_t)2 * workers * zl::kLseSlot * 4, 256);
   w.total = w.out_off + (size_t)2 * workers * zl::kHeadsPerUnit * dv * 4;
   return w;
 }
@@ -67,8 +66,7 @@ size_t gqa_ws_size(int batch, int num_q_heads, int num_kv_heads, int head_dim, i
   const Layout layout = head_dim == 128 ? zl::kGqaD128 : zl::kGqaD64;
   const int P = pick_workers(num_workers, layout);
   if (check_common(batch, num_q_heads, num_kv_heads, max_seqlen_k, dtype, P) != ZL_OK) return 0;
-  const long long units = (long long)num_kv_heads * head_blocks(num_q_heads / num_kv_heads);
-  return ws_layout(units * batch, P, head_dim).total;
+  return ws_layout(P, head_dim).total;
 }
 
 size_t mla_ws_size(int batch, int num_q_heads, int kv_lora_rank, int rope_dim, int max_seqlen_k,
@@ -76,20 +74,21 @@ size_t mla_ws_size(int batch, int num_q_heads, int kv_lora_rank, int rope_dim, i
   if (kv_lora_rank != 512 || rope_dim != 64) return 0;
   const int P = pick_workers(num_workers, zl::kMla576);
   if (check_common(batch, num_q_heads, 1, max_seqlen_k, dtype, P) != ZL_OK) return 0;
-  return ws_layout((long long)head_blocks(num_q_heads) * batch, P, kv_lora_rank).total;
+  return ws_layout(P, kv_lora_rank).total;
 }
 
-zl_status_t run_decode(zl::DecodeArgs a, Layout layout, int dv, zl_dtype_t dtype, void* workspace,
-                       size_t workspace_bytes, zl_stream_t stream) {
-  const long long units = (long long)a.Hkv * a.HB;
-  const WsLayout wl = ws_layout(units * a.B, a.P, dv);
+zl_status_t run_decode(zl::DecodeArgs a, Layout layout, int dv, zl_dtype_t dtype, int phases,
+                       void* workspace, size_t workspace_bytes, zl_stream_t stream) {
+  const WsLayout wl = ws_layout(a.P, dv);
   if (workspace == nullptr || !aligned(workspace, 256)) return ZL_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < wl.total) return ZL_ERR_WORKSPACE_TOO_SMALL;
   char* ws = static_cast<char*>(workspace);
-  a.counters = reinterpret_cast<uint32_t*>(ws + wl.counters_off);
   a.part_lse = reinterpret_cast<float*>(ws + wl.lse_off);
   a.part_o = reinterpret_cast<float*>(ws + wl.out_off);
-  const hipError_t e = zl::launch_decode(a, layout, dtype, reinterpret_cast<hipStream_t>(stream));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (phases & 1) e = zl::launch_decode(a, layout, dtype, st);
+  if (e == hipSuccess && (phases & 2)) e = zl::launch_merge(a, dv, dtype, st);
   return e == hipSuccess ? ZL_OK : ZL_ERR_HIP;
 }
 
@@ -112,9 +111,9 @@ zl_status_t zl_decode_attn_gqa_ex(const void* q, const void* k_cache, const void
                                   const int32_t* cu_seqlens, int batch, int num_q_heads,
                                   int num_kv_heads, int head_dim, int max_seqlen_k,
                                   float softmax_scale, zl_dtype_t dtype, void* out, float* lse,
-                                  int num_workers, void* workspace, size_t workspace_bytes,
-                                  zl_stream_t stream) {
-  if (num_workers < 0) return ZL_ERR_INVALID_ARGUMENT;
+                                  int num_workers, int phases, void* workspace,
+                                  size_t workspace_bytes, zl_stream_t stream) {
+  if (num_workers < 0 || phases < 1 || phases > 3) return ZL_ERR_INVALID_ARGUMENT;
   if (head_dim != 64 && head_dim != 128) {
     if (head_dim <= 0) return ZL_ERR_INVALID_ARGUMENT;
     return ZL_ERR_UNSUPPORTED;
@@ -145,7 +144,7 @@ zl_status_t zl_decode_attn_gqa_ex(const void* q, const void* k_cache, const void
   a.HB = head_blocks(a.G);
   a.P = P;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  return run_decode(a, layout, head_dim, dtype, workspace, workspace_bytes, stream);
+  return run_decode(a, layout, head_dim, dtype, phases, workspace, workspace_bytes, stream);
 }
 
 zl_status_t zl_decode_attn_gqa(const void* q, const void* k_cache, const void* v_cache,
@@ -154,8 +153,8 @@ zl_status_t zl_decode_attn_gqa(const void* q, const void* k_cache, const void* v
                                float softmax_scale, zl_dtype_t dtype, void* out, float* lse,
                                void* workspace, size_t workspace_bytes, zl_stream_t stream) {
   return zl_decode_attn_gqa_ex(q, k_cache, v_cache, cu_seqlens, batch, num_q_heads, num_kv_heads,
-                               head_dim, max_seqlen_k, softmax_scale, dtype, out, lse, 0, workspace,
-                               workspace_bytes, stream);
+                               head_dim, max_seqlen_k, softmax_scale, dtype, out, lse, 0, 3,
+                               workspace, workspace_bytes, stream);
 }
 
 size_t zl_decode_attn_mla_workspace_size(int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
@@ -173,9 +172,9 @@ size_t zl_decode_attn_mla_workspace_size_ex(int batch, int num_q_heads, int kv_l
 zl_status_t zl_decode_attn_mla_ex(const void* q, const void* kv_cache, const int32_t* cu_seqlens,
                                   int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
                                   int max_seqlen_k, float softmax_scale, zl_dtype_t dtype,
-                                  void* out, float* lse, int num_workers, void* workspace,
-                                  size_t workspace_bytes, zl_stream_t stream) {
-  if (num_workers < 0) return ZL_ERR_INVALID_ARGUMENT;
+                                  void* out, float* lse, int num_workers, int phases,
+                                  void* workspace, size_t workspace_bytes, zl_stream_t stream) {
+  if (num_workers < 0 || phases < 1 || phases > 3) return ZL_ERR_INVALID_ARGUMENT;
   if (kv_lora_rank <= 0 || rope_dim < 0) return ZL_ERR_INVALID_ARGUMENT;
   if (kv_lora_rank != 512 || rope_dim != 64) return ZL_ERR_UNSUPPORTED;
   const int P = pick_workers(num_workers, zl::kMla576);
@@ -201,7 +200,7 @@ zl_status_t zl_decode_attn_mla_ex(const void* q, const void* kv_cache, const int
   a.HB = head_blocks(num_q_heads);
   a.P = P;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  return run_decode(a, zl::kMla576, kv_lora_rank, dtype, workspace, workspace_bytes, stream);
+  return run_decode(a, zl::kMla576, kv_lora_rank, dtype, phases, workspace, workspace_bytes, stream);
 }
 
 zl_status_t zl_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* cu_seqlens,
@@ -210,7 +209,7 @@ zl_status_t zl_decode_attn_mla(const void* q, const void* kv_cache, const int32_
                                float* lse, void* workspace, size_t workspace_bytes,
                                zl_stream_t stream) {
   return zl_decode_attn_mla_ex(q, kv_cache, cu_seqlens, batch, num_q_heads, kv_lora_rank, rope_dim,
-                               max_seqlen_k, softmax_scale, dtype, out, lse, 0, workspace,
+                               max_seqlen_k, softmax_scale, dtype, out, lse, 0, 3, workspace,
                                workspace_bytes, stream);
 }
 

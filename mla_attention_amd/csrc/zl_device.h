@@ -140,56 +140,4 @@ __device__ __forceinline__ void touch(T& r) {
 
 __device__ __forceinline__ int readfirstlane(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Cross-XCD hand-off of partial results without an L2 writeback.
-// The 8 XCDs have separate, mutually non-coherent L2 caches.  A device-scope
-// release fence would write back every dirty line of this XCD's L2, which
-// costs microseconds per call when many workers do it.  Instead the partials
-// are written with system-scope (write-through) stores and read with
-// system-scope loads: both bypass the non-coherent L2 copies, so waiting for
-// the stores to be acknowledged (vmcnt(0)) is enough before the completion
-// counter is bumped.
-__device__ __forceinline__ void store_coherent(float* dst, f32x4 v) {
-  uint64_t* d = reinterpret_cast<uint64_t*>(dst);
-  const u32x4 u = __builtin_bit_cast(u32x4, v);
-  __hip_atomic_store(d, (uint64_t)u[0] | ((uint64_t)u[1] << 32), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_SYSTEM);
-  __hip_atomic_store(d + 1, (uint64_t)u[2] | ((uint64_t)u[3] << 32), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_SYSTEM);
-}
-
-__device__ __forceinline__ void store_coherent(float* dst, float v) {
-  __hip_atomic_store(reinterpret_cast<uint32_t*>(dst), __builtin_bit_cast(uint32_t, v),
-                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-
-__device__ __forceinline__ f32x4 load_coherent4(const float* src) {
-  const uint64_t* s = reinterpret_cast<const uint64_t*>(src);
-  const uint64_t a = __hip_atomic_load(s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  const uint64_t b = __hip_atomic_load(s + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  u32x4 u;
-  u[0] = (uint32_t)a;
-  u[1] = (uint32_t)(a >> 32);
-  u[2] = (uint32_t)b;
-  u[3] = (uint32_t)(b >> 32);
-  return __builtin_bit_cast(f32x4, u);
-}
-
-__device__ __forceinline__ float load_coherent(const float* src) {
-  return __builtin_bit_cast(
-      float, __hip_atomic_load(reinterpret_cast<const uint32_t*>(src), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_SYSTEM));
-}
-
-// All of this wave's stores acknowledged, and no memory access moved across.
-__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Device-scope counter increment; returns the previous value.
-__device__ __forceinline__ uint32_t counter_add(uint32_t* c) {
-  return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void counter_reset(uint32_t* c) {
-  __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 }  // namespace zl

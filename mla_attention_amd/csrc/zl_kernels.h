@@ -10,7 +10,9 @@ namespace zl {
 
 // Sizes shared by host planning and the kernels.
 constexpr int kHeadsPerUnit = 16;  // query heads packed into one MFMA N dimension
-constexpr int kMinPerWorker = 64;  // fewest (unit, token) positions a worker is given
+// Floats per partial-lse slot: one 128-byte cache line, so no two slots (which
+// different XCDs write and read) ever share a line.
+constexpr int kLseSlot = 32;
 
 enum Layout {
   kGqaD64 = 0,   // K, V [T, Hkv, 64]
@@ -27,8 +29,7 @@ struct DecodeArgs {
   uint16_t* out;        // [B, Hq, Dv]
   float* lse;           // [B, Hq] or nullptr
   float* part_o;        // [2P, 16, Dv]
-  float* part_lse;      // [2P, 16]
-  uint32_t* counters;   // [U * B], zero between calls (U = Hkv * HB)
+  float* part_lse;      // [2P, kLseSlot] (first 16 used)
   int B, Hq, Hkv, G, HB, P;
   float scale_log2;     // softmax_scale * log2(e)
 };
@@ -47,6 +48,7 @@ int mla_default_workers();
 hipError_t launch_mla(const DecodeArgs& a, int dtype, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs& a, Layout layout, int dtype, hipStream_t stream);
+hipError_t launch_merge(const DecodeArgs& a, int dv, int dtype, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t stream);
 
 }  // namespace zl

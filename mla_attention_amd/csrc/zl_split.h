@@ -6,8 +6,8 @@
 // (one wavefront each) owns an equal run of `per` positions, so every worker
 // streams the same number of K/V bytes whatever the mix of sequence lengths.
 // A run that covers a whole sequence writes that sequence's output directly;
-// a sequence cut between workers gets one fp32 partial (O / l, lse) per worker
-// and the last of them to finish merges the partials (log-sum-exp combine).
+// a sequence cut between workers gets one fp32 partial (O / l, lse) per worker,
+// merged by the split-merge kernel (split_merge.hip) launched right after.
 //
 // Partial slots: worker w owns slots 2w (the sequence its run starts in) and
 // 2w+1 (the sequence its run ends in, when that is another one).
@@ -17,10 +17,13 @@
 
 namespace zl {
 
-struct Split {
-  long long per;  // positions per worker
-  int T;          // total tokens (cu[B])
-};
+// Positions per worker for N positions over P workers (at least 64, so that a
+// tiny batch is not scattered over many workers).  The decode and the merge
+// kernels must agree on it exactly.
+__device__ __forceinline__ long long positions_per_worker(long long N, int P) {
+  const long long per = (N + P - 1) / P;
+  return per < 64 ? 64 : per;
+}
 
 // Largest b in [0, B) with cu[b] <= t; for 0 <= t < cu[B] this is the
 // sequence that owns token t (empty sequences are stepped over).

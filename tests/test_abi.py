@@ -54,9 +54,10 @@ def test_workspace_sizes(zl):
     lib = zl.library()
     s = lib.zl_decode_attn_workspace_size(32, 32, 8, 128, 4096, 0)
     assert s > 0 and s % 4 == 0
-    # larger batch -> more counters; more workers -> more partial slots
-    assert lib.zl_decode_attn_workspace_size(64, 32, 8, 128, 4096, 0) > s
+    # two partial slots per worker: independent of the batch, grows with workers and head dim
+    assert lib.zl_decode_attn_workspace_size(64, 32, 8, 128, 4096, 0) == s
     assert lib.zl_decode_attn_workspace_size_ex(32, 32, 8, 128, 4096, 0, 4096) > s
+    assert lib.zl_decode_attn_workspace_size_ex(32, 32, 8, 64, 4096, 0, 768) < s
     assert lib.zl_decode_attn_mla_workspace_size(32, 16, 512, 64, 8192, 1) > 0
     # invalid shapes -> 0
     for args in [(32, 32, 8, 96, 4096, 0), (32, 30, 8, 128, 4096, 0), (-1, 32, 8, 128, 4096, 0),
@@ -72,12 +73,12 @@ A = 0x100000  # a 256-byte aligned fake address: never dereferenced (validation 
 
 def gqa(lib, **kw):
     args = dict(q=A, k=A, v=A, cu=A, B=4, Hq=8, Hkv=2, D=128, maxL=128, scale=0.125, dt=0, out=A,
-                lse=None, workers=0, ws=A, wsb=BIG, stream=None)
+                lse=None, workers=0, phases=3, ws=A, wsb=BIG, stream=None)
     args.update(kw)
     return lib.zl_decode_attn_gqa_ex(args["q"], args["k"], args["v"], args["cu"], args["B"], args["Hq"],
                                      args["Hkv"], args["D"], args["maxL"], args["scale"], args["dt"],
-                                     args["out"], args["lse"], args["workers"], args["ws"], args["wsb"],
-                                     args["stream"])
+                                     args["out"], args["lse"], args["workers"], args["phases"], args["ws"],
+                                     args["wsb"], args["stream"])
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -86,7 +87,7 @@ def gqa(lib, **kw):
     (dict(ws=A + 16), 1), (dict(cu=A + 2), 1),
     (dict(B=-1), 1), (dict(Hq=0), 1), (dict(Hkv=0), 1), (dict(Hq=6, Hkv=4), 1),
     (dict(maxL=-1), 1), (dict(scale=float("inf")), 1), (dict(scale=float("nan")), 1),
-    (dict(dt=2), 1), (dict(workers=12), 1), (dict(workers=-8), 1),
+    (dict(dt=2), 1), (dict(workers=12), 1), (dict(workers=-8), 1), (dict(phases=0), 1), (dict(phases=4), 1),
     (dict(D=96), 2), (dict(D=256), 2), (dict(D=0), 1), (dict(Hq=40, Hkv=2), 2),
     (dict(wsb=16), 3),
     (dict(B=0, q=None, k=None, v=None, cu=None, out=None, ws=None), 0),   # empty batch: no-op
@@ -100,13 +101,13 @@ def test_mla_and_combine_reject_bad_arguments(zl):
 
     def mla(**kw):
         a = dict(q=A, c=A, cu=A, B=2, H=16, r=512, rope=64, maxL=10, scale=0.07, dt=1, out=A, lse=None,
-                 workers=0, ws=A, wsb=BIG, stream=None)
+                 workers=0, phases=3, ws=A, wsb=BIG, stream=None)
         a.update(kw)
         return lib.zl_decode_attn_mla_ex(a["q"], a["c"], a["cu"], a["B"], a["H"], a["r"], a["rope"],
                                          a["maxL"], a["scale"], a["dt"], a["out"], a["lse"], a["workers"],
-                                         a["ws"], a["wsb"], a["stream"])
+                                         a["phases"], a["ws"], a["wsb"], a["stream"])
     assert mla(r=256) == 2 and mla(rope=32) == 2 and mla(r=0) == 1
-    assert mla(H=0) == 1 and mla(H=24) == 2 and mla(q=None) == 1 and mla(wsb=8) == 3
+    assert mla(H=0) == 1 and mla(H=24) == 2 and mla(q=None) == 1 and mla(wsb=8) == 3 and mla(phases=7) == 1
     assert mla(B=0, q=None, c=None, cu=None, out=None, ws=None) == 0
 
     def comb(**kw):

@@ -165,16 +165,16 @@ def test_peaked_scores():
 
 
 def test_repeated_calls_reuse_workspace_and_are_bitwise_deterministic():
+    """Same inputs -> bitwise-identical output on every call; the workspace
+    (no initialisation needed) carries nothing between calls."""
     spec = workloads.with_shape(workloads.CONFIGS[3], batch=8, lens=("uniform", 100, 3000))
     x = workloads.make_inputs(spec, seed=31)
     B, H, D = x.q.shape
     ws = zl().new_workspace(zl().zl_decode_attn_workspace_size(B, H, 1, D, x.max_seqlen, x.q.dtype), DEV)
+    ws.fill_(0xAB)  # garbage in the workspace must not matter
     outs = [run_gpu(x, workspace=ws)[0].clone() for _ in range(5)]
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
-    # the counters are back at zero after every call
-    nctr = spec.batch * 1
-    assert int(ws[: 4 * nctr].view(torch.int32).abs().sum()) == 0
     ro, rl = run_oracle(x)
     gate(outs[0], ro, spec.torch_dtype, where="repeat")
     # a different batch through the same workspace
