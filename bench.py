@@ -1,8 +1,9 @@
 """Decode-attention benchmark on one MI355X.
 
-One step = one call of the fused decode attention for the whole batch (the
-split-KV work and the log-sum-exp combine both run inside the one kernel
-launch), on synthetic inputs already resident in HBM.  Inputs are replicated
+One step = one call of the fused decode attention for the whole batch: the
+decode kernel (every K/V byte streamed once, split evenly over the workers)
+then the split-merge kernel (log-sum-exp combine of the sequences that several
+workers share), on synthetic inputs already resident in HBM.  Inputs are replicated
 R = max(2, ceil(1 GiB / bytes)) times and the steps cycle through the
 replicas, so the 256 MB Infinity Cache cannot serve a step from the previous
 one.
