@@ -33,7 +33,8 @@
  *    asynchronous: nothing synchronises, nothing is allocated.  A decode call
  *    enqueues two kernels: the decode kernel, which splits the batch evenly
  *    over its workers and leaves fp32 partials for sequences that several
- *    workers share, and the merge kernel, which combines those partials.
+ *    workers share, and the merge kernel, which combines those partials and
+ *    writes the results of empty sequences.
  *  - Host-checkable arguments are validated before any HIP call; a bad argument
  *    returns an error status and enqueues nothing.  Device contents (the values
  *    in cu_seqlens) are preconditions: cu[0] = 0, non-decreasing, every length

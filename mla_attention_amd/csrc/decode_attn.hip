@@ -13,9 +13,9 @@
 //  * Data path: 32-token tiles go HBM -> LDS with 16-byte global_load_lds
 //    (no VGPR round trip), each 16-lane group reading contiguous bytes of one
 //    row.  STAGES tiles form an LDS ring, STAGES-1 of them in flight while the
-//    oldest is consumed.  16-byte slots are XOR-swizzled per row so that the
-//    MFMA operand reads (16 rows, one slot) and the transposing V reads (4 rows,
-//    two slots) fall in distinct banks.
+//    oldest is consumed.  16-byte slots are XOR-swizzled per row so that both
+//    the MFMA operand reads and the transposing V reads are free of bank
+//    conflicts (the LDS bank rules are in zl_tile.h).
 //  * QK^T: v_mfma_f32_16x16x32 with the K tile as A (16 tokens x 32 dims) and
 //    the unit's query heads as B (32 dims x 16 heads, zero-padded when fewer).
 //    Result lane (g, n) = 16g + n: head n, tokens 4g..4g+3 (and +16).
@@ -44,8 +44,9 @@ struct Geo<kGqaD64> {
   static constexpr int STAGES = 3;
   static constexpr int WAVES_PER_CU = 6;
   static constexpr int MAX_WAVES_PER_SIMD = 2;
-  // 128-byte rows: two rows per 256-byte bank line.
-  __device__ static int slot(int c, int r) { return c ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1)); }
+  // 128-byte rows: two rows per 256-byte bank line, so row parity already
+  // separates the two halves of the bank line; XOR the 8 slots with r / 2.
+  __device__ static int slot(int c, int r) { return c ^ ((r >> 1) & 7); }
 };
 
 template <>
@@ -55,8 +56,8 @@ struct Geo<kGqaD128> {
   static constexpr int STAGES = 3;
   static constexpr int WAVES_PER_CU = 3;
   static constexpr int MAX_WAVES_PER_SIMD = 1;
-  // 256-byte rows: XOR over all 16 slots.
-  __device__ static int slot(int c, int r) { return c ^ (((r << 1) & 15) | ((r >> 3) & 1)); }
+  // 256-byte rows, one bank line each: XOR the 16 slots with the row.
+  __device__ static int slot(int c, int r) { return c ^ (r & 15); }
 };
 
 template <int L>
@@ -137,45 +138,59 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
   const long long v_row = GE::SHARED_KV ? (long long)DK : (long long)a.Hkv * DV;
   const auto slot = [](int c, int r) { return GE::slot(c, r); };
 
-  // Empty sequences: out = 0, lse = -inf (no worker run covers them).
-  for (int idx = w; idx < B * U; idx += a.P) {
-    const int b = idx / U, u = idx - (idx / U) * U;
-    if (cu[b + 1] - cu[b] != 0) continue;
-    const int kvh = u / a.HB, hb = u - (u / a.HB) * a.HB;
-    const int h0 = kvh * a.G + hb * kHeadsPerUnit;
-    const int nh = min(kHeadsPerUnit, a.G - hb * kHeadsPerUnit);
-    for (int e = lane; e < nh * DV; e += 64) a.out[((long long)b * a.Hq + h0) * DV + e] = 0;
-    if (a.lse && lane < nh) a.lse[(long long)b * a.Hq + h0 + lane] = -INFINITY;
-  }
-
+  // (Empty sequences are written by the merge launch: no run covers them.)
   const int T = cu[B];
+  // Sequence boundaries for the lookups below, loaded alongside T (one round
+  // trip for both) and waited for here, so that no later lookup has to drain
+  // the tile loads in flight.
+  int window = bounds_window(cu, B);
+  asm volatile("" : "+v"(window));
   const long long N = (long long)U * T;
   const long long per = positions_per_worker(N, a.P);
   long long p = (long long)w * per;
   const long long p_end = N < p + per ? N : p + per;
 
-
   while (p < p_end) {
     // ---- segment: tokens [t0, t1) of sequence b, work unit u
     const int u = (int)(p / T);
     const int t0 = (int)(p - (long long)u * T);
-    const int b = seq_of_token(cu, B, t0);
-    const int cs = cu[b], ce = cu[b + 1];
     const long long rem = p_end - p;
+    // Tokens of unit u left in this worker's run: the segment is a prefix.
+    const int avail = (long long)(T - t0) < rem ? T - t0 : (int)rem;
+    const int kvh = u / a.HB, hb = u - (u / a.HB) * a.HB;
+    const uint16_t* kbase = a.k + (long long)kvh * DK;
+    const uint16_t* vbase = a.v + (long long)kvh * DV;
+
+    // Prologue: STAGES-1 tiles, requested before the sequence lookup (K/V
+    // rows depend only on unit and token).  They are clamped to the run, not
+    // to the segment: rows past the segment hold other tokens of the run and
+    // are masked out of the softmax.  A run shorter than the prologue
+    // re-reads its first tile into the unused stages, so the number of loads
+    // in flight never depends on lengths.
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) {
+      ZL_LDS char* st = smem + s * TL::STAGE_BYTES;
+      const bool real = 32 * s < avail;
+      const int tok = real ? t0 + 32 * s : t0;
+      const int nv = real ? min(32, avail - 32 * s) : min(32, avail);
+      dma_tile<L, TL::KCPR, TL::NI_K>(kbase, k_row, tok, nv, st, lane);
+      if constexpr (!GE::SHARED_KV)
+        dma_tile<L, TL::VCPR, TL::NI_V>(vbase, v_row, tok, nv, st + TL::KBYTES, lane);
+    }
+
+    const SeqSpan sq = find_seq(cu, B, t0, window);
+    const int b = sq.b, cs = sq.cs, ce = sq.ce;
     const int t1 = (long long)(ce - t0) < rem ? ce : (int)(t0 + rem);
     const int len = t1 - t0;
     const long long seq_p0 = (long long)u * T + cs;
     const long long seq_p1 = (long long)u * T + ce;
     const int w_first = (int)(seq_p0 / per);
     const int w_last = (int)((seq_p1 - 1) / per);
-    const int kvh = u / a.HB, hb = u - (u / a.HB) * a.HB;
     const int h0 = kvh * a.G + hb * kHeadsPerUnit;
     const int nh = min(kHeadsPerUnit, a.G - hb * kHeadsPerUnit);
-    const uint16_t* kbase = a.k + (long long)kvh * DK;
-    const uint16_t* vbase = a.v + (long long)kvh * DV;
     const int ntiles = (len + 31) >> 5;
 
-    // Query rows h0 .. h0+15 into LDS with the first tiles (padding heads
+    // Query rows h0 .. h0+15 into LDS after the prologue tiles (padding heads
     // repeat head h0; their results are never stored).  Slot-swizzled like a
     // K row so the operand read below is conflict-free.
     {
@@ -189,19 +204,6 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
         dma16(qb + (long long)(r < nh ? r : 0) * DK + c * 8, qlds + i * 1024);
       }
     }
-    // Prologue: always STAGES-1 tiles, so the number of loads in flight does
-    // not depend on the segment length (a segment shorter than the prologue
-    // re-reads its first tile into the unused stage).
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) {
-      ZL_LDS char* st = smem + s * TL::STAGE_BYTES;
-      const bool real = s < ntiles;
-      const int tok = real ? t0 + 32 * s : t0;
-      const int nv = real ? min(32, len - 32 * s) : min(32, len);
-      dma_tile<L, TL::KCPR, TL::NI_K>(kbase, k_row, tok, nv, st, lane);
-      if constexpr (!GE::SHARED_KV)
-        dma_tile<L, TL::VCPR, TL::NI_V>(vbase, v_row, tok, nv, st + TL::KBYTES, lane);
-    }
 
     f32x4 o[TL::VBLK];
 #pragma unroll
@@ -211,6 +213,14 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
 
     for (int j = 0; j < ntiles; ++j) {
       const int ahead = j + STAGES - 1;
+      if (j == 0) {
+        // The query rows were requested last: wait for everything, then
+        // refill.  B operand: lane (g, n) = head n, dims 32kb + 8g .. +7.
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int kb = 0; kb < TL::KSTEPS; ++kb)
+          qop[kb] = __builtin_bit_cast(i16x8, lds_read_b128(qlds + n * TL::KROWB + (slot(4 * kb + g, n) << 4)));
+      }
       if (ahead < ntiles) {
         ZL_LDS char* st = smem + (ahead % STAGES) * TL::STAGE_BYTES;
         const int nv = min(32, len - 32 * ahead);
@@ -218,13 +228,7 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
         if constexpr (!GE::SHARED_KV)
           dma_tile<L, TL::VCPR, TL::NI_V>(vbase, v_row, t0 + 32 * ahead, nv, st + TL::KBYTES, lane);
       }
-      wait_tiles_after<TL::PER_TILE, STAGES>(min(STAGES - 1, ntiles - 1 - j));
-      if (j == 0) {
-        // B operand: lane (g, n) = head n, dims 32kb + 8g .. +7
-#pragma unroll
-        for (int kb = 0; kb < TL::KSTEPS; ++kb)
-          qop[kb] = __builtin_bit_cast(i16x8, lds_read_b128(qlds + n * TL::KROWB + (slot(4 * kb + g, n) << 4)));
-      }
+      if (j > 0) wait_tiles_after<TL::PER_TILE, STAGES>(min(STAGES - 1, ntiles - 1 - j));
 
       const ZL_LDS char* kt = smem + (j % STAGES) * TL::STAGE_BYTES;
       const ZL_LDS char* vt = GE::SHARED_KV ? kt : kt + TL::KBYTES;

@@ -15,15 +15,23 @@
 //    number of 32 KB fp32 partials (one per split point) small; the split
 //    sequences are merged by split_merge.hip.
 //  * A 32-token tile is 36 KB of contiguous HBM.  The four waves DMA a quarter
-//    each (9 x 1 KB global_load_lds); a three-stage LDS ring keeps two tiles in
-//    flight while one is used, with a single barrier per tile.  The unit's 16
-//    query rows (18 KB) arrive by DMA with the first tiles of each segment.
-//    Slots are XOR-swizzled within groups of 8 (rows are 72 slots long).
-//  * QK^T: every wave computes the full 32 x 16 score tile (18 MFMA k-steps per
-//    16 tokens).  The duplicate work is cheap next to the memory time and keeps
-//    the waves free of score exchanges; the softmax is identical in all waves.
+//    each (9 x 1 KB global_load_lds); a four-stage LDS ring keeps three tiles in
+//    flight while one is used.  The unit's 16 query rows (18 KB) arrive by DMA
+//    into the last ring stage right after the first tiles of each segment and
+//    are moved to registers before that stage is refilled.  Slots are XOR-swizzled
+//    within groups of 8 (rows are 72 slots long).
+//  * QK^T is split over the waves: wave w computes the 16 x 16 score block of
+//    tokens 16(w % 2) .. +15 over k-steps 9(w / 2) .. +8 (half of the 576
+//    dims), leaves it in a 4 KB exchange area of LDS, and after a barrier every
+//    wave adds the two halves of both token blocks.  Each wave thus does a
+//    quarter of the QK^T work and reads a quarter of the tile for it; the
+//    softmax is computed identically in all waves.
 //  * PV: wave w accumulates output dims [128w, 128w + 128) as O^T = V^T P^T with
 //    V^T read transposed from the tile (ds_read_b64_tr_b16).
+//  * Two barriers per tile: one when the tile has landed (and every wave is done
+//    with the previous one), one when the score halves are in LDS.  The refill
+//    of the freed stage is issued after the second, which also orders it after
+//    the reads of the query rows at the first tile of a segment.
 #include "zl_device.h"
 #include "zl_kernels.h"
 #include "zl_split.h"
@@ -43,30 +51,57 @@ constexpr int kWaves = 4;
 constexpr int kNI = kTileB / 1024;               // 36 DMA instructions per tile
 constexpr int kNIw = kNI / kWaves;               // 9 per wave
 constexpr int kNIq = kQB / 1024;                 // 18 for the query rows
-constexpr int kStages = 3;
+constexpr int kStages = 4;
 constexpr int kKSteps = kDK / 32;                // 18
+constexpr int kKHalf = kKSteps / 2;              // 9 k-steps per wave
 constexpr int kBlkPerWave = kDV / 16 / kWaves;   // 8 output blocks of 16 dims
-constexpr int kWorkgroupsPerCU = 1;              // 3 x 36 KB + 18 KB of LDS
-constexpr int kLdsBytes = kStages * kTileB + kQB;
+constexpr int kWorkgroupsPerCU = 1;
+constexpr int kXchgB = kWaves * 1024;            // one f32x4 per lane per wave
+constexpr int kLdsBytes = kStages * kTileB + kXchgB;  // 148 KB of the 160 KB
+static_assert(kQB <= kTileB, "query rows fit one ring stage");
 
-// XOR inside each group of 8 slots; for 64 banks this keeps the 16 rows of an
-// operand read and the 4 rows of a transposing read in distinct banks.
-__device__ __forceinline__ int slot(int c, int r) {
-  return (c & ~7) | ((c & 7) ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1)));
-}
+// A 1152-byte row starts half a bank line (8 slots) after the previous one, so
+// row parity separates bank-line halves; XOR inside each group of 8 slots with
+// r / 2 makes the operand and transposing reads conflict-free (zl_tile.h).
+__device__ __forceinline__ int slot(int c, int r) { return (c & ~7) | ((c & 7) ^ ((r >> 1) & 7)); }
 
-// This wave's quarter of a tile: 1 KB instruction i covers slots 64i .. 64i+63
-// of the row-major tile; rows past the segment are clamped to its last row.
-__device__ __forceinline__ void dma_quarter(const uint16_t* c, int tok0, int nvalid, ZL_LDS char* dst,
-                                            int wave, int lane) {
+// This wave's quarter of a tile: 1 KB instruction k of wave w covers slots
+// 64(9w + k) .. +63 of the row-major tile, lane l loading row r = lin / 72
+// and chunk slot(lin % 72, r).  These per-lane byte offsets are the same for
+// every tile, so they are computed once; a tile then costs one scalar base
+// (its first token's row) plus one 32-bit offset per instruction.
+struct QuarterMap {
+  uint32_t off[kNIw];  // r * 1152 + 16 * chunk
+  int row[kNIw];       // r
+};
+
+__device__ __forceinline__ QuarterMap quarter_map(int wave, int lane) {
+  QuarterMap m;
 #pragma unroll
   for (int k = 0; k < kNIw; ++k) {
-    const int i = wave * kNIw + k;
-    const int lin = 64 * i + lane;
+    const int lin = 64 * (wave * kNIw + k) + lane;
     const int r = lin / kCPR;
-    const int s = lin - r * kCPR;
-    const int rr = r < nvalid ? r : nvalid - 1;
-    dma16(c + (long long)(tok0 + rr) * kDK + slot(s, r) * 8, dst + i * 1024);
+    m.row[k] = r;
+    m.off[k] = (uint32_t)(r * kRowB + 16 * slot(lin - r * kCPR, r));
+  }
+  return m;
+}
+
+// Rows past nvalid (< 32 only for a segment's last tile or a short run) are
+// clamped to row nvalid - 1: finite data, masked out of the softmax.
+__device__ __forceinline__ void dma_quarter(const uint16_t* rows, int tok0, int nvalid, const QuarterMap& m,
+                                            ZL_LDS char* dst, int wave) {
+  const char* base = (const char*)rows + (size_t)tok0 * kRowB;
+  if (nvalid >= 32) {
+#pragma unroll
+    for (int k = 0; k < kNIw; ++k) dma16(base + m.off[k], dst + (wave * kNIw + k) * 1024);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kNIw; ++k) {
+      const int over = m.row[k] - (nvalid - 1);
+      const uint32_t off = m.off[k] - (over > 0 ? (uint32_t)(over * kRowB) : 0u);
+      dma16(base + off, dst + (wave * kNIw + k) * 1024);
+    }
   }
 }
 
@@ -88,49 +123,82 @@ __device__ __forceinline__ void dma_query(const uint16_t* qb, int nh, ZL_LDS cha
 
 }  // namespace
 
+// Partial scores of one 16-token block over half of the k-steps:
+// lane (g, n) gets tokens 16tb + 4g .. +3 of head n, summed over dims
+// [288kh, 288kh + 288).  Two accumulators halve the MFMA dependency chain.
+template <int DT>
+__device__ __forceinline__ f32x4 half_scores(const ZL_LDS char* kt, const i16x8 (&qop)[kKHalf], int tb,
+                                             int kh, int n, int g) {
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  const int t = 16 * tb + n;
+#pragma unroll
+  for (int kb = 0; kb < kKHalf; ++kb) {
+    const int c = 4 * (kKHalf * kh + kb) + g;
+    const u32x4 av = lds_read_b128(kt + t * kRowB + (slot(c, t) << 4));
+    if (kb & 1)
+      acc1 = mfma16x16x32<DT>(__builtin_bit_cast(i16x8, av), qop[kb], acc1);
+    else
+      acc0 = mfma16x16x32<DT>(__builtin_bit_cast(i16x8, av), qop[kb], acc0);
+  }
+  return acc0 + acc1;
+}
+
 template <int DT>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kWaves, 64 * kWaves),
                           amdgpu_waves_per_eu(1, 1))) void
 mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
-  // One LDS object only (see decode_attn.hip): [3 tiles][query rows].
+  // One LDS object only (see decode_attn.hip): [4 tiles][score exchange].
   __shared__ __attribute__((aligned(1024))) char smem_raw[kLdsBytes];
   ZL_LDS char* smem = (ZL_LDS char*)smem_raw;
-  ZL_LDS char* qlds = smem + kStages * kTileB;
+  ZL_LDS char* qlds = smem + (kStages - 1) * kTileB;  // query rows: last stage
+  ZL_LDS char* xchg = smem + kStages * kTileB;
 
   const int tid = threadIdx.x;
   const int wave = readfirstlane(tid >> 6);  // wave-uniform (scalar) index
   const int lane = tid & 63;
   const int n = lane & 15;
   const int g = lane >> 4;
+  const int tb_own = wave & 1;   // token block of this wave's score half
+  const int kh_own = wave >> 1;  // k-step half of this wave's score half
   const int w = worker_id(blockIdx.x, a.P);
   const int B = a.B;
   const int U = a.HB;
   const int dim0 = wave * (kDV / kWaves) + 4 * g;
   const auto slot_fn = [](int c, int r) { return slot(c, r); };
+  const QuarterMap qmap = quarter_map(wave, lane);
 
-  // Empty sequences: out = 0, lse = -inf (no worker run covers them).
-  for (int idx = w; idx < B * U; idx += a.P) {
-    const int b = idx / U, hb = idx - (idx / U) * U;
-    if (cu[b + 1] - cu[b] != 0) continue;
-    const int h0 = hb * kHeadsPerUnit;
-    const int nh = min(kHeadsPerUnit, a.G - h0);
-    for (int e = tid; e < nh * kDV; e += 64 * kWaves) a.out[((long long)b * a.Hq + h0) * kDV + e] = 0;
-    if (a.lse && tid < nh) a.lse[(long long)b * a.Hq + h0 + tid] = -INFINITY;
-  }
-
+  // (Empty sequences are written by the merge launch: no run covers them.)
   const int T = cu[B];
+  // Sequence boundaries for the lookups below, loaded alongside T (one round
+  // trip for both) and waited for here, so that no later lookup has to drain
+  // the tile loads in flight.
+  int window = bounds_window(cu, B);
+  asm volatile("" : "+v"(window));
   const long long N = (long long)U * T;
   const long long per = positions_per_worker(N, a.P);
   long long p = (long long)w * per;
   const long long p_end = N < p + per ? N : p + per;
 
-
   while (p < p_end) {
     const int u = (int)(p / T);
     const int t0 = (int)(p - (long long)u * T);
-    const int b = seq_of_token(cu, B, t0);
-    const int cs = cu[b], ce = cu[b + 1];
     const long long rem = p_end - p;
+    // Tokens of unit u left in this worker's run: the segment is a prefix.
+    const int avail = (long long)(T - t0) < rem ? T - t0 : (int)rem;
+
+    barrier_lds();  // every wave is done with the LDS of the previous segment
+    // Prologue before the sequence lookup (rows depend only on the token);
+    // clamped to the run, rows past the segment are masked.  A run shorter
+    // than the prologue re-reads its first tile into the unused stages.
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s) {
+      const bool real = 32 * s < avail;
+      dma_quarter(a.k, real ? t0 + 32 * s : t0, real ? min(32, avail - 32 * s) : min(32, avail), qmap,
+                  smem + s * kTileB, wave);
+    }
+
+    const SeqSpan sq = find_seq(cu, B, t0, window);
+    const int b = sq.b, cs = sq.cs, ce = sq.ce;
     const int t1 = (long long)(ce - t0) < rem ? ce : (int)(t0 + rem);
     const int len = t1 - t0;
     const long long seq_p0 = (long long)u * T + cs;
@@ -140,42 +208,47 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
     const int h0 = u * kHeadsPerUnit;
     const int nh = min(kHeadsPerUnit, a.G - h0);
     const int ntiles = (len + 31) >> 5;
-
-    barrier_lds();  // every wave is done with the LDS of the previous segment
     dma_query(a.q + ((long long)b * a.Hq + h0) * kDK, nh, qlds, wave, lane);
-#pragma unroll
-    for (int s = 0; s < kStages - 1; ++s) {
-      const bool real = s < ntiles;
-      dma_quarter(a.k, real ? t0 + 32 * s : t0, real ? min(32, len - 32 * s) : min(32, len),
-                  smem + s * kTileB, wave, lane);
-    }
 
     f32x4 o[kBlkPerWave];
 #pragma unroll
     for (int i = 0; i < kBlkPerWave; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     SoftmaxState sm{-INFINITY, 0.f};
-    i16x8 qop[kKSteps];
+    i16x8 qop[kKHalf];
 
     for (int j = 0; j < ntiles; ++j) {
-      // This wave's share of tile j; tile j+1 (issued before) may still fly.
-      if (j + 1 < ntiles)
+      // This wave's share of tile j; the real tiles issued after it may fly.
+      // At the first tile the query rows, requested last, are waited for too.
+      if (j == 0)
+        wait_vmcnt<0>();
+      else if (j + 2 < ntiles)
+        wait_vmcnt<2 * kNIw>();
+      else if (j + 1 < ntiles)
         wait_vmcnt<kNIw>();
       else
         wait_vmcnt<0>();
       barrier_lds();  // tile j complete in LDS, and every wave is past tile j-1
-      if (j + kStages - 1 < ntiles) {
-        const int jn = j + kStages - 1;
-        dma_quarter(a.k, t0 + 32 * jn, min(32, len - 32 * jn), smem + (jn % kStages) * kTileB, wave,
-                    lane);
-      }
       if (j == 0) {
 #pragma unroll
-        for (int kb = 0; kb < kKSteps; ++kb)
-          qop[kb] = __builtin_bit_cast(i16x8, lds_read_b128(qlds + n * kRowB + (slot(4 * kb + g, n) << 4)));
+        for (int kb = 0; kb < kKHalf; ++kb) {
+          const int c = 4 * (kKHalf * kh_own + kb) + g;
+          qop[kb] = __builtin_bit_cast(i16x8, lds_read_b128(qlds + n * kRowB + (slot(c, n) << 4)));
+        }
       }
       const ZL_LDS char* kt = smem + (j % kStages) * kTileB;
+      const f32x4 part = half_scores<DT>(kt, qop, tb_own, kh_own, n, g);
+      *(ZL_LDS f32x4*)(xchg + wave * 1024 + lane * 16) = part;
+      barrier_lds();  // all score halves in LDS; query rows read
+      if (j + kStages - 1 < ntiles) {
+        const int jn = j + kStages - 1;
+        dma_quarter(a.k, t0 + 32 * jn, min(32, len - 32 * jn), qmap, smem + (jn % kStages) * kTileB, wave);
+      }
+      // Waves 0 and 2 hold the halves of token block 0, waves 1 and 3 block 1.
       f32x4 s[2];
-      scores<DT, kKSteps, kRowB>(kt, qop, n, g, slot_fn, s);
+      s[0] = *(const ZL_LDS f32x4*)(xchg + 0 * 1024 + lane * 16) +
+             *(const ZL_LDS f32x4*)(xchg + 2 * 1024 + lane * 16);
+      s[1] = *(const ZL_LDS f32x4*)(xchg + 1 * 1024 + lane * 16) +
+             *(const ZL_LDS f32x4*)(xchg + 3 * 1024 + lane * 16);
       float alpha;
       const POperand pop = softmax_update<DT>(s, g, min(32, len - 32 * j), a.scale_log2, sm, alpha);
 #pragma unroll

@@ -11,7 +11,8 @@
 // One thread per (unit, sequence, head, 4-float column): all split sequences
 // are merged at once across the whole GPU, in about one memory round trip per
 // four partials.  Sequences that one worker covered alone were already
-// written by the decode kernel; their threads return at once.  The partials
+// written by the decode kernel; their threads return at once.  Empty
+// sequences, which no worker covers, get out = 0 and lse = -inf here.  The partials
 // are visible here because kernels on one stream are ordered and caches are
 // written back / invalidated between launches.
 #include "zl_device.h"
@@ -37,8 +38,14 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a, const in
   const int kvh = u / a.HB, hb = u - (u / a.HB) * a.HB;
   const int nh = min(kHeadsPerUnit, a.G - hb * kHeadsPerUnit);
   if (h >= nh) return;
+  const int h0 = kvh * a.G + hb * kHeadsPerUnit;
   const int cs = cu[b], ce = cu[b + 1];
-  if (ce == cs) return;
+  if (ce == cs) {
+    // An empty sequence (no worker run covers it): out = 0, lse = -inf.
+    *(u32x2*)(a.out + ((long long)b * a.Hq + h0 + h) * DV + 4 * c4) = u32x2{0u, 0u};
+    if (a.lse && c4 == 0) a.lse[(long long)b * a.Hq + h0 + h] = -INFINITY;
+    return;
+  }
   const int T = cu[a.B];
   const long long per = positions_per_worker((long long)U * T, a.P);
   const long long seq_p0 = (long long)u * T + cs;
@@ -76,7 +83,6 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a, const in
     }
     M = m_new;
   }
-  const int h0 = kvh * a.G + hb * kHeadsPerUnit;
   const float winv = wsum > 0.f ? 1.f / wsum : 0.f;
   store_out4<DT>(a.out + ((long long)b * a.Hq + h0 + h) * DV + 4 * c4, acc, winv);
   if (a.lse && c4 == 0) a.lse[(long long)b * a.Hq + h0 + h] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;

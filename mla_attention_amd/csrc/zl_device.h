@@ -60,21 +60,48 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 // Hardware 2^x (v_exp_f32); 2^-inf = 0.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Cross-lane exchange by xor of the lane id (16 and 32 cross the 16-lane groups).
+// Value of lane (lane ^ mask) (a general exchange through the LDS crossbar).
 __device__ __forceinline__ float shfl_xor(float x, int mask) {
-  int lane = __lane_id();
-  int v = __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __builtin_bit_cast(int, x));
+  const int lane = __lane_id();
+  const int v = __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __builtin_bit_cast(int, x));
   return __builtin_bit_cast(float, v);
 }
 
+// Reductions over the four 16-lane groups (lanes n, n+16, n+32, n+48) with
+// the gfx950 lane-swap instructions, entirely in the VALU (no LDS round
+// trip).  Given two registers that both hold x, v_permlane16_swap leaves the
+// values of lanes l and l^16 in lane l of the two registers (one in each);
+// v_permlane32_swap does the same for l and l^32.  Every lane of a head gets
+// the bitwise same result (each stage combines the same two values, and max
+// and + commute).  The swaps are written as inline asm: the compiler's
+// builtin returns the pair, and when both halves feed one expression it has
+// been seen to use the first half twice.  s_nop 1 gives the two wait states
+// a lane swap needs after a VALU write of its operands.
+__device__ __forceinline__ void lane_swap16(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void lane_swap32(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
 __device__ __forceinline__ float max_over_groups(float x) {
-  x = fmaxf(x, shfl_xor(x, 16));
-  return fmaxf(x, shfl_xor(x, 32));
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  lane_swap16(a, b);
+  x = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  a = __builtin_bit_cast(uint32_t, x);
+  b = a;
+  lane_swap32(a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 
 __device__ __forceinline__ float sum_over_groups(float x) {
-  x += shfl_xor(x, 16);
-  return x + shfl_xor(x, 32);
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  lane_swap16(a, b);
+  x = __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+  a = __builtin_bit_cast(uint32_t, x);
+  b = a;
+  lane_swap32(a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 
 // 16 bytes from global memory straight into LDS: lane i's bytes land at

@@ -26,17 +26,52 @@ __device__ __forceinline__ long long positions_per_worker(long long N, int P) {
 }
 
 // Largest b in [0, B) with cu[b] <= t; for 0 <= t < cu[B] this is the
-// sequence that owns token t (empty sequences are stepped over).
+// sequence that owns token t (empty sequences are stepped over).  Because cu
+// is non-decreasing with cu[0] = 0, it equals the number of b in [1, B) with
+// cu[b] <= t.  The lanes of the wave load cu 64 entries at a time and count
+// with a ballot, so a batch of up to 64 sequences costs one memory round trip
+// instead of the log2(B) dependent loads of a bisection.  Call from
+// wave-uniform control flow with all 64 lanes active.
 __device__ __forceinline__ int seq_of_token(const int32_t* cu, int B, int t) {
-  int lo = 0, hi = B;
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (cu[mid] <= t)
-      lo = mid;
-    else
-      hi = mid;
+  const int lane = __lane_id();
+  int count = 0;
+  for (int i0 = 1; i0 < B; i0 += 64) {
+    const int i = i0 + lane;
+    const bool le = i < B && cu[i] <= t;
+    count += __popcll(__ballot(le));
   }
-  return lo;
+  return __builtin_amdgcn_readfirstlane(count);
+}
+
+// Lane l holds cu[1 + l] (INT_MAX past cu[B]): the boundaries of a batch of
+// up to 64 sequences in one vector load.  Issue it before a segment's
+// prologue DMA: its use then waits only for itself, not for the tiles.
+__device__ __forceinline__ int bounds_window(const int32_t* cu, int B) {
+  const int i = 1 + __lane_id();
+  const int v = cu[i < B ? i : B];  // unpredicated load (a branch here would
+                                    // make the compiler's wait drain the DMA)
+  return i <= B ? v : 0x7fffffff;
+}
+
+struct SeqSpan {
+  int b;       // sequence owning the token
+  int cs, ce;  // cu[b], cu[b + 1]
+};
+
+// The sequence owning token t (0 <= t < cu[B]) and its bounds: from the
+// window when B <= 64 (a ballot and two lane reads), else by the search above.
+__device__ __forceinline__ SeqSpan find_seq(const int32_t* cu, int B, int t, int window) {
+  SeqSpan r;
+  if (B <= 64) {
+    r.b = __popcll(__ballot(window <= t));
+    r.ce = __builtin_amdgcn_readlane(window, r.b);
+    r.cs = r.b == 0 ? 0 : __builtin_amdgcn_readlane(window, r.b - 1);
+  } else {
+    r.b = seq_of_token(cu, B, t);
+    r.cs = cu[r.b];
+    r.ce = cu[r.b + 1];
+  }
+  return r;
 }
 
 // Slot of worker w's partial for the sequence occupying positions

@@ -7,6 +7,17 @@
 // layout, and reused unchanged as the PV contraction order:
 //   score register r of 16-token block tb in lane (g, n) = token 16tb + 4g + r
 //   PV k-slot 8g + i                                  = token 16(i/4) + 4g + i%4
+//
+// LDS banks (gfx950, measured with the SQ_LDS_BANK_CONFLICT counter): 64
+// banks of 4 bytes, i.e. 16 groups of 16 bytes per 256-byte line.
+//  * ds_read_b128 serves a wave in four passes of 16 lanes: the lanes of one
+//    half-wave whose lane-index bits 2, 3 and 4 have the same parity.  A pass
+//    costs one cycle per lane that shares a 16-byte bank group with another.
+//    For the operand reads below (lane (g, n) reads row n, slot 4kb + g) a pass
+//    holds g = 2h with 8 rows and g = 2h + 1 with the other 8, so the swizzle
+//    must map those 16 (row, slot) pairs to 16 different bank groups.
+//  * ds_read_b64_tr_b16 serves all 64 lanes in two cycles and is free of
+//    conflicts when no bank is hit more than twice.
 #pragma once
 
 #include "zl_device.h"
