@@ -12,8 +12,9 @@
 //    between workers are merged by split_merge.hip, launched right after.
 //  * Data path: 32-token tiles go HBM -> LDS with 16-byte global_load_lds
 //    (no VGPR round trip), each 16-lane group reading contiguous bytes of one
-//    row.  STAGES tiles form an LDS ring, STAGES-1 of them in flight while the
-//    oldest is consumed.  16-byte slots are XOR-swizzled per row so that both
+//    row.  The worker's run is one stream of items through a STAGES-deep LDS
+//    ring (for each segment its query rows, then its tiles), STAGES-1 items
+//    in flight while the oldest is consumed, across segment boundaries.  16-byte slots are XOR-swizzled per row so that both
 //    the MFMA operand reads and the transposing V reads are free of bank
 //    conflicts (the LDS bank rules are in zl_tile.h).
 //  * QK^T: v_mfma_f32_16x16x32 with the K tile as A (16 tokens x 32 dims) and
@@ -97,18 +98,21 @@ __device__ __forceinline__ void dma_tile(const uint16_t* base, long long row_ele
   }
 }
 
-template <int PER_TILE, int STAGES>
-__device__ __forceinline__ void wait_tiles_after(int n_after) {
-  if constexpr (STAGES >= 3) {
-    if (n_after >= 2) {
-      wait_vmcnt<2 * PER_TILE>();
-      return;
-    }
+// The query item of a segment: rows h0 .. h0+15 (padding rows repeat h0; their
+// results are never stored) in the K-row slot layout, repeated to fill the
+// item's PER_TILE instructions so that every ring item costs the same.
+template <int L>
+__device__ __forceinline__ void dma_query_item(const uint16_t* qb, int nh, ZL_LDS char* dst, int lane) {
+  using TL = Tile<L>;
+  constexpr int QI = kHeadsPerUnit * TL::DK * 2 / 1024;  // 1 KB blocks of query rows
+  static_assert(TL::PER_TILE % QI == 0, "query copies fill the item");
+#pragma unroll
+  for (int i = 0; i < TL::PER_TILE; ++i) {
+    const int lin = 64 * (i % QI) + lane;
+    const int r = lin / TL::KCPR;
+    const int c = Geo<L>::slot(lin - r * TL::KCPR, r);
+    dma16(qb + (long long)(r < nh ? r : 0) * TL::DK + c * 8, dst + i * 1024);
   }
-  if (n_after >= 1)
-    wait_vmcnt<PER_TILE>();
-  else
-    wait_vmcnt<0>();
 }
 
 template <int L, int DT>
@@ -119,14 +123,11 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
   using GE = Geo<L>;
   constexpr int STAGES = GE::STAGES;
   constexpr int DK = TL::DK, DV = TL::DV;
-  constexpr int QBYTES = kHeadsPerUnit * DK * 2;  // the unit's query rows
-  static_assert(QBYTES % 1024 == 0, "query block must be whole DMA blocks");
-  // One LDS object: [STAGES K/V tiles][query rows].  (With a second
-  // __shared__ variable the compiler tracks DMA per object and makes every
-  // LDS read wait for all in-flight DMA.)
-  __shared__ __attribute__((aligned(1024))) char smem_raw[STAGES * TL::STAGE_BYTES + QBYTES];
+  // One LDS object: the ring.  (With a second __shared__ variable the
+  // compiler tracks DMA per object and makes every LDS read wait for all
+  // in-flight DMA.)
+  __shared__ __attribute__((aligned(1024))) char smem_raw[STAGES * TL::STAGE_BYTES];
   ZL_LDS char* smem = (ZL_LDS char*)smem_raw;
-  ZL_LDS char* qlds = smem + STAGES * TL::STAGE_BYTES;
 
   const int lane = __lane_id();
   const int n = lane & 15;
@@ -147,121 +148,122 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
   asm volatile("" : "+v"(window));
   const long long N = (long long)U * T;
   const long long per = positions_per_worker(N, a.P);
-  long long p = (long long)w * per;
-  const long long p_end = N < p + per ? N : p + per;
+  const long long p_begin = (long long)w * per;
+  const long long p_end = N < p_begin + per ? N : p_begin + per;
+  if (p_begin >= p_end) return;
 
-  while (p < p_end) {
-    // ---- segment: tokens [t0, t1) of sequence b, work unit u
-    const int u = (int)(p / T);
-    const int t0 = (int)(p - (long long)u * T);
-    const long long rem = p_end - p;
-    // Tokens of unit u left in this worker's run: the segment is a prefix.
-    const int avail = (long long)(T - t0) < rem ? T - t0 : (int)rem;
-    const int kvh = u / a.HB, hb = u - (u / a.HB) * a.HB;
-    const uint16_t* kbase = a.k + (long long)kvh * DK;
-    const uint16_t* vbase = a.v + (long long)kvh * DV;
-
-    // Prologue: STAGES-1 tiles, requested before the sequence lookup (K/V
-    // rows depend only on unit and token).  They are clamped to the run, not
-    // to the segment: rows past the segment hold other tokens of the run and
-    // are masked out of the softmax.  A run shorter than the prologue
-    // re-reads its first tile into the unused stages, so the number of loads
-    // in flight never depends on lengths.
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) {
-      ZL_LDS char* st = smem + s * TL::STAGE_BYTES;
-      const bool real = 32 * s < avail;
-      const int tok = real ? t0 + 32 * s : t0;
-      const int nv = real ? min(32, avail - 32 * s) : min(32, avail);
-      dma_tile<L, TL::KCPR, TL::NI_K>(kbase, k_row, tok, nv, st, lane);
+  // The run is one stream of ring items: for every segment (the part of one
+  // sequence of one work unit in the run) its query rows, then its 32-token
+  // K/V tiles.  Loads run STAGES-1 items ahead of the math, across segment
+  // boundaries, so a new segment does not drain the pipeline.
+  Segment ds = segment_at(p_begin, p_end, T, cu, B, window);
+  int dj = 0;  // next item of segment ds: 0 = query rows, 1 + k = tile k
+  bool dmore = true;
+  int issued = 0;
+  auto issue = [&]() {
+    ZL_LDS char* st = smem + (issued % STAGES) * TL::STAGE_BYTES;
+    const int ntl = (ds.len + 31) >> 5;
+    const int kvh = ds.u / a.HB, hb = ds.u - (ds.u / a.HB) * a.HB;
+    if (dj == 0) {
+      const int h0 = kvh * a.G + hb * kHeadsPerUnit;
+      const int nh = min(kHeadsPerUnit, a.G - hb * kHeadsPerUnit);
+      dma_query_item<L>(a.q + ((long long)ds.b * a.Hq + h0) * DK, nh, st, lane);
+    } else {
+      const int k = dj - 1;
+      const int tok = ds.t0 + 32 * k;
+      const int nv = min(32, ds.len - 32 * k);
+      dma_tile<L, TL::KCPR, TL::NI_K>(a.k + (long long)kvh * DK, k_row, tok, nv, st, lane);
       if constexpr (!GE::SHARED_KV)
-        dma_tile<L, TL::VCPR, TL::NI_V>(vbase, v_row, tok, nv, st + TL::KBYTES, lane);
+        dma_tile<L, TL::VCPR, TL::NI_V>(a.v + (long long)kvh * DV, v_row, tok, nv, st + TL::KBYTES, lane);
     }
-
-    const SeqSpan sq = find_seq(cu, B, t0, window);
-    const int b = sq.b, cs = sq.cs, ce = sq.ce;
-    const int t1 = (long long)(ce - t0) < rem ? ce : (int)(t0 + rem);
-    const int len = t1 - t0;
-    const long long seq_p0 = (long long)u * T + cs;
-    const long long seq_p1 = (long long)u * T + ce;
-    const int w_first = (int)(seq_p0 / per);
-    const int w_last = (int)((seq_p1 - 1) / per);
-    const int h0 = kvh * a.G + hb * kHeadsPerUnit;
-    const int nh = min(kHeadsPerUnit, a.G - hb * kHeadsPerUnit);
-    const int ntiles = (len + 31) >> 5;
-
-    // Query rows h0 .. h0+15 into LDS after the prologue tiles (padding heads
-    // repeat head h0; their results are never stored).  Slot-swizzled like a
-    // K row so the operand read below is conflict-free.
-    {
-      const uint16_t* qb = a.q + ((long long)b * a.Hq + h0) * DK;
-      constexpr int CPR = DK / 8;
-#pragma unroll
-      for (int i = 0; i < QBYTES / 1024; ++i) {
-        const int lin = 64 * i + lane;
-        const int r = lin / CPR;
-        const int c = slot(lin - r * CPR, r);
-        dma16(qb + (long long)(r < nh ? r : 0) * DK + c * 8, qlds + i * 1024);
-      }
-    }
-
-    f32x4 o[TL::VBLK];
-#pragma unroll
-    for (int i = 0; i < TL::VBLK; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    SoftmaxState sm{-INFINITY, 0.f};
-    i16x8 qop[TL::KSTEPS];
-
-    for (int j = 0; j < ntiles; ++j) {
-      const int ahead = j + STAGES - 1;
-      if (j == 0) {
-        // The query rows were requested last: wait for everything, then
-        // refill.  B operand: lane (g, n) = head n, dims 32kb + 8g .. +7.
-        wait_vmcnt<0>();
-#pragma unroll
-        for (int kb = 0; kb < TL::KSTEPS; ++kb)
-          qop[kb] = __builtin_bit_cast(i16x8, lds_read_b128(qlds + n * TL::KROWB + (slot(4 * kb + g, n) << 4)));
-      }
-      if (ahead < ntiles) {
-        ZL_LDS char* st = smem + (ahead % STAGES) * TL::STAGE_BYTES;
-        const int nv = min(32, len - 32 * ahead);
-        dma_tile<L, TL::KCPR, TL::NI_K>(kbase, k_row, t0 + 32 * ahead, nv, st, lane);
-        if constexpr (!GE::SHARED_KV)
-          dma_tile<L, TL::VCPR, TL::NI_V>(vbase, v_row, t0 + 32 * ahead, nv, st + TL::KBYTES, lane);
-      }
-      if (j > 0) wait_tiles_after<TL::PER_TILE, STAGES>(min(STAGES - 1, ntiles - 1 - j));
-
-      const ZL_LDS char* kt = smem + (j % STAGES) * TL::STAGE_BYTES;
-      const ZL_LDS char* vt = GE::SHARED_KV ? kt : kt + TL::KBYTES;
-      f32x4 s[2];
-      scores<DT, TL::KSTEPS, TL::KROWB>(kt, qop, n, g, slot, s);
-      float alpha;
-      const POperand pop = softmax_update<DT>(s, g, min(32, len - 32 * j), a.scale_log2, sm, alpha);
-#pragma unroll
-      for (int i = 0; i < TL::VBLK; ++i) o[i] *= alpha;
-      pv_blocks<DT, TL::VBLK, TL::VROWB>(vt, pop, n, g, 0, slot, o);
-    }
-
-    // ---- segment epilogue: lane (g, n) holds head n, dims 16blk + 4g .. +3.
-    // Stores only: nothing here waits, so the next segment starts at once.
-    // A split sequence leaves its partial for the merge launch.
-    const float l_tot = sum_over_groups(sm.l);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const float lse_v = l_tot > 0.f ? sm.m * kLn2 + __logf(l_tot) : -INFINITY;
-    if (n < nh) {
-      if (w_first == w_last) {
-        uint16_t* orow = a.out + ((long long)b * a.Hq + h0 + n) * DV + 4 * g;
-#pragma unroll
-        for (int blk = 0; blk < TL::VBLK; ++blk) store_out4<DT>(orow + 16 * blk, o[blk], inv);
-        if (a.lse && g == 0) a.lse[(long long)b * a.Hq + h0 + n] = lse_v;
+    ++issued;
+    if (++dj > ntl) {
+      const long long pn = ds.p + ds.len;
+      if (pn < p_end) {
+        ds = segment_at(pn, p_end, T, cu, B, window);
+        dj = 0;
       } else {
-        const int sl = partial_slot(w, per, seq_p0);
-        float* po = a.part_o + ((long long)sl * kHeadsPerUnit + n) * DV + 4 * g;
-#pragma unroll
-        for (int blk = 0; blk < TL::VBLK; ++blk) *(f32x4*)(po + 16 * blk) = o[blk] * inv;
-        if (g == 0) a.part_lse[sl * kLseSlot + n] = lse_v;
+        dmore = false;
       }
     }
-    p += len;
+  };
+  Segment sg = ds;  // the segment being computed
+  int cj = 0;       // its current item
+  for (int s = 0; s < STAGES - 1 && dmore; ++s) issue();
+
+  f32x4 o[TL::VBLK];
+  SoftmaxState sm{-INFINITY, 0.f};
+  i16x8 qop[TL::KSTEPS];
+
+  for (int i = 0;; ++i) {
+    // Refill the stage of item i-1 (consumed), then wait for item i: at most
+    // the items issued after it may still be in flight.
+    if (dmore) issue();
+    const int after = issued - i - 1;
+    if (after >= 2)
+      wait_vmcnt<2 * TL::PER_TILE>();
+    else if (after == 1)
+      wait_vmcnt<TL::PER_TILE>();
+    else
+      wait_vmcnt<0>();
+    const ZL_LDS char* st = smem + (i % STAGES) * TL::STAGE_BYTES;
+    const int ntl = (sg.len + 31) >> 5;
+    if (cj == 0) {
+      // Query item.  B operand: lane (g, n) = head n, dims 32kb + 8g .. +7.
+#pragma unroll
+      for (int kb = 0; kb < TL::KSTEPS; ++kb)
+        qop[kb] = __builtin_bit_cast(i16x8, lds_read_b128(st + n * TL::KROWB + (slot(4 * kb + g, n) << 4)));
+#pragma unroll
+      for (int bb = 0; bb < TL::VBLK; ++bb) o[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sm = SoftmaxState{-INFINITY, 0.f};
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // stage free for refill
+    } else {
+      const int j = cj - 1;
+      const ZL_LDS char* vt = GE::SHARED_KV ? st : st + TL::KBYTES;
+      f32x4 s[2];
+      scores<DT, TL::KSTEPS, TL::KROWB>(st, qop, n, g, slot, s);
+      float alpha;
+      const POperand pop = softmax_update<DT>(s, g, min(32, sg.len - 32 * j), a.scale_log2, sm, alpha);
+#pragma unroll
+      for (int bb = 0; bb < TL::VBLK; ++bb) o[bb] *= alpha;
+      pv_blocks<DT, TL::VBLK, TL::VROWB>(vt, pop, n, g, 0, slot, o);
+
+      if (j == ntl - 1) {
+        // ---- segment epilogue: lane (g, n) holds head n, dims 16blk + 4g .. +3.
+        // Stores only; the next items are already in flight.  A split
+        // sequence leaves its partial for the merge launch.
+        const long long seq_p0 = (long long)sg.u * T + sg.cs;
+        const long long seq_p1 = (long long)sg.u * T + sg.ce;
+        const int w_first = (int)(seq_p0 / per);
+        const int w_last = (int)((seq_p1 - 1) / per);
+        const int kvh = sg.u / a.HB, hb = sg.u - (sg.u / a.HB) * a.HB;
+        const int h0 = kvh * a.G + hb * kHeadsPerUnit;
+        const int nh = min(kHeadsPerUnit, a.G - hb * kHeadsPerUnit);
+        const float l_tot = sum_over_groups(sm.l);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const float lse_v = l_tot > 0.f ? sm.m * kLn2 + __logf(l_tot) : -INFINITY;
+        if (n < nh) {
+          if (w_first == w_last) {
+            uint16_t* orow = a.out + ((long long)sg.b * a.Hq + h0 + n) * DV + 4 * g;
+#pragma unroll
+            for (int blk = 0; blk < TL::VBLK; ++blk) store_out4<DT>(orow + 16 * blk, o[blk], inv);
+            if (a.lse && g == 0) a.lse[(long long)sg.b * a.Hq + h0 + n] = lse_v;
+          } else {
+            const int sl = partial_slot(w, per, seq_p0);
+            float* po = a.part_o + ((long long)sl * kHeadsPerUnit + n) * DV + 4 * g;
+#pragma unroll
+            for (int blk = 0; blk < TL::VBLK; ++blk) *(f32x4*)(po + 16 * blk) = o[blk] * inv;
+            if (g == 0) a.part_lse[sl * kLseSlot + n] = lse_v;
+          }
+        }
+      }
+    }
+    if (++cj > ntl) {
+      const long long pn = sg.p + sg.len;
+      if (pn >= p_end) break;
+      sg = segment_at(pn, p_end, T, cu, B, window);
+      cj = 0;
+    }
   }
 }
 

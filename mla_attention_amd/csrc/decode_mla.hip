@@ -14,12 +14,14 @@
 //    rows; see zl_split.h.  Fewer, larger workers than the GQA kernel keep the
 //    number of 32 KB fp32 partials (one per split point) small; the split
 //    sequences are merged by split_merge.hip.
-//  * A 32-token tile is 36 KB of contiguous HBM.  The four waves DMA a quarter
-//    each (9 x 1 KB global_load_lds); a four-stage LDS ring keeps three tiles in
-//    flight while one is used.  The unit's 16 query rows (18 KB) arrive by DMA
-//    into the last ring stage right after the first tiles of each segment and
-//    are moved to registers before that stage is refilled.  Slots are XOR-swizzled
-//    within groups of 8 (rows are 72 slots long).
+//  * A worker's run is one stream of items through a four-stage LDS ring: for
+//    each segment (the part of one sequence in the run) its query rows, then
+//    its 32-token tiles.  A tile is 36 KB of contiguous HBM; the four waves
+//    DMA a quarter each (9 x 1 KB global_load_lds) and the query item is
+//    loaded twice to cost the same.  Three items are in flight while one is
+//    used, across segment boundaries, so a new sequence does not drain the
+//    pipeline.  Slots are XOR-swizzled within groups of 8 (rows are 72 slots
+//    long).
 //  * QK^T is split over the waves: wave w computes the 16 x 16 score block of
 //    tokens 16(w % 2) .. +15 over k-steps 9(w / 2) .. +8 (half of the 576
 //    dims), leaves it in a 4 KB exchange area of LDS, and after a barrier every
@@ -28,10 +30,9 @@
 //    softmax is computed identically in all waves.
 //  * PV: wave w accumulates output dims [128w, 128w + 128) as O^T = V^T P^T with
 //    V^T read transposed from the tile (ds_read_b64_tr_b16).
-//  * Two barriers per tile: one when the tile has landed (and every wave is done
-//    with the previous one), one when the score halves are in LDS.  The refill
-//    of the freed stage is issued after the second, which also orders it after
-//    the reads of the query rows at the first tile of a segment.
+//  * Barriers: one per item when it has landed (every wave is then also done
+//    with the previous item, whose stage is refilled right after), and one per
+//    tile when the score halves are in LDS.
 #include "zl_device.h"
 #include "zl_kernels.h"
 #include "zl_split.h"
@@ -51,6 +52,7 @@ constexpr int kWaves = 4;
 constexpr int kNI = kTileB / 1024;               // 36 DMA instructions per tile
 constexpr int kNIw = kNI / kWaves;               // 9 per wave
 constexpr int kNIq = kQB / 1024;                 // 18 for the query rows
+static_assert(2 * kNIq == kNI, "a query item is two copies of the rows");
 constexpr int kStages = 4;
 constexpr int kKSteps = kDK / 32;                // 18
 constexpr int kKHalf = kKSteps / 2;              // 9 k-steps per wave
@@ -105,19 +107,18 @@ __device__ __forceinline__ void dma_quarter(const uint16_t* rows, int tok0, int 
   }
 }
 
-// Query rows h0 .. h0+15 (rows past nh repeat h0), same slot layout as a tile;
-// instruction i goes to wave i % 4.
-__device__ __forceinline__ void dma_query(const uint16_t* qb, int nh, ZL_LDS char* dst, int wave,
-                                          int lane) {
+// The query item of a segment: rows h0 .. h0+15 (rows past nh repeat h0) in
+// the tile's slot layout, 18 KB, loaded twice so that it costs the same nine
+// instructions per wave as a tile (the second copy is never read).
+__device__ __forceinline__ void dma_query_item(const uint16_t* qb, int nh, ZL_LDS char* dst, int wave,
+                                               int lane) {
 #pragma unroll
-  for (int k = 0; k < (kNIq + kWaves - 1) / kWaves; ++k) {
-    const int i = k * kWaves + wave;
-    if (i < kNIq) {
-      const int lin = 64 * i + lane;
-      const int r = lin / kCPR;
-      const int s = lin - r * kCPR;
-      dma16(qb + (long long)(r < nh ? r : 0) * kDK + slot(s, r) * 8, dst + i * 1024);
-    }
+  for (int k = 0; k < kNIw; ++k) {
+    const int i = wave * kNIw + k;
+    const int lin = 64 * (i % kNIq) + lane;
+    const int r = lin / kCPR;
+    const int s = lin - r * kCPR;
+    dma16(qb + (long long)(r < nh ? r : 0) * kDK + slot(s, r) * 8, dst + i * 1024);
   }
 }
 
@@ -147,10 +148,9 @@ template <int DT>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kWaves, 64 * kWaves),
                           amdgpu_waves_per_eu(1, 1))) void
 mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
-  // One LDS object only (see decode_attn.hip): [4 tiles][score exchange].
+  // One LDS object only (see decode_attn.hip): [4 ring stages][score exchange].
   __shared__ __attribute__((aligned(1024))) char smem_raw[kLdsBytes];
   ZL_LDS char* smem = (ZL_LDS char*)smem_raw;
-  ZL_LDS char* qlds = smem + (kStages - 1) * kTileB;  // query rows: last stage
   ZL_LDS char* xchg = smem + kStages * kTileB;
 
   const int tid = threadIdx.x;
@@ -176,73 +176,75 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
   asm volatile("" : "+v"(window));
   const long long N = (long long)U * T;
   const long long per = positions_per_worker(N, a.P);
-  long long p = (long long)w * per;
-  const long long p_end = N < p + per ? N : p + per;
+  const long long p_begin = (long long)w * per;
+  const long long p_end = N < p_begin + per ? N : p_begin + per;
+  if (p_begin >= p_end) return;  // the whole workgroup: w is per workgroup
 
-  while (p < p_end) {
-    const int u = (int)(p / T);
-    const int t0 = (int)(p - (long long)u * T);
-    const long long rem = p_end - p;
-    // Tokens of unit u left in this worker's run: the segment is a prefix.
-    const int avail = (long long)(T - t0) < rem ? T - t0 : (int)rem;
-
-    barrier_lds();  // every wave is done with the LDS of the previous segment
-    // Prologue before the sequence lookup (rows depend only on the token);
-    // clamped to the run, rows past the segment are masked.  A run shorter
-    // than the prologue re-reads its first tile into the unused stages.
-#pragma unroll
-    for (int s = 0; s < kStages - 1; ++s) {
-      const bool real = 32 * s < avail;
-      dma_quarter(a.k, real ? t0 + 32 * s : t0, real ? min(32, avail - 32 * s) : min(32, avail), qmap,
-                  smem + s * kTileB, wave);
+  // The run is one stream of ring items: for every segment its query item,
+  // then its 32-token tiles.  The issuing side runs up to three items ahead
+  // of the computing side, across segment boundaries, so a new segment does
+  // not drain the pipeline.  Every item is nine DMA instructions per wave.
+  Segment ds = segment_at(p_begin, p_end, T, cu, B, window);
+  int dj = 0;  // next item of segment ds: 0 = query rows, 1 + k = tile k
+  bool dmore = true;
+  int issued = 0;
+  auto issue = [&]() {
+    ZL_LDS char* dst = smem + (issued % kStages) * kTileB;
+    const int ntl = (ds.len + 31) >> 5;
+    if (dj == 0) {
+      const int h0 = ds.u * kHeadsPerUnit;
+      dma_query_item(a.q + ((long long)ds.b * a.Hq + h0) * kDK, min(kHeadsPerUnit, a.G - h0), dst, wave, lane);
+    } else {
+      const int k = dj - 1;
+      dma_quarter(a.k, ds.t0 + 32 * k, min(32, ds.len - 32 * k), qmap, dst, wave);
     }
-
-    const SeqSpan sq = find_seq(cu, B, t0, window);
-    const int b = sq.b, cs = sq.cs, ce = sq.ce;
-    const int t1 = (long long)(ce - t0) < rem ? ce : (int)(t0 + rem);
-    const int len = t1 - t0;
-    const long long seq_p0 = (long long)u * T + cs;
-    const long long seq_p1 = (long long)u * T + ce;
-    const int w_first = (int)(seq_p0 / per);
-    const int w_last = (int)((seq_p1 - 1) / per);
-    const int h0 = u * kHeadsPerUnit;
-    const int nh = min(kHeadsPerUnit, a.G - h0);
-    const int ntiles = (len + 31) >> 5;
-    dma_query(a.q + ((long long)b * a.Hq + h0) * kDK, nh, qlds, wave, lane);
-
-    f32x4 o[kBlkPerWave];
-#pragma unroll
-    for (int i = 0; i < kBlkPerWave; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    SoftmaxState sm{-INFINITY, 0.f};
-    i16x8 qop[kKHalf];
-
-    for (int j = 0; j < ntiles; ++j) {
-      // This wave's share of tile j; the real tiles issued after it may fly.
-      // At the first tile the query rows, requested last, are waited for too.
-      if (j == 0)
-        wait_vmcnt<0>();
-      else if (j + 2 < ntiles)
-        wait_vmcnt<2 * kNIw>();
-      else if (j + 1 < ntiles)
-        wait_vmcnt<kNIw>();
-      else
-        wait_vmcnt<0>();
-      barrier_lds();  // tile j complete in LDS, and every wave is past tile j-1
-      if (j == 0) {
-#pragma unroll
-        for (int kb = 0; kb < kKHalf; ++kb) {
-          const int c = 4 * (kKHalf * kh_own + kb) + g;
-          qop[kb] = __builtin_bit_cast(i16x8, lds_read_b128(qlds + n * kRowB + (slot(c, n) << 4)));
-        }
+    ++issued;
+    if (++dj > ntl) {
+      const long long pn = ds.p + ds.len;
+      if (pn < p_end) {
+        ds = segment_at(pn, p_end, T, cu, B, window);
+        dj = 0;
+      } else {
+        dmore = false;
       }
-      const ZL_LDS char* kt = smem + (j % kStages) * kTileB;
-      const f32x4 part = half_scores<DT>(kt, qop, tb_own, kh_own, n, g);
+    }
+  };
+  Segment sg = ds;  // the segment being computed
+  int cj = 0;       // its current item
+  for (int s = 0; s < kStages - 1 && dmore; ++s) issue();
+
+  f32x4 o[kBlkPerWave];
+  SoftmaxState sm{-INFINITY, 0.f};
+  i16x8 qop[kKHalf];
+
+  for (int i = 0;; ++i) {
+    // Item i has landed once at most the items issued after it are in flight.
+    const int after = issued - i - 1;
+    if (after >= 2)
+      wait_vmcnt<2 * kNIw>();
+    else if (after == 1)
+      wait_vmcnt<kNIw>();
+    else
+      wait_vmcnt<0>();
+    barrier_lds();  // item i complete in LDS, and every wave is past item i-1
+    if (dmore) issue();  // into the stage of item i-1
+    const ZL_LDS char* it = smem + (i % kStages) * kTileB;
+    const int ntl = (sg.len + 31) >> 5;
+    if (cj == 0) {
+      // Query item: this wave's half of the k-steps, B operand layout.
+#pragma unroll
+      for (int kb = 0; kb < kKHalf; ++kb) {
+        const int c = 4 * (kKHalf * kh_own + kb) + g;
+        qop[kb] = __builtin_bit_cast(i16x8, lds_read_b128(it + n * kRowB + (slot(c, n) << 4)));
+      }
+#pragma unroll
+      for (int bb = 0; bb < kBlkPerWave; ++bb) o[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sm = SoftmaxState{-INFINITY, 0.f};
+    } else {
+      const int j = cj - 1;
+      const f32x4 part = half_scores<DT>(it, qop, tb_own, kh_own, n, g);
       *(ZL_LDS f32x4*)(xchg + wave * 1024 + lane * 16) = part;
-      barrier_lds();  // all score halves in LDS; query rows read
-      if (j + kStages - 1 < ntiles) {
-        const int jn = j + kStages - 1;
-        dma_quarter(a.k, t0 + 32 * jn, min(32, len - 32 * jn), qmap, smem + (jn % kStages) * kTileB, wave);
-      }
+      barrier_lds();  // all score halves in LDS
       // Waves 0 and 2 hold the halves of token block 0, waves 1 and 3 block 1.
       f32x4 s[2];
       s[0] = *(const ZL_LDS f32x4*)(xchg + 0 * 1024 + lane * 16) +
@@ -250,31 +252,45 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
       s[1] = *(const ZL_LDS f32x4*)(xchg + 1 * 1024 + lane * 16) +
              *(const ZL_LDS f32x4*)(xchg + 3 * 1024 + lane * 16);
       float alpha;
-      const POperand pop = softmax_update<DT>(s, g, min(32, len - 32 * j), a.scale_log2, sm, alpha);
+      const POperand pop = softmax_update<DT>(s, g, min(32, sg.len - 32 * j), a.scale_log2, sm, alpha);
 #pragma unroll
-      for (int i = 0; i < kBlkPerWave; ++i) o[i] *= alpha;
-      pv_blocks<DT, kBlkPerWave, kRowB>(kt, pop, n, g, wave * kBlkPerWave, slot_fn, o);
-    }
+      for (int bb = 0; bb < kBlkPerWave; ++bb) o[bb] *= alpha;
+      pv_blocks<DT, kBlkPerWave, kRowB>(it, pop, n, g, wave * kBlkPerWave, slot_fn, o);
 
-    // ---- epilogue: lane (g, n) of wave w holds head n, dims 128w + 16bb + 4g .. +3
-    const float l_tot = sum_over_groups(sm.l);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const float lse_v = l_tot > 0.f ? sm.m * kLn2 + __logf(l_tot) : -INFINITY;
-    if (n < nh) {
-      if (w_first == w_last) {
-        uint16_t* orow = a.out + ((long long)b * a.Hq + h0 + n) * kDV + dim0;
+      if (j == ntl - 1) {
+        // ---- segment epilogue: lane (g, n) of wave w holds head n, dims
+        // 128w + 16bb + 4g .. +3.  Stores only; the next items are in flight.
+        const long long seq_p0 = (long long)sg.u * T + sg.cs;
+        const long long seq_p1 = (long long)sg.u * T + sg.ce;
+        const int w_first = (int)(seq_p0 / per);
+        const int w_last = (int)((seq_p1 - 1) / per);
+        const int h0 = sg.u * kHeadsPerUnit;
+        const int nh = min(kHeadsPerUnit, a.G - h0);
+        const float l_tot = sum_over_groups(sm.l);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const float lse_v = l_tot > 0.f ? sm.m * kLn2 + __logf(l_tot) : -INFINITY;
+        if (n < nh) {
+          if (w_first == w_last) {
+            uint16_t* orow = a.out + ((long long)sg.b * a.Hq + h0 + n) * kDV + dim0;
 #pragma unroll
-        for (int bb = 0; bb < kBlkPerWave; ++bb) store_out4<DT>(orow + 16 * bb, o[bb], inv);
-        if (a.lse && wave == 0 && g == 0) a.lse[(long long)b * a.Hq + h0 + n] = lse_v;
-      } else {
-        const int sl = partial_slot(w, per, seq_p0);
-        float* po = a.part_o + ((long long)sl * kHeadsPerUnit + n) * kDV + dim0;
+            for (int bb = 0; bb < kBlkPerWave; ++bb) store_out4<DT>(orow + 16 * bb, o[bb], inv);
+            if (a.lse && wave == 0 && g == 0) a.lse[(long long)sg.b * a.Hq + h0 + n] = lse_v;
+          } else {
+            const int sl = partial_slot(w, per, seq_p0);
+            float* po = a.part_o + ((long long)sl * kHeadsPerUnit + n) * kDV + dim0;
 #pragma unroll
-        for (int bb = 0; bb < kBlkPerWave; ++bb) *(f32x4*)(po + 16 * bb) = o[bb] * inv;
-        if (wave == 0 && g == 0) a.part_lse[sl * kLseSlot + n] = lse_v;
+            for (int bb = 0; bb < kBlkPerWave; ++bb) *(f32x4*)(po + 16 * bb) = o[bb] * inv;
+            if (wave == 0 && g == 0) a.part_lse[sl * kLseSlot + n] = lse_v;
+          }
+        }
       }
     }
-    p += len;
+    if (++cj > ntl) {
+      const long long pn = sg.p + sg.len;
+      if (pn >= p_end) break;
+      sg = segment_at(pn, p_end, T, cu, B, window);
+      cj = 0;
+    }
   }
 }
 

@@ -74,6 +74,39 @@ __device__ __forceinline__ SeqSpan find_seq(const int32_t* cu, int B, int t, int
   return r;
 }
 
+// One segment of a worker's run: tokens [t0, t0 + len) of sequence b (whose
+// tokens are [cs, ce)) in work unit u, starting at position p.
+struct Segment {
+  long long p;
+  int u, t0, len, b, cs, ce;
+};
+
+// Position p -> (unit, token); 32-bit division when the position line fits.
+__device__ __forceinline__ void split_position(long long p, int T, int& u, int& t) {
+  if (p < 0x7fffffffLL) {
+    u = (int)p / T;
+    t = (int)p - u * T;
+  } else {
+    u = (int)(p / T);
+    t = (int)(p - (long long)u * T);
+  }
+}
+
+// The segment that starts at position p of a run ending at p_end (p < p_end).
+__device__ __forceinline__ Segment segment_at(long long p, long long p_end, int T, const int32_t* cu, int B,
+                                              int window) {
+  Segment s;
+  s.p = p;
+  split_position(p, T, s.u, s.t0);
+  const SeqSpan q = find_seq(cu, B, s.t0, window);
+  s.b = q.b;
+  s.cs = q.cs;
+  s.ce = q.ce;
+  const long long rem = p_end - p;
+  s.len = (long long)(q.ce - s.t0) < rem ? q.ce - s.t0 : (int)rem;
+  return s;
+}
+
 // Slot of worker w's partial for the sequence occupying positions
 // [seq_p0, seq_p1), when that sequence is split between workers.
 __device__ __forceinline__ int partial_slot(int w, long long per, long long seq_p0) {
