@@ -38,7 +38,8 @@
  *  - Host-checkable arguments are validated before any HIP call; a bad argument
  *    returns an error status and enqueues nothing.  Device contents (the values
  *    in cu_seqlens) are preconditions: cu[0] = 0, non-decreasing, every length
- *    at most max_seqlen_k, cu[batch] = total_tokens of the caches.
+ *    at most max_seqlen_k, cu[batch] = total_tokens of the caches, and
+ *    cu[batch] + 64 * batch < 2^31.
  *  - 16-bit buffers (q, k, v, latent, out) must be 16-byte aligned.  Rows are
  *    dense: the layouts below have no padding.
  *  - Results are bitwise deterministic for identical inputs, arguments and
@@ -82,8 +83,8 @@ typedef struct ihipStream_t *zl_stream_t;
 /*
  * Bytes of device workspace that zl_decode_attn_gqa needs for these sizes
  * (host function, no HIP call).  Returns 0 for invalid sizes.  The workspace
- * holds two fp32 partial results per worker; it needs no initialisation and
- * its contents are meaningless between calls.
+ * holds two fp32 partial results and one int per worker; it needs no
+ * initialisation and its contents are meaningless between calls.
  */
 ZL_API size_t zl_decode_attn_workspace_size(int batch, int num_q_heads, int num_kv_heads,
                                      int head_dim, int max_seqlen_k, zl_dtype_t dtype);

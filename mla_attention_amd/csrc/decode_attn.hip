@@ -144,19 +144,21 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
   // Sequence boundaries for the lookups below, loaded alongside T (one round
   // trip for both) and waited for here, so that no later lookup has to drain
   // the tile loads in flight.
-  int window = bounds_window(cu, B);
+  int window = bounds_window(cu, B, a.seg_cost);
   asm volatile("" : "+v"(window));
-  const long long N = (long long)U * T;
+  const Line line = make_line(T, B, a.seg_cost);
+  const long long N = (long long)U * line.Tp;
   const long long per = positions_per_worker(N, a.P);
   const long long p_begin = (long long)w * per;
   const long long p_end = N < p_begin + per ? N : p_begin + per;
-  if (p_begin >= p_end) return;
+  Segment ds = segment_at(p_begin, p_end, line, cu, window);
+  if (lane == 0) a.first_key[w] = ds.len > 0 ? seq_key(ds.u, ds.b, B) : -1;
+  if (ds.len == 0) return;
 
   // The run is one stream of ring items: for every segment (the part of one
   // sequence of one work unit in the run) its query rows, then its 32-token
   // K/V tiles.  Loads run STAGES-1 items ahead of the math, across segment
   // boundaries, so a new segment does not drain the pipeline.
-  Segment ds = segment_at(p_begin, p_end, T, cu, B, window);
   int dj = 0;  // next item of segment ds: 0 = query rows, 1 + k = tile k
   bool dmore = true;
   int issued = 0;
@@ -178,17 +180,14 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
     }
     ++issued;
     if (++dj > ntl) {
-      const long long pn = ds.p + ds.len;
-      if (pn < p_end) {
-        ds = segment_at(pn, p_end, T, cu, B, window);
-        dj = 0;
-      } else {
-        dmore = false;
-      }
+      ds = segment_at(ds.p + ds.len, p_end, line, cu, window);
+      dj = 0;
+      dmore = ds.len > 0;
     }
   };
   Segment sg = ds;  // the segment being computed
   int cj = 0;       // its current item
+  bool first_seg = true;
   for (int s = 0; s < STAGES - 1 && dmore; ++s) issue();
 
   f32x4 o[TL::VBLK];
@@ -232,10 +231,8 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
         // ---- segment epilogue: lane (g, n) holds head n, dims 16blk + 4g .. +3.
         // Stores only; the next items are already in flight.  A split
         // sequence leaves its partial for the merge launch.
-        const long long seq_p0 = (long long)sg.u * T + sg.cs;
-        const long long seq_p1 = (long long)sg.u * T + sg.ce;
-        const int w_first = (int)(seq_p0 / per);
-        const int w_last = (int)((seq_p1 - 1) / per);
+        const int w_first = (int)(token_position(line, sg.u, sg.b, sg.cs) / per);
+        const int w_last = (int)(token_position(line, sg.u, sg.b, sg.ce - 1) / per);
         const int kvh = sg.u / a.HB, hb = sg.u - (sg.u / a.HB) * a.HB;
         const int h0 = kvh * a.G + hb * kHeadsPerUnit;
         const int nh = min(kHeadsPerUnit, a.G - hb * kHeadsPerUnit);
@@ -249,7 +246,7 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
             for (int blk = 0; blk < TL::VBLK; ++blk) store_out4<DT>(orow + 16 * blk, o[blk], inv);
             if (a.lse && g == 0) a.lse[(long long)sg.b * a.Hq + h0 + n] = lse_v;
           } else {
-            const int sl = partial_slot(w, per, seq_p0);
+            const int sl = 2 * w + (first_seg ? 0 : 1);
             float* po = a.part_o + ((long long)sl * kHeadsPerUnit + n) * DV + 4 * g;
 #pragma unroll
             for (int blk = 0; blk < TL::VBLK; ++blk) *(f32x4*)(po + 16 * blk) = o[blk] * inv;
@@ -259,10 +256,10 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
       }
     }
     if (++cj > ntl) {
-      const long long pn = sg.p + sg.len;
-      if (pn >= p_end) break;
-      sg = segment_at(pn, p_end, T, cu, B, window);
+      sg = segment_at(sg.p + sg.len, p_end, line, cu, window);
+      if (sg.len == 0) break;
       cj = 0;
+      first_seg = false;
     }
   }
 }

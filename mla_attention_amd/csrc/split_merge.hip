@@ -8,12 +8,14 @@
 // page names flash_decoding among the engine's kernels, section "技术架构"):
 //   M = max_s lse_s,  w_s = exp(lse_s - M),
 //   out = sum_s w_s O_s / sum_s w_s,  lse = M + ln(sum_s w_s).
-// One thread per (unit, sequence, head, 4-float column): all split sequences
-// are merged at once across the whole GPU, in about one memory round trip per
-// four partials.  Sequences that one worker covered alone were already
-// written by the decode kernel; their threads return at once.  Empty
-// sequences, which no worker covers, get out = 0 and lse = -inf here.  The partials
-// are visible here because kernels on one stream are ordered and caches are
+// One workgroup per (unit, sequence) -- several for wide rows -- so that the
+// sequence's bounds and its range of workers are worked out once, in scalar
+// registers; one thread per (head, 4-float column) then loads up to 16
+// partials at once, so a merge costs about one memory round trip after the
+// bounds.  Sequences that one worker covered alone were already written by
+// the decode kernel; their workgroups return at once.  Empty sequences, which
+// no worker covers, get out = 0 and lse = -inf here.  The partials are
+// visible here because kernels on one stream are ordered and caches are
 // written back / invalidated between launches.
 #include "zl_device.h"
 #include "zl_kernels.h"
@@ -24,21 +26,20 @@ namespace zl {
 
 template <int DT, int DV>
 __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a, const int32_t* __restrict__ cu,
-                                                          int heads_per_unit) {
+                                                          int heads_per_unit, int wg_per_seq) {
   constexpr int C4 = DV / 4;  // float4 columns per output row
-  const int U = a.Hkv * a.HB;
-  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= (long long)U * a.B * heads_per_unit * C4) return;
-  const int c4 = (int)(gid % C4);
-  long long r = gid / C4;
-  const int h = (int)(r % heads_per_unit);
-  r /= heads_per_unit;
-  const int b = (int)(r % a.B);
-  const int u = (int)(r / a.B);
+  // Workgroup -> (unit u, sequence b, part); all wave-uniform.
+  const int part = (int)blockIdx.x % wg_per_seq;
+  const int ub = (int)blockIdx.x / wg_per_seq;
+  const int b = ub % a.B;
+  const int u = ub / a.B;
   const int kvh = u / a.HB, hb = u - (u / a.HB) * a.HB;
   const int nh = min(kHeadsPerUnit, a.G - hb * kHeadsPerUnit);
-  if (h >= nh) return;
   const int h0 = kvh * a.G + hb * kHeadsPerUnit;
+  const int item = part * 256 + (int)threadIdx.x;
+  const int h = item / C4;
+  const int c4 = item - h * C4;
+  if (h >= nh || h >= heads_per_unit) return;
   const int cs = cu[b], ce = cu[b + 1];
   if (ce == cs) {
     // An empty sequence (no worker run covers it): out = 0, lse = -inf.
@@ -46,24 +47,27 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a, const in
     if (a.lse && c4 == 0) a.lse[(long long)b * a.Hq + h0 + h] = -INFINITY;
     return;
   }
-  const int T = cu[a.B];
-  const long long per = positions_per_worker((long long)U * T, a.P);
-  const long long seq_p0 = (long long)u * T + cs;
-  const int w_first = (int)(seq_p0 / per);
-  const int w_last = (int)(((long long)u * T + ce - 1) / per);
+  const int U = a.Hkv * a.HB;
+  const Line line = make_line(cu[a.B], a.B, a.seg_cost);
+  const long long per = positions_per_worker((long long)U * line.Tp, a.P);
+  const int w_first = (int)(token_position(line, u, b, cs) / per);
+  const int w_last = (int)(token_position(line, u, b, ce - 1) / per);
   if (w_first == w_last) return;
+  // Worker w_first used slot 2w if this sequence opened its run, else 2w+1;
+  // every later worker's run opens with this sequence (slot 2w).
+  const int first_slot = 2 * w_first + (a.first_key[w_first] == seq_key(u, b, a.B) ? 0 : 1);
 
   const int nparts = w_last - w_first + 1;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float M = -INFINITY, wsum = 0.f;
-  constexpr int BATCH = 4;  // partials whose loads are in flight together
+  constexpr int BATCH = 16;  // partials whose loads are in flight together
   for (int i0 = 0; i0 < nparts; i0 += BATCH) {
     float ls[BATCH];
     f32x4 v[BATCH];
 #pragma unroll
     for (int j = 0; j < BATCH; ++j) {
       const int i = min(i0 + j, nparts - 1);  // tail of the batch re-reads the last one
-      const int sl = partial_slot(w_first + i, per, seq_p0);
+      const int sl = i == 0 ? first_slot : 2 * (w_first + i);
       ls[j] = i0 + j < nparts ? a.part_lse[sl * kLseSlot + h] : -INFINITY;
       v[j] = *(const f32x4*)(a.part_o + ((long long)sl * kHeadsPerUnit + h) * DV + 4 * c4);
     }
@@ -91,10 +95,11 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a, const in
 template <int DT, int DV>
 static hipError_t launch_merge_t(const DecodeArgs& a, hipStream_t stream) {
   const int hpu = a.G < kHeadsPerUnit ? a.G : kHeadsPerUnit;
-  const long long threads = (long long)a.Hkv * a.HB * a.B * hpu * (DV / 4);
-  const long long blocks = (threads + 255) / 256;
+  const int wg_per_seq = (hpu * (DV / 4) + 255) / 256;
+  const long long blocks = (long long)a.Hkv * a.HB * a.B * wg_per_seq;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((split_merge_kernel<DT, DV>), dim3((unsigned)blocks), dim3(256), 0, stream, a, a.cu, hpu);
+  hipLaunchKernelGGL((split_merge_kernel<DT, DV>), dim3((unsigned)blocks), dim3(256), 0, stream, a, a.cu, hpu,
+                     wg_per_seq);
   return hipGetLastError();
 }
 

@@ -22,16 +22,18 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t lse_off, out_off, total;
+  size_t lse_off, out_off, key_off, total;
 };
 
-// Workspace: [part_lse 2P*32 f32][part_o 2P*16*Dv f32], 256-byte aligned:
-// two fp32 partial slots per worker (see zl_split.h).
+// Workspace: [part_lse 2P*32 f32][part_o 2P*16*Dv f32][first_key P i32], each
+// part 256-byte aligned: two fp32 partial slots per worker and the key of
+// each run's first segment (see zl_split.h).
 WsLayout ws_layout(int workers, int dv) {
   WsLayout w;
   w.lse_off = 0;
   w.out_off = round_up((size_t)2 * workers * zl::kLseSlot * 4, 256);
-  w.total = w.out_off + (size_t)2 * workers * zl::kHeadsPerUnit * dv * 4;
+  w.key_off = w.out_off + round_up((size_t)2 * workers * zl::kHeadsPerUnit * dv * 4, 256);
+  w.total = w.key_off + round_up((size_t)workers * 4, 256);
   return w;
 }
 
@@ -85,6 +87,8 @@ zl_status_t run_decode(zl::DecodeArgs a, Layout layout, int dv, zl_dtype_t dtype
   char* ws = static_cast<char*>(workspace);
   a.part_lse = reinterpret_cast<float*>(ws + wl.lse_off);
   a.part_o = reinterpret_cast<float*>(ws + wl.out_off);
+  a.first_key = reinterpret_cast<int*>(ws + wl.key_off);
+  a.seg_cost = layout == zl::kMla576 ? zl::kSegCostMla : zl::kSegCostGqa;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (phases & 1) e = zl::launch_decode(a, layout, dtype, st);

@@ -30,9 +30,17 @@ struct DecodeArgs {
   float* lse;           // [B, Hq] or nullptr
   float* part_o;        // [2P, 16, Dv]
   float* part_lse;      // [2P, kLseSlot] (first 16 used)
+  int* first_key;       // [P]: (unit, sequence) of each run's first segment
   int B, Hq, Hkv, G, HB, P;
+  int seg_cost;         // phantom positions per sequence (zl_split.h)
   float scale_log2;     // softmax_scale * log2(e)
 };
+
+// Phantom positions per sequence on the work line (the fixed cost of starting
+// a sequence in a run, in tokens): measured per-segment overheads of the two
+// kernels, rounded.
+constexpr int kSegCostGqa = 32;
+constexpr int kSegCostMla = 64;
 
 struct CombineArgs {
   const float* part_o;   // [S, rows, Dv]

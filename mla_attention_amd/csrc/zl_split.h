@@ -1,16 +1,26 @@
-// zl_split.h -- token-balanced work split shared by the decode kernels.
+// zl_split.h -- the work split shared by the decode kernels and the merge.
 //
-// The ragged batch is viewed as one line of "positions": position
-// p = u * T + t for work unit u (a key/value head, or a block of up to 16 query
-// heads of it) and packed token t (T = total tokens).  Each of the P workers
-// (one wavefront each) owns an equal run of `per` positions, so every worker
-// streams the same number of K/V bytes whatever the mix of sequence lengths.
+// The ragged batch is viewed as one line of "positions".  Work unit u (a
+// key/value head, or a block of up to 16 query heads of it) owns positions
+// [u*Tp, (u+1)*Tp) with Tp = T + B*C (T = total tokens, B = batch, C = the
+// segment cost below).  Inside a unit, sequence b owns [cpos(b), cpos(b+1))
+// with cpos(b) = cu[b] + b*C: first C "phantom" positions that carry no token,
+// then one position per token.  Each of the P workers owns an equal run of
+// `per` positions.
+//
+// The phantom positions stand for the fixed cost of starting a sequence in a
+// run (its query rows, a partly filled last tile, the epilogue stores): a run
+// that starts k sequences carries about k*C fewer tokens, so runs that cross
+// sequence boundaries do not finish last.  A run starting inside a phantom
+// stretch begins at the sequence's first token.
+//
 // A run that covers a whole sequence writes that sequence's output directly;
-// a sequence cut between workers gets one fp32 partial (O / l, lse) per worker,
+// a sequence cut between runs gets one fp32 partial (O / l, lse) per run,
 // merged by the split-merge kernel (split_merge.hip) launched right after.
-//
-// Partial slots: worker w owns slots 2w (the sequence its run starts in) and
-// 2w+1 (the sequence its run ends in, when that is another one).
+// Partial slots: worker w writes slot 2w for the first segment of its run and
+// 2w+1 for its last (a run has at most these two cut segments), and records in
+// first_key[w] which (unit, sequence) its first segment belongs to, so that
+// the merge knows which slot the first worker of a sequence used.
 #pragma once
 
 #include <stdint.h>
@@ -25,99 +35,134 @@ __device__ __forceinline__ long long positions_per_worker(long long N, int P) {
   return per < 64 ? 64 : per;
 }
 
-// Largest b in [0, B) with cu[b] <= t; for 0 <= t < cu[B] this is the
-// sequence that owns token t (empty sequences are stepped over).  Because cu
-// is non-decreasing with cu[0] = 0, it equals the number of b in [1, B) with
-// cu[b] <= t.  The lanes of the wave load cu 64 entries at a time and count
-// with a ballot, so a batch of up to 64 sequences costs one memory round trip
-// instead of the log2(B) dependent loads of a bisection.  Call from
-// wave-uniform control flow with all 64 lanes active.
-__device__ __forceinline__ int seq_of_token(const int32_t* cu, int B, int t) {
+// Largest b in [0, B) with cpos(b) <= r, for 0 <= r < Tp: the sequence whose
+// stretch holds in-unit position r (an empty sequence owns only its phantom
+// stretch).  Because cpos is non-decreasing with cpos(0) = 0, it equals the
+// number of b in [1, B) with cpos(b) <= r.  The lanes of the wave load cu 64
+// entries at a time and count with a ballot.  Call from wave-uniform control
+// flow with all 64 lanes active.
+__device__ __forceinline__ int seq_at(const int32_t* cu, int B, int C, int r) {
   const int lane = __lane_id();
   int count = 0;
   for (int i0 = 1; i0 < B; i0 += 64) {
     const int i = i0 + lane;
-    const bool le = i < B && cu[i] <= t;
+    const bool le = i < B && cu[i] + i * C <= r;
     count += __popcll(__ballot(le));
   }
   return __builtin_amdgcn_readfirstlane(count);
 }
 
-// Lane l holds cu[1 + l] (INT_MAX past cu[B]): the boundaries of a batch of
-// up to 64 sequences in one vector load.  Issue it before a segment's
-// prologue DMA: its use then waits only for itself, not for the tiles.
-__device__ __forceinline__ int bounds_window(const int32_t* cu, int B) {
+// Lane l holds cpos(1 + l) = cu[1 + l] + (1 + l)*C (INT_MAX past the batch):
+// the boundaries of a batch of up to 64 sequences in one vector load.  Load it
+// once per kernel, before any tile DMA: its use then never has to drain the
+// tile loads in flight.
+__device__ __forceinline__ int bounds_window(const int32_t* cu, int B, int C) {
   const int i = 1 + __lane_id();
   const int v = cu[i < B ? i : B];  // unpredicated load (a branch here would
                                     // make the compiler's wait drain the DMA)
-  return i <= B ? v : 0x7fffffff;
+  return i <= B ? v + i * C : 0x7fffffff;
 }
 
 struct SeqSpan {
-  int b;       // sequence owning the token
+  int b;       // sequence whose stretch holds the position
   int cs, ce;  // cu[b], cu[b + 1]
 };
 
-// The sequence owning token t (0 <= t < cu[B]) and its bounds: from the
-// window when B <= 64 (a ballot and two lane reads), else by the search above.
-__device__ __forceinline__ SeqSpan find_seq(const int32_t* cu, int B, int t, int window) {
-  SeqSpan r;
+// The sequence owning in-unit position r and its token bounds: from the window
+// when B <= 64 (a ballot and two lane reads), else by the search above.
+__device__ __forceinline__ SeqSpan find_seq(const int32_t* cu, int B, int C, int r, int window) {
+  SeqSpan s;
   if (B <= 64) {
-    r.b = __popcll(__ballot(window <= t));
-    r.ce = __builtin_amdgcn_readlane(window, r.b);
-    r.cs = r.b == 0 ? 0 : __builtin_amdgcn_readlane(window, r.b - 1);
+    s.b = __popcll(__ballot(window <= r));
+    s.ce = __builtin_amdgcn_readlane(window, s.b) - (s.b + 1) * C;
+    s.cs = s.b == 0 ? 0 : __builtin_amdgcn_readlane(window, s.b - 1) - s.b * C;
   } else {
-    r.b = seq_of_token(cu, B, t);
-    r.cs = cu[r.b];
-    r.ce = cu[r.b + 1];
+    s.b = seq_at(cu, B, C, r);
+    s.cs = cu[s.b];
+    s.ce = cu[s.b + 1];
   }
-  return r;
+  return s;
+}
+
+// The position line of one call.
+struct Line {
+  int T;         // total tokens
+  int B;         // batch
+  int C;         // phantom positions per sequence
+  long long Tp;  // positions per unit
+};
+
+__device__ __forceinline__ Line make_line(int T, int B, int C) {
+  return Line{T, B, C, (long long)T + (long long)B * C};
+}
+
+// Position of token t of sequence b in unit u.
+__device__ __forceinline__ long long token_position(const Line& L, int u, int b, int t) {
+  return (long long)u * L.Tp + t + (long long)(b + 1) * L.C;
 }
 
 // One segment of a worker's run: tokens [t0, t0 + len) of sequence b (whose
-// tokens are [cs, ce)) in work unit u, starting at position p.
+// tokens are [cs, ce)) in work unit u; p is the position of token t0.
+// len == 0 means that the run holds no further token.
 struct Segment {
   long long p;
   int u, t0, len, b, cs, ce;
 };
 
-// Position p -> (unit, token); 32-bit division when the position line fits.
-__device__ __forceinline__ void split_position(long long p, int T, int& u, int& t) {
-  if (p < 0x7fffffffLL) {
-    u = (int)p / T;
-    t = (int)p - u * T;
+// Position -> (unit, in-unit position); 32-bit division when it fits.
+__device__ __forceinline__ void split_position(long long p, long long Tp, int& u, int& r) {
+  if (p < 0x7fffffffLL && Tp < 0x7fffffffLL) {
+    u = (int)p / (int)Tp;
+    r = (int)p - u * (int)Tp;
   } else {
-    u = (int)(p / T);
-    t = (int)(p - (long long)u * T);
+    u = (int)(p / Tp);
+    r = (int)(p - (long long)u * Tp);
   }
 }
 
-// The segment that starts at position p of a run ending at p_end (p < p_end).
-__device__ __forceinline__ Segment segment_at(long long p, long long p_end, int T, const int32_t* cu, int B,
+// The first segment of the run [p, p_end): its first token is the first token
+// at a position >= p (phantom stretches and empty sequences are stepped over).
+__device__ __forceinline__ Segment segment_at(long long p, long long p_end, const Line& L, const int32_t* cu,
                                               int window) {
   Segment s;
   s.p = p;
-  split_position(p, T, s.u, s.t0);
-  const SeqSpan q = find_seq(cu, B, s.t0, window);
-  s.b = q.b;
-  s.cs = q.cs;
-  s.ce = q.ce;
-  const long long rem = p_end - p;
-  s.len = (long long)(q.ce - s.t0) < rem ? q.ce - s.t0 : (int)rem;
+  s.u = 0;
+  s.t0 = 0;
+  s.len = 0;
+  s.b = 0;
+  s.cs = 0;
+  s.ce = 0;
+  while (p < p_end) {
+    int u, r;
+    split_position(p, L.Tp, u, r);
+    const SeqSpan q = find_seq(cu, L.B, L.C, r, window);
+    const int o = r - (q.cs + q.b * L.C);  // offset inside the sequence's stretch
+    const int t0 = o < L.C ? q.cs : q.cs + (o - L.C);
+    // Tokens t < lim of this sequence lie inside the run.
+    const long long lim = p_end - (long long)u * L.Tp - (long long)(q.b + 1) * L.C;
+    if (lim <= t0) return s;  // the run ends before this sequence's next token
+    const int t1 = (long long)q.ce < lim ? q.ce : (int)lim;
+    if (t1 > t0) {
+      s.p = token_position(L, u, q.b, t0);
+      s.u = u;
+      s.t0 = t0;
+      s.len = t1 - t0;
+      s.b = q.b;
+      s.cs = q.cs;
+      s.ce = q.ce;
+      return s;
+    }
+    // An empty sequence: go on at the start of the next one.
+    p = (long long)u * L.Tp + q.ce + (long long)(q.b + 1) * L.C;
+  }
   return s;
 }
 
-// Slot of worker w's partial for the sequence occupying positions
-// [seq_p0, seq_p1), when that sequence is split between workers.
-__device__ __forceinline__ int partial_slot(int w, long long per, long long seq_p0) {
-  long long w_first = seq_p0 / per;
-  bool run_started_before = (w == w_first) && (seq_p0 > (long long)w * per);
-  return 2 * w + (run_started_before ? 1 : 0);
-}
+// Key of (unit u, sequence b) in first_key.
+__device__ __forceinline__ int seq_key(int u, int b, int B) { return u * B + b; }
 
 // Worker id from the block id: consecutive worker ids are placed on the same
-// XCD (blocks are dealt round-robin over the 8 XCDs), so the workers that
-// share a split sequence mostly share one L2.
+// XCD (blocks are dealt round-robin over the 8 XCDs).
 __device__ __forceinline__ int worker_id(int block, int P) {
   int per_xcd = P >> 3;
   return (block & 7) * per_xcd + (block >> 3);
