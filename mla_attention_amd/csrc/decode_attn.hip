@@ -81,20 +81,46 @@ struct Tile {
 };
 
 // DMA one tensor's 32-row tile: 1 KB instruction i covers the tile's 16-byte
-// slots 64i .. 64i+63 in row-major order; lane picks the global chunk that the
-// swizzle stores in its slot.  Rows past the segment are clamped to its last
-// row (finite data, masked out of the softmax).
+// slots 64i .. 64i+63 in row-major order, lane l loading row r = lin / CPR and
+// the global chunk that the swizzle stores in slot lin % CPR (the slot
+// permutation is an involution).  These per-lane byte offsets do not change
+// from tile to tile, so they are computed once: a tile then costs a scalar
+// base (its first row) and one 32-bit offset per instruction.  Rows past
+// nvalid (a segment's last tile) are clamped to row nvalid - 1: finite data,
+// masked out of the softmax.
+template <int L, int NI>
+struct TileMap {
+  uint32_t off[NI];  // r * row_bytes + 16 * chunk
+  int row[NI];       // r
+  uint32_t chunk[NI];
+};
+
 template <int L, int CPR, int NI>
-__device__ __forceinline__ void dma_tile(const uint16_t* base, long long row_elems, int tok0,
-                                         int nvalid, ZL_LDS char* dst, int lane) {
+__device__ __forceinline__ TileMap<L, NI> tile_map(uint32_t row_bytes, int lane) {
+  TileMap<L, NI> m;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int lin = 64 * i + lane;
     const int r = lin / CPR;
-    const int s = lin - r * CPR;
-    const int c = Geo<L>::slot(s, r);  // the slot permutation is an involution
-    const int rr = r < nvalid ? r : nvalid - 1;
-    dma16(base + (long long)(tok0 + rr) * row_elems + c * 8, dst + i * 1024);
+    m.row[i] = r;
+    m.chunk[i] = 16u * (uint32_t)Geo<L>::slot(lin - r * CPR, r);
+    m.off[i] = (uint32_t)r * row_bytes + m.chunk[i];
+  }
+  return m;
+}
+
+template <int L, int NI>
+__device__ __forceinline__ void dma_tile(const char* rows, uint32_t row_bytes, const TileMap<L, NI>& m, int nvalid,
+                                         ZL_LDS char* dst) {
+  if (nvalid >= 32) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma16_saddr(rows, m.off[i], dst + i * 1024);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int rr = m.row[i] < nvalid ? m.row[i] : nvalid - 1;
+      dma16_saddr(rows, (uint32_t)rr * row_bytes + m.chunk[i], dst + i * 1024);
+    }
   }
 }
 
@@ -135,9 +161,11 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
   const int w = worker_id(blockIdx.x, a.P);
   const int B = a.B;
   const int U = a.Hkv * a.HB;
-  const long long k_row = GE::SHARED_KV ? (long long)DK : (long long)a.Hkv * DK;
-  const long long v_row = GE::SHARED_KV ? (long long)DK : (long long)a.Hkv * DV;
+  const uint32_t k_row_bytes = (uint32_t)a.Hkv * DK * 2;  // one token's K row (all kv heads)
+  const uint32_t v_row_bytes = (uint32_t)a.Hkv * DV * 2;
   const auto slot = [](int c, int r) { return GE::slot(c, r); };
+  const TileMap<L, TL::NI_K> kmap = tile_map<L, TL::KCPR, TL::NI_K>(k_row_bytes, lane);
+  const TileMap<L, TL::NI_V> vmap = tile_map<L, TL::VCPR, TL::NI_V>(v_row_bytes, lane);
 
   // (Empty sequences are written by the merge launch: no run covers them.)
   const int T = cu[B];
@@ -174,9 +202,10 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
       const int k = dj - 1;
       const int tok = ds.t0 + 32 * k;
       const int nv = min(32, ds.len - 32 * k);
-      dma_tile<L, TL::KCPR, TL::NI_K>(a.k + (long long)kvh * DK, k_row, tok, nv, st, lane);
-      if constexpr (!GE::SHARED_KV)
-        dma_tile<L, TL::VCPR, TL::NI_V>(a.v + (long long)kvh * DV, v_row, tok, nv, st + TL::KBYTES, lane);
+      dma_tile<L, TL::NI_K>((const char*)(a.k + (long long)kvh * DK) + (size_t)tok * k_row_bytes, k_row_bytes,
+                            kmap, nv, st);
+      dma_tile<L, TL::NI_V>((const char*)(a.v + (long long)kvh * DV) + (size_t)tok * v_row_bytes, v_row_bytes,
+                            vmap, nv, st + TL::KBYTES);
     }
     ++issued;
     if (++dj > ntl) {

@@ -96,13 +96,13 @@ __device__ __forceinline__ void dma_quarter(const uint16_t* rows, int tok0, int 
   const char* base = (const char*)rows + (size_t)tok0 * kRowB;
   if (nvalid >= 32) {
 #pragma unroll
-    for (int k = 0; k < kNIw; ++k) dma16(base + m.off[k], dst + (wave * kNIw + k) * 1024);
+    for (int k = 0; k < kNIw; ++k) dma16_saddr(base, m.off[k], dst + (wave * kNIw + k) * 1024);
   } else {
 #pragma unroll
     for (int k = 0; k < kNIw; ++k) {
       const int over = m.row[k] - (nvalid - 1);
       const uint32_t off = m.off[k] - (over > 0 ? (uint32_t)(over * kRowB) : 0u);
-      dma16(base + off, dst + (wave * kNIw + k) * 1024);
+      dma16_saddr(base, off, dst + (wave * kNIw + k) * 1024);
     }
   }
 }

@@ -110,6 +110,17 @@ __device__ __forceinline__ void dma16(const void* gptr, ZL_LDS void* lds_base) {
   __builtin_amdgcn_global_load_lds(gptr, lds_base, 16, 0, 0);
 }
 
+// The same with a wave-uniform 64-bit base in scalar registers and a 32-bit
+// per-lane byte offset (the instruction's SADDR form): no vector address
+// arithmetic per instruction.  Written as inline asm because the compiler
+// widens the offset to a 64-bit vector address.  The compiler does not see
+// this load, so it must be waited for explicitly (wait_vmcnt) before its LDS
+// bytes are read, as every DMA here is; the s_nop separates the M0 write from
+// the load.
+__device__ __forceinline__ void dma16_saddr(const void* base, uint32_t off, ZL_LDS void* lds_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_base) : "memory");
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding.
 // (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt/lgkmcnt left at max.)
 template <int N>
