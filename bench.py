@@ -3,17 +3,22 @@
 One step = one call of the fused decode attention for the whole batch: the
 decode kernel (every K/V byte streamed once, split evenly over the workers)
 then the split-merge kernel (log-sum-exp combine of the sequences that several
-workers share), on synthetic inputs already resident in HBM.  Inputs are replicated
+workers share), on synthetic inputs already resident in HBM.  The timed region
+is K such calls back to back; a second pass of K calls with an event around
+each kernel gives the decode kernel's own duration for the roofline.  Inputs are replicated
 R = max(2, ceil(1 GiB / bytes)) times and the steps cycle through the
 replicas, so the 256 MB Infinity Cache cannot serve a step from the previous
 one.
 
 Prints one JSON line:
   value      KV GB/s = algorithmic bytes (every K and V element, or every
-             latent row, read once) / wall time per step
+             latent row, read once) / time per step
   roofline   the decode kernel against the 8 TB/s HBM peak; achieved = the
-             same bytes / the kernel's own average duration, from HIP events
-             recorded around every launch on the launch stream
+             same bytes / the kernel's average duration, from HIP events
+             recorded around every launch on the launch stream (these include
+             the launch's dispatch, about 2 us more than a kernel trace shows);
+             traffic and mfma_busy come from the committed rocprofv3 counter
+             record when it was taken on the current kernel sources
   cpu_baseline  the fp64 oracle on the host cores, on a bounded sample
 """
 from __future__ import annotations
@@ -44,17 +49,18 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources; else None."""
+def profile_record(workload: str) -> dict:
+    """The committed rocprofv3 counter record for this workload (HBM bytes per
+    launch, matrix-core busy share), if it was taken on the current kernel
+    sources; else an empty dict."""
     path = os.path.join(PROFILES, f"traffic_{workload}.json")
     if not os.path.exists(path):
-        return None
+        return {}
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_source_sha") != kernel_source_sha():
-        return None
-    return rec.get("hbm_bytes_per_launch")
+        return {}
+    return rec
 
 
 def parse():
@@ -149,32 +155,45 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # Each step is the decode kernel then the merge kernel (the two phases of
-    # one call, enqueued separately so that an event can sit between them).
+    # Timed region: K whole calls (decode kernel + merge kernel), back to back
+    # on the launch stream, events only at the two ends.
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(K):
-        ev[i][0].record(stream)
-        step(args.warmup + i, phases=1)
-        ev[i][1].record(stream)
-        step(args.warmup + i, phases=2)
-        ev[i][2].record(stream)
+        step(args.warmup + i)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
-    span_ms = ev[0][0].elapsed_time(ev[-1][2])
+    ms_per_step = ev0.elapsed_time(ev1) / K
+    value_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # Per-kernel pass for the roofline: the same K steps with the two phases
+    # of each call enqueued separately and an event around each launch.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        ev[i][0].record(stream)
+        step(args.warmup + K + i, phases=1)
+        ev[i][1].record(stream)
+        step(args.warmup + K + i, phases=2)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
     kern_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]))
     merge_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]))
-    ms_per_step = span_ms / K
-    value_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved_gbs = kv_bytes / (kern_ms * 1e-3) / 1e9
+    prof = profile_record(spec.name)
 
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(x, spec, args.cpu_seconds)
 
     workload = spec.name
+    # Useful matrix flops of one step: QK^T and PV, 2 flops per multiply-add.
+    flops = 2.0 * x.total_tokens * spec.num_q_heads * (spec.head_dim_k + spec.head_dim_v)
     rec = {
         "metric": "decode-attn KV GB/s (algorithmic K+V bytes / step time) and us/step, % of MI355X HBM peak",
         "value": round(value_gbs, 1),
@@ -211,9 +230,11 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-            "traffic": traffic_from_profile(workload),
+            "traffic": prof.get("hbm_bytes_per_launch"),
             "avg_launch_us": round(kern_ms * 1e3, 2),
             "merge_launch_us": round(merge_ms * 1e3, 2),
+            "mfma_busy": prof.get("mfma_busy_frac"),
+            "math_tflops": round(flops / (kern_ms * 1e-3) / 1e12, 2),
         },
         "cpu_baseline": cpu,
         "wall_ms_timed_region": round(wall_ms, 2),
