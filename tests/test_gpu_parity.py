@@ -117,6 +117,10 @@ GQA_EDGE = [
     ([129, 2, 70], 32, 1, 64, torch.float16),      # G = 32: two 16-head blocks
     ([96, 95, 97], 6, 2, 128, torch.bfloat16),     # G = 3 (padding heads)
     ([2000], 2, 1, 64, torch.float16),
+    # more than 64 sequences: the lookups take the looped path instead of the
+    # one-load boundary window; empty and one-token sequences mixed in
+    ([(i * 37) % 50 for i in range(100)], 8, 2, 128, torch.float16),
+    ([1] * 65, 4, 4, 64, torch.bfloat16),
 ]
 
 
@@ -133,6 +137,7 @@ MLA_EDGE = [
     ([0, 257, 31], 16, torch.float16),
     ([100, 3], 8, torch.bfloat16),
     ([70, 0, 150], 32, torch.bfloat16),
+    ([(i * 53) % 90 for i in range(80)], 16, torch.bfloat16),  # > 64 sequences
 ]
 
 
