@@ -196,6 +196,53 @@ ZL_API zl_status_t zl_decode_attn_mla_ex(const void *q, const void *kv_cache, co
                                   void *out, float *lse, int num_workers, int phases,
                                   void *workspace, size_t workspace_bytes, zl_stream_t stream);
 
+/*
+ * Paged caches.  Requests that share a prompt prefix can share its key/value
+ * rows when the cache is kept in fixed-size pages: the first ZhiLight page
+ * lists a prefix cache among the engine's features (section "功能生态") and
+ * places it in the C++ runtime's batch generator (section "技术架构"); the
+ * second page lists it beside fused batch attention for decoding (section
+ * "Dual streams, host all-reduce and the memory model").  The attention is
+ * the operation in the file header; only where a token's row lives changes:
+ *   token i of sequence b is row (i % page_size) of page
+ *   block_table[b * max_pages_per_seq + i / page_size]
+ *   k_pages, v_pages [num_pages, page_size, num_kv_heads, head_dim]  dtype
+ *   kv_pages         [num_pages, page_size, kv_lora_rank + rope_dim] dtype
+ *   block_table      [batch, max_pages_per_seq] int32 (device), every entry a
+ *                    sequence uses is a valid page id (precondition)
+ *   cu_seqlens       as above: the prefix sums of the sequence lengths (a
+ *                    logical numbering; no cache row sits at those indices)
+ *   page_size        a power of two, 16 .. 256 (else ZL_ERR_UNSUPPORTED)
+ *   max_seqlen_k <= max_pages_per_seq * page_size
+ * The workspace is sized by the same functions as for packed caches.  The
+ * _ex forms take num_workers and phases as above.
+ */
+ZL_API zl_status_t zl_decode_attn_gqa_paged(const void *q, const void *k_pages, const void *v_pages,
+                                            const int32_t *block_table, int max_pages_per_seq, int page_size,
+                                            const int32_t *cu_seqlens, int batch, int num_q_heads,
+                                            int num_kv_heads, int head_dim, int max_seqlen_k,
+                                            float softmax_scale, zl_dtype_t dtype, void *out, float *lse,
+                                            void *workspace, size_t workspace_bytes, zl_stream_t stream);
+ZL_API zl_status_t zl_decode_attn_gqa_paged_ex(const void *q, const void *k_pages, const void *v_pages,
+                                               const int32_t *block_table, int max_pages_per_seq,
+                                               int page_size, const int32_t *cu_seqlens, int batch,
+                                               int num_q_heads, int num_kv_heads, int head_dim,
+                                               int max_seqlen_k, float softmax_scale, zl_dtype_t dtype,
+                                               void *out, float *lse, int num_workers, int phases,
+                                               void *workspace, size_t workspace_bytes, zl_stream_t stream);
+ZL_API zl_status_t zl_decode_attn_mla_paged(const void *q, const void *kv_pages, const int32_t *block_table,
+                                            int max_pages_per_seq, int page_size, const int32_t *cu_seqlens,
+                                            int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
+                                            int max_seqlen_k, float softmax_scale, zl_dtype_t dtype,
+                                            void *out, float *lse, void *workspace, size_t workspace_bytes,
+                                            zl_stream_t stream);
+ZL_API zl_status_t zl_decode_attn_mla_paged_ex(const void *q, const void *kv_pages, const int32_t *block_table,
+                                               int max_pages_per_seq, int page_size, const int32_t *cu_seqlens,
+                                               int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
+                                               int max_seqlen_k, float softmax_scale, zl_dtype_t dtype,
+                                               void *out, float *lse, int num_workers, int phases,
+                                               void *workspace, size_t workspace_bytes, zl_stream_t stream);
+
 /* Static, human-readable name of a status code (host). */
 ZL_API const char *zl_status_string(zl_status_t status);
 

@@ -8,6 +8,8 @@ or no GPU is present, the calls raise.
 Entry points (same names as the C ABI):
   zl_decode_attn_gqa      grouped-query decode attention over a packed ragged cache
   zl_decode_attn_mla      absorbed multi-head latent attention decode
+  zl_decode_attn_gqa_paged / zl_decode_attn_mla_paged
+                          the same over paged caches (block table)
   zl_attn_combine         log-sum-exp combine of split partial results
   zl_decode_attn_workspace_size / zl_decode_attn_mla_workspace_size
   zl_status_string
@@ -49,6 +51,17 @@ SIGNATURES = {
                                     _c_int, _vp, _vp, _vp, _c_size, _vp]),
     "zl_decode_attn_mla_ex": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _c_float, _c_int, _vp, _vp, _c_int, _c_int, _vp, _c_size, _vp]),
+    "zl_decode_attn_gqa_paged": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _vp, _c_int, _c_int,
+                                          _c_int, _c_int, _c_int, _c_float, _c_int, _vp, _vp, _vp,
+                                          _c_size, _vp]),
+    "zl_decode_attn_gqa_paged_ex": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _vp, _c_int, _c_int,
+                                             _c_int, _c_int, _c_int, _c_float, _c_int, _vp, _vp, _c_int,
+                                             _c_int, _vp, _c_size, _vp]),
+    "zl_decode_attn_mla_paged": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _vp, _c_int, _c_int, _c_int,
+                                          _c_int, _c_int, _c_float, _c_int, _vp, _vp, _vp, _c_size, _vp]),
+    "zl_decode_attn_mla_paged_ex": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _vp, _c_int, _c_int, _c_int,
+                                             _c_int, _c_int, _c_float, _c_int, _vp, _vp, _c_int, _c_int,
+                                             _vp, _c_size, _vp]),
     "zl_attn_combine": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
     "zl_status_string": (ctypes.c_char_p, [_c_int]),
 }
@@ -209,6 +222,91 @@ def zl_decode_attn_mla(q, kv_cache, cu_seqlens, max_seqlen_k: int, softmax_scale
         float(softmax_scale), _DTYPE[q.dtype], _ptr(out), _ptr(lse), int(num_workers), int(phases),
         _ptr(workspace), workspace.numel(), _stream(stream, dev))
     _check(st, "zl_decode_attn_mla")
+    return (out, lse) if lse is not None else out
+
+
+def _paging_args(block_table, dev):
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    return _ptr(block_table), int(block_table.shape[1])
+
+
+def zl_decode_attn_gqa_paged(q, k_pages, v_pages, block_table, cu_seqlens, max_seqlen_k: int,
+                             softmax_scale: float, out=None, lse=None, workspace=None, num_workers: int = 0,
+                             stream=None, return_lse: bool = False, phases: int = 3):
+    """zl_decode_attn_gqa over paged caches: k_pages/v_pages [pages, page_size, Hkv, D],
+    block_table int32 [B, max_pages]; token i of sequence b is row i % page_size of page
+    block_table[b, i // page_size].  cu_seqlens int32 [B+1] holds the length prefix sums."""
+    _need(q, "q", ndim=3)
+    dev = q.device
+    if q.dtype not in _DTYPE:
+        raise ValueError("q must be float16 or bfloat16")
+    _need(k_pages, "k_pages", q.dtype, 4, dev)
+    _need(v_pages, "v_pages", q.dtype, 4, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1, dev)
+    table, max_pages = _paging_args(block_table, dev)
+    B, Hq, D = q.shape
+    _, page_size, Hkv, Dk = k_pages.shape
+    if Dk != D or v_pages.shape != k_pages.shape:
+        raise ValueError("k_pages / v_pages must be [pages, page_size, Hkv, head_dim] like q")
+    if cu_seqlens.numel() != B + 1 or block_table.shape[0] != B:
+        raise ValueError("cu_seqlens must have batch + 1 entries and block_table batch rows")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, 3, dev)
+    if out.shape != q.shape:
+        raise ValueError("out must be [B, Hq, head_dim]")
+    if lse is None and return_lse:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2, dev)
+    nbytes = zl_decode_attn_workspace_size(B, Hq, Hkv, D, max_seqlen_k, q.dtype, num_workers)
+    if workspace is None:
+        workspace = new_workspace(nbytes, dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    st = library().zl_decode_attn_gqa_paged_ex(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), table, max_pages, int(page_size), _ptr(cu_seqlens), B, Hq, Hkv,
+        D, int(max_seqlen_k), float(softmax_scale), _DTYPE[q.dtype], _ptr(out), _ptr(lse), int(num_workers),
+        int(phases), _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    _check(st, "zl_decode_attn_gqa_paged")
+    return (out, lse) if lse is not None else out
+
+
+def zl_decode_attn_mla_paged(q, kv_pages, block_table, cu_seqlens, max_seqlen_k: int, softmax_scale: float,
+                             kv_lora_rank: int = 512, rope_dim: int = 64, out=None, lse=None, workspace=None,
+                             num_workers: int = 0, stream=None, return_lse: bool = False, phases: int = 3):
+    """zl_decode_attn_mla over a paged latent pool kv_pages [pages, page_size, rank+rope]."""
+    _need(q, "q", ndim=3)
+    dev = q.device
+    if q.dtype not in _DTYPE:
+        raise ValueError("q must be float16 or bfloat16")
+    _need(kv_pages, "kv_pages", q.dtype, 3, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1, dev)
+    table, max_pages = _paging_args(block_table, dev)
+    B, H, Dk = q.shape
+    page_size = kv_pages.shape[1]
+    if Dk != kv_lora_rank + rope_dim or kv_pages.shape[2] != Dk:
+        raise ValueError("q and kv_pages rows must be kv_lora_rank + rope_dim wide")
+    if cu_seqlens.numel() != B + 1 or block_table.shape[0] != B:
+        raise ValueError("cu_seqlens must have batch + 1 entries and block_table batch rows")
+    if out is None:
+        out = torch.empty(B, H, kv_lora_rank, dtype=q.dtype, device=dev)
+    _need(out, "out", q.dtype, 3, dev)
+    if tuple(out.shape) != (B, H, kv_lora_rank):
+        raise ValueError("out must be [B, H, kv_lora_rank]")
+    if lse is None and return_lse:
+        lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2, dev)
+    nbytes = zl_decode_attn_mla_workspace_size(B, H, kv_lora_rank, rope_dim, max_seqlen_k, q.dtype,
+                                               num_workers)
+    if workspace is None:
+        workspace = new_workspace(nbytes, dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    st = library().zl_decode_attn_mla_paged_ex(
+        _ptr(q), _ptr(kv_pages), table, max_pages, int(page_size), _ptr(cu_seqlens), B, H, kv_lora_rank,
+        rope_dim, int(max_seqlen_k), float(softmax_scale), _DTYPE[q.dtype], _ptr(out), _ptr(lse),
+        int(num_workers), int(phases), _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    _check(st, "zl_decode_attn_mla_paged")
     return (out, lse) if lse is not None else out
 
 

@@ -124,6 +124,20 @@ __device__ __forceinline__ void dma_tile(const char* rows, uint32_t row_bytes, c
   }
 }
 
+// The same tile from a paged cache: row r is token l0 + min(r, nvalid - 1) of
+// its sequence, in row (l & (page - 1)) of page tp.page_of(l) of the pool.
+template <int L, int NI>
+__device__ __forceinline__ void dma_tile_paged(const char* pool, uint32_t row_bytes, const TileMap<L, NI>& m,
+                                               const TilePages& tp, int l0, int nvalid, ZL_LDS char* dst) {
+  const int mask = (1 << tp.shift) - 1;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int l = l0 + (m.row[i] < nvalid ? m.row[i] : nvalid - 1);
+    const size_t row = ((size_t)tp.page_of(l) << tp.shift) | (size_t)(l & mask);
+    dma16(pool + row * row_bytes + m.chunk[i], dst + i * 1024);
+  }
+}
+
 // The query item of a segment: rows h0 .. h0+15 (padding rows repeat h0; their
 // results are never stored) in the K-row slot layout, repeated to fill the
 // item's PER_TILE instructions so that every ring item costs the same.
@@ -141,10 +155,10 @@ __device__ __forceinline__ void dma_query_item(const uint16_t* qb, int nh, ZL_LD
   }
 }
 
-template <int L, int DT>
+template <int L, int DT, bool PAGED>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, 64),
                           amdgpu_waves_per_eu(1, Geo<L>::MAX_WAVES_PER_SIMD))) void
-decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
+decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __restrict__ block_table) {
   using TL = Tile<L>;
   using GE = Geo<L>;
   constexpr int STAGES = GE::STAGES;
@@ -202,10 +216,19 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
       const int k = dj - 1;
       const int tok = ds.t0 + 32 * k;
       const int nv = min(32, ds.len - 32 * k);
-      dma_tile<L, TL::NI_K>((const char*)(a.k + (long long)kvh * DK) + (size_t)tok * k_row_bytes, k_row_bytes,
-                            kmap, nv, st);
-      dma_tile<L, TL::NI_V>((const char*)(a.v + (long long)kvh * DV) + (size_t)tok * v_row_bytes, v_row_bytes,
-                            vmap, nv, st + TL::KBYTES);
+      if constexpr (PAGED) {
+        const int l0 = tok - ds.cs;
+        const TilePages tp =
+            tile_pages(block_table + (long long)ds.b * a.max_pages, l0, nv, a.page_shift);
+        dma_tile_paged<L, TL::NI_K>((const char*)(a.k + (long long)kvh * DK), k_row_bytes, kmap, tp, l0, nv, st);
+        dma_tile_paged<L, TL::NI_V>((const char*)(a.v + (long long)kvh * DV), v_row_bytes, vmap, tp, l0, nv,
+                                    st + TL::KBYTES);
+      } else {
+        dma_tile<L, TL::NI_K>((const char*)(a.k + (long long)kvh * DK) + (size_t)tok * k_row_bytes, k_row_bytes,
+                              kmap, nv, st);
+        dma_tile<L, TL::NI_V>((const char*)(a.v + (long long)kvh * DV) + (size_t)tok * v_row_bytes, v_row_bytes,
+                              vmap, nv, st + TL::KBYTES);
+      }
     }
     ++issued;
     if (++dj > ntl) {
@@ -303,7 +326,10 @@ int default_workers(Layout layout) {
 
 template <int L, int DT>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<L, DT>), dim3(a.P), dim3(64), 0, stream, a, a.cu);
+  if (a.block_table)
+    hipLaunchKernelGGL((decode_kernel<L, DT, true>), dim3(a.P), dim3(64), 0, stream, a, a.cu, a.block_table);
+  else
+    hipLaunchKernelGGL((decode_kernel<L, DT, false>), dim3(a.P), dim3(64), 0, stream, a, a.cu, a.block_table);
   return hipGetLastError();
 }
 

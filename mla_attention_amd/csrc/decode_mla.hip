@@ -107,6 +107,21 @@ __device__ __forceinline__ void dma_quarter(const uint16_t* rows, int tok0, int 
   }
 }
 
+// The same quarter from a paged pool: row r is token l0 + min(r, nvalid - 1)
+// of its sequence, in row (l & (page - 1)) of page tp.page_of(l).
+__device__ __forceinline__ void dma_quarter_paged(const uint16_t* pool, const TilePages& tp, int l0, int nvalid,
+                                                  const QuarterMap& m, ZL_LDS char* dst, int wave) {
+  const int mask = (1 << tp.shift) - 1;
+#pragma unroll
+  for (int k = 0; k < kNIw; ++k) {
+    const int r = m.row[k];
+    const int l = l0 + (r < nvalid ? r : nvalid - 1);
+    const size_t row = ((size_t)tp.page_of(l) << tp.shift) | (size_t)(l & mask);
+    const uint32_t chunk = m.off[k] - (uint32_t)r * kRowB;
+    dma16((const char*)pool + row * kRowB + chunk, dst + (wave * kNIw + k) * 1024);
+  }
+}
+
 // The query item of a segment: rows h0 .. h0+15 (rows past nh repeat h0) in
 // the tile's slot layout, 18 KB, loaded twice so that it costs the same nine
 // instructions per wave as a tile (the second copy is never read).
@@ -144,10 +159,10 @@ __device__ __forceinline__ f32x4 half_scores(const ZL_LDS char* kt, const i16x8 
   return acc0 + acc1;
 }
 
-template <int DT>
+template <int DT, bool PAGED>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kWaves, 64 * kWaves),
                           amdgpu_waves_per_eu(1, 1))) void
-mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
+mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __restrict__ block_table) {
   // One LDS object only (see decode_attn.hip): [4 ring stages][score exchange].
   __shared__ __attribute__((aligned(1024))) char smem_raw[kLdsBytes];
   ZL_LDS char* smem = (ZL_LDS char*)smem_raw;
@@ -198,7 +213,14 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
       dma_query_item(a.q + ((long long)ds.b * a.Hq + h0) * kDK, min(kHeadsPerUnit, a.G - h0), dst, wave, lane);
     } else {
       const int k = dj - 1;
-      dma_quarter(a.k, ds.t0 + 32 * k, min(32, ds.len - 32 * k), qmap, dst, wave);
+      const int nv = min(32, ds.len - 32 * k);
+      if constexpr (PAGED) {
+        const int l0 = ds.t0 + 32 * k - ds.cs;
+        const TilePages tp = tile_pages(block_table + (long long)ds.b * a.max_pages, l0, nv, a.page_shift);
+        dma_quarter_paged(a.k, tp, l0, nv, qmap, dst, wave);
+      } else {
+        dma_quarter(a.k, ds.t0 + 32 * k, nv, qmap, dst, wave);
+      }
     }
     ++issued;
     if (++dj > ntl) {
@@ -294,10 +316,18 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu) {
 int mla_default_workers() { return 256 * kWorkgroupsPerCU; }
 
 hipError_t launch_mla(const DecodeArgs& a, int dtype, hipStream_t stream) {
-  if (dtype == kF16)
-    hipLaunchKernelGGL(mla_decode_kernel<kF16>, dim3(a.P), dim3(64 * kWaves), 0, stream, a, a.cu);
-  else
-    hipLaunchKernelGGL(mla_decode_kernel<kBF16>, dim3(a.P), dim3(64 * kWaves), 0, stream, a, a.cu);
+  const dim3 grid(a.P), block(64 * kWaves);
+  if (a.block_table) {
+    if (dtype == kF16)
+      hipLaunchKernelGGL((mla_decode_kernel<kF16, true>), grid, block, 0, stream, a, a.cu, a.block_table);
+    else
+      hipLaunchKernelGGL((mla_decode_kernel<kBF16, true>), grid, block, 0, stream, a, a.cu, a.block_table);
+  } else {
+    if (dtype == kF16)
+      hipLaunchKernelGGL((mla_decode_kernel<kF16, false>), grid, block, 0, stream, a, a.cu, a.block_table);
+    else
+      hipLaunchKernelGGL((mla_decode_kernel<kBF16, false>), grid, block, 0, stream, a, a.cu, a.block_table);
+  }
   return hipGetLastError();
 }
 

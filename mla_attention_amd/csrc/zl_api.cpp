@@ -111,12 +111,35 @@ size_t zl_decode_attn_workspace_size_ex(int batch, int num_q_heads, int num_kv_h
   return gqa_ws_size(batch, num_q_heads, num_kv_heads, head_dim, max_seqlen_k, dtype, num_workers);
 }
 
-zl_status_t zl_decode_attn_gqa_ex(const void* q, const void* k_cache, const void* v_cache,
-                                  const int32_t* cu_seqlens, int batch, int num_q_heads,
-                                  int num_kv_heads, int head_dim, int max_seqlen_k,
-                                  float softmax_scale, zl_dtype_t dtype, void* out, float* lse,
-                                  int num_workers, int phases, void* workspace,
-                                  size_t workspace_bytes, zl_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Paging parameters: a block table, its row length and the page size (a power
+// of two, 16 .. 256 tokens; tiles of 32 tokens then touch at most 3 pages).
+struct Paging {
+  const int32_t* table = nullptr;
+  int max_pages = 0;
+  int page_size = 0;
+};
+
+zl_status_t check_paging(const Paging& pg, int max_seqlen_k, int& shift) {
+  shift = 0;
+  if (!pg.table) return ZL_OK;
+  if (!aligned(pg.table, 4)) return ZL_ERR_INVALID_ARGUMENT;
+  if (pg.page_size < 16 || pg.page_size > 256 || (pg.page_size & (pg.page_size - 1)) != 0)
+    return ZL_ERR_UNSUPPORTED;
+  if (pg.max_pages < 1 || pg.max_pages > (1 << 24)) return ZL_ERR_INVALID_ARGUMENT;
+  if ((long long)max_seqlen_k > (long long)pg.max_pages * pg.page_size) return ZL_ERR_INVALID_ARGUMENT;
+  while ((1 << shift) < pg.page_size) ++shift;
+  return ZL_OK;
+}
+
+zl_status_t gqa_impl(const void* q, const void* k_cache, const void* v_cache, const Paging& pg,
+                     const int32_t* cu_seqlens, int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                     int max_seqlen_k, float softmax_scale, zl_dtype_t dtype, void* out, float* lse,
+                     int num_workers, int phases, void* workspace, size_t workspace_bytes,
+                     zl_stream_t stream) {
   if (num_workers < 0 || phases < 1 || phases > 3) return ZL_ERR_INVALID_ARGUMENT;
   if (head_dim != 64 && head_dim != 128) {
     if (head_dim <= 0) return ZL_ERR_INVALID_ARGUMENT;
@@ -127,6 +150,9 @@ zl_status_t zl_decode_attn_gqa_ex(const void* q, const void* k_cache, const void
   const zl_status_t st = check_common(batch, num_q_heads, num_kv_heads, max_seqlen_k, dtype, P);
   if (st != ZL_OK) return st;
   if (!std::isfinite(softmax_scale)) return ZL_ERR_INVALID_ARGUMENT;
+  int shift = 0;
+  const zl_status_t sp = check_paging(pg, max_seqlen_k, shift);
+  if (sp != ZL_OK) return sp;
   if (batch == 0) return ZL_OK;
   // k_cache / v_cache may be NULL only when every sequence is empty (the
   // kernel never reads a cache row then); the host cannot see the lengths.
@@ -147,8 +173,55 @@ zl_status_t zl_decode_attn_gqa_ex(const void* q, const void* k_cache, const void
   a.G = num_q_heads / num_kv_heads;
   a.HB = head_blocks(a.G);
   a.P = P;
+  a.block_table = pg.table;
+  a.max_pages = pg.max_pages;
+  a.page_shift = shift;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   return run_decode(a, layout, head_dim, dtype, phases, workspace, workspace_bytes, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+zl_status_t zl_decode_attn_gqa_ex(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* cu_seqlens, int batch, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int max_seqlen_k,
+                                  float softmax_scale, zl_dtype_t dtype, void* out, float* lse,
+                                  int num_workers, int phases, void* workspace,
+                                  size_t workspace_bytes, zl_stream_t stream) {
+  return gqa_impl(q, k_cache, v_cache, Paging{}, cu_seqlens, batch, num_q_heads, num_kv_heads, head_dim,
+                  max_seqlen_k, softmax_scale, dtype, out, lse, num_workers, phases, workspace,
+                  workspace_bytes, stream);
+}
+
+zl_status_t zl_decode_attn_gqa_paged_ex(const void* q, const void* k_pages, const void* v_pages,
+                                        const int32_t* block_table, int max_pages_per_seq, int page_size,
+                                        const int32_t* cu_seqlens, int batch, int num_q_heads,
+                                        int num_kv_heads, int head_dim, int max_seqlen_k,
+                                        float softmax_scale, zl_dtype_t dtype, void* out, float* lse,
+                                        int num_workers, int phases, void* workspace,
+                                        size_t workspace_bytes, zl_stream_t stream) {
+  if (!block_table) return ZL_ERR_INVALID_ARGUMENT;
+  Paging pg;
+  pg.table = block_table;
+  pg.max_pages = max_pages_per_seq;
+  pg.page_size = page_size;
+  return gqa_impl(q, k_pages, v_pages, pg, cu_seqlens, batch, num_q_heads, num_kv_heads, head_dim,
+                  max_seqlen_k, softmax_scale, dtype, out, lse, num_workers, phases, workspace,
+                  workspace_bytes, stream);
+}
+
+zl_status_t zl_decode_attn_gqa_paged(const void* q, const void* k_pages, const void* v_pages,
+                                     const int32_t* block_table, int max_pages_per_seq, int page_size,
+                                     const int32_t* cu_seqlens, int batch, int num_q_heads,
+                                     int num_kv_heads, int head_dim, int max_seqlen_k, float softmax_scale,
+                                     zl_dtype_t dtype, void* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, zl_stream_t stream) {
+  return zl_decode_attn_gqa_paged_ex(q, k_pages, v_pages, block_table, max_pages_per_seq, page_size,
+                                     cu_seqlens, batch, num_q_heads, num_kv_heads, head_dim, max_seqlen_k,
+                                     softmax_scale, dtype, out, lse, 0, 3, workspace, workspace_bytes,
+                                     stream);
 }
 
 zl_status_t zl_decode_attn_gqa(const void* q, const void* k_cache, const void* v_cache,
@@ -173,11 +246,14 @@ size_t zl_decode_attn_mla_workspace_size_ex(int batch, int num_q_heads, int kv_l
   return mla_ws_size(batch, num_q_heads, kv_lora_rank, rope_dim, max_seqlen_k, dtype, num_workers);
 }
 
-zl_status_t zl_decode_attn_mla_ex(const void* q, const void* kv_cache, const int32_t* cu_seqlens,
-                                  int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
-                                  int max_seqlen_k, float softmax_scale, zl_dtype_t dtype,
-                                  void* out, float* lse, int num_workers, int phases,
-                                  void* workspace, size_t workspace_bytes, zl_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+zl_status_t mla_impl(const void* q, const void* kv_cache, const Paging& pg, const int32_t* cu_seqlens, int batch,
+                     int num_q_heads, int kv_lora_rank, int rope_dim, int max_seqlen_k, float softmax_scale,
+                     zl_dtype_t dtype, void* out, float* lse, int num_workers, int phases, void* workspace,
+                     size_t workspace_bytes, zl_stream_t stream) {
   if (num_workers < 0 || phases < 1 || phases > 3) return ZL_ERR_INVALID_ARGUMENT;
   if (kv_lora_rank <= 0 || rope_dim < 0) return ZL_ERR_INVALID_ARGUMENT;
   if (kv_lora_rank != 512 || rope_dim != 64) return ZL_ERR_UNSUPPORTED;
@@ -185,6 +261,9 @@ zl_status_t zl_decode_attn_mla_ex(const void* q, const void* kv_cache, const int
   const zl_status_t st = check_common(batch, num_q_heads, 1, max_seqlen_k, dtype, P);
   if (st != ZL_OK) return st;
   if (!std::isfinite(softmax_scale)) return ZL_ERR_INVALID_ARGUMENT;
+  int shift = 0;
+  const zl_status_t sp = check_paging(pg, max_seqlen_k, shift);
+  if (sp != ZL_OK) return sp;
   if (batch == 0) return ZL_OK;
   if (!q || !cu_seqlens || !out) return ZL_ERR_INVALID_ARGUMENT;  // kv_cache: see above
   if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(cu_seqlens, 4) ||
@@ -203,8 +282,49 @@ zl_status_t zl_decode_attn_mla_ex(const void* q, const void* kv_cache, const int
   a.G = num_q_heads;
   a.HB = head_blocks(num_q_heads);
   a.P = P;
+  a.block_table = pg.table;
+  a.max_pages = pg.max_pages;
+  a.page_shift = shift;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   return run_decode(a, zl::kMla576, kv_lora_rank, dtype, phases, workspace, workspace_bytes, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+zl_status_t zl_decode_attn_mla_ex(const void* q, const void* kv_cache, const int32_t* cu_seqlens,
+                                  int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
+                                  int max_seqlen_k, float softmax_scale, zl_dtype_t dtype,
+                                  void* out, float* lse, int num_workers, int phases,
+                                  void* workspace, size_t workspace_bytes, zl_stream_t stream) {
+  return mla_impl(q, kv_cache, Paging{}, cu_seqlens, batch, num_q_heads, kv_lora_rank, rope_dim, max_seqlen_k,
+                  softmax_scale, dtype, out, lse, num_workers, phases, workspace, workspace_bytes, stream);
+}
+
+zl_status_t zl_decode_attn_mla_paged_ex(const void* q, const void* kv_pages, const int32_t* block_table,
+                                        int max_pages_per_seq, int page_size, const int32_t* cu_seqlens,
+                                        int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
+                                        int max_seqlen_k, float softmax_scale, zl_dtype_t dtype, void* out,
+                                        float* lse, int num_workers, int phases, void* workspace,
+                                        size_t workspace_bytes, zl_stream_t stream) {
+  if (!block_table) return ZL_ERR_INVALID_ARGUMENT;
+  Paging pg;
+  pg.table = block_table;
+  pg.max_pages = max_pages_per_seq;
+  pg.page_size = page_size;
+  return mla_impl(q, kv_pages, pg, cu_seqlens, batch, num_q_heads, kv_lora_rank, rope_dim, max_seqlen_k,
+                  softmax_scale, dtype, out, lse, num_workers, phases, workspace, workspace_bytes, stream);
+}
+
+zl_status_t zl_decode_attn_mla_paged(const void* q, const void* kv_pages, const int32_t* block_table,
+                                     int max_pages_per_seq, int page_size, const int32_t* cu_seqlens,
+                                     int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
+                                     int max_seqlen_k, float softmax_scale, zl_dtype_t dtype, void* out,
+                                     float* lse, void* workspace, size_t workspace_bytes, zl_stream_t stream) {
+  return zl_decode_attn_mla_paged_ex(q, kv_pages, block_table, max_pages_per_seq, page_size, cu_seqlens, batch,
+                                     num_q_heads, kv_lora_rank, rope_dim, max_seqlen_k, softmax_scale, dtype, out,
+                                     lse, 0, 3, workspace, workspace_bytes, stream);
 }
 
 zl_status_t zl_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* cu_seqlens,

@@ -31,6 +31,12 @@ struct DecodeArgs {
   float* part_o;        // [2P, 16, Dv]
   float* part_lse;      // [2P, kLseSlot] (first 16 used)
   int* first_key;       // [P]: (unit, sequence) of each run's first segment
+  // Paged caches (block table): k / v are page pools [pages, 2^page_shift,
+  // row]; token i of sequence b lives in page block_table[b*max_pages +
+  // (i >> page_shift)], row i & (2^page_shift - 1).  block_table == nullptr:
+  // packed caches, token t (cu numbering) is row t.
+  const int32_t* block_table;
+  int max_pages, page_shift;
   int B, Hq, Hkv, G, HB, P;
   int seg_cost;         // phantom positions per sequence (zl_split.h)
   float scale_log2;     // softmax_scale * log2(e)

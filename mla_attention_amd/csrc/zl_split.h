@@ -158,6 +158,33 @@ __device__ __forceinline__ Segment segment_at(long long p, long long p_end, cons
   return s;
 }
 
+// The pages of one 32-token tile of a paged cache: tokens l0 .. l0+nvalid-1
+// of one sequence (l counted from the sequence's start) lie in at most three
+// consecutive pages when pages hold 16 or more tokens.  The page ids are read
+// with scalar loads (the block table row is wave-uniform); page_of(l) then
+// selects a lane's page without memory traffic.
+struct TilePages {
+  int pi0;       // page index (in the sequence's list) of token l0
+  int p0, p1, p2;  // page ids of pages pi0, pi0+1, pi0+2 (clamped to the last used)
+  int shift;
+
+  __device__ __forceinline__ int page_of(int l) const {
+    const int d = (l >> shift) - pi0;
+    return d == 0 ? p0 : (d == 1 ? p1 : p2);
+  }
+};
+
+__device__ __forceinline__ TilePages tile_pages(const int32_t* table_row, int l0, int nvalid, int shift) {
+  TilePages tp;
+  tp.shift = shift;
+  tp.pi0 = l0 >> shift;
+  const int pil = (l0 + nvalid - 1) >> shift;
+  tp.p0 = table_row[tp.pi0];
+  tp.p1 = table_row[tp.pi0 + 1 < pil ? tp.pi0 + 1 : pil];
+  tp.p2 = table_row[tp.pi0 + 2 < pil ? tp.pi0 + 2 : pil];
+  return tp;
+}
+
 // Key of (unit u, sequence b) in first_key.
 __device__ __forceinline__ int seq_key(int u, int b, int B) { return u * B + b; }
 

@@ -187,3 +187,38 @@ def combine(part_out, part_lse):
     _load().zo_combine(po.ctypes.data_as(_f64p), pl.ctypes.data_as(_f64p), S, rows, dv,
                        out.ctypes.data_as(_f64p), lse.ctypes.data_as(_f64p))
     return out, lse
+
+
+def gather_paged(pages, block_table, cu_seqlens, page_size: int):
+    """Paged cache -> packed rows: row cu[b] + i of the result is row
+    i % page_size of page block_table[b, i // page_size] (the paged layout's
+    definition; pure data movement, no arithmetic).  pages [P, page_size, ...]."""
+    pages = np.asarray(pages)
+    table = np.asarray(block_table)
+    cu = np.asarray(cu_seqlens).astype(np.int64)
+    if pages.shape[1] != page_size:
+        raise ValueError("pages must be [num_pages, page_size, ...]")
+    T = int(cu[-1])
+    out = np.empty((T,) + pages.shape[2:], dtype=pages.dtype)
+    for b in range(len(cu) - 1):
+        for i in range(int(cu[b + 1] - cu[b])):
+            out[cu[b] + i] = pages[table[b, i // page_size], i % page_size]
+    return out
+
+
+def gqa_decode_paged(q, k_pages, v_pages, block_table, cu_seqlens, num_kv_heads: int, scale: float,
+                     dtype: int, pairs=None, threads: int = 0):
+    """Decode attention over paged caches: the plain definition applied to
+    the gathered rows."""
+    ps = np.asarray(k_pages).shape[1]
+    k = gather_paged(k_pages, block_table, cu_seqlens, ps)
+    v = gather_paged(v_pages, block_table, cu_seqlens, ps)
+    return gqa_decode(q, k, v, cu_seqlens, num_kv_heads, scale, dtype, pairs=pairs, threads=threads)
+
+
+def mla_decode_paged(q, kv_pages, block_table, cu_seqlens, scale: float, dtype: int, kv_lora_rank: int = 512,
+                     rope_dim: int = 64, pairs=None, threads: int = 0):
+    """Absorbed MLA decode over a paged latent pool (gather, then the plain form)."""
+    ps = np.asarray(kv_pages).shape[1]
+    c = gather_paged(kv_pages, block_table, cu_seqlens, ps)
+    return mla_decode(q, c, cu_seqlens, scale, dtype, kv_lora_rank, rope_dim, pairs=pairs, threads=threads)

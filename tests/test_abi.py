@@ -118,3 +118,36 @@ def test_mla_and_combine_reject_bad_arguments(zl):
     assert comb(S=0) == 1 and comb(S=1025) == 1 and comb(Dv=6) == 1 and comb(H=0) == 1
     assert comb(po=None) == 1 and comb(po=A + 4) == 1 and comb(dt=5) == 1
     assert comb(B=0, po=None, pl=None, out=None) == 0
+
+
+def test_paged_entry_points_reject_bad_arguments(zl):
+    lib = zl.library()
+
+    def gqa_paged(**kw):
+        a = dict(q=A, k=A, v=A, table=A, maxp=8, ps=16, cu=A, B=4, Hq=8, Hkv=2, D=128, maxL=128, scale=0.125,
+                 dt=0, out=A, lse=None, workers=0, phases=3, ws=A, wsb=BIG, stream=None)
+        a.update(kw)
+        return lib.zl_decode_attn_gqa_paged_ex(a["q"], a["k"], a["v"], a["table"], a["maxp"], a["ps"], a["cu"],
+                                               a["B"], a["Hq"], a["Hkv"], a["D"], a["maxL"], a["scale"], a["dt"],
+                                               a["out"], a["lse"], a["workers"], a["phases"], a["ws"], a["wsb"],
+                                               a["stream"])
+
+    def mla_paged(**kw):
+        a = dict(q=A, c=A, table=A, maxp=4, ps=64, cu=A, B=2, H=16, r=512, rope=64, maxL=200, scale=0.07,
+                 dt=1, out=A, lse=None, workers=0, phases=3, ws=A, wsb=BIG, stream=None)
+        a.update(kw)
+        return lib.zl_decode_attn_mla_paged_ex(a["q"], a["c"], a["table"], a["maxp"], a["ps"], a["cu"], a["B"],
+                                               a["H"], a["r"], a["rope"], a["maxL"], a["scale"], a["dt"],
+                                               a["out"], a["lse"], a["workers"], a["phases"], a["ws"],
+                                               a["wsb"], a["stream"])
+    # page size: a power of two in 16 .. 256
+    for ps, expect in [(8, 2), (24, 2), (512, 2), (0, 2), (16, 0), (256, 0)]:
+        got = gqa_paged(ps=ps, maxp=64, B=0, q=None, k=None, v=None, cu=None, out=None, ws=None)
+        assert got == expect, (ps, got)
+    assert gqa_paged(table=None) == 1 and gqa_paged(table=A + 2) == 1
+    assert gqa_paged(maxp=0) == 1
+    assert gqa_paged(maxL=129) == 1          # longer than 8 pages of 16
+    assert gqa_paged(D=96) == 2 and gqa_paged(q=None) == 1 and gqa_paged(wsb=16) == 3
+    assert mla_paged(ps=48) == 2 and mla_paged(table=None) == 1 and mla_paged(maxL=257) == 1
+    assert mla_paged(r=256) == 2 and mla_paged(wsb=8) == 3
+    assert mla_paged(B=0, q=None, c=None, cu=None, out=None, ws=None) == 0

@@ -415,3 +415,40 @@ def test_golden_worked_examples(case):
     out, lse = run_gqa(q, k, v, workloads.cu_from_lens([k.shape[0]]), 1, scale, torch.float16)
     np.testing.assert_allclose(out[0, 0], ev(case["out"]), rtol=1e-14, atol=1e-15)
     assert lse[0, 0] == pytest.approx(ev(case["lse"]), rel=1e-14, abs=1e-15)
+
+
+# ------------------------------------------------------------ paged caches
+def test_gather_paged_hand_example():
+    """A hand-laid pool: two sequences (3 and 2 tokens), pages of 2 rows.
+    Sequence 0 uses pages 2 then 0, sequence 1 uses page 1; row values name
+    their (page, row)."""
+    pages = np.array([[[0], [1]], [[10], [11]], [[20], [21]]], dtype=np.uint16)  # [page, row, width 1]
+    table = np.array([[2, 0], [1, 1]], dtype=np.int32)
+    cu = np.array([0, 3, 5], dtype=np.int32)
+    got = oracle.gather_paged(pages, table, cu, 2)
+    assert got[:, 0].tolist() == [20, 21, 0, 10, 11]
+
+
+def test_gather_paged_inverts_the_pool_layout():
+    """The oracle's gather undoes the shuffled page pool built by the input
+    generator (an independent scatter), for several page sizes."""
+    x = workloads.make_inputs(workloads.CONFIGS[1])
+    for ps in (16, 32, 64):
+        p = workloads.make_paged(x, ps, seed=ps)
+        k = oracle.gather_paged(p.k_pages.view(torch.int16).numpy().view(np.uint16), p.block_table.numpy(),
+                                x.cu_seqlens.numpy(), ps)
+        assert np.array_equal(k, x.bits("k")), ps
+
+
+def test_paged_decode_equals_packed_decode():
+    """Attention over the paged layout is the attention over the same rows
+    packed (the layout changes where rows live, not what is computed)."""
+    spec = workloads.with_shape(workloads.CONFIGS[1], lens=(17, 0, 33, 64))
+    x = workloads.make_inputs(spec)
+    p = workloads.make_paged(x, 16, seed=3)
+    u16 = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+    o1, l1 = oracle.gqa_decode(x.bits("q"), x.bits("k"), x.bits("v"), x.cu_seqlens.numpy(), 2, spec.scale,
+                               oracle.F16)
+    o2, l2 = oracle.gqa_decode_paged(x.bits("q"), u16(p.k_pages), u16(p.v_pages), p.block_table.numpy(),
+                                     x.cu_seqlens.numpy(), 2, spec.scale, oracle.F16)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)

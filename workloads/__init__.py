@@ -161,3 +161,59 @@ def make_inputs(spec: Spec, seed: Optional[int] = None, lens: Optional[Sequence[
 def with_shape(spec: Spec, **changes) -> Spec:
     """A copy of `spec` with some fields replaced (for edge-case tests)."""
     return dataclasses.replace(spec, **changes)
+
+
+@dataclasses.dataclass
+class PagedInputs:
+    """The caches of an Inputs batch laid out in fixed-size pages, as a serving
+    engine's page pool holds them: pages of each sequence are placed at
+    seeded random pool positions (pool pages that no sequence uses stay filled
+    with other random data), and block_table lists each sequence's pages in
+    order.  Token i of sequence b is row i % page_size of page
+    block_table[b, i // page_size]."""
+    page_size: int
+    block_table: torch.Tensor          # int32 [B, max_pages]
+    k_pages: Optional[torch.Tensor] = None   # [pages, page_size, Hkv, D]
+    v_pages: Optional[torch.Tensor] = None
+    kv_pages: Optional[torch.Tensor] = None  # [pages, page_size, Dk] (MLA)
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.block_table.shape[1])
+
+
+def make_paged(x: Inputs, page_size: int, seed: int = 0, spare_pages: int = 3) -> PagedInputs:
+    """Scatter the packed caches of `x` into a shuffled page pool (data layout
+    only).  Unused table entries and spare pool pages hold values that a
+    correct kernel never reads."""
+    gen = torch.Generator("cpu")
+    gen.manual_seed(1000 + seed)
+    lens = [int(v) for v in x.lens]
+    cu = x.cu_seqlens.numpy().astype(np.int64)
+    npages_seq = [(L + page_size - 1) // page_size for L in lens]
+    max_pages = max(1, max(npages_seq) if npages_seq else 1)
+    total = sum(npages_seq) + spare_pages
+    perm = torch.randperm(total, generator=gen).numpy()
+    table = np.full((len(lens), max_pages), total - 1, dtype=np.int32)  # unused entries: some valid id
+    nxt = 0
+    for b, npg in enumerate(npages_seq):
+        for i in range(npg):
+            table[b, i] = perm[nxt]
+            nxt += 1
+    rows_of = []  # (pool page, packed token range) for the scatter
+    for b, npg in enumerate(npages_seq):
+        for i in range(npg):
+            t0 = cu[b] + i * page_size
+            t1 = min(cu[b + 1], t0 + page_size)
+            rows_of.append((table[b, i], t0, t1))
+
+    def scatter(src: torch.Tensor) -> torch.Tensor:
+        pool = torch.randn((total, page_size) + tuple(src.shape[1:]), generator=gen).to(src.dtype)
+        for page, t0, t1 in rows_of:
+            pool[page, : t1 - t0] = src[t0:t1]
+        return pool
+
+    bt = torch.from_numpy(table)
+    if x.latent is not None:
+        return PagedInputs(page_size, bt, kv_pages=scatter(x.latent))
+    return PagedInputs(page_size, bt, k_pages=scatter(x.k), v_pages=scatter(x.v))
