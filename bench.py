@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
                     help="workload (default 2: batch 32, 32/8 heads, D 128, ragged 512..4096)")
     ap.add_argument("--workers", type=int, default=0, help="decode workers (0 = library default)")
+    ap.add_argument("--paged", type=int, default=0, metavar="PAGE_SIZE",
+                    help="read the caches from a shuffled page pool through a block table "
+                         "(pages of PAGE_SIZE tokens; 0 = packed rows)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target host time of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
@@ -121,12 +124,18 @@ def main():
         reps = 1
     cu = x.cu_seqlens.to(dev)
     q = x.q.to(dev)
+    paged = workloads.make_paged(x, args.paged) if args.paged else None
+    table = paged.block_table.to(dev) if paged else None
+    if paged:
+        pools = (paged.kv_pages,) if spec.kind == "mla" else (paged.k_pages, paged.v_pages)
+        caches = [tuple(t.to(dev) for t in pools) for _ in range(reps)]
+    else:
+        caches = [(x.latent.to(dev),) if spec.kind == "mla" else (x.k.to(dev), x.v.to(dev))
+                  for _ in range(reps)]
     if spec.kind == "mla":
-        caches = [(x.latent.to(dev),) for _ in range(reps)]
         ws_bytes = zl.zl_decode_attn_mla_workspace_size(spec.batch, spec.num_q_heads, 512, 64,
                                                         x.max_seqlen, spec.torch_dtype, args.workers)
     else:
-        caches = [(x.k.to(dev), x.v.to(dev)) for _ in range(reps)]
         ws_bytes = zl.zl_decode_attn_workspace_size(spec.batch, spec.num_q_heads, spec.num_kv_heads,
                                                     spec.head_dim_k, x.max_seqlen, spec.torch_dtype,
                                                     args.workers)
@@ -137,7 +146,13 @@ def main():
 
     def step(i, phases=3):
         c = caches[i % reps]
-        if spec.kind == "mla":
+        if paged and spec.kind == "mla":
+            zl.zl_decode_attn_mla_paged(q, c[0], table, cu, x.max_seqlen, spec.scale, out=out, lse=lse,
+                                        workspace=ws, num_workers=args.workers, stream=stream, phases=phases)
+        elif paged:
+            zl.zl_decode_attn_gqa_paged(q, c[0], c[1], table, cu, x.max_seqlen, spec.scale, out=out, lse=lse,
+                                        workspace=ws, num_workers=args.workers, stream=stream, phases=phases)
+        elif spec.kind == "mla":
             zl.zl_decode_attn_mla(q, c[0], cu, x.max_seqlen, spec.scale, out=out, lse=lse, workspace=ws,
                                   num_workers=args.workers, stream=stream, phases=phases)
         else:
@@ -148,7 +163,7 @@ def main():
         for i in range(max(3, args.steps)):
             step(i)
         torch.cuda.synchronize()
-        print(f"profile run: {spec.name}, {max(3, args.steps)} launches", flush=True)
+        print(f"profile run: {spec.name}{' paged' if paged else ''}, {max(3, args.steps)} launches", flush=True)
         return
 
     for i in range(args.warmup):
@@ -185,13 +200,13 @@ def main():
     kern_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]))
     merge_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]))
     achieved_gbs = kv_bytes / (kern_ms * 1e-3) / 1e9
-    prof = profile_record(spec.name)
+    workload = spec.name + (f"+paged{args.paged}" if paged else "")
+    prof = profile_record(workload)
 
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(x, spec, args.cpu_seconds)
 
-    workload = spec.name
     # Useful matrix flops of one step: QK^T and PV, 2 flops per multiply-add.
     flops = 2.0 * x.total_tokens * spec.num_q_heads * (spec.head_dim_k + spec.head_dim_v)
     rec = {
@@ -222,6 +237,7 @@ def main():
             "kv_bytes_per_step": kv_bytes,
             "cold_cache_replicas": reps,
             "workers": args.workers or "default",
+            "kv_layout": f"paged, {args.paged}-token pages in a shuffled pool" if paged else "packed rows",
         },
         "roofline": {
             "bound": "hbm",

@@ -125,11 +125,17 @@ __device__ __forceinline__ void dma_tile(const char* rows, uint32_t row_bytes, c
 }
 
 // The same tile from a paged cache: row r is token l0 + min(r, nvalid - 1) of
-// its sequence, in row (l & (page - 1)) of page tp.page_of(l) of the pool.
+// its sequence, in row (l & (page - 1)) of page tp.page_of(l) of the pool.  A
+// tile inside one page is a run of rows like a packed tile (scalar base).
 template <int L, int NI>
 __device__ __forceinline__ void dma_tile_paged(const char* pool, uint32_t row_bytes, const TileMap<L, NI>& m,
                                                const TilePages& tp, int l0, int nvalid, ZL_LDS char* dst) {
   const int mask = (1 << tp.shift) - 1;
+  if (tp.span == 0) {
+    const size_t row0 = ((size_t)tp.p0 << tp.shift) | (size_t)(l0 & mask);
+    dma_tile<L, NI>(pool + row0 * row_bytes, row_bytes, m, nvalid, dst);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int l = l0 + (m.row[i] < nvalid ? m.row[i] : nvalid - 1);
@@ -204,6 +210,18 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
   int dj = 0;  // next item of segment ds: 0 = query rows, 1 + k = tile k
   bool dmore = true;
   int issued = 0;
+  // Paged caches: the page ids of the next tile to issue, read one item ahead
+  // so that the scalar loads' latency passes under a tile of math.
+  TilePages pf{0, 0, 0, 0, 0, 0};
+  auto prefetch_pages = [&]() {
+    if constexpr (PAGED) {
+      if (dmore && dj >= 1) {
+        const int k = dj - 1;
+        pf = tile_pages(block_table + (long long)ds.b * a.max_pages, ds.t0 + 32 * k - ds.cs,
+                        min(32, ds.len - 32 * k), a.page_shift);
+      }
+    }
+  };
   auto issue = [&]() {
     ZL_LDS char* st = smem + (issued % STAGES) * TL::STAGE_BYTES;
     const int ntl = (ds.len + 31) >> 5;
@@ -218,10 +236,8 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
       const int nv = min(32, ds.len - 32 * k);
       if constexpr (PAGED) {
         const int l0 = tok - ds.cs;
-        const TilePages tp =
-            tile_pages(block_table + (long long)ds.b * a.max_pages, l0, nv, a.page_shift);
-        dma_tile_paged<L, TL::NI_K>((const char*)(a.k + (long long)kvh * DK), k_row_bytes, kmap, tp, l0, nv, st);
-        dma_tile_paged<L, TL::NI_V>((const char*)(a.v + (long long)kvh * DV), v_row_bytes, vmap, tp, l0, nv,
+        dma_tile_paged<L, TL::NI_K>((const char*)(a.k + (long long)kvh * DK), k_row_bytes, kmap, pf, l0, nv, st);
+        dma_tile_paged<L, TL::NI_V>((const char*)(a.v + (long long)kvh * DV), v_row_bytes, vmap, pf, l0, nv,
                                     st + TL::KBYTES);
       } else {
         dma_tile<L, TL::NI_K>((const char*)(a.k + (long long)kvh * DK) + (size_t)tok * k_row_bytes, k_row_bytes,
@@ -236,6 +252,7 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
       dj = 0;
       dmore = ds.len > 0;
     }
+    prefetch_pages();
   };
   Segment sg = ds;  // the segment being computed
   int cj = 0;       // its current item

@@ -108,10 +108,16 @@ __device__ __forceinline__ void dma_quarter(const uint16_t* rows, int tok0, int 
 }
 
 // The same quarter from a paged pool: row r is token l0 + min(r, nvalid - 1)
-// of its sequence, in row (l & (page - 1)) of page tp.page_of(l).
+// of its sequence, in row (l & (page - 1)) of page tp.page_of(l).  A tile
+// inside one page is a run of rows like a packed tile (scalar base).
 __device__ __forceinline__ void dma_quarter_paged(const uint16_t* pool, const TilePages& tp, int l0, int nvalid,
                                                   const QuarterMap& m, ZL_LDS char* dst, int wave) {
   const int mask = (1 << tp.shift) - 1;
+  if (tp.span == 0) {
+    const size_t row0 = ((size_t)tp.p0 << tp.shift) | (size_t)(l0 & mask);
+    dma_quarter(pool + row0 * kDK, 0, nvalid, m, dst, wave);
+    return;
+  }
 #pragma unroll
   for (int k = 0; k < kNIw; ++k) {
     const int r = m.row[k];
@@ -205,6 +211,18 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
   int dj = 0;  // next item of segment ds: 0 = query rows, 1 + k = tile k
   bool dmore = true;
   int issued = 0;
+  // Paged caches: the page ids of the next tile to issue, read one item ahead
+  // so that the scalar loads' latency passes under a tile of math.
+  TilePages pf{0, 0, 0, 0, 0, 0};
+  auto prefetch_pages = [&]() {
+    if constexpr (PAGED) {
+      if (dmore && dj >= 1) {
+        const int k = dj - 1;
+        pf = tile_pages(block_table + (long long)ds.b * a.max_pages, ds.t0 + 32 * k - ds.cs,
+                        min(32, ds.len - 32 * k), a.page_shift);
+      }
+    }
+  };
   auto issue = [&]() {
     ZL_LDS char* dst = smem + (issued % kStages) * kTileB;
     const int ntl = (ds.len + 31) >> 5;
@@ -216,8 +234,7 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
       const int nv = min(32, ds.len - 32 * k);
       if constexpr (PAGED) {
         const int l0 = ds.t0 + 32 * k - ds.cs;
-        const TilePages tp = tile_pages(block_table + (long long)ds.b * a.max_pages, l0, nv, a.page_shift);
-        dma_quarter_paged(a.k, tp, l0, nv, qmap, dst, wave);
+        dma_quarter_paged(a.k, pf, l0, nv, qmap, dst, wave);
       } else {
         dma_quarter(a.k, ds.t0 + 32 * k, nv, qmap, dst, wave);
       }
@@ -228,6 +245,7 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
       dj = 0;
       dmore = ds.len > 0;
     }
+    prefetch_pages();
   };
   Segment sg = ds;  // the segment being computed
   int cj = 0;       // its current item

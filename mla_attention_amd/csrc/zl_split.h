@@ -167,10 +167,15 @@ struct TilePages {
   int pi0;       // page index (in the sequence's list) of token l0
   int p0, p1, p2;  // page ids of pages pi0, pi0+1, pi0+2 (clamped to the last used)
   int shift;
+  int span;      // pages the tile touches beyond the first (0, 1 or 2)
 
+  // Written as sums of differences: a choice between the members themselves
+  // is folded by the optimiser into an indexed load from the struct, which
+  // then stays in memory (the compiler may place it in LDS, where its stores
+  // wait for every tile load in flight).
   __device__ __forceinline__ int page_of(int l) const {
     const int d = (l >> shift) - pi0;
-    return d == 0 ? p0 : (d == 1 ? p1 : p2);
+    return p0 + (d >= 1 ? p1 - p0 : 0) + (d >= 2 ? p2 - p1 : 0);
   }
 };
 
@@ -182,6 +187,7 @@ __device__ __forceinline__ TilePages tile_pages(const int32_t* table_row, int l0
   tp.p0 = table_row[tp.pi0];
   tp.p1 = table_row[tp.pi0 + 1 < pil ? tp.pi0 + 1 : pil];
   tp.p2 = table_row[tp.pi0 + 2 < pil ? tp.pi0 + 2 : pil];
+  tp.span = pil - tp.pi0;
   return tp;
 }
 
