@@ -125,15 +125,30 @@ __device__ __forceinline__ void dma_tile(const char* rows, uint32_t row_bytes, c
 }
 
 // The same tile from a paged cache: row r is token l0 + min(r, nvalid - 1) of
-// its sequence, in row (l & (page - 1)) of page tp.page_of(l) of the pool.  A
-// tile inside one page is a run of rows like a packed tile (scalar base).
+// its sequence, in row (l & (page - 1)) of page tp.page_of(l) of the pool.
+// Tiles start on the 32-token grid of their sequence, so a tile lies inside
+// one page when pages hold 32 tokens or more: a run of rows like a packed tile
+// (scalar base).  With 16-token pages a full tile is rows 0-15 of one page and
+// rows 0-15 of another, and each DMA instruction covers rows of one half
+// only, so each half is a scalar-base run too.  Other tiles (a short last tile
+// over two pages) take a per-lane page lookup.
 template <int L, int NI>
 __device__ __forceinline__ void dma_tile_paged(const char* pool, uint32_t row_bytes, const TileMap<L, NI>& m,
                                                const TilePages& tp, int l0, int nvalid, ZL_LDS char* dst) {
+  static_assert(NI % 2 == 0 && 32 % NI == 0, "each instruction covers 32 / NI whole rows of one 16-row half");
   const int mask = (1 << tp.shift) - 1;
   if (tp.span == 0) {
     const size_t row0 = ((size_t)tp.p0 << tp.shift) | (size_t)(l0 & mask);
     dma_tile<L, NI>(pool + row0 * row_bytes, row_bytes, m, nvalid, dst);
+    return;
+  }
+  if (tp.span == 1 && tp.shift == 4 && nvalid == 32) {
+    // Instruction i covers rows 32 i / NI .. 32 (i + 1) / NI - 1.  The second
+    // base is set back 16 rows so that the same lane offsets apply.
+    const char* b0 = pool + ((size_t)tp.p0 << 4) * row_bytes;
+    const char* b1 = (const char*)((uintptr_t)pool + (((uintptr_t)tp.p1 << 4) - 16u) * row_bytes);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma16_saddr(i < NI / 2 ? b0 : b1, m.off[i], dst + i * 1024);
     return;
   }
 #pragma unroll
@@ -300,8 +315,7 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
         // ---- segment epilogue: lane (g, n) holds head n, dims 16blk + 4g .. +3.
         // Stores only; the next items are already in flight.  A split
         // sequence leaves its partial for the merge launch.
-        const int w_first = (int)(token_position(line, sg.u, sg.b, sg.cs) / per);
-        const int w_last = (int)(token_position(line, sg.u, sg.b, sg.ce - 1) / per);
+        const SeqWorkers sw = seq_workers(line, sg.u, sg.b, sg.cs, sg.ce, per);
         const int kvh = sg.u / a.HB, hb = sg.u - (sg.u / a.HB) * a.HB;
         const int h0 = kvh * a.G + hb * kHeadsPerUnit;
         const int nh = min(kHeadsPerUnit, a.G - hb * kHeadsPerUnit);
@@ -309,7 +323,7 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         const float lse_v = l_tot > 0.f ? sm.m * kLn2 + __logf(l_tot) : -INFINITY;
         if (n < nh) {
-          if (w_first == w_last) {
+          if (sw.first == sw.last) {
             uint16_t* orow = a.out + ((long long)sg.b * a.Hq + h0 + n) * DV + 4 * g;
 #pragma unroll
             for (int blk = 0; blk < TL::VBLK; ++blk) store_out4<DT>(orow + 16 * blk, o[blk], inv);

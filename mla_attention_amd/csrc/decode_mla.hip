@@ -108,14 +108,27 @@ __device__ __forceinline__ void dma_quarter(const uint16_t* rows, int tok0, int 
 }
 
 // The same quarter from a paged pool: row r is token l0 + min(r, nvalid - 1)
-// of its sequence, in row (l & (page - 1)) of page tp.page_of(l).  A tile
-// inside one page is a run of rows like a packed tile (scalar base).
+// of its sequence, in row (l & (page - 1)) of page tp.page_of(l).  Tiles start
+// on the 32-token grid of their sequence, so a tile lies inside one page when
+// pages hold 32 tokens or more: a run of rows like a packed tile (scalar
+// base).  With 16-token pages the first 16 rows of a full tile (18 KB, waves 0
+// and 1) lie in one page and the last 16 (waves 2 and 3) in another, so each
+// wave still reads one scalar-base run.  Other tiles (a short last tile over
+// two pages) take a per-lane page lookup.
 __device__ __forceinline__ void dma_quarter_paged(const uint16_t* pool, const TilePages& tp, int l0, int nvalid,
                                                   const QuarterMap& m, ZL_LDS char* dst, int wave) {
+  static_assert(16 * kRowB == 2 * kNIw * 1024, "16 rows are the quarters of two waves");
   const int mask = (1 << tp.shift) - 1;
   if (tp.span == 0) {
     const size_t row0 = ((size_t)tp.p0 << tp.shift) | (size_t)(l0 & mask);
     dma_quarter(pool + row0 * kDK, 0, nvalid, m, dst, wave);
+    return;
+  }
+  if (tp.span == 1 && tp.shift == 4 && nvalid == 32) {
+    // Waves 2 and 3 hold rows 16-31: their base is set back 16 rows so that
+    // the same lane offsets apply.
+    const uintptr_t page = wave < 2 ? ((uintptr_t)tp.p0 << 4) : ((uintptr_t)tp.p1 << 4) - 16u;
+    dma_quarter((const uint16_t*)((uintptr_t)pool + page * kRowB), 0, 32, m, dst, wave);
     return;
   }
 #pragma unroll
@@ -299,15 +312,14 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
       if (j == ntl - 1) {
         // ---- segment epilogue: lane (g, n) of wave w holds head n, dims
         // 128w + 16bb + 4g .. +3.  Stores only; the next items are in flight.
-        const int w_first = (int)(token_position(line, sg.u, sg.b, sg.cs) / per);
-        const int w_last = (int)(token_position(line, sg.u, sg.b, sg.ce - 1) / per);
+        const SeqWorkers sw = seq_workers(line, sg.u, sg.b, sg.cs, sg.ce, per);
         const int h0 = sg.u * kHeadsPerUnit;
         const int nh = min(kHeadsPerUnit, a.G - h0);
         const float l_tot = sum_over_groups(sm.l);
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         const float lse_v = l_tot > 0.f ? sm.m * kLn2 + __logf(l_tot) : -INFINITY;
         if (n < nh) {
-          if (w_first == w_last) {
+          if (sw.first == sw.last) {
             uint16_t* orow = a.out + ((long long)sg.b * a.Hq + h0 + n) * kDV + dim0;
 #pragma unroll
             for (int bb = 0; bb < kBlkPerWave; ++bb) store_out4<DT>(orow + 16 * bb, o[bb], inv);

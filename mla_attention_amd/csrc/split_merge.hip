@@ -50,8 +50,8 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a, const in
   const int U = a.Hkv * a.HB;
   const Line line = make_line(cu[a.B], a.B, a.seg_cost);
   const long long per = positions_per_worker((long long)U * line.Tp, a.P);
-  const int w_first = (int)(token_position(line, u, b, cs) / per);
-  const int w_last = (int)(token_position(line, u, b, ce - 1) / per);
+  const SeqWorkers sw = seq_workers(line, u, b, cs, ce, per);
+  const int w_first = sw.first, w_last = sw.last;
   if (w_first == w_last) return;
   // Worker w_first used slot 2w if this sequence opened its run, else 2w+1;
   // every later worker's run opens with this sequence (slot 2w).  Both

@@ -14,6 +14,16 @@
 // sequence boundaries do not finish last.  A run starting inside a phantom
 // stretch begins at the sequence's first token.
 //
+// Cuts between runs are aligned to a grid of kTokenGrid tokens counted from
+// each sequence's first token: the cut for a run boundary at position B is
+// the first grid token at or after the first token at a position >= B.  So
+// every tile of a run starts on the grid (only a sequence's last tile is
+// partial), and with a paged cache a tile never straddles a page boundary
+// when pages hold at least kTokenGrid tokens.  Token t is then held by the
+// run that holds position token_position(cs + floor_grid(t - cs)), and every
+// run between a sequence's first and last holds at least kTokenGrid of its
+// tokens (runs are at least 64 positions long).
+//
 // A run that covers a whole sequence writes that sequence's output directly;
 // a sequence cut between runs gets one fp32 partial (O / l, lse) per run,
 // merged by the split-merge kernel (split_merge.hip) launched right after.
@@ -26,6 +36,8 @@
 #include <stdint.h>
 
 namespace zl {
+
+constexpr int kTokenGrid = 32;  // the tile height of both decode kernels
 
 // Positions per worker for N positions over P workers (at least 64, so that a
 // tiny batch is not scattered over many workers).  The decode and the merge
@@ -120,8 +132,19 @@ __device__ __forceinline__ void split_position(long long p, long long Tp, int& u
   }
 }
 
-// The first segment of the run [p, p_end): its first token is the first token
-// at a position >= p (phantom stretches and empty sequences are stepped over).
+// The cut in sequence [cs, ce) for a run boundary whose token index is x (the
+// boundary lies at the position of token x, which may be outside [cs, ce)):
+// the first grid token at or after clamp(x, cs, ce), at most ce.
+__device__ __forceinline__ int grid_cut(long long x, int cs, int ce) {
+  const int raw = x <= cs ? cs : (x >= ce ? ce : (int)x);
+  const int up = cs + ((raw - cs + kTokenGrid - 1) & ~(kTokenGrid - 1));
+  return up < ce ? up : ce;
+}
+
+// The first segment of the run [p, p_end): tokens [grid_cut(p), grid_cut(p_end))
+// of the first sequence, at a position >= p, where that range is not empty
+// (phantom stretches, empty sequences and sequences whose share of the run
+// rounds away are stepped over).
 __device__ __forceinline__ Segment segment_at(long long p, long long p_end, const Line& L, const int32_t* cu,
                                               int window) {
   Segment s;
@@ -136,14 +159,12 @@ __device__ __forceinline__ Segment segment_at(long long p, long long p_end, cons
     int u, r;
     split_position(p, L.Tp, u, r);
     const SeqSpan q = find_seq(cu, L.B, L.C, r, window);
-    const int o = r - (q.cs + q.b * L.C);  // offset inside the sequence's stretch
-    const int t0 = o < L.C ? q.cs : q.cs + (o - L.C);
-    // Tokens t < lim of this sequence lie inside the run.
-    const long long lim = p_end - (long long)u * L.Tp - (long long)(q.b + 1) * L.C;
-    if (lim <= t0) return s;  // the run ends before this sequence's next token
-    const int t1 = (long long)q.ce < lim ? q.ce : (int)lim;
+    // Position of token t of this sequence: base + t.
+    const long long base = (long long)u * L.Tp + (long long)(q.b + 1) * L.C;
+    const int t0 = grid_cut(p - base, q.cs, q.ce);
+    const int t1 = grid_cut(p_end - base, q.cs, q.ce);
     if (t1 > t0) {
-      s.p = token_position(L, u, q.b, t0);
+      s.p = base + t0;
       s.u = u;
       s.t0 = t0;
       s.len = t1 - t0;
@@ -152,10 +173,22 @@ __device__ __forceinline__ Segment segment_at(long long p, long long p_end, cons
       s.ce = q.ce;
       return s;
     }
-    // An empty sequence: go on at the start of the next one.
-    p = (long long)u * L.Tp + q.ce + (long long)(q.b + 1) * L.C;
+    if (p_end - base < q.ce) return s;  // the run ends inside this sequence
+    // Nothing of this sequence in the run: go on at the start of the next one.
+    p = base + q.ce;
   }
   return s;
+}
+
+// The runs (workers) holding tokens of sequence [cs, ce) of unit u, for a
+// non-empty sequence: first .. last.
+struct SeqWorkers {
+  int first, last;
+};
+
+__device__ __forceinline__ SeqWorkers seq_workers(const Line& L, int u, int b, int cs, int ce, long long per) {
+  const int t_last = cs + ((ce - 1 - cs) & ~(kTokenGrid - 1));
+  return SeqWorkers{(int)(token_position(L, u, b, cs) / per), (int)(token_position(L, u, b, t_last) / per)};
 }
 
 // The pages of one 32-token tile of a paged cache: tokens l0 .. l0+nvalid-1
