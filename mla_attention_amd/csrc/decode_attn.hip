@@ -124,38 +124,25 @@ __device__ __forceinline__ void dma_tile(const char* rows, uint32_t row_bytes, c
   }
 }
 
-// The same tile from a paged cache: row r is token l0 + min(r, nvalid - 1) of
-// its sequence, in row (l & (page - 1)) of page tp.page_of(l) of the pool.
-// Tiles start on the 32-token grid of their sequence, so a tile lies inside
-// one page when pages hold 32 tokens or more: a run of rows like a packed tile
-// (scalar base).  With 16-token pages a full tile is rows 0-15 of one page and
-// rows 0-15 of another, and each DMA instruction covers rows of one half
-// only, so each half is a scalar-base run too.  Other tiles (a short last tile
-// over two pages) take a per-lane page lookup.
+// The same tile from a paged cache: tile rows 0-15 and 16-31 are runs of
+// rows from two scalar bases (one per half of the DMA instructions; the same
+// base unless pages hold 16 tokens).  Rows past nvalid are clamped to row
+// nvalid - 1, which lies in the half whose base the instruction uses.
 template <int L, int NI>
 __device__ __forceinline__ void dma_tile_paged(const char* pool, uint32_t row_bytes, const TileMap<L, NI>& m,
-                                               const TilePages& tp, int l0, int nvalid, ZL_LDS char* dst) {
+                                               const TileRows& tr, int nvalid, ZL_LDS char* dst) {
   static_assert(NI % 2 == 0 && 32 % NI == 0, "each instruction covers 32 / NI whole rows of one 16-row half");
-  const int mask = (1 << tp.shift) - 1;
-  if (tp.span == 0) {
-    const size_t row0 = ((size_t)tp.p0 << tp.shift) | (size_t)(l0 & mask);
-    dma_tile<L, NI>(pool + row0 * row_bytes, row_bytes, m, nvalid, dst);
-    return;
-  }
-  if (tp.span == 1 && tp.shift == 4 && nvalid == 32) {
-    // Instruction i covers rows 32 i / NI .. 32 (i + 1) / NI - 1.  The second
-    // base is set back 16 rows so that the same lane offsets apply.
-    const char* b0 = pool + ((size_t)tp.p0 << 4) * row_bytes;
-    const char* b1 = (const char*)((uintptr_t)pool + (((uintptr_t)tp.p1 << 4) - 16u) * row_bytes);
+  const char* b0 = (const char*)((uintptr_t)pool + (uintptr_t)(tr.half0 * row_bytes));
+  const char* b1 = (const char*)((uintptr_t)pool + (uintptr_t)(tr.half1 * row_bytes));
+  if (nvalid >= 32) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) dma16_saddr(i < NI / 2 ? b0 : b1, m.off[i], dst + i * 1024);
-    return;
-  }
+  } else {
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int l = l0 + (m.row[i] < nvalid ? m.row[i] : nvalid - 1);
-    const size_t row = ((size_t)tp.page_of(l) << tp.shift) | (size_t)(l & mask);
-    dma16(pool + row * row_bytes + m.chunk[i], dst + i * 1024);
+    for (int i = 0; i < NI; ++i) {
+      const int rr = m.row[i] < nvalid ? m.row[i] : nvalid - 1;
+      dma16_saddr(i < NI / 2 ? b0 : b1, (uint32_t)rr * row_bytes + m.chunk[i], dst + i * 1024);
+    }
   }
 }
 
@@ -227,13 +214,13 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
   int issued = 0;
   // Paged caches: the page ids of the next tile to issue, read one item ahead
   // so that the scalar loads' latency passes under a tile of math.
-  TilePages pf{0, 0, 0, 0, 0, 0};
+  TileRows pf{0, 0};
   auto prefetch_pages = [&]() {
     if constexpr (PAGED) {
       if (dmore && dj >= 1) {
         const int k = dj - 1;
-        pf = tile_pages(block_table + (long long)ds.b * a.max_pages, ds.t0 + 32 * k - ds.cs,
-                        min(32, ds.len - 32 * k), a.page_shift);
+        pf = tile_rows(block_table + (long long)ds.b * a.max_pages, ds.t0 + 32 * k - ds.cs,
+                       min(32, ds.len - 32 * k), a.page_shift);
       }
     }
   };
@@ -250,9 +237,8 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
       const int tok = ds.t0 + 32 * k;
       const int nv = min(32, ds.len - 32 * k);
       if constexpr (PAGED) {
-        const int l0 = tok - ds.cs;
-        dma_tile_paged<L, TL::NI_K>((const char*)(a.k + (long long)kvh * DK), k_row_bytes, kmap, pf, l0, nv, st);
-        dma_tile_paged<L, TL::NI_V>((const char*)(a.v + (long long)kvh * DV), v_row_bytes, vmap, pf, l0, nv,
+        dma_tile_paged<L, TL::NI_K>((const char*)(a.k + (long long)kvh * DK), k_row_bytes, kmap, pf, nv, st);
+        dma_tile_paged<L, TL::NI_V>((const char*)(a.v + (long long)kvh * DV), v_row_bytes, vmap, pf, nv,
                                     st + TL::KBYTES);
       } else {
         dma_tile<L, TL::NI_K>((const char*)(a.k + (long long)kvh * DK) + (size_t)tok * k_row_bytes, k_row_bytes,

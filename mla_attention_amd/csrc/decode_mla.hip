@@ -107,38 +107,15 @@ __device__ __forceinline__ void dma_quarter(const uint16_t* rows, int tok0, int 
   }
 }
 
-// The same quarter from a paged pool: row r is token l0 + min(r, nvalid - 1)
-// of its sequence, in row (l & (page - 1)) of page tp.page_of(l).  Tiles start
-// on the 32-token grid of their sequence, so a tile lies inside one page when
-// pages hold 32 tokens or more: a run of rows like a packed tile (scalar
-// base).  With 16-token pages the first 16 rows of a full tile (18 KB, waves 0
-// and 1) lie in one page and the last 16 (waves 2 and 3) in another, so each
-// wave still reads one scalar-base run.  Other tiles (a short last tile over
-// two pages) take a per-lane page lookup.
-__device__ __forceinline__ void dma_quarter_paged(const uint16_t* pool, const TilePages& tp, int l0, int nvalid,
+// The same quarter from a paged pool.  Tile rows 0-15 (18 KB: the quarters of
+// waves 0 and 1) and rows 16-31 (waves 2 and 3) are runs of rows from one
+// scalar base each (the same base unless pages hold 16 tokens); rows past
+// nvalid are clamped to row nvalid - 1, which lies in the wave's own half.
+__device__ __forceinline__ void dma_quarter_paged(const uint16_t* pool, const TileRows& tr, int nvalid,
                                                   const QuarterMap& m, ZL_LDS char* dst, int wave) {
   static_assert(16 * kRowB == 2 * kNIw * 1024, "16 rows are the quarters of two waves");
-  const int mask = (1 << tp.shift) - 1;
-  if (tp.span == 0) {
-    const size_t row0 = ((size_t)tp.p0 << tp.shift) | (size_t)(l0 & mask);
-    dma_quarter(pool + row0 * kDK, 0, nvalid, m, dst, wave);
-    return;
-  }
-  if (tp.span == 1 && tp.shift == 4 && nvalid == 32) {
-    // Waves 2 and 3 hold rows 16-31: their base is set back 16 rows so that
-    // the same lane offsets apply.
-    const uintptr_t page = wave < 2 ? ((uintptr_t)tp.p0 << 4) : ((uintptr_t)tp.p1 << 4) - 16u;
-    dma_quarter((const uint16_t*)((uintptr_t)pool + page * kRowB), 0, 32, m, dst, wave);
-    return;
-  }
-#pragma unroll
-  for (int k = 0; k < kNIw; ++k) {
-    const int r = m.row[k];
-    const int l = l0 + (r < nvalid ? r : nvalid - 1);
-    const size_t row = ((size_t)tp.page_of(l) << tp.shift) | (size_t)(l & mask);
-    const uint32_t chunk = m.off[k] - (uint32_t)r * kRowB;
-    dma16((const char*)pool + row * kRowB + chunk, dst + (wave * kNIw + k) * 1024);
-  }
+  const long long half = wave < 2 ? tr.half0 : tr.half1;
+  dma_quarter((const uint16_t*)((uintptr_t)pool + (uintptr_t)(half * kRowB)), 0, nvalid, m, dst, wave);
 }
 
 // The query item of a segment: rows h0 .. h0+15 (rows past nh repeat h0) in
@@ -226,13 +203,13 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
   int issued = 0;
   // Paged caches: the page ids of the next tile to issue, read one item ahead
   // so that the scalar loads' latency passes under a tile of math.
-  TilePages pf{0, 0, 0, 0, 0, 0};
+  TileRows pf{0, 0};
   auto prefetch_pages = [&]() {
     if constexpr (PAGED) {
       if (dmore && dj >= 1) {
         const int k = dj - 1;
-        pf = tile_pages(block_table + (long long)ds.b * a.max_pages, ds.t0 + 32 * k - ds.cs,
-                        min(32, ds.len - 32 * k), a.page_shift);
+        pf = tile_rows(block_table + (long long)ds.b * a.max_pages, ds.t0 + 32 * k - ds.cs,
+                       min(32, ds.len - 32 * k), a.page_shift);
       }
     }
   };
@@ -246,8 +223,7 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
       const int k = dj - 1;
       const int nv = min(32, ds.len - 32 * k);
       if constexpr (PAGED) {
-        const int l0 = ds.t0 + 32 * k - ds.cs;
-        dma_quarter_paged(a.k, pf, l0, nv, qmap, dst, wave);
+        dma_quarter_paged(a.k, pf, nv, qmap, dst, wave);
       } else {
         dma_quarter(a.k, ds.t0 + 32 * k, nv, qmap, dst, wave);
       }

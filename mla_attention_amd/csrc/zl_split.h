@@ -191,37 +191,27 @@ __device__ __forceinline__ SeqWorkers seq_workers(const Line& L, int u, int b, i
   return SeqWorkers{(int)(token_position(L, u, b, cs) / per), (int)(token_position(L, u, b, t_last) / per)};
 }
 
-// The pages of one 32-token tile of a paged cache: tokens l0 .. l0+nvalid-1
-// of one sequence (l counted from the sequence's start) lie in at most three
-// consecutive pages when pages hold 16 or more tokens.  The page ids are read
-// with scalar loads (the block table row is wave-uniform); page_of(l) then
-// selects a lane's page without memory traffic.
-struct TilePages {
-  int pi0;       // page index (in the sequence's list) of token l0
-  int p0, p1, p2;  // page ids of pages pi0, pi0+1, pi0+2 (clamped to the last used)
-  int shift;
-  int span;      // pages the tile touches beyond the first (0, 1 or 2)
-
-  // Written as sums of differences: a choice between the members themselves
-  // is folded by the optimiser into an indexed load from the struct, which
-  // then stays in memory (the compiler may place it in LDS, where its stores
-  // wait for every tile load in flight).
-  __device__ __forceinline__ int page_of(int l) const {
-    const int d = (l >> shift) - pi0;
-    return p0 + (d >= 1 ? p1 - p0 : 0) + (d >= 2 ? p2 - p1 : 0);
-  }
+// The rows of one tile of a paged cache (token i of a sequence is row
+// i & (2^shift - 1) of page table_row[i >> shift]).  Tiles start on the token
+// grid of their sequence and pages hold 2^shift >= 16 tokens, so tile rows
+// 0-15 lie in one page and rows 16-31 in the same page or, with 16-token
+// pages, in the next page of the sequence.  Tile row r < 16 is pool row
+// half0 + r; tile row r >= 16 is pool row half1 + r, and so is the clamped row
+// nvalid - 1 of a short tile.  The page ids are read with scalar loads (the
+// table row is wave-uniform).
+struct TileRows {
+  long long half0, half1;
 };
 
-__device__ __forceinline__ TilePages tile_pages(const int32_t* table_row, int l0, int nvalid, int shift) {
-  TilePages tp;
-  tp.shift = shift;
-  tp.pi0 = l0 >> shift;
-  const int pil = (l0 + nvalid - 1) >> shift;
-  tp.p0 = table_row[tp.pi0];
-  tp.p1 = table_row[tp.pi0 + 1 < pil ? tp.pi0 + 1 : pil];
-  tp.p2 = table_row[tp.pi0 + 2 < pil ? tp.pi0 + 2 : pil];
-  tp.span = pil - tp.pi0;
-  return tp;
+__device__ __forceinline__ TileRows tile_rows(const int32_t* table_row, int l0, int nvalid, int shift) {
+  const int pi = l0 >> shift;
+  const bool two = shift == 4 && nvalid > 16;
+  const long long p0 = table_row[pi];
+  const long long p1 = table_row[two ? pi + 1 : pi];
+  TileRows t;
+  t.half0 = (p0 << shift) + (l0 & ((1 << shift) - 1));
+  t.half1 = two ? (p1 << 4) - 16 : t.half0;
+  return t;
 }
 
 // Key of (unit u, sequence b) in first_key.
