@@ -54,6 +54,11 @@ def load_library(path: str):
                                    ctypes.c_long, ctypes.c_double, ctypes.c_int, _i32p,
                                    ctypes.c_int, _f64p, _f64p, ctypes.c_int]
     lib.zo_decode_attn.restype = ctypes.c_int
+    lib.zo_varlen_attn.argtypes = [_u16p, _u16p, _u16p, _i32p, _i32p, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_long,
+                                   ctypes.c_long, ctypes.c_double, ctypes.c_int, ctypes.c_int, _i32p,
+                                   ctypes.c_int, _f64p, _f64p, ctypes.c_int]
+    lib.zo_varlen_attn.restype = ctypes.c_int
     lib.zo_combine.argtypes = [_f64p, _f64p, ctypes.c_int, ctypes.c_long, ctypes.c_int,
                                _f64p, _f64p]
     lib.zo_combine.restype = None
@@ -171,6 +176,54 @@ def decode_attn(q, k, v, cu_seqlens, num_kv_heads: int, dk: int, dv: int, k_row_
     if rc != 0:
         raise ValueError("oracle rejected arguments")
     return out, lse
+
+
+def varlen_attn(q, k, v, cu_seqlens_q, cu_seqlens_k, num_kv_heads: int, dk: int, dv: int,
+                k_row_stride: int, v_row_stride: int, scale: float, dtype: int, causal: bool = True,
+                rows=None, threads: int = 0):
+    """Several new query tokens per sequence: q [Tq, Hq, dk] (sequence b owns
+    query rows cu_q[b] .. cu_q[b+1]-1), keys/values as in decode_attn with
+    cu_k.  New token i of Lq sits at cache position Lk - Lq + i and, with
+    `causal`, sees cache rows 0 .. Lk - Lq + i.  Returns (out [Tq, Hq, dv],
+    lse [Tq, Hq]); with `rows` (an iterable of (t, h)) only those rows are
+    computed and the others are NaN."""
+    lib = _load()
+    q, qp = _u16(q)
+    k, kp = _u16(k)
+    v, vp = _u16(v)
+    cq, cqp = _i32(cu_seqlens_q)
+    ck, ckp = _i32(cu_seqlens_k)
+    Tq, Hq, _ = q.shape
+    B = cq.shape[0] - 1
+    if ck.shape[0] != B + 1 or cq[-1] != Tq:
+        raise ValueError("cu_seqlens mismatch")
+    p, pp, n = _pairs(rows)
+    out = np.full((Tq, Hq, dv), np.nan)
+    lse = np.full((Tq, Hq), np.nan)
+    rc = lib.zo_varlen_attn(qp, kp, vp, cqp, ckp, B, Hq, num_kv_heads, dk, dv, k_row_stride,
+                            v_row_stride, float(scale), int(bool(causal)), dtype, pp, n,
+                            out.ctypes.data_as(_f64p), lse.ctypes.data_as(_f64p), threads)
+    if rc != 0:
+        raise ValueError("oracle rejected arguments")
+    return out, lse
+
+
+def gqa_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, num_kv_heads: int, scale: float, dtype: int,
+               causal: bool = True, rows=None, threads: int = 0):
+    """varlen_attn with K/V [T, Hkv, D] (GQA/MQA/MHA)."""
+    D = np.asarray(q).shape[2]
+    stride = num_kv_heads * D
+    return varlen_attn(q, k, v, cu_seqlens_q, cu_seqlens_k, num_kv_heads, D, D, stride, stride, scale,
+                       dtype, causal, rows, threads)
+
+
+def mla_varlen(q, latent, cu_seqlens_q, cu_seqlens_k, scale: float, dtype: int, causal: bool = True,
+               kv_lora_rank: int = 512, rope_dim: int = 64, rows=None, threads: int = 0):
+    """varlen_attn for absorbed MLA: K = the whole latent row, V its first
+    kv_lora_rank columns."""
+    row = kv_lora_rank + rope_dim
+    return varlen_attn(q, latent, latent, cu_seqlens_q, cu_seqlens_k, 1, row, kv_lora_rank, row, row, scale,
+                       dtype, causal, rows, threads)
 
 
 def combine(part_out, part_lse):

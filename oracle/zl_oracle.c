@@ -189,6 +189,85 @@ int zo_decode_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     return bad ? -1 : 0;
 }
 
+/*
+ * Attention of several new query tokens per sequence (chunked prefill, or
+ * several draft tokens verified at once).  The first ZhiLight page lists
+ * chunked prefill among the engine's features (section "功能生态"), and the
+ * second page lists it beside flash-attention prefill (section "Dual streams,
+ * host all-reduce and the memory model").  Sequence b has Lq = cu_q[b+1] -
+ * cu_q[b] new query tokens, whose keys and values are already the last Lq of
+ * its Lk = cu_k[b+1] - cu_k[b] cached rows.  New token i (0 <= i < Lq) sits at
+ * cache position Lk - Lq + i; with `causal` it attends to cache rows
+ * 0 .. Lk - Lq + i (none when that is negative), otherwise to all Lk rows.
+ * Each query row is then the decode definition above over its visible rows.
+ *   q   : [total_q, num_q_heads, dk],  K/V as in zo_decode_attn with cu_k
+ *   rows: optional list of nrows (t, h) query rows to compute; NULL = all.
+ *   out : [total_q, num_q_heads, dv],  lse : [total_q, num_q_heads]
+ */
+int zo_varlen_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                   const int32_t *cu_q, const int32_t *cu_k, int batch,
+                   int num_q_heads, int num_kv_heads, int dk, int dv,
+                   long k_row_stride, long v_row_stride, double scale,
+                   int causal, int dtype, const int32_t *rows, int nrows,
+                   double *out, double *lse, int nthreads)
+{
+    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || dk <= 0 ||
+        dv <= 0 || num_q_heads % num_kv_heads != 0 || cu_q[0] != 0)
+        return -1;
+    int group = num_q_heads / num_kv_heads;
+    int max_len = 0;
+    for (int b = 0; b < batch; ++b) {
+        int Lq = cu_q[b + 1] - cu_q[b], Lk = cu_k[b + 1] - cu_k[b];
+        if (Lq < 0 || Lk < 0)
+            return -1;
+        if (Lk > max_len)
+            max_len = Lk;
+    }
+    long total_q = cu_q[batch];
+    long total = rows ? (long)nrows : total_q * num_q_heads;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#endif
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
+        if (!s) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (long p = 0; p < total; ++p) {
+            if (!s)
+                continue;
+            long t = rows ? rows[2 * p] : p / num_q_heads;
+            int h = rows ? rows[2 * p + 1] : (int)(p % num_q_heads);
+            if (t < 0 || t >= total_q || h < 0 || h >= num_q_heads)
+                continue;
+            int b = 0; /* the sequence holding query token t */
+            while (cu_q[b + 1] <= t)
+                ++b;
+            int Lq = cu_q[b + 1] - cu_q[b], Lk = cu_k[b + 1] - cu_k[b];
+            int i = (int)(t - cu_q[b]);
+            int L = causal ? Lk - Lq + i + 1 : Lk;
+            if (L < 0)
+                L = 0;
+            if (L > Lk)
+                L = Lk;
+            int g = h / group;
+            attend_one(q + (t * num_q_heads + h) * dk,
+                       k + (long)cu_k[b] * k_row_stride + (long)g * dk, k_row_stride,
+                       v + (long)cu_k[b] * v_row_stride + (long)g * dv, v_row_stride,
+                       L, dk, dv, scale, dtype,
+                       out + (t * num_q_heads + h) * dv,
+                       lse + t * num_q_heads + h, s);
+        }
+        free(s);
+    }
+    return bad ? -1 : 0;
+}
+
 /* GQA/MQA/MHA: K and V are [total_tokens, num_kv_heads, head_dim]. */
 int zo_gqa_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                   const int32_t *cu, int batch, int num_q_heads,

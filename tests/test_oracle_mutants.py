@@ -37,6 +37,10 @@ MUTANTS = {
     "f16-bias-off-by-one": ("v = ldexp((double)(m | 0x400), e - 25);", "v = ldexp((double)(m | 0x400), e - 24);"),
     "bf16-hidden-bit-missing": ("v = ldexp((double)(m | 0x80), e - 134);", "v = ldexp((double)m, e - 134);"),
     "f16-subnormal-scale": ("v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
+    "varlen-causal-off-by-one": ("int L = causal ? Lk - Lq + i + 1 : Lk;", "int L = causal ? Lk - Lq + i : Lk;"),
+    "varlen-top-left-causal": ("int L = causal ? Lk - Lq + i + 1 : Lk;", "int L = causal ? i + 1 : Lk;"),
+    "varlen-query-row-within-sequence": ("attend_one(q + (t * num_q_heads + h) * dk,",
+                                         "attend_one(q + ((long)i * num_q_heads + h) * dk,"),
     "mla-value-offset": ("return zo_decode_attn(q, latent, latent, cu,", "return zo_decode_attn(q, latent, latent + rope_dim, cu,"),
 }
 
@@ -62,6 +66,11 @@ def _battery():
         pins.test_p10_mla_equals_gqa_with_materialised_value_copy,
         pins.test_p10_absorbed_equals_unabsorbed_attention,
         pins.test_p12_dominant_key_selects_its_value,
+        lambda: pins.test_varlen_whole_prompt_equals_causal_sdpa(4, 2),
+        lambda: pins.test_varlen_chunk_equals_tail_of_whole_prompt(3),
+        pins.test_varlen_without_mask_equals_sdpa,
+        pins.test_varlen_rows_that_see_no_key,
+        pins.test_mla_varlen_equals_gqa_varlen_with_materialised_value,
     ]
 
 

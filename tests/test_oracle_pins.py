@@ -452,3 +452,115 @@ def test_paged_decode_equals_packed_decode():
     o2, l2 = oracle.gqa_decode_paged(x.bits("q"), u16(p.k_pages), u16(p.v_pages), p.block_table.numpy(),
                                      x.cu_seqlens.numpy(), 2, spec.scale, oracle.F16)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ------------------------------------------------ several new query tokens
+def whole_prompt_reference(qfull, k, v, num_kv_heads, scale):
+    """Causal self-attention of a whole prompt (every position is a query):
+    torch's scaled_dot_product_attention(is_causal=True) in float64, key/value
+    heads repeated to the query heads.  Returns (out [L, Hq, D], lse [L, Hq])."""
+    L, Hq, D = qfull.shape
+    G = Hq // num_kv_heads
+    qd = qfull.to(torch.float64).permute(1, 0, 2)                               # [Hq, L, D]
+    kd = k.to(torch.float64).permute(1, 0, 2).repeat_interleave(G, dim=0)
+    vd = v.to(torch.float64).permute(1, 0, 2).repeat_interleave(G, dim=0)
+    o = torch.nn.functional.scaled_dot_product_attention(qd, kd, vd, is_causal=True, scale=scale)
+    scores = (qd @ kd.transpose(1, 2)) * scale
+    scores = scores.masked_fill(torch.ones(L, L, dtype=torch.bool).triu(1), -math.inf)
+    return o.permute(1, 0, 2).numpy(), torch.logsumexp(scores, dim=-1).permute(1, 0).numpy()
+
+
+def run_varlen(q, k, v, cu_q, cu_k, num_kv_heads, scale, dtype, causal=True):
+    dt = oracle.F16 if dtype == torch.float16 else oracle.BF16
+    return oracle.gqa_varlen(bits(q), bits(k), bits(v), np.asarray(cu_q, dtype=np.int32),
+                             np.asarray(cu_k, dtype=np.int32), num_kv_heads, scale, dt, causal=causal)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (8, 1), (3, 3)])
+def test_varlen_whole_prompt_equals_causal_sdpa(Hq, Hkv):
+    """Every token of the prompt is new (Lq = Lk): plain causal self-attention."""
+    gen = torch.Generator().manual_seed(300 + Hq)
+    lens = [1, 7, 40]
+    cu = workloads.cu_from_lens(lens)
+    T, D = int(cu[-1]), 32
+    q = rand16((T, Hq, D), torch.float16, gen)
+    k = rand16((T, Hkv, D), torch.float16, gen)
+    v = rand16((T, Hkv, D), torch.float16, gen)
+    out, lse = run_varlen(q, k, v, cu, cu, Hkv, 0.3, torch.float16)
+    for b in range(len(lens)):
+        s, e = int(cu[b]), int(cu[b + 1])
+        ro, rl = whole_prompt_reference(q[s:e], k[s:e], v[s:e], Hkv, 0.3)
+        np.testing.assert_allclose(out[s:e], ro, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse[s:e], rl, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("Lq", [1, 3, 16])
+def test_varlen_chunk_equals_tail_of_whole_prompt(Lq):
+    """Chunked prefill: the last Lq tokens of a prompt, attended against the
+    whole cache, give the same rows as attending the whole prompt at once
+    (the new tokens sit at the end of the cache)."""
+    gen = torch.Generator().manual_seed(400 + Lq)
+    Hq, Hkv, D = 4, 2, 24
+    lens_k = [Lq, 40, 100]
+    prompts = [(rand16((L, Hq, D), torch.bfloat16, gen), rand16((L, Hkv, D), torch.bfloat16, gen),
+                rand16((L, Hkv, D), torch.bfloat16, gen)) for L in lens_k]
+    q = torch.cat([p[0][-Lq:] for p in prompts])
+    k = torch.cat([p[1] for p in prompts])
+    v = torch.cat([p[2] for p in prompts])
+    cu_q = workloads.cu_from_lens([Lq] * len(lens_k))
+    cu_k = workloads.cu_from_lens(lens_k)
+    out, lse = run_varlen(q, k, v, cu_q, cu_k, Hkv, 0.25, torch.bfloat16)
+    for b, (qf, kf, vf) in enumerate(prompts):
+        ro, rl = whole_prompt_reference(qf, kf, vf, Hkv, 0.25)
+        np.testing.assert_allclose(out[b * Lq:(b + 1) * Lq], ro[-Lq:], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse[b * Lq:(b + 1) * Lq], rl[-Lq:], rtol=1e-13, atol=1e-13)
+
+
+def test_varlen_without_mask_equals_sdpa():
+    gen = torch.Generator().manual_seed(500)
+    Hq, Hkv, D, Lq, Lk = 6, 3, 16, 5, 29
+    q = rand16((Lq, Hq, D), torch.float16, gen)
+    k = rand16((Lk, Hkv, D), torch.float16, gen)
+    v = rand16((Lk, Hkv, D), torch.float16, gen)
+    out, lse = run_varlen(q, k, v, [0, Lq], [0, Lk], Hkv, 0.2, torch.float16, causal=False)
+    qd = q.to(torch.float64).permute(1, 0, 2)
+    kd = k.to(torch.float64).permute(1, 0, 2).repeat_interleave(2, dim=0)
+    vd = v.to(torch.float64).permute(1, 0, 2).repeat_interleave(2, dim=0)
+    ro = torch.nn.functional.scaled_dot_product_attention(qd, kd, vd, scale=0.2).permute(1, 0, 2).numpy()
+    rl = torch.logsumexp((qd @ kd.transpose(1, 2)) * 0.2, dim=-1).permute(1, 0).numpy()
+    np.testing.assert_allclose(out, ro, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, rl, rtol=1e-13, atol=1e-13)
+
+
+def test_varlen_rows_that_see_no_key():
+    """More new tokens than cached rows: the first Lq - Lk new tokens see no
+    key (out 0, lse -inf); the others see keys 0 .. i - (Lq - Lk).  An empty
+    query range contributes no rows."""
+    gen = torch.Generator().manual_seed(600)
+    Hq, D, Lq, Lk = 2, 8, 5, 3
+    q = rand16((Lq, Hq, D), torch.float16, gen)
+    k = rand16((Lk, 1, D), torch.float16, gen)
+    v = rand16((Lk, 1, D), torch.float16, gen)
+    kk = torch.cat([rand16((4, 1, D), torch.float16, gen), k])
+    vv = torch.cat([rand16((4, 1, D), torch.float16, gen), v])
+    out, lse = run_varlen(q, kk, vv, [0, 0, Lq], [0, 4, 4 + Lk], 1, 1.0, torch.float16)
+    assert np.all(out[:Lq - Lk] == 0) and np.all(lse[:Lq - Lk] == -np.inf)
+    ro, rl = whole_prompt_reference(q[Lq - Lk:], k, v, 1, 1.0)
+    np.testing.assert_allclose(out[Lq - Lk:], ro, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse[Lq - Lk:], rl, rtol=1e-13, atol=1e-13)
+
+
+def test_mla_varlen_equals_gqa_varlen_with_materialised_value():
+    gen = torch.Generator().manual_seed(700)
+    lens_q, lens_k = [2, 1, 4], [9, 1, 40]
+    cu_q, cu_k = workloads.cu_from_lens(lens_q), workloads.cu_from_lens(lens_k)
+    H, R, P = 4, 32, 8
+    q = rand16((int(cu_q[-1]), H, R + P), torch.bfloat16, gen)
+    c = rand16((int(cu_k[-1]), R + P), torch.bfloat16, gen)
+    out, lse = oracle.mla_varlen(bits(q), bits(c), cu_q.numpy(), cu_k.numpy(), 0.17, oracle.BF16,
+                                 kv_lora_rank=R, rope_dim=P)
+    vcopy = c[:, :R].contiguous()
+    ro, rl = oracle.varlen_attn(bits(q), bits(c), bits(vcopy), cu_q.numpy(), cu_k.numpy(), 1, R + P, R,
+                                R + P, R, 0.17, oracle.BF16)
+    np.testing.assert_array_equal(out, ro)
+    np.testing.assert_array_equal(lse, rl)
