@@ -243,6 +243,61 @@ ZL_API zl_status_t zl_decode_attn_mla_paged_ex(const void *q, const void *kv_pag
                                                void *out, float *lse, int num_workers, int phases,
                                                void *workspace, size_t workspace_bytes, zl_stream_t stream);
 
+/*
+ * Several new query tokens per sequence: chunked prefill (the first ZhiLight
+ * page lists it among the engine's features, section "功能生态": a long
+ * prompt's prefill is split into chunks; the second page lists it beside
+ * flash-attention prefill, section "Dual streams, host all-reduce and the
+ * memory model"), and several draft tokens checked in one step.  Sequence b
+ * has nq = cu_seqlens_q[b+1] - cu_seqlens_q[b] new query tokens, whose keys
+ * and values are already the last nq of its lk = cu_seqlens_k[b+1] -
+ * cu_seqlens_k[b] cached rows.  New token i (0 <= i < nq) sits at cache
+ * position lk - nq + i; with causal = 1 it attends to cache rows
+ * 0 .. lk - nq + i (none if that is negative: out 0, lse -inf), with
+ * causal = 0 to all lk rows.  Each (token, head) row is the attention in the
+ * file header over its visible rows.
+ *   q            [total_q, num_q_heads, head_dim]              dtype
+ *   k/v_cache    [cu_seqlens_k[batch], num_kv_heads, head_dim]  dtype (GQA)
+ *   kv_cache     [cu_seqlens_k[batch], kv_lora_rank + rope_dim] dtype (MLA;
+ *                V = the first kv_lora_rank columns)
+ *   cu_seqlens_q [batch + 1] int32 (device), cu_seqlens_q[0] = 0,
+ *                non-decreasing, cu_seqlens_q[batch] = total_q (precondition)
+ *   cu_seqlens_k [batch + 1] int32 (device), as cu_seqlens above
+ *   total_q      rows of q (host); 0 is a no-op
+ *   out          [total_q, num_q_heads, Dv] dtype;  lse [total_q, num_q_heads]
+ * The kernels cut each sequence's (token, head) rows of one key/value head
+ * into blocks of 16 and stream the sequence's rows once per block, so the
+ * key/value bytes read are those of a decode step times
+ * ceil(nq * group / 16).  ZL_ERR_UNSUPPORTED when
+ * (ceil((total_q * group + 15 * batch) / 16)) * (max_seqlen_k + 64) >= 2^31.
+ * The workspace is sized by zl_decode_attn_workspace_size(_ex) (GQA) or
+ * zl_decode_attn_mla_workspace_size(_ex) (MLA) with the same arguments; the
+ * _ex forms take num_workers and phases as above.
+ */
+ZL_API zl_status_t zl_attn_varlen_gqa(const void *q, const void *k_cache, const void *v_cache,
+                                      const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int batch,
+                                      int total_q, int num_q_heads, int num_kv_heads, int head_dim,
+                                      int max_seqlen_k, float softmax_scale, int causal, zl_dtype_t dtype,
+                                      void *out, float *lse, void *workspace, size_t workspace_bytes,
+                                      zl_stream_t stream);
+ZL_API zl_status_t zl_attn_varlen_gqa_ex(const void *q, const void *k_cache, const void *v_cache,
+                                         const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int batch,
+                                         int total_q, int num_q_heads, int num_kv_heads, int head_dim,
+                                         int max_seqlen_k, float softmax_scale, int causal, zl_dtype_t dtype,
+                                         void *out, float *lse, int num_workers, int phases, void *workspace,
+                                         size_t workspace_bytes, zl_stream_t stream);
+ZL_API zl_status_t zl_attn_varlen_mla(const void *q, const void *kv_cache, const int32_t *cu_seqlens_q,
+                                      const int32_t *cu_seqlens_k, int batch, int total_q, int num_q_heads,
+                                      int kv_lora_rank, int rope_dim, int max_seqlen_k, float softmax_scale,
+                                      int causal, zl_dtype_t dtype, void *out, float *lse, void *workspace,
+                                      size_t workspace_bytes, zl_stream_t stream);
+ZL_API zl_status_t zl_attn_varlen_mla_ex(const void *q, const void *kv_cache, const int32_t *cu_seqlens_q,
+                                         const int32_t *cu_seqlens_k, int batch, int total_q, int num_q_heads,
+                                         int kv_lora_rank, int rope_dim, int max_seqlen_k, float softmax_scale,
+                                         int causal, zl_dtype_t dtype, void *out, float *lse, int num_workers,
+                                         int phases, void *workspace, size_t workspace_bytes,
+                                         zl_stream_t stream);
+
 /* Static, human-readable name of a status code (host). */
 ZL_API const char *zl_status_string(zl_status_t status);
 

@@ -62,6 +62,14 @@ SIGNATURES = {
     "zl_decode_attn_mla_paged_ex": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _vp, _c_int, _c_int, _c_int,
                                              _c_int, _c_int, _c_float, _c_int, _vp, _vp, _c_int, _c_int,
                                              _vp, _c_size, _vp]),
+    "zl_attn_varlen_gqa": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                    _c_float, _c_int, _c_int, _vp, _vp, _vp, _c_size, _vp]),
+    "zl_attn_varlen_gqa_ex": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                       _c_float, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _vp, _c_size, _vp]),
+    "zl_attn_varlen_mla": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                    _c_float, _c_int, _c_int, _vp, _vp, _vp, _c_size, _vp]),
+    "zl_attn_varlen_mla_ex": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                       _c_float, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _vp, _c_size, _vp]),
     "zl_attn_combine": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
     "zl_status_string": (ctypes.c_char_p, [_c_int]),
 }
@@ -307,6 +315,81 @@ def zl_decode_attn_mla_paged(q, kv_pages, block_table, cu_seqlens, max_seqlen_k:
         rope_dim, int(max_seqlen_k), float(softmax_scale), _DTYPE[q.dtype], _ptr(out), _ptr(lse),
         int(num_workers), int(phases), _ptr(workspace), workspace.numel(), _stream(stream, dev))
     _check(st, "zl_decode_attn_mla_paged")
+    return (out, lse) if lse is not None else out
+
+
+def _varlen_common(q, cu_seqlens_q, cu_seqlens_k, dv, out, lse, return_lse):
+    _need(q, "q", ndim=3)
+    dev = q.device
+    if q.dtype not in _DTYPE:
+        raise ValueError("q must be float16 or bfloat16")
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, dev)
+    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1, dev)
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both have batch + 1 entries")
+    Tq, Hq, _ = q.shape
+    if out is None:
+        out = torch.empty(Tq, Hq, dv, dtype=q.dtype, device=dev)
+    _need(out, "out", q.dtype, 3, dev)
+    if tuple(out.shape) != (Tq, Hq, dv):
+        raise ValueError(f"out must be [total_q, num_q_heads, {dv}]")
+    if lse is None and return_lse:
+        lse = torch.empty(Tq, Hq, dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2, dev)
+    return dev, cu_seqlens_q.numel() - 1, out, lse
+
+
+def zl_attn_varlen_gqa(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, max_seqlen_k: int,
+                       softmax_scale: float, causal: bool = True, out=None, lse=None, workspace=None,
+                       num_workers: int = 0, stream=None, return_lse: bool = False, phases: int = 3):
+    """Several new query tokens per sequence (chunked prefill, draft tokens).
+
+    q [total_q, Hq, D]: sequence b's new tokens are rows cu_seqlens_q[b] ..
+    cu_seqlens_q[b+1]-1, and their keys/values are already the last ones of
+    its cache rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of k_cache/v_cache
+    [T, Hkv, D].  With causal, new token i of nq sees cache rows up to
+    lk - nq + i.  Returns out [total_q, Hq, D] (and lse [total_q, Hq])."""
+    dev, B, out, lse = _varlen_common(q, cu_seqlens_q, cu_seqlens_k, q.shape[2], out, lse, return_lse)
+    _need(k_cache, "k_cache", q.dtype, 3, dev)
+    _need(v_cache, "v_cache", q.dtype, 3, dev)
+    Tq, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    if k_cache.shape[2] != D or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache / v_cache must be [T, Hkv, head_dim] like q")
+    nbytes = zl_decode_attn_workspace_size(B, Hq, Hkv, D, max_seqlen_k, q.dtype, num_workers)
+    if workspace is None:
+        workspace = new_workspace(nbytes, dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    st = library().zl_attn_varlen_gqa_ex(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, Tq, Hq, Hkv, D,
+        int(max_seqlen_k), float(softmax_scale), int(bool(causal)), _DTYPE[q.dtype], _ptr(out), _ptr(lse),
+        int(num_workers), int(phases), _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    _check(st, "zl_attn_varlen_gqa")
+    return (out, lse) if lse is not None else out
+
+
+def zl_attn_varlen_mla(q, kv_cache, cu_seqlens_q, cu_seqlens_k, max_seqlen_k: int, softmax_scale: float,
+                       causal: bool = True, kv_lora_rank: int = 512, rope_dim: int = 64, out=None, lse=None,
+                       workspace=None, num_workers: int = 0, stream=None, return_lse: bool = False,
+                       phases: int = 3):
+    """zl_attn_varlen_gqa for absorbed MLA: q [total_q, H, rank+rope], kv_cache
+    [T, rank+rope] (V = its first kv_lora_rank columns); out [total_q, H, rank]."""
+    dev, B, out, lse = _varlen_common(q, cu_seqlens_q, cu_seqlens_k, kv_lora_rank, out, lse, return_lse)
+    _need(kv_cache, "kv_cache", q.dtype, 2, dev)
+    Tq, H, Dk = q.shape
+    if Dk != kv_lora_rank + rope_dim or kv_cache.shape[1] != Dk:
+        raise ValueError("q and kv_cache rows must be kv_lora_rank + rope_dim wide")
+    nbytes = zl_decode_attn_mla_workspace_size(B, H, kv_lora_rank, rope_dim, max_seqlen_k, q.dtype,
+                                               num_workers)
+    if workspace is None:
+        workspace = new_workspace(nbytes, dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    st = library().zl_attn_varlen_mla_ex(
+        _ptr(q), _ptr(kv_cache), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, Tq, H, kv_lora_rank, rope_dim,
+        int(max_seqlen_k), float(softmax_scale), int(bool(causal)), _DTYPE[q.dtype], _ptr(out), _ptr(lse),
+        int(num_workers), int(phases), _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    _check(st, "zl_attn_varlen_mla")
     return (out, lse) if lse is not None else out
 
 

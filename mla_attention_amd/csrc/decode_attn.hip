@@ -163,10 +163,33 @@ __device__ __forceinline__ void dma_query_item(const uint16_t* qb, int nh, ZL_LD
   }
 }
 
-template <int L, int DT, bool PAGED>
+// The query item of a virtual sequence (several new tokens per sequence): row
+// r of the block is query row 16 hb + r of the sequence (new token (16 hb +
+// r) / G, head kvh*G + (16 hb + r) % G); rows past the sequence's last repeat
+// it.
+template <int L>
+__device__ __forceinline__ void dma_query_item_mq(const uint16_t* q, const VSeqInfo& si, int kvh, int G, int Hq,
+                                                  ZL_LDS char* dst, int lane) {
+  using TL = Tile<L>;
+  constexpr int QI = kHeadsPerUnit * TL::DK * 2 / 1024;
+  static_assert(TL::PER_TILE % QI == 0, "query copies fill the item");
+  const uint16_t* src[QI];
+#pragma unroll
+  for (int i = 0; i < QI; ++i) {
+    const int lin = 64 * i + lane;
+    const int r = lin / TL::KCPR;
+    const int c = Geo<L>::slot(lin - r * TL::KCPR, r);
+    src[i] = q + mq_column(si, r, kvh, G, Hq, false).row * TL::DK + c * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < TL::PER_TILE; ++i) dma16(src[i % QI], dst + i * 1024);
+}
+
+template <int L, int DT, bool PAGED, bool MQ>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, 64),
                           amdgpu_waves_per_eu(1, Geo<L>::MAX_WAVES_PER_SIMD))) void
 decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __restrict__ block_table) {
+  static_assert(!(PAGED && MQ), "several new tokens per sequence: packed caches only");
   using TL = Tile<L>;
   using GE = Geo<L>;
   constexpr int STAGES = GE::STAGES;
@@ -190,20 +213,41 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
   const TileMap<L, TL::NI_V> vmap = tile_map<L, TL::VCPR, TL::NI_V>(v_row_bytes, lane);
 
   // (Empty sequences are written by the merge launch: no run covers them.)
-  const int T = cu[B];
-  // Sequence boundaries for the lookups below, loaded alongside T (one round
-  // trip for both) and waited for here, so that no later lookup has to drain
-  // the tile loads in flight.
-  int window = bounds_window(cu, B, a.seg_cost);
-  asm volatile("" : "+v"(window));
-  const Line line = make_line(T, B, a.seg_cost);
+  // The batch: decode sequences, or with several new tokens per sequence the
+  // virtual sequences of 16 query rows.  Sequence boundaries for the lookups
+  // are loaded here, before any tile load, and waited for, so that no later
+  // lookup has to drain the tile loads in flight (B <= 64).
+  int window = 0;
+  VirtualSeqs vs;
+  int NB;  // sequences on the work line
+  int T;
+  if constexpr (MQ) {
+    vs.init(a.cu_q, cu, B, a.G, a.seg_cost);
+    asm volatile("" : "+v"(vs.first.q0), "+v"(vs.first.nq), "+v"(vs.first.k0), "+v"(vs.first.lk));
+    NB = vs.V;
+    T = vs.T;
+  } else {
+    T = cu[B];
+    window = bounds_window(cu, B, a.seg_cost);
+    asm volatile("" : "+v"(window));
+    NB = B;
+  }
+  const Line line = make_line(T, NB, a.seg_cost);
   const long long N = (long long)U * line.Tp;
   const long long per = positions_per_worker(N, a.P);
   const long long p_begin = (long long)w * per;
   const long long p_end = N < p_begin + per ? N : p_begin + per;
-  Segment ds = segment_at(p_begin, p_end, line, cu, window);
-  if (lane == 0) a.first_key[w] = ds.len > 0 ? seq_key(ds.u, ds.b, B) : -1;
+  const auto next_segment = [&](long long p) {
+    if constexpr (MQ)
+      return segment_at(p, p_end, line, vs);
+    else
+      return segment_at(p, p_end, line, cu, window);
+  };
+  Segment ds = next_segment(p_begin);
+  if (lane == 0) a.first_key[w] = ds.len > 0 ? seq_key(ds.u, ds.b, NB) : -1;
   if (ds.len == 0) return;
+  VSeqInfo dsi{}, sgi{};  // several new tokens: the virtual sequences of ds, sg
+  if constexpr (MQ) dsi = vs.info(ds.b);
 
   // The run is one stream of ring items: for every segment (the part of one
   // sequence of one work unit in the run) its query rows, then its 32-token
@@ -229,12 +273,18 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
     const int ntl = (ds.len + 31) >> 5;
     const int kvh = ds.u / a.HB, hb = ds.u - (ds.u / a.HB) * a.HB;
     if (dj == 0) {
-      const int h0 = kvh * a.G + hb * kHeadsPerUnit;
-      const int nh = min(kHeadsPerUnit, a.G - hb * kHeadsPerUnit);
-      dma_query_item<L>(a.q + ((long long)ds.b * a.Hq + h0) * DK, nh, st, lane);
+      if constexpr (MQ) {
+        dma_query_item_mq<L>(a.q, dsi, kvh, a.G, a.Hq, st, lane);
+      } else {
+        const int h0 = kvh * a.G + hb * kHeadsPerUnit;
+        const int nh = min(kHeadsPerUnit, a.G - hb * kHeadsPerUnit);
+        dma_query_item<L>(a.q + ((long long)ds.b * a.Hq + h0) * DK, nh, st, lane);
+      }
     } else {
       const int k = dj - 1;
-      const int tok = ds.t0 + 32 * k;
+      // Cache row of the tile's first token (virtual tokens map onto the
+      // sequence's rows).
+      const int tok = MQ ? dsi.k0 + (ds.t0 - ds.cs) + 32 * k : ds.t0 + 32 * k;
       const int nv = min(32, ds.len - 32 * k);
       if constexpr (PAGED) {
         dma_tile_paged<L, TL::NI_K>((const char*)(a.k + (long long)kvh * DK), k_row_bytes, kmap, pf, nv, st);
@@ -249,15 +299,22 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
     }
     ++issued;
     if (++dj > ntl) {
-      ds = segment_at(ds.p + ds.len, p_end, line, cu, window);
+      ds = next_segment(ds.p + ds.len);
       dj = 0;
       dmore = ds.len > 0;
+      if constexpr (MQ)
+        if (dmore) dsi = vs.info(ds.b);
     }
     prefetch_pages();
   };
   Segment sg = ds;  // the segment being computed
   int cj = 0;       // its current item
   bool first_seg = true;
+  MqColumn col{};   // several new tokens: this lane's column of sg's row block
+  if constexpr (MQ) {
+    sgi = dsi;
+    col = mq_column(sgi, n, sg.u, a.G, a.Hq, a.causal != 0);
+  }
   for (int s = 0; s < STAGES - 1 && dmore; ++s) issue();
 
   f32x4 o[TL::VBLK];
@@ -292,7 +349,13 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
       f32x4 s[2];
       scores<DT, TL::KSTEPS, TL::KROWB>(st, qop, n, g, slot, s);
       float alpha;
-      const POperand pop = softmax_update<DT>(s, g, min(32, sg.len - 32 * j), a.scale_log2, sm, alpha);
+      int nvalid = min(32, sg.len - 32 * j);
+      if constexpr (MQ) {
+        // Causal limit of this lane's query row: cache rows up to col.lim.
+        const int j0 = sg.t0 - sg.cs + 32 * j;
+        nvalid = min(nvalid, col.lim - j0 + 1);
+      }
+      const POperand pop = softmax_update<DT>(s, g, nvalid, a.scale_log2, sm, alpha);
 #pragma unroll
       for (int bb = 0; bb < TL::VBLK; ++bb) o[bb] *= alpha;
       pv_blocks<DT, TL::VBLK, TL::VROWB>(vt, pop, n, g, 0, slot, o);
@@ -308,12 +371,14 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
         const float l_tot = sum_over_groups(sm.l);
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         const float lse_v = l_tot > 0.f ? sm.m * kLn2 + __logf(l_tot) : -INFINITY;
-        if (n < nh) {
+        const bool has_row = MQ ? col.valid : n < nh;
+        const long long row = MQ ? col.row : (long long)sg.b * a.Hq + h0 + n;
+        if (has_row) {
           if (sw.first == sw.last) {
-            uint16_t* orow = a.out + ((long long)sg.b * a.Hq + h0 + n) * DV + 4 * g;
+            uint16_t* orow = a.out + row * DV + 4 * g;
 #pragma unroll
             for (int blk = 0; blk < TL::VBLK; ++blk) store_out4<DT>(orow + 16 * blk, o[blk], inv);
-            if (a.lse && g == 0) a.lse[(long long)sg.b * a.Hq + h0 + n] = lse_v;
+            if (a.lse && g == 0) a.lse[row] = lse_v;
           } else {
             const int sl = 2 * w + (first_seg ? 0 : 1);
             float* po = a.part_o + ((long long)sl * kHeadsPerUnit + n) * DV + 4 * g;
@@ -325,10 +390,14 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
       }
     }
     if (++cj > ntl) {
-      sg = segment_at(sg.p + sg.len, p_end, line, cu, window);
+      sg = next_segment(sg.p + sg.len);
       if (sg.len == 0) break;
       cj = 0;
       first_seg = false;
+      if constexpr (MQ) {
+        sgi = vs.info(sg.b);
+        col = mq_column(sgi, n, sg.u, a.G, a.Hq, a.causal != 0);
+      }
     }
   }
 }
@@ -343,10 +412,15 @@ int default_workers(Layout layout) {
 
 template <int L, int DT>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  if (a.block_table)
-    hipLaunchKernelGGL((decode_kernel<L, DT, true>), dim3(a.P), dim3(64), 0, stream, a, a.cu, a.block_table);
+  if (a.cu_q)
+    hipLaunchKernelGGL((decode_kernel<L, DT, false, true>), dim3(a.P), dim3(64), 0, stream, a, a.cu,
+                       a.block_table);
+  else if (a.block_table)
+    hipLaunchKernelGGL((decode_kernel<L, DT, true, false>), dim3(a.P), dim3(64), 0, stream, a, a.cu,
+                       a.block_table);
   else
-    hipLaunchKernelGGL((decode_kernel<L, DT, false>), dim3(a.P), dim3(64), 0, stream, a, a.cu, a.block_table);
+    hipLaunchKernelGGL((decode_kernel<L, DT, false, false>), dim3(a.P), dim3(64), 0, stream, a, a.cu,
+                       a.block_table);
   return hipGetLastError();
 }
 

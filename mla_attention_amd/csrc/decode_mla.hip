@@ -133,6 +133,21 @@ __device__ __forceinline__ void dma_query_item(const uint16_t* qb, int nh, ZL_LD
   }
 }
 
+// The query item of a virtual sequence (several new tokens per sequence): row
+// r is query row 16 hb + r of the sequence (new token (16 hb + r) / H, head
+// (16 hb + r) % H); rows past the sequence's last repeat it.
+__device__ __forceinline__ void dma_query_item_mq(const uint16_t* q, const VSeqInfo& si, int H, ZL_LDS char* dst,
+                                                  int wave, int lane) {
+#pragma unroll
+  for (int k = 0; k < kNIw; ++k) {
+    const int i = wave * kNIw + k;
+    const int lin = 64 * (i % kNIq) + lane;
+    const int r = lin / kCPR;
+    const int s = lin - r * kCPR;
+    dma16(q + mq_column(si, r, 0, H, H, false).row * kDK + slot(s, r) * 8, dst + i * 1024);
+  }
+}
+
 }  // namespace
 
 // Partial scores of one 16-token block over half of the k-steps:
@@ -155,10 +170,11 @@ __device__ __forceinline__ f32x4 half_scores(const ZL_LDS char* kt, const i16x8 
   return acc0 + acc1;
 }
 
-template <int DT, bool PAGED>
+template <int DT, bool PAGED, bool MQ>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kWaves, 64 * kWaves),
                           amdgpu_waves_per_eu(1, 1))) void
 mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __restrict__ block_table) {
+  static_assert(!(PAGED && MQ), "several new tokens per sequence: packed caches only");
   // One LDS object only (see decode_attn.hip): [4 ring stages][score exchange].
   __shared__ __attribute__((aligned(1024))) char smem_raw[kLdsBytes];
   ZL_LDS char* smem = (ZL_LDS char*)smem_raw;
@@ -179,20 +195,41 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
   const QuarterMap qmap = quarter_map(wave, lane);
 
   // (Empty sequences are written by the merge launch: no run covers them.)
-  const int T = cu[B];
-  // Sequence boundaries for the lookups below, loaded alongside T (one round
-  // trip for both) and waited for here, so that no later lookup has to drain
-  // the tile loads in flight.
-  int window = bounds_window(cu, B, a.seg_cost);
-  asm volatile("" : "+v"(window));
-  const Line line = make_line(T, B, a.seg_cost);
+  // The batch: decode sequences, or with several new tokens per sequence the
+  // virtual sequences of 16 query rows.  Sequence boundaries for the lookups
+  // are loaded here, before any tile load, and waited for, so that no later
+  // lookup has to drain the tile loads in flight (B <= 64).
+  int window = 0;
+  VirtualSeqs vs;
+  int NB;  // sequences on the work line
+  int T;
+  if constexpr (MQ) {
+    vs.init(a.cu_q, cu, B, a.G, a.seg_cost);
+    asm volatile("" : "+v"(vs.first.q0), "+v"(vs.first.nq), "+v"(vs.first.k0), "+v"(vs.first.lk));
+    NB = vs.V;
+    T = vs.T;
+  } else {
+    T = cu[B];
+    window = bounds_window(cu, B, a.seg_cost);
+    asm volatile("" : "+v"(window));
+    NB = B;
+  }
+  const Line line = make_line(T, NB, a.seg_cost);
   const long long N = (long long)U * line.Tp;
   const long long per = positions_per_worker(N, a.P);
   const long long p_begin = (long long)w * per;
   const long long p_end = N < p_begin + per ? N : p_begin + per;
-  Segment ds = segment_at(p_begin, p_end, line, cu, window);
-  if (tid == 0) a.first_key[w] = ds.len > 0 ? seq_key(ds.u, ds.b, B) : -1;
+  const auto next_segment = [&](long long p) {
+    if constexpr (MQ)
+      return segment_at(p, p_end, line, vs);
+    else
+      return segment_at(p, p_end, line, cu, window);
+  };
+  Segment ds = next_segment(p_begin);
+  if (tid == 0) a.first_key[w] = ds.len > 0 ? seq_key(ds.u, ds.b, NB) : -1;
   if (ds.len == 0) return;  // the whole workgroup: w is per workgroup
+  VSeqInfo dsi{}, sgi{};  // several new tokens: the virtual sequences of ds, sg
+  if constexpr (MQ) dsi = vs.info(ds.b);
 
   // The run is one stream of ring items: for every segment its query item,
   // then its 32-token tiles.  The issuing side runs up to three items ahead
@@ -217,28 +254,44 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
     ZL_LDS char* dst = smem + (issued % kStages) * kTileB;
     const int ntl = (ds.len + 31) >> 5;
     if (dj == 0) {
-      const int h0 = ds.u * kHeadsPerUnit;
-      dma_query_item(a.q + ((long long)ds.b * a.Hq + h0) * kDK, min(kHeadsPerUnit, a.G - h0), dst, wave, lane);
+      if constexpr (MQ) {
+        dma_query_item_mq(a.q, dsi, a.G, dst, wave, lane);
+      } else {
+        const int h0 = ds.u * kHeadsPerUnit;
+        dma_query_item(a.q + ((long long)ds.b * a.Hq + h0) * kDK, min(kHeadsPerUnit, a.G - h0), dst, wave,
+                       lane);
+      }
     } else {
       const int k = dj - 1;
       const int nv = min(32, ds.len - 32 * k);
       if constexpr (PAGED) {
         dma_quarter_paged(a.k, pf, nv, qmap, dst, wave);
+      } else if constexpr (MQ) {
+        // Cache row of the tile's first token (virtual tokens map onto the
+        // sequence's rows).
+        dma_quarter(a.k, dsi.k0 + (ds.t0 - ds.cs) + 32 * k, nv, qmap, dst, wave);
       } else {
         dma_quarter(a.k, ds.t0 + 32 * k, nv, qmap, dst, wave);
       }
     }
     ++issued;
     if (++dj > ntl) {
-      ds = segment_at(ds.p + ds.len, p_end, line, cu, window);
+      ds = next_segment(ds.p + ds.len);
       dj = 0;
       dmore = ds.len > 0;
+      if constexpr (MQ)
+        if (dmore) dsi = vs.info(ds.b);
     }
     prefetch_pages();
   };
   Segment sg = ds;  // the segment being computed
   int cj = 0;       // its current item
   bool first_seg = true;
+  MqColumn col{};   // several new tokens: this lane's column of sg's row block
+  if constexpr (MQ) {
+    sgi = dsi;
+    col = mq_column(sgi, n, 0, a.G, a.Hq, a.causal != 0);
+  }
   for (int s = 0; s < kStages - 1 && dmore; ++s) issue();
 
   f32x4 o[kBlkPerWave];
@@ -280,7 +333,13 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
       s[1] = *(const ZL_LDS f32x4*)(xchg + 1 * 1024 + lane * 16) +
              *(const ZL_LDS f32x4*)(xchg + 3 * 1024 + lane * 16);
       float alpha;
-      const POperand pop = softmax_update<DT>(s, g, min(32, sg.len - 32 * j), a.scale_log2, sm, alpha);
+      int nvalid = min(32, sg.len - 32 * j);
+      if constexpr (MQ) {
+        // Causal limit of this lane's query row: cache rows up to col.lim.
+        const int j0 = sg.t0 - sg.cs + 32 * j;
+        nvalid = min(nvalid, col.lim - j0 + 1);
+      }
+      const POperand pop = softmax_update<DT>(s, g, nvalid, a.scale_log2, sm, alpha);
 #pragma unroll
       for (int bb = 0; bb < kBlkPerWave; ++bb) o[bb] *= alpha;
       pv_blocks<DT, kBlkPerWave, kRowB>(it, pop, n, g, wave * kBlkPerWave, slot_fn, o);
@@ -294,12 +353,14 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
         const float l_tot = sum_over_groups(sm.l);
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         const float lse_v = l_tot > 0.f ? sm.m * kLn2 + __logf(l_tot) : -INFINITY;
-        if (n < nh) {
+        const bool has_row = MQ ? col.valid : n < nh;
+        const long long row = MQ ? col.row : (long long)sg.b * a.Hq + h0 + n;
+        if (has_row) {
           if (sw.first == sw.last) {
-            uint16_t* orow = a.out + ((long long)sg.b * a.Hq + h0 + n) * kDV + dim0;
+            uint16_t* orow = a.out + row * kDV + dim0;
 #pragma unroll
             for (int bb = 0; bb < kBlkPerWave; ++bb) store_out4<DT>(orow + 16 * bb, o[bb], inv);
-            if (a.lse && wave == 0 && g == 0) a.lse[(long long)sg.b * a.Hq + h0 + n] = lse_v;
+            if (a.lse && wave == 0 && g == 0) a.lse[row] = lse_v;
           } else {
             const int sl = 2 * w + (first_seg ? 0 : 1);
             float* po = a.part_o + ((long long)sl * kHeadsPerUnit + n) * kDV + dim0;
@@ -311,29 +372,36 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
       }
     }
     if (++cj > ntl) {
-      sg = segment_at(sg.p + sg.len, p_end, line, cu, window);
+      sg = next_segment(sg.p + sg.len);
       if (sg.len == 0) break;
       cj = 0;
       first_seg = false;
+      if constexpr (MQ) {
+        sgi = vs.info(sg.b);
+        col = mq_column(sgi, n, 0, a.G, a.Hq, a.causal != 0);
+      }
     }
   }
 }
 
 int mla_default_workers() { return 256 * kWorkgroupsPerCU; }
 
-hipError_t launch_mla(const DecodeArgs& a, int dtype, hipStream_t stream) {
+template <int DT>
+static void launch_mla_t(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.P), block(64 * kWaves);
-  if (a.block_table) {
-    if (dtype == kF16)
-      hipLaunchKernelGGL((mla_decode_kernel<kF16, true>), grid, block, 0, stream, a, a.cu, a.block_table);
-    else
-      hipLaunchKernelGGL((mla_decode_kernel<kBF16, true>), grid, block, 0, stream, a, a.cu, a.block_table);
-  } else {
-    if (dtype == kF16)
-      hipLaunchKernelGGL((mla_decode_kernel<kF16, false>), grid, block, 0, stream, a, a.cu, a.block_table);
-    else
-      hipLaunchKernelGGL((mla_decode_kernel<kBF16, false>), grid, block, 0, stream, a, a.cu, a.block_table);
-  }
+  if (a.cu_q)
+    hipLaunchKernelGGL((mla_decode_kernel<DT, false, true>), grid, block, 0, stream, a, a.cu, a.block_table);
+  else if (a.block_table)
+    hipLaunchKernelGGL((mla_decode_kernel<DT, true, false>), grid, block, 0, stream, a, a.cu, a.block_table);
+  else
+    hipLaunchKernelGGL((mla_decode_kernel<DT, false, false>), grid, block, 0, stream, a, a.cu, a.block_table);
+}
+
+hipError_t launch_mla(const DecodeArgs& a, int dtype, hipStream_t stream) {
+  if (dtype == kF16)
+    launch_mla_t<kF16>(a, stream);
+  else
+    launch_mla_t<kBF16>(a, stream);
   return hipGetLastError();
 }
 

@@ -24,31 +24,54 @@
 
 namespace zl {
 
-template <int DT, int DV>
+// Several new query tokens per sequence (MQ): one workgroup per (key/value
+// head, virtual sequence), for an upper bound on the number of virtual
+// sequences; the workgroups past the batch's count return at once.
+template <int DT, int DV, bool MQ>
 __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a, const int32_t* __restrict__ cu,
-                                                          int heads_per_unit, int wg_per_seq) {
+                                                          int heads_per_unit, int wg_per_seq, int seqs) {
   constexpr int C4 = DV / 4;  // float4 columns per output row
   // Workgroup -> (unit u, sequence b, part); all wave-uniform.
   const int part = (int)blockIdx.x % wg_per_seq;
   const int ub = (int)blockIdx.x / wg_per_seq;
-  const int b = ub % a.B;
-  const int u = ub / a.B;
+  const int b = ub % seqs;
+  const int u = ub / seqs;
   const int kvh = u / a.HB, hb = u - (u / a.HB) * a.HB;
-  const int nh = min(kHeadsPerUnit, a.G - hb * kHeadsPerUnit);
+  const int nh = MQ ? kHeadsPerUnit : min(kHeadsPerUnit, a.G - hb * kHeadsPerUnit);
   const int h0 = kvh * a.G + hb * kHeadsPerUnit;
   const int item = part * 256 + (int)threadIdx.x;
   const int h = item / C4;
   const int c4 = item - h * C4;
   if (h >= nh || h >= heads_per_unit) return;
-  const int cs = cu[b], ce = cu[b + 1];
+  int NB, T, cs, ce;
+  long long row;  // output row of this thread's column
+  VirtualSeqs vs;
+  if constexpr (MQ) {
+    vs.init(a.cu_q, cu, a.B, a.G, a.seg_cost);
+    if (b >= vs.V) return;
+    const VSeqInfo si = vs.info(b);
+    const MqColumn col = mq_column(si, h, kvh, a.G, a.Hq, false);
+    if (!col.valid) return;
+    NB = vs.V;
+    T = vs.T;
+    cs = si.cs;
+    ce = si.ce;
+    row = col.row;
+  } else {
+    NB = a.B;
+    T = cu[a.B];
+    cs = cu[b];
+    ce = cu[b + 1];
+    row = (long long)b * a.Hq + h0 + h;
+  }
   if (ce == cs) {
     // An empty sequence (no worker run covers it): out = 0, lse = -inf.
-    *(u32x2*)(a.out + ((long long)b * a.Hq + h0 + h) * DV + 4 * c4) = u32x2{0u, 0u};
-    if (a.lse && c4 == 0) a.lse[(long long)b * a.Hq + h0 + h] = -INFINITY;
+    *(u32x2*)(a.out + row * DV + 4 * c4) = u32x2{0u, 0u};
+    if (a.lse && c4 == 0) a.lse[row] = -INFINITY;
     return;
   }
   const int U = a.Hkv * a.HB;
-  const Line line = make_line(cu[a.B], a.B, a.seg_cost);
+  const Line line = make_line(T, NB, a.seg_cost);
   const long long per = positions_per_worker((long long)U * line.Tp, a.P);
   const SeqWorkers sw = seq_workers(line, u, b, cs, ce, per);
   const int w_first = sw.first, w_last = sw.last;
@@ -79,7 +102,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a, const in
       v[j] = *(const f32x4*)(a.part_o + ((long long)sl * kHeadsPerUnit + h) * DV + 4 * c4);
     }
     if (i0 == 0) {
-      const bool opened = key_first == seq_key(u, b, a.B);
+      const bool opened = key_first == seq_key(u, b, NB);
       ls[0] = opened ? ls_a : ls_b;
       v[0] = opened ? v_a : v_b;
     }
@@ -100,27 +123,36 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a, const in
     M = m_new;
   }
   const float winv = wsum > 0.f ? 1.f / wsum : 0.f;
-  store_out4<DT>(a.out + ((long long)b * a.Hq + h0 + h) * DV + 4 * c4, acc, winv);
-  if (a.lse && c4 == 0) a.lse[(long long)b * a.Hq + h0 + h] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
+  store_out4<DT>(a.out + row * DV + 4 * c4, acc, winv);
+  if (a.lse && c4 == 0) a.lse[row] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
 }
 
 template <int DT, int DV>
-static hipError_t launch_merge_t(const DecodeArgs& a, hipStream_t stream) {
-  const int hpu = a.G < kHeadsPerUnit ? a.G : kHeadsPerUnit;
+static hipError_t launch_merge_t(const DecodeArgs& a, int max_vseqs, hipStream_t stream) {
+  const bool mq = a.cu_q != nullptr;
+  const int hpu = mq ? kHeadsPerUnit : (a.G < kHeadsPerUnit ? a.G : kHeadsPerUnit);
   const int wg_per_seq = (hpu * (DV / 4) + 255) / 256;
-  const long long blocks = (long long)a.Hkv * a.HB * a.B * wg_per_seq;
+  const int seqs = mq ? max_vseqs : a.B;
+  const long long blocks = (long long)a.Hkv * a.HB * seqs * wg_per_seq;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((split_merge_kernel<DT, DV>), dim3((unsigned)blocks), dim3(256), 0, stream, a, a.cu, hpu,
-                     wg_per_seq);
+  if (mq)
+    hipLaunchKernelGGL((split_merge_kernel<DT, DV, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a, a.cu,
+                       hpu, wg_per_seq, seqs);
+  else
+    hipLaunchKernelGGL((split_merge_kernel<DT, DV, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a,
+                       a.cu, hpu, wg_per_seq, seqs);
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const DecodeArgs& a, int dv, int dtype, hipStream_t stream) {
+hipError_t launch_merge(const DecodeArgs& a, int dv, int dtype, int max_vseqs, hipStream_t stream) {
   if (dv == 64)
-    return dtype == kF16 ? launch_merge_t<kF16, 64>(a, stream) : launch_merge_t<kBF16, 64>(a, stream);
+    return dtype == kF16 ? launch_merge_t<kF16, 64>(a, max_vseqs, stream)
+                         : launch_merge_t<kBF16, 64>(a, max_vseqs, stream);
   if (dv == 128)
-    return dtype == kF16 ? launch_merge_t<kF16, 128>(a, stream) : launch_merge_t<kBF16, 128>(a, stream);
-  return dtype == kF16 ? launch_merge_t<kF16, 512>(a, stream) : launch_merge_t<kBF16, 512>(a, stream);
+    return dtype == kF16 ? launch_merge_t<kF16, 128>(a, max_vseqs, stream)
+                         : launch_merge_t<kBF16, 128>(a, max_vseqs, stream);
+  return dtype == kF16 ? launch_merge_t<kF16, 512>(a, max_vseqs, stream)
+                       : launch_merge_t<kBF16, 512>(a, max_vseqs, stream);
 }
 
 }  // namespace zl

@@ -80,7 +80,7 @@ size_t mla_ws_size(int batch, int num_q_heads, int kv_lora_rank, int rope_dim, i
 }
 
 zl_status_t run_decode(zl::DecodeArgs a, Layout layout, int dv, zl_dtype_t dtype, int phases,
-                       void* workspace, size_t workspace_bytes, zl_stream_t stream) {
+                       void* workspace, size_t workspace_bytes, zl_stream_t stream, int max_vseqs = 0) {
   const WsLayout wl = ws_layout(a.P, dv);
   if (workspace == nullptr || !aligned(workspace, 256)) return ZL_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < wl.total) return ZL_ERR_WORKSPACE_TOO_SMALL;
@@ -92,7 +92,7 @@ zl_status_t run_decode(zl::DecodeArgs a, Layout layout, int dv, zl_dtype_t dtype
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (phases & 1) e = zl::launch_decode(a, layout, dtype, st);
-  if (e == hipSuccess && (phases & 2)) e = zl::launch_merge(a, dv, dtype, st);
+  if (e == hipSuccess && (phases & 2)) e = zl::launch_merge(a, dv, dtype, max_vseqs, st);
   return e == hipSuccess ? ZL_OK : ZL_ERR_HIP;
 }
 
@@ -123,6 +123,30 @@ struct Paging {
   int page_size = 0;
 };
 
+// Several new query tokens per sequence: their bounds, count and mask.
+struct Varlen {
+  const int32_t* cu_q = nullptr;
+  int total_q = 0;
+  int causal = 0;
+};
+
+// Upper bound on the virtual sequences (blocks of 16 query rows of one
+// sequence) of a call: sum over b of ceil(nq_b * G / 16).
+long long max_virtual_seqs(const Varlen& vl, int batch, int group) {
+  return ((long long)vl.total_q * group + 15LL * batch + 15) / 16;
+}
+
+zl_status_t check_varlen(const Varlen& vl, int batch, int group, int max_seqlen_k, int seg_cost) {
+  if (!vl.cu_q) return ZL_OK;
+  if (!aligned(vl.cu_q, 4) || vl.total_q < 0 || (vl.causal != 0 && vl.causal != 1))
+    return ZL_ERR_INVALID_ARGUMENT;
+  // Positions of the work line (virtual tokens plus the per-sequence cost)
+  // are 32-bit inside the kernels.
+  const long long V = max_virtual_seqs(vl, batch, group);
+  if (V * ((long long)max_seqlen_k + seg_cost) >= (1LL << 31)) return ZL_ERR_UNSUPPORTED;
+  return ZL_OK;
+}
+
 zl_status_t check_paging(const Paging& pg, int max_seqlen_k, int& shift) {
   shift = 0;
   if (!pg.table) return ZL_OK;
@@ -135,7 +159,7 @@ zl_status_t check_paging(const Paging& pg, int max_seqlen_k, int& shift) {
   return ZL_OK;
 }
 
-zl_status_t gqa_impl(const void* q, const void* k_cache, const void* v_cache, const Paging& pg,
+zl_status_t gqa_impl(const void* q, const void* k_cache, const void* v_cache, const Paging& pg, const Varlen& vl,
                      const int32_t* cu_seqlens, int batch, int num_q_heads, int num_kv_heads, int head_dim,
                      int max_seqlen_k, float softmax_scale, zl_dtype_t dtype, void* out, float* lse,
                      int num_workers, int phases, void* workspace, size_t workspace_bytes,
@@ -153,7 +177,9 @@ zl_status_t gqa_impl(const void* q, const void* k_cache, const void* v_cache, co
   int shift = 0;
   const zl_status_t sp = check_paging(pg, max_seqlen_k, shift);
   if (sp != ZL_OK) return sp;
-  if (batch == 0) return ZL_OK;
+  const zl_status_t sv = check_varlen(vl, batch, num_q_heads / num_kv_heads, max_seqlen_k, zl::kSegCostGqa);
+  if (sv != ZL_OK) return sv;
+  if (batch == 0 || (vl.cu_q && vl.total_q == 0)) return ZL_OK;
   // k_cache / v_cache may be NULL only when every sequence is empty (the
   // kernel never reads a cache row then); the host cannot see the lengths.
   if (!q || !cu_seqlens || !out) return ZL_ERR_INVALID_ARGUMENT;
@@ -171,13 +197,16 @@ zl_status_t gqa_impl(const void* q, const void* k_cache, const void* v_cache, co
   a.Hq = num_q_heads;
   a.Hkv = num_kv_heads;
   a.G = num_q_heads / num_kv_heads;
-  a.HB = head_blocks(a.G);
+  a.HB = vl.cu_q ? 1 : head_blocks(a.G);
   a.P = P;
   a.block_table = pg.table;
   a.max_pages = pg.max_pages;
   a.page_shift = shift;
+  a.cu_q = vl.cu_q;
+  a.causal = vl.causal;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  return run_decode(a, layout, head_dim, dtype, phases, workspace, workspace_bytes, stream);
+  return run_decode(a, layout, head_dim, dtype, phases, workspace, workspace_bytes, stream,
+                    (int)max_virtual_seqs(vl, batch, a.G));
 }
 
 }  // namespace
@@ -190,7 +219,7 @@ zl_status_t zl_decode_attn_gqa_ex(const void* q, const void* k_cache, const void
                                   float softmax_scale, zl_dtype_t dtype, void* out, float* lse,
                                   int num_workers, int phases, void* workspace,
                                   size_t workspace_bytes, zl_stream_t stream) {
-  return gqa_impl(q, k_cache, v_cache, Paging{}, cu_seqlens, batch, num_q_heads, num_kv_heads, head_dim,
+  return gqa_impl(q, k_cache, v_cache, Paging{}, Varlen{}, cu_seqlens, batch, num_q_heads, num_kv_heads, head_dim,
                   max_seqlen_k, softmax_scale, dtype, out, lse, num_workers, phases, workspace,
                   workspace_bytes, stream);
 }
@@ -207,7 +236,7 @@ zl_status_t zl_decode_attn_gqa_paged_ex(const void* q, const void* k_pages, cons
   pg.table = block_table;
   pg.max_pages = max_pages_per_seq;
   pg.page_size = page_size;
-  return gqa_impl(q, k_pages, v_pages, pg, cu_seqlens, batch, num_q_heads, num_kv_heads, head_dim,
+  return gqa_impl(q, k_pages, v_pages, pg, Varlen{}, cu_seqlens, batch, num_q_heads, num_kv_heads, head_dim,
                   max_seqlen_k, softmax_scale, dtype, out, lse, num_workers, phases, workspace,
                   workspace_bytes, stream);
 }
@@ -250,7 +279,8 @@ size_t zl_decode_attn_mla_workspace_size_ex(int batch, int num_q_heads, int kv_l
 
 namespace {
 
-zl_status_t mla_impl(const void* q, const void* kv_cache, const Paging& pg, const int32_t* cu_seqlens, int batch,
+zl_status_t mla_impl(const void* q, const void* kv_cache, const Paging& pg, const Varlen& vl,
+                     const int32_t* cu_seqlens, int batch,
                      int num_q_heads, int kv_lora_rank, int rope_dim, int max_seqlen_k, float softmax_scale,
                      zl_dtype_t dtype, void* out, float* lse, int num_workers, int phases, void* workspace,
                      size_t workspace_bytes, zl_stream_t stream) {
@@ -264,7 +294,9 @@ zl_status_t mla_impl(const void* q, const void* kv_cache, const Paging& pg, cons
   int shift = 0;
   const zl_status_t sp = check_paging(pg, max_seqlen_k, shift);
   if (sp != ZL_OK) return sp;
-  if (batch == 0) return ZL_OK;
+  const zl_status_t sv = check_varlen(vl, batch, num_q_heads, max_seqlen_k, zl::kSegCostMla);
+  if (sv != ZL_OK) return sv;
+  if (batch == 0 || (vl.cu_q && vl.total_q == 0)) return ZL_OK;
   if (!q || !cu_seqlens || !out) return ZL_ERR_INVALID_ARGUMENT;  // kv_cache: see above
   if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(cu_seqlens, 4) ||
       !aligned(lse, 4))
@@ -280,13 +312,16 @@ zl_status_t mla_impl(const void* q, const void* kv_cache, const Paging& pg, cons
   a.Hq = num_q_heads;
   a.Hkv = 1;
   a.G = num_q_heads;
-  a.HB = head_blocks(num_q_heads);
+  a.HB = vl.cu_q ? 1 : head_blocks(num_q_heads);
   a.P = P;
   a.block_table = pg.table;
   a.max_pages = pg.max_pages;
   a.page_shift = shift;
+  a.cu_q = vl.cu_q;
+  a.causal = vl.causal;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  return run_decode(a, zl::kMla576, kv_lora_rank, dtype, phases, workspace, workspace_bytes, stream);
+  return run_decode(a, zl::kMla576, kv_lora_rank, dtype, phases, workspace, workspace_bytes, stream,
+                    (int)max_virtual_seqs(vl, batch, num_q_heads));
 }
 
 }  // namespace
@@ -298,7 +333,7 @@ zl_status_t zl_decode_attn_mla_ex(const void* q, const void* kv_cache, const int
                                   int max_seqlen_k, float softmax_scale, zl_dtype_t dtype,
                                   void* out, float* lse, int num_workers, int phases,
                                   void* workspace, size_t workspace_bytes, zl_stream_t stream) {
-  return mla_impl(q, kv_cache, Paging{}, cu_seqlens, batch, num_q_heads, kv_lora_rank, rope_dim, max_seqlen_k,
+  return mla_impl(q, kv_cache, Paging{}, Varlen{}, cu_seqlens, batch, num_q_heads, kv_lora_rank, rope_dim, max_seqlen_k,
                   softmax_scale, dtype, out, lse, num_workers, phases, workspace, workspace_bytes, stream);
 }
 
@@ -313,7 +348,7 @@ zl_status_t zl_decode_attn_mla_paged_ex(const void* q, const void* kv_pages, con
   pg.table = block_table;
   pg.max_pages = max_pages_per_seq;
   pg.page_size = page_size;
-  return mla_impl(q, kv_pages, pg, cu_seqlens, batch, num_q_heads, kv_lora_rank, rope_dim, max_seqlen_k,
+  return mla_impl(q, kv_pages, pg, Varlen{}, cu_seqlens, batch, num_q_heads, kv_lora_rank, rope_dim, max_seqlen_k,
                   softmax_scale, dtype, out, lse, num_workers, phases, workspace, workspace_bytes, stream);
 }
 
@@ -334,6 +369,57 @@ zl_status_t zl_decode_attn_mla(const void* q, const void* kv_cache, const int32_
                                zl_stream_t stream) {
   return zl_decode_attn_mla_ex(q, kv_cache, cu_seqlens, batch, num_q_heads, kv_lora_rank, rope_dim,
                                max_seqlen_k, softmax_scale, dtype, out, lse, 0, 3, workspace,
+                               workspace_bytes, stream);
+}
+
+zl_status_t zl_attn_varlen_gqa_ex(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch, int total_q,
+                                  int num_q_heads, int num_kv_heads, int head_dim, int max_seqlen_k,
+                                  float softmax_scale, int causal, zl_dtype_t dtype, void* out, float* lse,
+                                  int num_workers, int phases, void* workspace, size_t workspace_bytes,
+                                  zl_stream_t stream) {
+  if (!cu_seqlens_q) return ZL_ERR_INVALID_ARGUMENT;
+  Varlen vl;
+  vl.cu_q = cu_seqlens_q;
+  vl.total_q = total_q;
+  vl.causal = causal;
+  return gqa_impl(q, k_cache, v_cache, Paging{}, vl, cu_seqlens_k, batch, num_q_heads, num_kv_heads, head_dim,
+                  max_seqlen_k, softmax_scale, dtype, out, lse, num_workers, phases, workspace, workspace_bytes,
+                  stream);
+}
+
+zl_status_t zl_attn_varlen_gqa(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch, int total_q,
+                               int num_q_heads, int num_kv_heads, int head_dim, int max_seqlen_k,
+                               float softmax_scale, int causal, zl_dtype_t dtype, void* out, float* lse,
+                               void* workspace, size_t workspace_bytes, zl_stream_t stream) {
+  return zl_attn_varlen_gqa_ex(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, batch, total_q, num_q_heads,
+                               num_kv_heads, head_dim, max_seqlen_k, softmax_scale, causal, dtype, out, lse, 0, 3,
+                               workspace, workspace_bytes, stream);
+}
+
+zl_status_t zl_attn_varlen_mla_ex(const void* q, const void* kv_cache, const int32_t* cu_seqlens_q,
+                                  const int32_t* cu_seqlens_k, int batch, int total_q, int num_q_heads,
+                                  int kv_lora_rank, int rope_dim, int max_seqlen_k, float softmax_scale, int causal,
+                                  zl_dtype_t dtype, void* out, float* lse, int num_workers, int phases,
+                                  void* workspace, size_t workspace_bytes, zl_stream_t stream) {
+  if (!cu_seqlens_q) return ZL_ERR_INVALID_ARGUMENT;
+  Varlen vl;
+  vl.cu_q = cu_seqlens_q;
+  vl.total_q = total_q;
+  vl.causal = causal;
+  return mla_impl(q, kv_cache, Paging{}, vl, cu_seqlens_k, batch, num_q_heads, kv_lora_rank, rope_dim,
+                  max_seqlen_k, softmax_scale, dtype, out, lse, num_workers, phases, workspace, workspace_bytes,
+                  stream);
+}
+
+zl_status_t zl_attn_varlen_mla(const void* q, const void* kv_cache, const int32_t* cu_seqlens_q,
+                               const int32_t* cu_seqlens_k, int batch, int total_q, int num_q_heads,
+                               int kv_lora_rank, int rope_dim, int max_seqlen_k, float softmax_scale, int causal,
+                               zl_dtype_t dtype, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                               zl_stream_t stream) {
+  return zl_attn_varlen_mla_ex(q, kv_cache, cu_seqlens_q, cu_seqlens_k, batch, total_q, num_q_heads, kv_lora_rank,
+                               rope_dim, max_seqlen_k, softmax_scale, causal, dtype, out, lse, 0, 3, workspace,
                                workspace_bytes, stream);
 }
 

@@ -67,6 +67,18 @@ __device__ __forceinline__ float shfl_xor(float x, int mask) {
   return __builtin_bit_cast(float, v);
 }
 
+// Sum of x over lanes 0 .. lane (an inclusive scan across the wave), in six
+// doubling steps through the LDS crossbar.
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __builtin_amdgcn_ds_bpermute((lane >= d ? lane - d : lane) << 2, x);
+    x += lane >= d ? y : 0;
+  }
+  return x;
+}
+
 // Reductions over the four 16-lane groups (lanes n, n+16, n+32, n+48) with
 // the gfx950 lane-swap instructions, entirely in the VALU (no LDS round
 // trip).  Given two registers that both hold x, v_permlane16_swap leaves the

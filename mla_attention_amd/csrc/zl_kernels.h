@@ -37,6 +37,13 @@ struct DecodeArgs {
   // packed caches, token t (cu numbering) is row t.
   const int32_t* block_table;
   int max_pages, page_shift;
+  // Several new query tokens per sequence (cu_q != nullptr): q, out are
+  // [cu_q[B], Hq, D] and lse [cu_q[B], Hq]; cu holds the cache bounds; the
+  // work units are the key/value heads (HB = 1) and the batch is cut into
+  // virtual sequences of 16 query rows (zl_split.h).  causal: new token i of
+  // nq sees cache rows 0 .. lk - nq + i.
+  const int32_t* cu_q;
+  int causal;
   int B, Hq, Hkv, G, HB, P;
   int seg_cost;         // phantom positions per sequence (zl_split.h)
   float scale_log2;     // softmax_scale * log2(e)
@@ -62,7 +69,9 @@ int mla_default_workers();
 hipError_t launch_mla(const DecodeArgs& a, int dtype, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs& a, Layout layout, int dtype, hipStream_t stream);
-hipError_t launch_merge(const DecodeArgs& a, int dv, int dtype, hipStream_t stream);
+// max_vseqs: with several new tokens per sequence, an upper bound on the
+// virtual sequences (ignored otherwise).
+hipError_t launch_merge(const DecodeArgs& a, int dv, int dtype, int max_vseqs, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t stream);
 
 }  // namespace zl

@@ -145,8 +145,8 @@ __device__ __forceinline__ int grid_cut(long long x, int cs, int ce) {
 // of the first sequence, at a position >= p, where that range is not empty
 // (phantom stretches, empty sequences and sequences whose share of the run
 // rounds away are stepped over).
-__device__ __forceinline__ Segment segment_at(long long p, long long p_end, const Line& L, const int32_t* cu,
-                                              int window) {
+template <class Seqs>
+__device__ __forceinline__ Segment segment_at(long long p, long long p_end, const Line& L, const Seqs& seqs) {
   Segment s;
   s.p = p;
   s.u = 0;
@@ -158,7 +158,7 @@ __device__ __forceinline__ Segment segment_at(long long p, long long p_end, cons
   while (p < p_end) {
     int u, r;
     split_position(p, L.Tp, u, r);
-    const SeqSpan q = find_seq(cu, L.B, L.C, r, window);
+    const SeqSpan q = seqs.span(r);
     // Position of token t of this sequence: base + t.
     const long long base = (long long)u * L.Tp + (long long)(q.b + 1) * L.C;
     const int t0 = grid_cut(p - base, q.cs, q.ce);
@@ -178,6 +178,164 @@ __device__ __forceinline__ Segment segment_at(long long p, long long p_end, cons
     p = base + q.ce;
   }
   return s;
+}
+
+// The sequences of a decode batch (one query token each): sequence b is
+// tokens [cu[b], cu[b+1]).
+struct PlainSeqs {
+  const int32_t* cu;
+  int B, C;
+  int window;  // bounds_window(cu, B, C)
+  __device__ __forceinline__ SeqSpan span(int r) const { return find_seq(cu, B, C, r, window); }
+};
+
+__device__ __forceinline__ Segment segment_at(long long p, long long p_end, const Line& L, const int32_t* cu,
+                                              int window) {
+  return segment_at(p, p_end, L, PlainSeqs{cu, L.B, L.C, window});
+}
+
+// Several new query tokens per sequence.  Sequence b has nq = cu_q[b+1] -
+// cu_q[b] new tokens and lk = cu_k[b+1] - cu_k[b] cached key/value rows.  For
+// one key/value head, its query rows (new token i, head hh of the head's
+// group of G) are numbered r = i*G + hh and cut into nblk = ceil(nq*G / 16)
+// blocks of 16 -- one MFMA N dimension each.  Virtual sequence (b, hb) pairs
+// row block hb with all lk rows of b.  The virtual sequences of all b, in
+// order, are the ragged batch that the work split cuts: virtual sequence v =
+// VB(b) + hb owns virtual tokens [KB(b) + hb*lk, + lk), where VB and KB count
+// the virtual sequences and virtual tokens of the sequences before b.  With
+// one new token per sequence and G <= 16 this is the decode batch itself.
+struct VSeqInfo {
+  int v;       // virtual sequence
+  int cs, ce;  // its virtual tokens
+  int b, hb;   // sequence and row block
+  int q0, nq;  // cu_q[b] and the sequence's new tokens
+  int k0, lk;  // cu_k[b] (the key row of virtual token cs) and the cached rows
+};
+
+// Lane l describes sequence c0 + l (an empty one past the batch) given the
+// virtual sequences (vcarry) and tokens (kcarry) of the sequences before c0.
+struct VChunk {
+  int q0, nq, k0, lk, nblk;
+  int vb, vbi;     // virtual sequences before / up to and including this one
+  int kb;          // virtual tokens before this one
+  int start, end;  // in-unit positions of its virtual sequences: [start, end)
+};
+
+__device__ __forceinline__ VChunk vchunk(const int32_t* cu_q, const int32_t* cu_k, int B, int G, int C, int c0,
+                                         int vcarry, int kcarry) {
+  const int b = c0 + __lane_id();
+  const int i0 = b < B ? b : B, i1 = b < B ? b + 1 : B;
+  // Unpredicated loads (clamped indices): a branch here would make the
+  // compiler's wait drain the tile loads in flight.
+  const int q0 = cu_q[i0], q1 = cu_q[i1], k0 = cu_k[i0], k1 = cu_k[i1];
+  VChunk c;
+  c.q0 = q0;
+  c.nq = q1 - q0;
+  c.k0 = k0;
+  c.lk = k1 - k0;
+  c.nblk = (c.nq * G + 15) >> 4;
+  const int tok = c.nblk * c.lk;
+  c.vbi = vcarry + wave_inclusive_sum(c.nblk);
+  c.vb = c.vbi - c.nblk;
+  c.kb = kcarry + wave_inclusive_sum(tok) - tok;
+  c.start = c.kb + c.vb * C;
+  c.end = c.kb + tok + c.vbi * C;
+  return c;
+}
+
+struct VirtualSeqs {
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int B, G, C;
+  VChunk first;  // sequences 0 .. 63 (the whole batch when B <= 64)
+  int V, T;      // virtual sequences and tokens of the batch
+
+  __device__ __forceinline__ void init(const int32_t* cq, const int32_t* ck, int b, int g, int c) {
+    cu_q = cq;
+    cu_k = ck;
+    B = b;
+    G = g;
+    C = c;
+    first = vchunk(cu_q, cu_k, B, G, C, 0, 0, 0);
+    V = __builtin_amdgcn_readlane(first.vbi, 63);
+    T = __builtin_amdgcn_readlane(first.kb + first.nblk * first.lk, 63);
+    for (int c0 = 64; c0 < B; c0 += 64) {
+      const VChunk ch = vchunk(cu_q, cu_k, B, G, C, c0, V, T);
+      V = __builtin_amdgcn_readlane(ch.vbi, 63);
+      T = __builtin_amdgcn_readlane(ch.kb + ch.nblk * ch.lk, 63);
+    }
+  }
+
+  // The chunk holding the sequence that `pred` selects: pred(chunk) is the
+  // ballot of lanes lying wholly before the target; the target is in the
+  // first chunk where not every lane does.
+  template <class Before>
+  __device__ __forceinline__ VSeqInfo locate(Before before, int v_or_r, bool by_position) const {
+    VChunk ch = first;
+    int c0 = 0;
+    unsigned long long m = __ballot(before(ch));
+    while (m == ~0ull && c0 + 64 < B) {
+      c0 += 64;
+      ch = vchunk(cu_q, cu_k, B, G, C, c0, __builtin_amdgcn_readlane(ch.vbi, 63),
+                  __builtin_amdgcn_readlane(ch.kb + ch.nblk * ch.lk, 63));
+      m = __ballot(before(ch));
+    }
+    const int l = __popcll(m);
+    VSeqInfo s;
+    s.b = c0 + l;
+    s.q0 = __builtin_amdgcn_readlane(ch.q0, l);
+    s.nq = __builtin_amdgcn_readlane(ch.nq, l);
+    s.k0 = __builtin_amdgcn_readlane(ch.k0, l);
+    s.lk = __builtin_amdgcn_readlane(ch.lk, l);
+    const int vb = __builtin_amdgcn_readlane(ch.vb, l);
+    const int kb = __builtin_amdgcn_readlane(ch.kb, l);
+    if (by_position) {
+      const int o = v_or_r - __builtin_amdgcn_readlane(ch.start, l);
+      s.hb = o / (s.lk + C);
+    } else {
+      s.hb = v_or_r - vb;
+    }
+    s.v = vb + s.hb;
+    s.cs = kb + s.hb * s.lk;
+    s.ce = s.cs + s.lk;
+    return s;
+  }
+
+  // The virtual sequence whose stretch holds in-unit position r (0 <= r < Tp).
+  __device__ __forceinline__ VSeqInfo at_position(int r) const {
+    return locate([r](const VChunk& c) { return c.end <= r; }, r, true);
+  }
+
+  // Virtual sequence v (0 <= v < V).
+  __device__ __forceinline__ VSeqInfo info(int v) const {
+    return locate([v](const VChunk& c) { return c.vbi <= v; }, v, false);
+  }
+
+  __device__ __forceinline__ SeqSpan span(int r) const {
+    const VSeqInfo s = at_position(r);
+    return SeqSpan{s.v, s.cs, s.ce};
+  }
+};
+
+// Column n of a virtual sequence's row block, for key/value head kvh: the
+// query row it holds (row index into [tokens, Hq] arrays), whether that row
+// exists, and the last cache row (counted from the sequence's first) it sees.
+struct MqColumn {
+  long long row;
+  bool valid;
+  int lim;
+};
+
+__device__ __forceinline__ MqColumn mq_column(const VSeqInfo& s, int n, int kvh, int G, int Hq, bool causal) {
+  const int last = s.nq * G - 1;  // the sequence's last query row
+  const int r = 16 * s.hb + n;
+  const int rr = r < last ? r : last;
+  const int qi = rr / G;
+  MqColumn c;
+  c.row = (long long)(s.q0 + qi) * Hq + kvh * G + (rr - qi * G);
+  c.valid = r <= last;
+  c.lim = causal ? s.lk - s.nq + qi : s.lk - 1;
+  return c;
 }
 
 // The runs (workers) holding tokens of sequence [cs, ce) of unit u, for a

@@ -151,3 +151,34 @@ def test_paged_entry_points_reject_bad_arguments(zl):
     assert mla_paged(ps=48) == 2 and mla_paged(table=None) == 1 and mla_paged(maxL=257) == 1
     assert mla_paged(r=256) == 2 and mla_paged(wsb=8) == 3
     assert mla_paged(B=0, q=None, c=None, cu=None, out=None, ws=None) == 0
+
+
+def test_varlen_entry_points_reject_bad_arguments(zl):
+    lib = zl.library()
+
+    def gqa(**kw):
+        a = dict(q=A, k=A, v=A, cq=A, ck=A, B=4, Tq=16, Hq=8, Hkv=2, D=128, maxL=128, scale=0.125, causal=1,
+                 dt=0, out=A, lse=None, workers=0, phases=3, ws=A, wsb=BIG, stream=None)
+        a.update(kw)
+        return lib.zl_attn_varlen_gqa_ex(a["q"], a["k"], a["v"], a["cq"], a["ck"], a["B"], a["Tq"], a["Hq"],
+                                         a["Hkv"], a["D"], a["maxL"], a["scale"], a["causal"], a["dt"], a["out"],
+                                         a["lse"], a["workers"], a["phases"], a["ws"], a["wsb"], a["stream"])
+
+    def mla(**kw):
+        a = dict(q=A, c=A, cq=A, ck=A, B=2, Tq=4, H=16, r=512, rope=64, maxL=200, scale=0.07, causal=1, dt=1,
+                 out=A, lse=None, workers=0, phases=3, ws=A, wsb=BIG, stream=None)
+        a.update(kw)
+        return lib.zl_attn_varlen_mla_ex(a["q"], a["c"], a["cq"], a["ck"], a["B"], a["Tq"], a["H"], a["r"],
+                                         a["rope"], a["maxL"], a["scale"], a["causal"], a["dt"], a["out"],
+                                         a["lse"], a["workers"], a["phases"], a["ws"], a["wsb"], a["stream"])
+    assert gqa(cq=None) == 1 and gqa(cq=A + 2) == 1
+    assert gqa(Tq=-1) == 1 and gqa(causal=2) == 1
+    assert gqa(D=96) == 2 and gqa(q=None) == 1 and gqa(wsb=16) == 3 and gqa(Hq=7) == 1
+    # nothing to compute: no rows of q, or no sequences
+    assert gqa(Tq=0, q=None, k=None, v=None, ck=None, out=None, ws=None) == 0
+    assert gqa(B=0, Tq=0, q=None, k=None, v=None, ck=None, out=None, ws=None) == 0
+    # work-line positions beyond 32 bits
+    assert gqa(Tq=1 << 20, maxL=1 << 20) == 2
+    assert mla(cq=None) == 1 and mla(r=256) == 2 and mla(wsb=8) == 3 and mla(causal=-1) == 1
+    assert mla(Tq=1 << 16, maxL=1 << 16) == 2
+    assert mla(Tq=0, q=None, c=None, ck=None, out=None, ws=None) == 0

@@ -1,0 +1,174 @@
+"""GPU parity for several new query tokens per sequence (chunked prefill,
+draft tokens): the HIP kernels through the C ABI against the fp64 oracle on
+identical seeded inputs.
+
+Every case compares all rows except the full-size ones, which compare
+sampled (token, head) rows that the oracle computes one by one.  One new
+token per sequence must give the decode path's bits exactly.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.parity import gate
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_attention_amd as zl
+    zl.library()
+    yield
+
+
+def zl():
+    import mla_attention_amd
+    return mla_attention_amd
+
+
+def odt(dtype):
+    return oracle.F16 if dtype == torch.float16 else oracle.BF16
+
+
+def spec_gqa(lens, Hq, Hkv, D, dt, seed=7):
+    return workloads.Spec("varlen", "gqa", len(lens), Hq, Hkv, D, D, tuple(lens),
+                          "f16" if dt == torch.float16 else "bf16", float(np.float32(1 / math.sqrt(D))), seed)
+
+
+def spec_mla(lens, H, dt, seed=9):
+    return workloads.Spec("varlen-mla", "mla", len(lens), H, 1, 576, 512, tuple(lens),
+                          "f16" if dt == torch.float16 else "bf16", float(np.float32(1 / math.sqrt(192))), seed)
+
+
+def run_gpu(x, vq, causal=True, num_workers=0):
+    s = x.spec
+    q = vq.q.to(DEV)
+    cq, ck = vq.cu_q.to(DEV), x.cu_seqlens.to(DEV)
+    if s.kind == "mla":
+        out, lse = zl().zl_attn_varlen_mla(q, x.latent.to(DEV), cq, ck, x.max_seqlen, s.scale, causal=causal,
+                                           num_workers=num_workers, return_lse=True)
+    else:
+        out, lse = zl().zl_attn_varlen_gqa(q, x.k.to(DEV), x.v.to(DEV), cq, ck, x.max_seqlen, s.scale,
+                                           causal=causal, num_workers=num_workers, return_lse=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def run_oracle(x, vq, causal=True, rows=None):
+    s = x.spec
+    qb = vq.q.contiguous().view(torch.int16).numpy().view(np.uint16)
+    cq, ck = vq.cu_q.numpy(), x.cu_seqlens.numpy()
+    if s.kind == "mla":
+        return oracle.mla_varlen(qb, x.bits("latent"), cq, ck, s.scale, odt(s.torch_dtype), causal=causal,
+                                 rows=rows)
+    return oracle.gqa_varlen(qb, x.bits("k"), x.bits("v"), cq, ck, s.num_kv_heads, s.scale, odt(s.torch_dtype),
+                             causal=causal, rows=rows)
+
+
+def check(x, vq, where, causal=True, **kw):
+    print(where, flush=True)
+    out, lse = run_gpu(x, vq, causal, **kw)
+    ro, rl = run_oracle(x, vq, causal)
+    return gate(out, ro, x.spec.torch_dtype, lse, rl, where=where)
+
+
+GQA_CASES = [
+    # (cache lens, new tokens per sequence, Hq, Hkv, D, dtype)
+    ([17, 64, 100, 128], [1, 2, 3, 4], 8, 2, 64, torch.float16),
+    ([100, 1, 300, 64, 33], [100, 1, 37, 0, 33], 8, 2, 128, torch.bfloat16),   # prefill, decode, chunk, none
+    ([200, 150], [4, 4], 32, 8, 128, torch.float16),                          # G*q = 16: one row block
+    ([129, 70], [2, 3], 32, 1, 64, torch.float16),                            # G = 32: blocks of 16 rows
+    ([96, 95, 97], [5, 1, 6], 6, 2, 128, torch.bfloat16),                    # G = 3: blocks across tokens
+    ([3, 40], [5, 2], 4, 4, 64, torch.float16),                               # more new tokens than rows
+    ([0, 50, 0], [2, 3, 0], 8, 2, 128, torch.float16),                        # empty caches
+    ([(i * 37) % 90 for i in range(80)], [(i * 7) % 4 for i in range(80)], 8, 2, 128, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("lens,q_lens,Hq,Hkv,D,dt", GQA_CASES)
+def test_gqa_varlen(lens, q_lens, Hq, Hkv, D, dt):
+    x = workloads.make_inputs(spec_gqa(lens, Hq, Hkv, D, dt))
+    vq = workloads.make_varlen_query(x, q_lens, seed=len(lens))
+    check(x, vq, f"gqa varlen {lens[:6]} q {q_lens[:6]} {Hq}/{Hkv} D{D} {dt}")
+
+
+def test_gqa_varlen_without_mask():
+    x = workloads.make_inputs(spec_gqa([40, 300, 7], 8, 2, 128, torch.float16))
+    vq = workloads.make_varlen_query(x, [3, 20, 9], seed=3)
+    check(x, vq, "gqa varlen, no mask", causal=False)
+
+
+MLA_CASES = [
+    ([40, 300, 1], [2, 1, 1], 16, torch.bfloat16),
+    ([257, 33], [2, 2], 8, torch.float16),       # H*q = 16: one row block
+    ([70, 150], [3, 1], 32, torch.bfloat16),
+    ([5, 64], [9, 64], 16, torch.bfloat16),      # more new tokens than rows; a whole prompt
+    ([(i * 53) % 90 for i in range(70)], [(i * 5) % 3 for i in range(70)], 16, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("lens,q_lens,H,dt", MLA_CASES)
+def test_mla_varlen(lens, q_lens, H, dt):
+    x = workloads.make_inputs(spec_mla(lens, H, dt))
+    vq = workloads.make_varlen_query(x, q_lens, seed=len(lens))
+    check(x, vq, f"mla varlen {lens[:6]} q {q_lens[:6]} H{H} {dt}")
+
+
+@pytest.mark.parametrize("workers", [8, 64, 256, 2048])
+def test_any_worker_count_gives_the_same_attention(workers):
+    x = workloads.make_inputs(workloads.with_shape(workloads.CONFIGS[2], batch=5, lens=("uniform", 1, 2000)),
+                              seed=23)
+    vq = workloads.make_varlen_query(x, [1, 4, 16, 2, 7], seed=5)
+    check(x, vq, f"gqa varlen workers={workers}", num_workers=workers)
+    xm = workloads.make_inputs(workloads.with_shape(workloads.CONFIGS[5], batch=3, lens=("uniform", 1, 1500)),
+                               seed=24)
+    vqm = workloads.make_varlen_query(xm, [2, 1, 3], seed=6)
+    check(xm, vqm, f"mla varlen workers={workers}", num_workers=workers)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 5])
+def test_one_new_token_gives_the_decode_bits(cfg):
+    """With one new token per sequence the virtual sequences are the decode
+    batch itself, so the arithmetic, and the bits, are those of decode."""
+    x = workloads.make_inputs(workloads.CONFIGS[cfg])
+    vq = workloads.VarlenQuery(np.ones(x.spec.batch, dtype=np.int64),
+                               workloads.cu_from_lens([1] * x.spec.batch), x.q.clone())
+    out, lse = run_gpu(x, vq)
+    cu = x.cu_seqlens.to(DEV)
+    if x.spec.kind == "mla":
+        ro, rl = zl().zl_decode_attn_mla(x.q.to(DEV), x.latent.to(DEV), cu, x.max_seqlen, x.spec.scale,
+                                         return_lse=True)
+    else:
+        ro, rl = zl().zl_decode_attn_gqa(x.q.to(DEV), x.k.to(DEV), x.v.to(DEV), cu, x.max_seqlen, x.spec.scale,
+                                         return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ro) and torch.equal(lse, rl)
+
+
+@pytest.mark.parametrize("cfg,q_len", [(2, 4), (5, 2)])
+def test_full_size_draft_tokens_sampled(cfg, q_len):
+    """Full-size batches with q_len new tokens per sequence (draft-token
+    verification), compared on sampled rows: every sequence, its first and
+    last new token, and heads spanning every key/value head."""
+    spec = workloads.CONFIGS[cfg]
+    print(f"config {cfg}, {q_len} new tokens per sequence", flush=True)
+    x = workloads.make_inputs(spec)
+    vq = workloads.make_varlen_query(x, [q_len] * spec.batch, seed=cfg)
+    out, lse = run_gpu(x, vq)
+    heads = sorted({0, spec.num_q_heads - 1} | {kv * spec.group for kv in range(spec.num_kv_heads)})
+    rows = [(int(vq.cu_q[b]) + i, h) for b in range(spec.batch) for i in {0, q_len - 1} for h in heads]
+    ro, rl = run_oracle(x, vq, rows=rows)
+    t = np.array([r[0] for r in rows])
+    h = np.array([r[1] for r in rows])
+    tt, th = torch.from_numpy(t).to(DEV), torch.from_numpy(h).to(DEV)
+    gate(out[tt, th], ro[t, h], spec.torch_dtype, lse[tt, th], rl[t, h], where=f"config {cfg} q_len {q_len}")
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()

@@ -217,3 +217,33 @@ def make_paged(x: Inputs, page_size: int, seed: int = 0, spare_pages: int = 3) -
     if x.latent is not None:
         return PagedInputs(page_size, bt, kv_pages=scatter(x.latent))
     return PagedInputs(page_size, bt, k_pages=scatter(x.k), v_pages=scatter(x.v))
+
+
+@dataclasses.dataclass
+class VarlenQuery:
+    """Several new query tokens per sequence over the caches of an Inputs
+    batch: sequence b's q_lens[b] new tokens are rows cu_q[b] .. cu_q[b+1]-1
+    of q, and their keys/values are the last q_lens[b] rows of its cache."""
+    q_lens: np.ndarray
+    cu_q: torch.Tensor      # int32 [B + 1]
+    q: torch.Tensor         # [total_q, Hq, Dk]
+
+    @property
+    def total_q(self) -> int:
+        return int(self.cu_q[-1])
+
+
+def make_varlen_query(x: Inputs, q_lens, seed: int = 0, q_mult: float = 1.0) -> VarlenQuery:
+    """Seeded N(0,1) query rows (rounded once to the batch's dtype) for
+    q_lens[b] new tokens of each sequence.  q_lens may exceed a cache length
+    (the first tokens then see no key under the causal mask)."""
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    if len(q_lens) != x.spec.batch:
+        raise ValueError("q_lens must have batch entries")
+    gen = torch.Generator("cpu")
+    gen.manual_seed(2000 + seed)
+    cu_q = cu_from_lens(q_lens)
+    q = torch.randn(int(cu_q[-1]), x.spec.num_q_heads, x.spec.head_dim_k, generator=gen)
+    if q_mult != 1.0:
+        q = q * q_mult
+    return VarlenQuery(q_lens, cu_q, q.to(x.spec.torch_dtype))
