@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
                     help="workload (default 2: batch 32, 32/8 heads, D 128, ragged 512..4096)")
     ap.add_argument("--workers", type=int, default=0, help="decode workers (0 = library default)")
+    ap.add_argument("--q-len", type=int, default=1, metavar="N",
+                    help="new query tokens per sequence (N > 1: draft tokens checked in one step, "
+                         "causal among themselves, through the several-new-tokens entry points)")
     ap.add_argument("--paged", type=int, default=0, metavar="PAGE_SIZE",
                     help="read the caches from a shuffled page pool through a block table "
                          "(pages of PAGE_SIZE tokens; 0 = packed rows)")
@@ -122,8 +125,12 @@ def main():
     reps = max(2, math.ceil((1 << 30) / kv_bytes))
     if args.profile_run:
         reps = 1
+    if args.q_len > 1 and args.paged:
+        sys.exit("--q-len and --paged: the several-new-tokens path reads packed caches")
+    vq = workloads.make_varlen_query(x, [args.q_len] * spec.batch, seed=args.config) if args.q_len > 1 else None
     cu = x.cu_seqlens.to(dev)
-    q = x.q.to(dev)
+    q = vq.q.to(dev) if vq else x.q.to(dev)
+    cu_q = vq.cu_q.to(dev) if vq else None
     paged = workloads.make_paged(x, args.paged) if args.paged else None
     table = paged.block_table.to(dev) if paged else None
     if paged:
@@ -140,13 +147,20 @@ def main():
                                                     spec.head_dim_k, x.max_seqlen, spec.torch_dtype,
                                                     args.workers)
     ws = zl.new_workspace(ws_bytes, dev)
-    out = torch.empty(spec.batch, spec.num_q_heads, spec.head_dim_v, dtype=spec.torch_dtype, device=dev)
-    lse = torch.empty(spec.batch, spec.num_q_heads, dtype=torch.float32, device=dev)
+    rows = q.shape[0]
+    out = torch.empty(rows, spec.num_q_heads, spec.head_dim_v, dtype=spec.torch_dtype, device=dev)
+    lse = torch.empty(rows, spec.num_q_heads, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(i, phases=3):
         c = caches[i % reps]
-        if paged and spec.kind == "mla":
+        if vq is not None and spec.kind == "mla":
+            zl.zl_attn_varlen_mla(q, c[0], cu_q, cu, x.max_seqlen, spec.scale, out=out, lse=lse, workspace=ws,
+                                  num_workers=args.workers, stream=stream, phases=phases)
+        elif vq is not None:
+            zl.zl_attn_varlen_gqa(q, c[0], c[1], cu_q, cu, x.max_seqlen, spec.scale, out=out, lse=lse,
+                                  workspace=ws, num_workers=args.workers, stream=stream, phases=phases)
+        elif paged and spec.kind == "mla":
             zl.zl_decode_attn_mla_paged(q, c[0], table, cu, x.max_seqlen, spec.scale, out=out, lse=lse,
                                         workspace=ws, num_workers=args.workers, stream=stream, phases=phases)
         elif paged:
@@ -200,15 +214,15 @@ def main():
     kern_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]))
     merge_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]))
     achieved_gbs = kv_bytes / (kern_ms * 1e-3) / 1e9
-    workload = spec.name + (f"+paged{args.paged}" if paged else "")
+    workload = spec.name + (f"+paged{args.paged}" if paged else "") + (f"+q{args.q_len}" if vq else "")
     prof = profile_record(workload)
 
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and vq is None:  # (the oracle baseline covers one new token per sequence)
         cpu = cpu_baseline(x, spec, args.cpu_seconds)
 
     # Useful matrix flops of one step: QK^T and PV, 2 flops per multiply-add.
-    flops = 2.0 * x.total_tokens * spec.num_q_heads * (spec.head_dim_k + spec.head_dim_v)
+    flops = 2.0 * x.total_tokens * spec.num_q_heads * (spec.head_dim_k + spec.head_dim_v) * args.q_len
     rec = {
         "metric": "decode-attn KV GB/s (algorithmic K+V bytes / step time) and us/step, % of MI355X HBM peak",
         "value": round(value_gbs, 1),
@@ -238,6 +252,7 @@ def main():
             "cold_cache_replicas": reps,
             "workers": args.workers or "default",
             "kv_layout": f"paged, {args.paged}-token pages in a shuffled pool" if paged else "packed rows",
+            "new_tokens_per_seq": args.q_len,
         },
         "roofline": {
             "bound": "hbm",
