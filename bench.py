@@ -74,6 +74,10 @@ def parse():
     ap.add_argument("--q-len", type=int, default=1, metavar="N",
                     help="new query tokens per sequence (N > 1: draft tokens checked in one step, "
                          "causal among themselves, through the several-new-tokens entry points)")
+    ap.add_argument("--codec", choices=["quantize", "dequantize", "reduce"], default=None,
+                    help="instead: time the INT8 all-reduce payload codec kernel on --codec-mib of fp16 payload")
+    ap.add_argument("--codec-mib", type=int, default=64)
+    ap.add_argument("--codec-chunk", type=int, default=512)
     ap.add_argument("--paged", type=int, default=0, metavar="PAGE_SIZE",
                     help="read the caches from a shuffled page pool through a block table "
                          "(pages of PAGE_SIZE tokens; 0 = packed rows)")
@@ -110,6 +114,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, max(3, args.steps))
+        return
+    if args.codec:
+        bench_codec(args)
         return
 
     import numpy as np
@@ -271,6 +278,83 @@ def main():
         "wall_ms_timed_region": round(wall_ms, 2),
     }
     print(json.dumps(rec), flush=True)
+
+
+def bench_codec(args):
+    """One codec kernel on a cold payload: the same K steps protocol; bytes are
+    the arrays the kernel must read and write once (16-bit values, codes, one
+    fp32 scale per chunk)."""
+    import numpy as np
+    import torch
+
+    import mla_attention_amd as zl
+
+    dev = torch.device("cuda:0")
+    n = (args.codec_mib << 20) // 2
+    C = args.codec_chunk
+    nch = (n + C - 1) // C
+    per_call = {"quantize": 3 * n + 4 * nch, "dequantize": 3 * n + 4 * nch, "reduce": 6 * n + 8 * nch}[args.codec]
+    reps = max(2, math.ceil((1 << 30) / per_call))
+    if args.profile_run:
+        reps = 1
+    g = torch.Generator(device="cpu").manual_seed(0)
+    base = torch.randn(n, generator=g).to(torch.float16)
+    xs = [base.to(dev) for _ in range(reps)]
+    codes0, scales0 = zl.zl_int8_quantize(xs[0], chunk=C)
+    codes = [codes0.clone() for _ in range(reps)]
+    scales = [scales0.clone() for _ in range(reps)]
+    outs = [torch.empty(n, dtype=torch.float16, device=dev) for _ in range(reps)]
+    co = [torch.empty(n, dtype=torch.int8, device=dev) for _ in range(reps)]
+    so = [torch.empty(nch, dtype=torch.float32, device=dev) for _ in range(reps)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        j = i % reps
+        if args.codec == "quantize":
+            zl.zl_int8_quantize(xs[j], chunk=C, codes=co[j], scales=so[j], stream=stream)
+        elif args.codec == "dequantize":
+            zl.zl_int8_dequantize(codes[j], scales[j], dtype=torch.float16, chunk=C, out=outs[j], stream=stream)
+        else:
+            zl.zl_int8_reduce_step(codes[j], scales[j], xs[j], chunk=C, codes_out=co[j], scales_out=so[j],
+                                   sum_out=outs[j], stream=stream)
+
+    if args.profile_run:
+        for i in range(max(3, args.steps)):
+            step(i)
+        torch.cuda.synchronize()
+        print(f"profile run: codec {args.codec}, {max(3, args.steps)} launches", flush=True)
+        return
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(K):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    for i in range(K):
+        ev[i][0].record(stream)
+        step(args.warmup + K + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    gbs = per_call / (ms * 1e-3) / 1e9
+    kgbs = per_call / (kern_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": f"INT8 all-reduce payload codec ({args.codec}) GB/s of algorithmic bytes",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16->i8", "data": "synthetic (seeded N(0,1) fp16 payload)",
+        "config": {"workload": f"codec-{args.codec}-{args.codec_mib}MiB-fp16-chunk{C}", "elements": n,
+                   "bytes_per_call": per_call, "cold_cache_replicas": reps},
+        "roofline": {"bound": "hbm", "kernel": "codec_kernel", "achieved": round(kgbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(kern_ms * 1e3, 2)},
+        "cpu_baseline": None}), flush=True)
 
 
 def cpu_baseline(x, spec, target_s: float):

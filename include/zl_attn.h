@@ -298,6 +298,37 @@ ZL_API zl_status_t zl_attn_varlen_mla_ex(const void *q, const void *kv_cache, co
                                          int phases, void *workspace, size_t workspace_bytes,
                                          zl_stream_t stream);
 
+/*
+ * INT8 coding of an all-reduce payload: the single-GPU half of the INT8
+ * all-reduce (the first ZhiLight page, section 1: the all-reduce of tensor
+ * parallelism can move INT8 data to cut the bytes between GPUs; the second
+ * page, section "Dual streams, host all-reduce and the memory model": an
+ * Int8-quantized all-reduce cuts the bytes per collective).  The pages give
+ * no scheme; this library codes chunks of `chunk` consecutive elements
+ * (256, 512 or 1024, else ZL_ERR_UNSUPPORTED), each with one fp32 scale, 127
+ * levels per sign:
+ *   amax = max |x| over the chunk,  code = rint(x * (127 / amax)) (ties to
+ *   even; 0 when amax = 0),  scale = amax / 127,  value = code * scale
+ * in fp32 with every product, sum and quotient rounded on its own (a short
+ * last chunk is coded on its own).  All pointers are device pointers; the
+ * 16-bit arrays and the codes must be 16-byte aligned, the scales 4-byte
+ * aligned; n == 0 is a no-op.  The collective itself (moving the codes
+ * between GPUs) is not part of this library.
+ *   zl_int8_quantize:   x [n] dtype -> codes [n] int8, scales [ceil(n/chunk)] fp32
+ *   zl_int8_dequantize: codes, scales -> out [n] dtype (value rounded to dtype)
+ *   zl_int8_reduce_step: one hop of a ring all-reduce: y = code_in *
+ *     scale_in + local (fp32); codes_out/scales_out = y coded again (both or
+ *     neither given), sum_out = y rounded to dtype (optional; at least one of
+ *     codes_out and sum_out).
+ */
+ZL_API zl_status_t zl_int8_quantize(const void *x, zl_dtype_t dtype, long long n, int chunk, int8_t *codes,
+                                    float *scales, zl_stream_t stream);
+ZL_API zl_status_t zl_int8_dequantize(const int8_t *codes, const float *scales, long long n, int chunk,
+                                      zl_dtype_t dtype, void *out, zl_stream_t stream);
+ZL_API zl_status_t zl_int8_reduce_step(const int8_t *codes_in, const float *scales_in, const void *local,
+                                       zl_dtype_t dtype, long long n, int chunk, int8_t *codes_out,
+                                       float *scales_out, void *sum_out, zl_stream_t stream);
+
 /* Static, human-readable name of a status code (host). */
 ZL_API const char *zl_status_string(zl_status_t status);
 

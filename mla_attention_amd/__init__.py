@@ -71,6 +71,9 @@ SIGNATURES = {
     "zl_attn_varlen_mla_ex": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _c_float, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _vp, _c_size, _vp]),
     "zl_attn_combine": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
+    "zl_int8_quantize": (_c_int, [_vp, _c_int, ctypes.c_longlong, _c_int, _vp, _vp, _vp]),
+    "zl_int8_dequantize": (_c_int, [_vp, _vp, ctypes.c_longlong, _c_int, _c_int, _vp, _vp]),
+    "zl_int8_reduce_step": (_c_int, [_vp, _vp, _vp, _c_int, ctypes.c_longlong, _c_int, _vp, _vp, _vp, _vp]),
     "zl_status_string": (ctypes.c_char_p, [_c_int]),
 }
 
@@ -414,3 +417,79 @@ def zl_attn_combine(partial_out, partial_lse, out_dtype: torch.dtype = torch.bfl
                                    _DTYPE[out_dtype], _ptr(out), _ptr(lse), _stream(stream, dev))
     _check(st, "zl_attn_combine")
     return (out, lse) if lse is not None else out
+
+
+# --------------------------------------------------------- INT8 payload codec
+def _codec_nchunks(n: int, chunk: int) -> int:
+    return (n + chunk - 1) // chunk
+
+
+def zl_int8_quantize(x, chunk: int = 512, codes=None, scales=None, stream=None):
+    """Per-chunk INT8 codes of a 16-bit payload x (any shape, contiguous):
+    returns (codes int8 [x.numel()], scales fp32 [ceil(numel / chunk)])."""
+    _need(x, "x")
+    if x.dtype not in _DTYPE:
+        raise ValueError("x must be float16 or bfloat16")
+    dev, n = x.device, x.numel()
+    if codes is None:
+        codes = torch.empty(n, dtype=torch.int8, device=dev)
+    if scales is None:
+        scales = torch.empty(_codec_nchunks(n, chunk), dtype=torch.float32, device=dev)
+    _need(codes, "codes", torch.int8, 1, dev)
+    _need(scales, "scales", torch.float32, 1, dev)
+    if codes.numel() != n or scales.numel() < _codec_nchunks(n, chunk):
+        raise ValueError("codes must have x.numel() entries and scales one per chunk")
+    st = library().zl_int8_quantize(_ptr(x), _DTYPE[x.dtype], n, int(chunk), _ptr(codes), _ptr(scales),
+                                    _stream(stream, dev))
+    _check(st, "zl_int8_quantize")
+    return codes, scales
+
+
+def zl_int8_dequantize(codes, scales, dtype: torch.dtype = torch.float16, chunk: int = 512, out=None, stream=None):
+    """Values code * scale rounded to dtype: returns out [codes.numel()]."""
+    _need(codes, "codes", torch.int8, 1)
+    dev, n = codes.device, codes.numel()
+    _need(scales, "scales", torch.float32, 1, dev)
+    if dtype not in _DTYPE:
+        raise ValueError("dtype must be float16 or bfloat16")
+    if out is None:
+        out = torch.empty(n, dtype=dtype, device=dev)
+    _need(out, "out", dtype, 1, dev)
+    if out.numel() != n or scales.numel() < _codec_nchunks(n, chunk):
+        raise ValueError("out must have codes.numel() entries and scales one per chunk")
+    st = library().zl_int8_dequantize(_ptr(codes), _ptr(scales), n, int(chunk), _DTYPE[dtype], _ptr(out),
+                                      _stream(stream, dev))
+    _check(st, "zl_int8_dequantize")
+    return out
+
+
+def zl_int8_reduce_step(codes_in, scales_in, local, chunk: int = 512, code_out: bool = True,
+                        write_sum: bool = True, codes_out=None, scales_out=None, sum_out=None, stream=None):
+    """One ring-all-reduce hop: y = code_in * scale_in + local (fp32); returns
+    (codes_out, scales_out, sum_out) with the parts not asked for as None."""
+    _need(local, "local")
+    if local.dtype not in _DTYPE:
+        raise ValueError("local must be float16 or bfloat16")
+    dev, n = local.device, local.numel()
+    _need(codes_in, "codes_in", torch.int8, 1, dev)
+    _need(scales_in, "scales_in", torch.float32, 1, dev)
+    if codes_in.numel() != n or scales_in.numel() < _codec_nchunks(n, chunk):
+        raise ValueError("codes_in must have local.numel() entries and scales_in one per chunk")
+    if code_out:
+        codes_out = torch.empty(n, dtype=torch.int8, device=dev) if codes_out is None else codes_out
+        scales_out = (torch.empty(_codec_nchunks(n, chunk), dtype=torch.float32, device=dev)
+                      if scales_out is None else scales_out)
+        _need(codes_out, "codes_out", torch.int8, 1, dev)
+        _need(scales_out, "scales_out", torch.float32, 1, dev)
+    else:
+        codes_out = scales_out = None
+    if write_sum:
+        sum_out = torch.empty(n, dtype=local.dtype, device=dev) if sum_out is None else sum_out
+        _need(sum_out, "sum_out", local.dtype, 1, dev)
+    else:
+        sum_out = None
+    st = library().zl_int8_reduce_step(_ptr(codes_in), _ptr(scales_in), _ptr(local), _DTYPE[local.dtype], n,
+                                       int(chunk), _ptr(codes_out), _ptr(scales_out), _ptr(sum_out),
+                                       _stream(stream, dev))
+    _check(st, "zl_int8_reduce_step")
+    return codes_out, scales_out, sum_out

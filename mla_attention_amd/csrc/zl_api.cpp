@@ -449,6 +449,79 @@ zl_status_t zl_attn_combine(const float* partial_out, const float* partial_lse, 
   return e == hipSuccess ? ZL_OK : ZL_ERR_HIP;
 }
 
+}  // extern "C"
+
+namespace {
+
+constexpr long long kMaxCodecElems = 1LL << 40;
+
+bool codec_chunk_ok(int chunk) { return chunk == 256 || chunk == 512 || chunk == 1024; }
+
+zl_status_t run_codec(const zl::CodecArgs& a, int op, int chunk, zl_dtype_t dtype, zl_stream_t stream) {
+  const hipError_t e = zl::launch_codec(a, op, chunk, dtype, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ZL_OK : ZL_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+zl_status_t zl_int8_quantize(const void* x, zl_dtype_t dtype, long long n, int chunk, int8_t* codes,
+                             float* scales, zl_stream_t stream) {
+  if (dtype != ZL_DTYPE_F16 && dtype != ZL_DTYPE_BF16) return ZL_ERR_INVALID_ARGUMENT;
+  if (n < 0 || n > kMaxCodecElems) return ZL_ERR_INVALID_ARGUMENT;
+  if (!codec_chunk_ok(chunk)) return ZL_ERR_UNSUPPORTED;
+  if (n == 0) return ZL_OK;
+  if (!x || !codes || !scales) return ZL_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return ZL_ERR_INVALID_ARGUMENT;
+  zl::CodecArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.codes_out = codes;
+  a.scales_out = scales;
+  a.n = n;
+  return run_codec(a, zl::kCodecQuantize, chunk, dtype, stream);
+}
+
+zl_status_t zl_int8_dequantize(const int8_t* codes, const float* scales, long long n, int chunk, zl_dtype_t dtype,
+                               void* out, zl_stream_t stream) {
+  if (dtype != ZL_DTYPE_F16 && dtype != ZL_DTYPE_BF16) return ZL_ERR_INVALID_ARGUMENT;
+  if (n < 0 || n > kMaxCodecElems) return ZL_ERR_INVALID_ARGUMENT;
+  if (!codec_chunk_ok(chunk)) return ZL_ERR_UNSUPPORTED;
+  if (n == 0) return ZL_OK;
+  if (!codes || !scales || !out) return ZL_ERR_INVALID_ARGUMENT;
+  if (!aligned(codes, 16) || !aligned(scales, 4) || !aligned(out, 16)) return ZL_ERR_INVALID_ARGUMENT;
+  zl::CodecArgs a{};
+  a.codes_in = codes;
+  a.scales_in = scales;
+  a.out16 = static_cast<uint16_t*>(out);
+  a.n = n;
+  return run_codec(a, zl::kCodecDequantize, chunk, dtype, stream);
+}
+
+zl_status_t zl_int8_reduce_step(const int8_t* codes_in, const float* scales_in, const void* local, zl_dtype_t dtype,
+                                long long n, int chunk, int8_t* codes_out, float* scales_out, void* sum_out,
+                                zl_stream_t stream) {
+  if (dtype != ZL_DTYPE_F16 && dtype != ZL_DTYPE_BF16) return ZL_ERR_INVALID_ARGUMENT;
+  if (n < 0 || n > kMaxCodecElems) return ZL_ERR_INVALID_ARGUMENT;
+  if (!codec_chunk_ok(chunk)) return ZL_ERR_UNSUPPORTED;
+  if ((codes_out == nullptr) != (scales_out == nullptr)) return ZL_ERR_INVALID_ARGUMENT;
+  if (!codes_out && !sum_out) return ZL_ERR_INVALID_ARGUMENT;
+  if (n == 0) return ZL_OK;
+  if (!codes_in || !scales_in || !local) return ZL_ERR_INVALID_ARGUMENT;
+  if (!aligned(codes_in, 16) || !aligned(scales_in, 4) || !aligned(local, 16) || !aligned(codes_out, 16) ||
+      !aligned(scales_out, 4) || !aligned(sum_out, 16))
+    return ZL_ERR_INVALID_ARGUMENT;
+  zl::CodecArgs a{};
+  a.x = static_cast<const uint16_t*>(local);
+  a.codes_in = codes_in;
+  a.scales_in = scales_in;
+  a.codes_out = codes_out;
+  a.scales_out = scales_out;
+  a.out16 = static_cast<uint16_t*>(sum_out);
+  a.n = n;
+  return run_codec(a, zl::kCodecReduce, chunk, dtype, stream);
+}
+
 const char* zl_status_string(zl_status_t status) {
   switch (status) {
     case ZL_OK: return "ZL_OK";

@@ -63,6 +63,21 @@ struct CombineArgs {
   int S, rows, Dv;
 };
 
+// INT8 coding of an all-reduce payload (int8_codec.hip).
+enum CodecOp { kCodecQuantize = 0, kCodecDequantize = 1, kCodecReduce = 2 };
+
+struct CodecArgs {
+  const uint16_t* x;        // quantize: the payload; reduce: the local values
+  const int8_t* codes_in;   // dequantize, reduce
+  const float* scales_in;
+  int8_t* codes_out;        // quantize; reduce (nullptr: no coding)
+  float* scales_out;
+  uint16_t* out16;          // dequantize: the values; reduce: the sum (or nullptr)
+  long long n;              // elements
+};
+
+hipError_t launch_codec(const CodecArgs& a, int op, int chunk, int dtype, hipStream_t stream);
+
 // Workers (one wavefront each, a multiple of 8) a decode call launches.
 int default_workers(Layout layout);
 int mla_default_workers();

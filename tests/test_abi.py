@@ -182,3 +182,26 @@ def test_varlen_entry_points_reject_bad_arguments(zl):
     assert mla(cq=None) == 1 and mla(r=256) == 2 and mla(wsb=8) == 3 and mla(causal=-1) == 1
     assert mla(Tq=1 << 16, maxL=1 << 16) == 2
     assert mla(Tq=0, q=None, c=None, ck=None, out=None, ws=None) == 0
+
+
+def test_codec_entry_points_reject_bad_arguments(zl):
+    lib = zl.library()
+    q = lambda **kw: lib.zl_int8_quantize(kw.get("x", A), kw.get("dt", 0), kw.get("n", 1000), kw.get("chunk", 512),
+                                          kw.get("codes", A), kw.get("scales", A), None)
+    d = lambda **kw: lib.zl_int8_dequantize(kw.get("codes", A), kw.get("scales", A), kw.get("n", 1000),
+                                            kw.get("chunk", 512), kw.get("dt", 1), kw.get("out", A), None)
+
+    def r(**kw):
+        return lib.zl_int8_reduce_step(kw.get("codes", A), kw.get("scales", A), kw.get("local", A), kw.get("dt", 0),
+                                       kw.get("n", 1000), kw.get("chunk", 256), kw.get("codes_out", A),
+                                       kw.get("scales_out", A), kw.get("sum_out", A), None)
+    for f in (q, d, r):
+        assert f(chunk=128) == 2 and f(chunk=2048) == 2 and f(chunk=300) == 2
+        assert f(dt=5) == 1 and f(n=-1) == 1 and f(n=1 << 41) == 1
+    assert q(x=None) == 1 and q(codes=A + 4) == 1 and q(scales=A + 2) == 1 and q(x=A + 8) == 1
+    assert q(n=0, x=None, codes=None, scales=None) == 0
+    assert d(out=None) == 1 and d(codes=A + 8) == 1
+    assert r(codes_out=None) == 1                      # codes without scales
+    assert r(codes_out=None, scales_out=None, sum_out=None) == 1
+    assert r(local=None) == 1 and r(sum_out=A + 2) == 1
+    assert r(n=0, codes=None, scales=None, local=None, codes_out=None, scales_out=None) == 0
