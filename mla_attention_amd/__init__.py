@@ -71,6 +71,8 @@ SIGNATURES = {
     "zl_attn_varlen_mla_ex": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _c_float, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _vp, _c_size, _vp]),
     "zl_attn_combine": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
+    "zl_attn_prefill_gqa": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                     _c_float, _c_int, _c_int, _vp, _vp, _vp]),
     "zl_int8_quantize": (_c_int, [_vp, _c_int, ctypes.c_longlong, _c_int, _vp, _vp, _vp]),
     "zl_int8_dequantize": (_c_int, [_vp, _vp, ctypes.c_longlong, _c_int, _c_int, _vp, _vp]),
     "zl_int8_reduce_step": (_c_int, [_vp, _vp, _vp, _c_int, ctypes.c_longlong, _c_int, _vp, _vp, _vp, _vp]),
@@ -369,6 +371,26 @@ def zl_attn_varlen_gqa(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, max_seql
         int(max_seqlen_k), float(softmax_scale), int(bool(causal)), _DTYPE[q.dtype], _ptr(out), _ptr(lse),
         int(num_workers), int(phases), _ptr(workspace), workspace.numel(), _stream(stream, dev))
     _check(st, "zl_attn_varlen_gqa")
+    return (out, lse) if lse is not None else out
+
+
+def zl_attn_prefill_gqa(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, max_seqlen_k: int,
+                        softmax_scale: float, causal: bool = True, out=None, lse=None, stream=None,
+                        return_lse: bool = False):
+    """zl_attn_varlen_gqa through the prefill kernel (many new tokens per
+    sequence; no workspace)."""
+    dev, B, out, lse = _varlen_common(q, cu_seqlens_q, cu_seqlens_k, q.shape[2], out, lse, return_lse)
+    _need(k_cache, "k_cache", q.dtype, 3, dev)
+    _need(v_cache, "v_cache", q.dtype, 3, dev)
+    Tq, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    if k_cache.shape[2] != D or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache / v_cache must be [T, Hkv, head_dim] like q")
+    st = library().zl_attn_prefill_gqa(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, Tq, Hq, Hkv, D,
+        int(max_seqlen_k), float(softmax_scale), int(bool(causal)), _DTYPE[q.dtype], _ptr(out), _ptr(lse),
+        _stream(stream, dev))
+    _check(st, "zl_attn_prefill_gqa")
     return (out, lse) if lse is not None else out
 
 

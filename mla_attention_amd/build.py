@@ -7,7 +7,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libzl_attn.so")
-SOURCES = ["decode_attn.hip", "decode_mla.hip", "split_merge.hip", "attn_combine.hip", "int8_codec.hip", "zl_api.cpp"]
+SOURCES = ["decode_attn.hip", "decode_mla.hip", "split_merge.hip", "attn_combine.hip", "int8_codec.hip", "prefill_attn.hip",
+           "zl_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

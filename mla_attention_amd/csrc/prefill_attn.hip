@@ -1,0 +1,314 @@
+// prefill_attn.hip -- causal attention of long runs of new tokens (prefill and
+// large prefill chunks) for gfx950 (MI355X), grouped-query layout (K, V [T,
+// Hkv, D], D = 64 or 128).  The pages list flash-attention prefill and chunked
+// prefill among the engine's kernels (first page, sections "技术架构" and
+// "功能生态"; second page, section "Dual streams, host all-reduce and the memory
+// model").  The operation is the one of zl_attn_varlen_gqa: new token i of the
+// nq of sequence b sees its cache rows 0 .. lk - nq + i (causal, aligned to
+// the bottom right) or all lk rows.
+//
+// Unlike decode, every cache row is used by many query rows, so the work is
+// matrix-unit bound.  Structure (one workgroup of four wavefronts per CU):
+//  * A workgroup takes one key/value head and a block of 256 query rows of
+//    one sequence -- the pairs (new token i, head hh of the head's group),
+//    numbered i*G + hh, so the group's heads share every K/V tile.  Wave w
+//    owns rows 64w .. 64w+63 as four 16-row MFMA column blocks.  Blocks are
+//    launched longest first (the last blocks of a sequence see the most keys).
+//  * The block streams the keys its last token can see in 32-token tiles
+//    through a four-stage LDS ring; each wave DMAs a quarter of every tile
+//    (global_load_lds, SADDR form) and one barrier per tile both publishes
+//    the tile and frees the stage refilled next.
+//  * Per tile and wave: S^T = K Q^T for 2 token blocks x 4 column blocks
+//    (each K fragment read from LDS once and used for four MFMAs), the causal
+//    mask and online softmax per column, and O^T += V^T P^T (each transposed V
+//    fragment read once, four MFMAs) -- the decode kernels' tile math and
+//    layouts (zl_tile.h), widened to 64 query rows per wave.
+#include "zl_device.h"
+#include "zl_kernels.h"
+#include "zl_split.h"
+#include "zl_tile.h"
+
+namespace zl {
+namespace {
+
+constexpr int kPfWaves = 4;
+constexpr int kPfCB = 4;                       // 16-row column blocks per wave
+constexpr int kPfRowsLog2 = 8;                 // 256 query rows per workgroup
+constexpr int kPfStages = 4;
+
+template <int D>
+struct PfGeo {
+  static constexpr int ROWB = D * 2;           // bytes per K or V row in LDS
+  static constexpr int CPR = D / 8;            // 16-byte slots per row
+  static constexpr int KBYTES = 32 * ROWB;
+  static constexpr int STAGE = 2 * KBYTES;     // K tile then V tile
+  static constexpr int NI = STAGE / 1024;      // 1 KB DMA instructions per tile
+  static constexpr int NIW = NI / kPfWaves;    // per wave
+  static constexpr int KSTEPS = D / 32;
+  static constexpr int VBLK = D / 16;
+  static_assert(NI % kPfWaves == 0, "tile splits evenly over the waves");
+  // The decode kernels' conflict-free swizzles (zl_tile.h bank rules).
+  __device__ static int slot(int c, int r) {
+    if constexpr (D == 128)
+      return c ^ (r & 15);
+    else
+      return c ^ ((r >> 1) & 7);
+  }
+};
+
+// This wave's quarter of a tile: instruction k covers 1 KB block i = NIW*w + k
+// of [K tile | V tile]; lane l loads row r = lin / CPR, slot slot(lin % CPR, r)
+// of that tile, lin = 64*(i mod NI/2) + l.
+template <int D>
+struct PfMap {
+  uint32_t chunk[PfGeo<D>::NIW];  // 16 * source slot
+  int row[PfGeo<D>::NIW];
+};
+
+template <int D>
+__device__ __forceinline__ PfMap<D> pf_map(int wave, int lane) {
+  using GE = PfGeo<D>;
+  PfMap<D> m;
+#pragma unroll
+  for (int k = 0; k < GE::NIW; ++k) {
+    const int i = GE::NIW * wave + k;
+    const int half = GE::NI / 2;
+    const int lin = 64 * (i % half) + lane;
+    const int r = lin / GE::CPR;
+    m.row[k] = r;
+    m.chunk[k] = 16u * (uint32_t)GE::slot(lin - r * GE::CPR, r);
+  }
+  return m;
+}
+
+// Rows past nvalid repeat row nvalid - 1 (finite data, masked out).
+template <int D>
+__device__ __forceinline__ void pf_dma_tile(const char* kbase, const char* vbase, uint32_t row_bytes,
+                                            const PfMap<D>& m, int nvalid, ZL_LDS char* stage, int wave) {
+  using GE = PfGeo<D>;
+#pragma unroll
+  for (int k = 0; k < GE::NIW; ++k) {
+    const int i = GE::NIW * wave + k;
+    const int rr = m.row[k] < nvalid ? m.row[k] : nvalid - 1;
+    const char* base = (i >= GE::NI / 2) ? vbase : kbase;  // wave-uniform
+    dma16_saddr(base, (uint32_t)rr * row_bytes + m.chunk[k], stage + i * 1024);
+  }
+}
+
+// S^T for the tile's 2 token blocks and this wave's column blocks: lane (g, n)
+// gets tokens 16tb + 4g .. +3 of column 16cb + n.
+template <int DT, int D, typename SlotFn>
+__device__ __forceinline__ void pf_scores(const ZL_LDS char* kt, const i16x8 (&qop)[kPfCB][PfGeo<D>::KSTEPS], int n,
+                                          int g, SlotFn slot, f32x4 (&s)[kPfCB][2]) {
+  using GE = PfGeo<D>;
+#pragma unroll
+  for (int cb = 0; cb < kPfCB; ++cb) s[cb][0] = s[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < GE::KSTEPS; ++kb) {
+    const int c = 4 * kb + g;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int t = 16 * tb + n;
+      const i16x8 av = __builtin_bit_cast(i16x8, lds_read_b128(kt + t * GE::ROWB + (slot(c, t) << 4)));
+#pragma unroll
+      for (int cb = 0; cb < kPfCB; ++cb) s[cb][tb] = mfma16x16x32<DT>(av, qop[cb][kb], s[cb][tb]);
+    }
+  }
+}
+
+// O^T[cb] += V^T P^T[cb] over all D/16 output blocks; every transposed V
+// fragment is read once and used for the four column blocks.  Reads go out in
+// groups of 4 blocks with one group of lookahead (as pv_blocks).
+template <int DT, int D, typename SlotFn>
+__device__ __forceinline__ void pf_pv(const ZL_LDS char* vt, const POperand (&pop)[kPfCB], int n, int g,
+                                      SlotFn slot, f32x4 (&o)[kPfCB][PfGeo<D>::VBLK]) {
+  using GE = PfGeo<D>;
+  constexpr int NG = GE::VBLK / 4;
+  const int r0 = 4 * g + (n >> 2);
+  const int r1 = r0 + 16;
+  const int half = (n & 1) << 3;
+  const int csub = (n & 3) >> 1;
+  const ZL_LDS char* row0 = vt + r0 * GE::ROWB + half;
+  const ZL_LDS char* row1 = vt + r1 * GE::ROWB + half;
+  i16x4 lo[2][4], hi[2][4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = 2 * k + csub;
+    lo[0][k] = lds_read_tr16(row0 + (slot(c, r0) << 4));
+    hi[0][k] = lds_read_tr16(row1 + (slot(c, r1) << 4));
+  }
+#pragma unroll
+  for (int grp = 0; grp < NG; ++grp) {
+    const int buf = grp & 1;
+    if (grp + 1 < NG) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int c = 2 * (4 * (grp + 1) + k) + csub;
+        lo[buf ^ 1][k] = lds_read_tr16(row0 + (slot(c, r0) << 4));
+        hi[buf ^ 1][k] = lds_read_tr16(row1 + (slot(c, r1) << 4));
+      }
+      lds_wait<8>(lo[buf][0], lo[buf][1], lo[buf][2], lo[buf][3], hi[buf][0], hi[buf][1], hi[buf][2],
+                  hi[buf][3]);
+    } else {
+      lds_wait<0>(lo[buf][0], lo[buf][1], lo[buf][2], lo[buf][3], hi[buf][0], hi[buf][1], hi[buf][2],
+                  hi[buf][3]);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const i16x8 av = __builtin_shufflevector(lo[buf][k], hi[buf][k], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int cb = 0; cb < kPfCB; ++cb) {
+        o[cb][4 * grp + k] = mfma16x16x32<DT>(av, pop[cb].hi, o[cb][4 * grp + k]);
+        if constexpr (DT == kBF16) o[cb][4 * grp + k] = mfma16x16x32<DT>(av, pop[cb].lo, o[cb][4 * grp + k]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+template <int D, int DT>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kPfWaves, 64 * kPfWaves),
+                          amdgpu_waves_per_eu(1, 1))) void
+prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, int nblocks) {
+  using GE = PfGeo<D>;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kPfStages * GE::STAGE];
+  ZL_LDS char* smem = (ZL_LDS char*)smem_raw;
+  const int tid = threadIdx.x;
+  const int wave = readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const auto slot = [](int c, int r) { return PfGeo<D>::slot(c, r); };
+
+  // Workgroup -> (key/value head, block of 256 query rows), longest first.
+  const int kvh = (int)blockIdx.x % a.Hkv;
+  const int j = (int)blockIdx.x / a.Hkv;
+  VirtualSeqs vs;
+  vs.init(a.cu_q, cu, a.B, a.G, 0, kPfRowsLog2);
+  if (j >= vs.V) return;
+  const VSeqInfo si = vs.info(vs.V - 1 - j);
+  const bool causal = a.causal != 0;
+
+  // This lane's four columns: query rows 256 hb + 64 wave + 16 cb + n.
+  long long orow[kPfCB];
+  bool valid[kPfCB];
+  int lim[kPfCB];  // last visible cache row, counted from the sequence's first
+  const int last_row = si.nq * a.G - 1;
+#pragma unroll
+  for (int cb = 0; cb < kPfCB; ++cb) {
+    const int r = (si.hb << kPfRowsLog2) + 64 * wave + 16 * cb + n;
+    const int rr = r < last_row ? r : last_row;
+    const int qi = rr / a.G;
+    orow[cb] = (long long)(si.q0 + qi) * a.Hq + kvh * a.G + (rr - qi * a.G);
+    valid[cb] = r <= last_row;
+    lim[cb] = causal ? si.lk - si.nq + qi : si.lk - 1;
+  }
+  // Keys the block's last row can see.
+  const int blk_last = ((si.hb + 1) << kPfRowsLog2) - 1;
+  const int last_tok = (blk_last < last_row ? blk_last : last_row) / a.G;
+  int kend = causal ? si.lk - si.nq + last_tok + 1 : si.lk;
+  kend = kend < si.lk ? kend : si.lk;
+  const int ntiles = kend > 0 ? (kend + 31) >> 5 : 0;
+
+  // Query operands straight from global memory (waited for before any DMA).
+  i16x8 qop[kPfCB][GE::KSTEPS];
+#pragma unroll
+  for (int cb = 0; cb < kPfCB; ++cb)
+#pragma unroll
+    for (int kb = 0; kb < GE::KSTEPS; ++kb)
+      qop[cb][kb] = *(const i16x8*)(a.q + orow[cb] * D + 32 * kb + 8 * g);
+#pragma unroll
+  for (int cb = 0; cb < kPfCB; ++cb)
+#pragma unroll
+    for (int kb = 0; kb < GE::KSTEPS; ++kb) touch(qop[cb][kb]);
+
+  const uint32_t row_bytes = (uint32_t)a.Hkv * D * 2;
+  const char* kseq = (const char*)(a.k + ((long long)si.k0 * a.Hkv + kvh) * D);
+  const char* vseq = (const char*)(a.v + ((long long)si.k0 * a.Hkv + kvh) * D);
+  const PfMap<D> map = pf_map<D>(wave, lane);
+  int issued = 0;
+  auto issue = [&]() {
+    const int t0 = 32 * issued;
+    const int nv = kend - t0 < 32 ? kend - t0 : 32;
+    pf_dma_tile<D>(kseq + (size_t)t0 * row_bytes, vseq + (size_t)t0 * row_bytes, row_bytes, map, nv,
+                   smem + (issued % kPfStages) * GE::STAGE, wave);
+    ++issued;
+  };
+  for (int s = 0; s < kPfStages - 1 && issued < ntiles; ++s) issue();
+
+  f32x4 o[kPfCB][GE::VBLK];
+  SoftmaxState sm[kPfCB];
+#pragma unroll
+  for (int cb = 0; cb < kPfCB; ++cb) {
+    sm[cb] = SoftmaxState{-INFINITY, 0.f};
+#pragma unroll
+    for (int bb = 0; bb < GE::VBLK; ++bb) o[cb][bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int i = 0; i < ntiles; ++i) {
+    // Tile i has landed once at most the tiles issued after it are in flight.
+    const int after = issued - i - 1;
+    if (after >= 2)
+      wait_vmcnt<2 * GE::NIW>();
+    else if (after == 1)
+      wait_vmcnt<GE::NIW>();
+    else
+      wait_vmcnt<0>();
+    barrier_lds();  // tile i complete in LDS; every wave is past tile i-1
+    if (issued < ntiles) issue();  // into the stage of tile i-1
+    const ZL_LDS char* kt = smem + (i % kPfStages) * GE::STAGE;
+    const ZL_LDS char* vt = kt + GE::KBYTES;
+    f32x4 s[kPfCB][2];
+    pf_scores<DT, D>(kt, qop, n, g, slot, s);
+    const int nv = kend - 32 * i < 32 ? kend - 32 * i : 32;
+    POperand pop[kPfCB];
+#pragma unroll
+    for (int cb = 0; cb < kPfCB; ++cb) {
+      const int lv = lim[cb] - 32 * i + 1;
+      float alpha;
+      pop[cb] = softmax_update<DT>(s[cb], g, nv < lv ? nv : lv, a.scale_log2, sm[cb], alpha);
+#pragma unroll
+      for (int bb = 0; bb < GE::VBLK; ++bb) o[cb][bb] *= alpha;
+    }
+    pf_pv<DT, D>(vt, pop, n, g, slot, o);
+  }
+
+  // Epilogue: lane (g, n) holds column 16cb + n, dims 16blk + 4g .. +3.
+#pragma unroll
+  for (int cb = 0; cb < kPfCB; ++cb) {
+    const float l_tot = sum_over_groups(sm[cb].l);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse_v = l_tot > 0.f ? sm[cb].m * kLn2 + __logf(l_tot) : -INFINITY;
+    if (valid[cb]) {
+      uint16_t* dst = a.out + orow[cb] * D + 4 * g;
+#pragma unroll
+      for (int bb = 0; bb < GE::VBLK; ++bb) store_out4<DT>(dst + 16 * bb, o[cb][bb], inv);
+      if (a.lse && g == 0) a.lse[orow[cb]] = lse_v;
+    }
+  }
+}
+
+template <int D, int DT>
+static void launch_prefill_t(const DecodeArgs& a, int nblocks, hipStream_t stream) {
+  hipLaunchKernelGGL((prefill_kernel<D, DT>), dim3((unsigned)(a.Hkv * nblocks)), dim3(64 * kPfWaves), 0, stream, a,
+                     a.cu, nblocks);
+}
+
+hipError_t launch_prefill(const DecodeArgs& a, int head_dim, int dtype, int max_blocks, hipStream_t stream) {
+  if (max_blocks <= 0) return hipSuccess;
+  if (head_dim == 128) {
+    if (dtype == kF16)
+      launch_prefill_t<128, kF16>(a, max_blocks, stream);
+    else
+      launch_prefill_t<128, kBF16>(a, max_blocks, stream);
+  } else {
+    if (dtype == kF16)
+      launch_prefill_t<64, kF16>(a, max_blocks, stream);
+    else
+      launch_prefill_t<64, kBF16>(a, max_blocks, stream);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace zl

@@ -63,6 +63,10 @@ struct CombineArgs {
   int S, rows, Dv;
 };
 
+// Long runs of new tokens (prefill_attn.hip): one workgroup per (key/value
+// head, block of 256 query rows); max_blocks bounds the blocks of the batch.
+hipError_t launch_prefill(const DecodeArgs& a, int head_dim, int dtype, int max_blocks, hipStream_t stream);
+
 // INT8 coding of an all-reduce payload (int8_codec.hip).
 enum CodecOp { kCodecQuantize = 0, kCodecDequantize = 1, kCodecReduce = 2 };
 

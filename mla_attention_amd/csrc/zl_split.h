@@ -198,7 +198,8 @@ __device__ __forceinline__ Segment segment_at(long long p, long long p_end, cons
 // cu_q[b] new tokens and lk = cu_k[b+1] - cu_k[b] cached key/value rows.  For
 // one key/value head, its query rows (new token i, head hh of the head's
 // group of G) are numbered r = i*G + hh and cut into nblk = ceil(nq*G / 16)
-// blocks of 16 -- one MFMA N dimension each.  Virtual sequence (b, hb) pairs
+// blocks of 16 -- one MFMA N dimension each (the prefill kernel uses blocks
+// of 256 rows: rows_log2 = 8).  Virtual sequence (b, hb) pairs
 // row block hb with all lk rows of b.  The virtual sequences of all b, in
 // order, are the ragged batch that the work split cuts: virtual sequence v =
 // VB(b) + hb owns virtual tokens [KB(b) + hb*lk, + lk), where VB and KB count
@@ -222,7 +223,7 @@ struct VChunk {
 };
 
 __device__ __forceinline__ VChunk vchunk(const int32_t* cu_q, const int32_t* cu_k, int B, int G, int C, int c0,
-                                         int vcarry, int kcarry) {
+                                         int vcarry, int kcarry, int shift) {
   const int b = c0 + __lane_id();
   const int i0 = b < B ? b : B, i1 = b < B ? b + 1 : B;
   // Unpredicated loads (clamped indices): a branch here would make the
@@ -233,7 +234,7 @@ __device__ __forceinline__ VChunk vchunk(const int32_t* cu_q, const int32_t* cu_
   c.nq = q1 - q0;
   c.k0 = k0;
   c.lk = k1 - k0;
-  c.nblk = (c.nq * G + 15) >> 4;
+  c.nblk = (c.nq * G + (1 << shift) - 1) >> shift;
   const int tok = c.nblk * c.lk;
   c.vbi = vcarry + wave_inclusive_sum(c.nblk);
   c.vb = c.vbi - c.nblk;
@@ -247,20 +248,22 @@ struct VirtualSeqs {
   const int32_t* cu_q;
   const int32_t* cu_k;
   int B, G, C;
+  int shift;     // rows per block: 2^shift
   VChunk first;  // sequences 0 .. 63 (the whole batch when B <= 64)
   int V, T;      // virtual sequences and tokens of the batch
 
-  __device__ __forceinline__ void init(const int32_t* cq, const int32_t* ck, int b, int g, int c) {
+  __device__ __forceinline__ void init(const int32_t* cq, const int32_t* ck, int b, int g, int c, int rows_log2 = 4) {
     cu_q = cq;
     cu_k = ck;
     B = b;
     G = g;
     C = c;
-    first = vchunk(cu_q, cu_k, B, G, C, 0, 0, 0);
+    shift = rows_log2;
+    first = vchunk(cu_q, cu_k, B, G, C, 0, 0, 0, shift);
     V = __builtin_amdgcn_readlane(first.vbi, 63);
     T = __builtin_amdgcn_readlane(first.kb + first.nblk * first.lk, 63);
     for (int c0 = 64; c0 < B; c0 += 64) {
-      const VChunk ch = vchunk(cu_q, cu_k, B, G, C, c0, V, T);
+      const VChunk ch = vchunk(cu_q, cu_k, B, G, C, c0, V, T, shift);
       V = __builtin_amdgcn_readlane(ch.vbi, 63);
       T = __builtin_amdgcn_readlane(ch.kb + ch.nblk * ch.lk, 63);
     }
@@ -277,7 +280,7 @@ struct VirtualSeqs {
     while (m == ~0ull && c0 + 64 < B) {
       c0 += 64;
       ch = vchunk(cu_q, cu_k, B, G, C, c0, __builtin_amdgcn_readlane(ch.vbi, 63),
-                  __builtin_amdgcn_readlane(ch.kb + ch.nblk * ch.lk, 63));
+                  __builtin_amdgcn_readlane(ch.kb + ch.nblk * ch.lk, 63), shift);
       m = __ballot(before(ch));
     }
     const int l = __popcll(m);

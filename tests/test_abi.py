@@ -205,3 +205,20 @@ def test_codec_entry_points_reject_bad_arguments(zl):
     assert r(codes_out=None, scales_out=None, sum_out=None) == 1
     assert r(local=None) == 1 and r(sum_out=A + 2) == 1
     assert r(n=0, codes=None, scales=None, local=None, codes_out=None, scales_out=None) == 0
+
+
+def test_prefill_entry_point_rejects_bad_arguments(zl):
+    lib = zl.library()
+
+    def pf(**kw):
+        a = dict(q=A, k=A, v=A, cq=A, ck=A, B=2, Tq=300, Hq=8, Hkv=2, D=128, maxL=300, scale=0.1, causal=1, dt=1,
+                 out=A, lse=None, stream=None)
+        a.update(kw)
+        return lib.zl_attn_prefill_gqa(a["q"], a["k"], a["v"], a["cq"], a["ck"], a["B"], a["Tq"], a["Hq"], a["Hkv"],
+                                       a["D"], a["maxL"], a["scale"], a["causal"], a["dt"], a["out"], a["lse"],
+                                       a["stream"])
+    assert pf(cq=None) == 1 and pf(ck=None) == 1 and pf(q=None) == 1 and pf(out=A + 2) == 1
+    assert pf(D=96) == 2 and pf(D=0) == 1 and pf(Hq=7) == 1 and pf(causal=3) == 1 and pf(dt=4) == 1
+    assert pf(scale=float("inf")) == 1 and pf(Tq=-1) == 1
+    assert pf(Tq=0, q=None, k=None, v=None, cq=None, ck=None, out=None) == 0
+    assert pf(Tq=1 << 30, Hq=1024, Hkv=1024) == 2   # 2^22 blocks x 1024 heads
