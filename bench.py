@@ -77,6 +77,10 @@ def parse():
     ap.add_argument("--codec", choices=["quantize", "dequantize", "reduce"], default=None,
                     help="instead: time the INT8 all-reduce payload codec kernel on --codec-mib of fp16 payload")
     ap.add_argument("--codec-mib", type=int, default=64)
+    ap.add_argument("--prefill", type=int, default=0, metavar="LEN",
+                    help="instead: time the prefill kernel on --prefill-batch whole prompts of LEN tokens "
+                         "(heads, head dim and dtype of --config), causal")
+    ap.add_argument("--prefill-batch", type=int, default=4)
     ap.add_argument("--codec-chunk", type=int, default=512)
     ap.add_argument("--paged", type=int, default=0, metavar="PAGE_SIZE",
                     help="read the caches from a shuffled page pool through a block table "
@@ -117,6 +121,9 @@ def main():
         return
     if args.codec:
         bench_codec(args)
+        return
+    if args.prefill:
+        bench_prefill(args)
         return
 
     import numpy as np
@@ -278,6 +285,65 @@ def main():
         "wall_ms_timed_region": round(wall_ms, 2),
     }
     print(json.dumps(rec), flush=True)
+
+
+MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16
+
+
+def bench_prefill(args):
+    """Whole prompts through the prefill kernel.  Useful flops: QK^T and PV over
+    the causal triangle, 2 * 2 * Hq * D * L (L + 1) / 2 per prompt."""
+    import numpy as np
+    import torch
+
+    import mla_attention_amd as zl
+    import workloads
+
+    spec0 = workloads.CONFIGS[args.config]
+    L, B = args.prefill, args.prefill_batch
+    spec = workloads.with_shape(spec0, batch=B, lens=tuple([L] * B))
+    dev = torch.device("cuda:0")
+    x = workloads.make_inputs(spec)
+    vq = workloads.make_varlen_query(x, [L] * B, seed=args.config)
+    q, k, v = vq.q.to(dev), x.k.to(dev), x.v.to(dev)
+    cq, ck = vq.cu_q.to(dev), x.cu_seqlens.to(dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+    flops = 4.0 * spec.num_q_heads * spec.head_dim_k * B * L * (L + 1) / 2
+
+    def step(i):
+        zl.zl_attn_prefill_gqa(q, k, v, cq, ck, L, spec.scale, out=out, stream=stream)
+
+    if args.profile_run:
+        for i in range(max(3, args.steps)):
+            step(i)
+        torch.cuda.synchronize()
+        print(f"profile run: prefill {B} x {L}, {max(3, args.steps)} launches", flush=True)
+        return
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(K):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    tf = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "prefill attention TFLOP/s (useful causal QK^T + PV flops / step time)",
+        "value": round(tf, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16" if spec.dtype == "f16" else "bf16", "data": "synthetic (seeded N(0,1) Q/K/V)",
+        "config": {"workload": f"prefill-b{B}-L{L}-h{spec.num_q_heads}kv{spec.num_kv_heads}-d{spec.head_dim_k}",
+                   "batch": B, "prompt_len": L, "num_q_heads": spec.num_q_heads,
+                   "num_kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim_k, "causal": True},
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tf, 1),
+                     "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": None}), flush=True)
 
 
 def bench_codec(args):

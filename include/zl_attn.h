@@ -304,12 +304,12 @@ ZL_API zl_status_t zl_attn_varlen_mla_ex(const void *q, const void *kv_cache, co
  * "技术架构" and "功能生态"; the second page lists them in section "Dual
  * streams, host all-reduce and the memory model").  The operation, layouts and
  * argument checks are those of zl_attn_varlen_gqa; only the kernel differs: it
- * reads every key/value row the block's query rows can see once per 256 query
+ * reads every key/value row the block's query rows can see once per 128 query
  * rows of one key/value head (for the causal mask, only the keys up to the
  * block's last token), so it suits many new tokens per sequence; for a few
  * new tokens per sequence zl_attn_varlen_gqa streams fewer bytes.  No
  * workspace.  ZL_ERR_UNSUPPORTED when num_kv_heads *
- * ceil((total_q * group + 255 * batch) / 256) >= 2^31.
+ * ceil((total_q * group + 127 * batch) / 128) >= 2^31.
  */
 ZL_API zl_status_t zl_attn_prefill_gqa(const void *q, const void *k_cache, const void *v_cache,
                                        const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int batch,

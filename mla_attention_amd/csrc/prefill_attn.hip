@@ -32,8 +32,8 @@ namespace zl {
 namespace {
 
 constexpr int kPfWaves = 4;
-constexpr int kPfCB = 4;                       // 16-row column blocks per wave
-constexpr int kPfRowsLog2 = 8;                 // 256 query rows per workgroup
+constexpr int kPfCB = 2;                       // 16-row column blocks per wave
+constexpr int kPfRowsLog2 = kPrefillRowsLog2;  // 128 query rows per workgroup
 constexpr int kPfStages = 4;
 
 template <int D>
@@ -47,6 +47,7 @@ struct PfGeo {
   static constexpr int KSTEPS = D / 32;
   static constexpr int VBLK = D / 16;
   static_assert(NI % kPfWaves == 0, "tile splits evenly over the waves");
+  static_assert(kPfWaves * kPfCB * 16 == 1 << kPfRowsLog2, "the waves' columns are the block's rows");
   // The decode kernels' conflict-free swizzles (zl_tile.h bank rules).
   __device__ static int slot(int c, int r) {
     if constexpr (D == 128)
@@ -165,11 +166,99 @@ __device__ __forceinline__ void pf_pv(const ZL_LDS char* vt, const POperand (&po
   }
 }
 
+// Online-softmax update of the wave's four column blocks at once (as
+// softmax_update in zl_tile.h per block).  The four blocks are independent, so
+// every step is written across them: the reductions and exponentials form four
+// interleavable chains instead of one long one.  The token mask is compiled
+// in only where a tile needs it.
+template <int DT, bool MASK>
+__device__ __forceinline__ void pf_softmax4(const f32x4 (&s)[kPfCB][2], int g, const int (&nvalid)[kPfCB],
+                                            float scale_log2, SoftmaxState (&st)[kPfCB], float (&alpha)[kPfCB],
+                                            POperand (&p)[kPfCB]) {
+  static_assert(kPfCB == 2 || kPfCB == 4, "two or four column blocks");
+  float x[kPfCB][8];
+  float tmax[kPfCB];
+#pragma unroll
+  for (int cb = 0; cb < kPfCB; ++cb) tmax[cb] = -INFINITY;
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int cb = 0; cb < kPfCB; ++cb) {
+        float xv = s[cb][tb][r] * scale_log2;
+        if constexpr (MASK) xv = 16 * tb + 4 * g + r < nvalid[cb] ? xv : -INFINITY;
+        x[cb][4 * tb + r] = xv;
+        tmax[cb] = fmaxf(tmax[cb], xv);
+      }
+  {
+    float t4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t4[i] = tmax[i % kPfCB];
+    max_over_groups4(t4);
+#pragma unroll
+    for (int cb = 0; cb < kPfCB; ++cb) tmax[cb] = t4[cb];
+  }
+  float m_use[kPfCB], psum[kPfCB];
+#pragma unroll
+  for (int cb = 0; cb < kPfCB; ++cb) {
+    const float m_new = fmaxf(st[cb].m, tmax[cb]);
+    m_use[cb] = (m_new == -INFINITY) ? 0.f : m_new;
+    alpha[cb] = exp2_fast(st[cb].m - m_use[cb]);
+    st[cb].m = m_new;
+    psum[cb] = 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int cb = 0; cb < kPfCB; ++cb) {
+      x[cb][i] = exp2_fast(x[cb][i] - m_use[cb]);
+      psum[cb] += x[cb][i];
+    }
+#pragma unroll
+  for (int cb = 0; cb < kPfCB; ++cb) {
+    st[cb].l = st[cb].l * alpha[cb] + psum[cb];
+    u32x4 pw;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pw[i] = pack2<DT>(x[cb][2 * i], x[cb][2 * i + 1]);
+    p[cb].hi = __builtin_bit_cast(i16x8, pw);
+    if constexpr (DT == kBF16) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[cb][i] -= __builtin_bit_cast(float, (uint32_t)to16<DT>(x[cb][i]) << 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pw[i] = pack2<DT>(x[cb][2 * i], x[cb][2 * i + 1]);
+      p[cb].lo = __builtin_bit_cast(i16x8, pw);
+    } else {
+      p[cb].lo = p[cb].hi;
+    }
+  }
+}
+
+// Scheduling request for the block above: the K reads first, then each
+// score MFMA followed by a few softmax vector instructions, so the vector unit
+// works while the matrix unit runs (an MFMA occupies it for 16 cycles).
+template <int D>
+__device__ __forceinline__ void interleave_scores_softmax() {
+  constexpr int NMFMA = 2 * kPfCB * PfGeo<D>::KSTEPS;
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * PfGeo<D>::KSTEPS, 0);  // DS reads
+#pragma unroll
+  for (int k = 0; k < NMFMA; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+  }
+}
+
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = min(v, __builtin_amdgcn_ds_bpermute((__lane_id() ^ m) << 2, v));
+  return v;
+}
+
 }  // namespace
 
 template <int D, int DT>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kPfWaves, 64 * kPfWaves),
-                          amdgpu_waves_per_eu(1, 1))) void
+                          amdgpu_waves_per_eu(2, 2))) void
 prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, int nblocks) {
   using GE = PfGeo<D>;
   __shared__ __attribute__((aligned(1024))) char smem_raw[kPfStages * GE::STAGE];
@@ -190,20 +279,25 @@ prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, int nblocks) {
   const VSeqInfo si = vs.info(vs.V - 1 - j);
   const bool causal = a.causal != 0;
 
-  // This lane's four columns: query rows 256 hb + 64 wave + 16 cb + n.
+  // This lane's columns: query rows 256 hb + 16 kPfCB wave + 16 cb + n.
   long long orow[kPfCB];
   bool valid[kPfCB];
   int lim[kPfCB];  // last visible cache row, counted from the sequence's first
   const int last_row = si.nq * a.G - 1;
 #pragma unroll
   for (int cb = 0; cb < kPfCB; ++cb) {
-    const int r = (si.hb << kPfRowsLog2) + 64 * wave + 16 * cb + n;
+    const int r = (si.hb << kPfRowsLog2) + 16 * kPfCB * wave + 16 * cb + n;
     const int rr = r < last_row ? r : last_row;
     const int qi = rr / a.G;
     orow[cb] = (long long)(si.q0 + qi) * a.Hq + kvh * a.G + (rr - qi * a.G);
     valid[cb] = r <= last_row;
     lim[cb] = causal ? si.lk - si.nq + qi : si.lk - 1;
   }
+  // Tiles below every column's limit need no mask (wave-uniform).
+  int lim_lane = lim[0];
+#pragma unroll
+  for (int cb = 1; cb < kPfCB; ++cb) lim_lane = min(lim_lane, lim[cb]);
+  const int lim_min = readfirstlane(wave_min(lim_lane));
   // Keys the block's last row can see.
   const int blk_last = ((si.hb + 1) << kPfRowsLog2) - 1;
   const int last_tok = (blk_last < last_row ? blk_last : last_row) / a.G;
@@ -246,32 +340,68 @@ prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, int nblocks) {
     for (int bb = 0; bb < GE::VBLK; ++bb) o[cb][bb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int i = 0; i < ntiles; ++i) {
-    // Tile i has landed once at most the tiles issued after it are in flight.
-    const int after = issued - i - 1;
+  // Software pipeline: the scores of tile i+1 (matrix units) are computed in
+  // the same basic block as the softmax of tile i (vector unit), so the two
+  // overlap; then tile i's PV.  Ring: tile i+1 must have landed before its
+  // scores; the stage of tile i-1 (whose PV every wave has finished at the
+  // barrier) takes tile i+3.
+  auto wait_tile = [&](int t) {
+    const int after = issued - t - 1;  // tiles issued after t may be in flight
     if (after >= 2)
       wait_vmcnt<2 * GE::NIW>();
     else if (after == 1)
       wait_vmcnt<GE::NIW>();
     else
       wait_vmcnt<0>();
-    barrier_lds();  // tile i complete in LDS; every wave is past tile i-1
-    if (issued < ntiles) issue();  // into the stage of tile i-1
-    const ZL_LDS char* kt = smem + (i % kPfStages) * GE::STAGE;
-    const ZL_LDS char* vt = kt + GE::KBYTES;
-    f32x4 s[kPfCB][2];
-    pf_scores<DT, D>(kt, qop, n, g, slot, s);
+    barrier_lds();
+  };
+  f32x4 s_cur[kPfCB][2], s_nxt[kPfCB][2];
+  if (ntiles > 0) {
+    wait_tile(0);
+    pf_scores<DT, D>(smem, qop, n, g, slot, s_cur);
+  }
+  for (int i = 0; i < ntiles; ++i) {
+    const bool more = i + 1 < ntiles;
+    if (more) {
+      wait_tile(i + 1);
+      if (issued < ntiles) issue();  // into the stage of tile i-1
+    }
+    const ZL_LDS char* knext = smem + ((i + 1) % kPfStages) * GE::STAGE;
     const int nv = kend - 32 * i < 32 ? kend - 32 * i : 32;
     POperand pop[kPfCB];
+    float alpha[kPfCB];
+    int nvc[kPfCB];
 #pragma unroll
     for (int cb = 0; cb < kPfCB; ++cb) {
       const int lv = lim[cb] - 32 * i + 1;
-      float alpha;
-      pop[cb] = softmax_update<DT>(s[cb], g, nv < lv ? nv : lv, a.scale_log2, sm[cb], alpha);
-#pragma unroll
-      for (int bb = 0; bb < GE::VBLK; ++bb) o[cb][bb] *= alpha;
+      nvc[cb] = nv < lv ? nv : lv;
     }
-    pf_pv<DT, D>(vt, pop, n, g, slot, o);
+    const bool full = nv == 32 && 32 * i + 31 <= lim_min;
+    if (more && full) {
+      pf_scores<DT, D>(knext, qop, n, g, slot, s_nxt);
+      pf_softmax4<DT, false>(s_cur, g, nvc, a.scale_log2, sm, alpha, pop);
+      interleave_scores_softmax<D>();
+    } else if (more) {
+      pf_scores<DT, D>(knext, qop, n, g, slot, s_nxt);
+      pf_softmax4<DT, true>(s_cur, g, nvc, a.scale_log2, sm, alpha, pop);
+      interleave_scores_softmax<D>();
+    } else {
+      pf_softmax4<DT, true>(s_cur, g, nvc, a.scale_log2, sm, alpha, pop);
+    }
+#pragma unroll
+    for (int cb = 0; cb < kPfCB; ++cb) {
+      // Rescale only when some column's running maximum moved (alpha != 1).
+      if (__ballot(alpha[cb] != 1.f)) {
+#pragma unroll
+        for (int bb = 0; bb < GE::VBLK; ++bb) o[cb][bb] *= alpha[cb];
+      }
+    }
+    pf_pv<DT, D>(smem + (i % kPfStages) * GE::STAGE + GE::KBYTES, pop, n, g, slot, o);
+#pragma unroll
+    for (int cb = 0; cb < kPfCB; ++cb) {
+      s_cur[cb][0] = s_nxt[cb][0];
+      s_cur[cb][1] = s_nxt[cb][1];
+    }
   }
 
   // Epilogue: lane (g, n) holds column 16cb + n, dims 16blk + 4g .. +3.

@@ -435,8 +435,9 @@ zl_status_t zl_attn_prefill_gqa(const void* q, const void* k_cache, const void* 
   if (!std::isfinite(softmax_scale)) return ZL_ERR_INVALID_ARGUMENT;
   if (head_dim != 64 && head_dim != 128) return head_dim <= 0 ? ZL_ERR_INVALID_ARGUMENT : ZL_ERR_UNSUPPORTED;
   const int group = num_q_heads / num_kv_heads;
-  // Blocks of 256 query rows: sum over b of ceil(nq_b * G / 256).
-  const long long blocks = ((long long)total_q * group + 255LL * batch + 255) / 256;
+  // Blocks of R = 2^kPrefillRowsLog2 query rows: sum over b of ceil(nq_b * G / R).
+  const long long R = 1LL << zl::kPrefillRowsLog2;
+  const long long blocks = ((long long)total_q * group + (R - 1) * batch + R - 1) / R;
   if (blocks * num_kv_heads >= (1LL << 31)) return ZL_ERR_UNSUPPORTED;
   if (batch == 0 || total_q == 0) return ZL_OK;
   if (!q || !cu_seqlens_q || !cu_seqlens_k || !out) return ZL_ERR_INVALID_ARGUMENT;

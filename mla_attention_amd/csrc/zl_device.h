@@ -106,6 +106,31 @@ __device__ __forceinline__ float max_over_groups(float x) {
   return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 
+// max_over_groups of four independent values at once: the four swaps of each
+// stage go out back to back after one s_nop, so the four reductions overlap.
+// The asm has no side effects beyond its operands (not volatile), so the
+// scheduler may move other work around it.
+__device__ __forceinline__ void max_over_groups4(float (&x)[4]) {
+  uint32_t a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = b[i] = __builtin_bit_cast(uint32_t, x[i]);
+  asm(
+      "s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_permlane16_swap_b32 %2, %3\n\t"
+      "v_permlane16_swap_b32 %4, %5\n\tv_permlane16_swap_b32 %6, %7"
+      : "+v"(a[0]), "+v"(b[0]), "+v"(a[1]), "+v"(b[1]), "+v"(a[2]), "+v"(b[2]), "+v"(a[3]), "+v"(b[3]));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = fmaxf(__builtin_bit_cast(float, a[i]), __builtin_bit_cast(float, b[i]));
+    a[i] = b[i] = __builtin_bit_cast(uint32_t, x[i]);
+  }
+  asm(
+      "s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\tv_permlane32_swap_b32 %2, %3\n\t"
+      "v_permlane32_swap_b32 %4, %5\n\tv_permlane32_swap_b32 %6, %7"
+      : "+v"(a[0]), "+v"(b[0]), "+v"(a[1]), "+v"(b[1]), "+v"(a[2]), "+v"(b[2]), "+v"(a[3]), "+v"(b[3]));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = fmaxf(__builtin_bit_cast(float, a[i]), __builtin_bit_cast(float, b[i]));
+}
+
 __device__ __forceinline__ float sum_over_groups(float x) {
   uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
   lane_swap16(a, b);

@@ -64,7 +64,9 @@ struct CombineArgs {
 };
 
 // Long runs of new tokens (prefill_attn.hip): one workgroup per (key/value
-// head, block of 256 query rows); max_blocks bounds the blocks of the batch.
+// head, block of 2^kPrefillRowsLog2 query rows); max_blocks bounds the blocks
+// of the batch.
+constexpr int kPrefillRowsLog2 = 7;
 hipError_t launch_prefill(const DecodeArgs& a, int head_dim, int dtype, int max_blocks, hipStream_t stream);
 
 // INT8 coding of an all-reduce payload (int8_codec.hip).
