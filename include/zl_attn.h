@@ -266,10 +266,11 @@ ZL_API zl_status_t zl_decode_attn_mla_paged_ex(const void *q, const void *kv_pag
  *   total_q      rows of q (host); 0 is a no-op
  *   out          [total_q, num_q_heads, Dv] dtype;  lse [total_q, num_q_heads]
  * The kernels cut each sequence's (token, head) rows of one key/value head
- * into blocks of 16 and stream the sequence's rows once per block, so the
- * key/value bytes read are those of a decode step times
- * ceil(nq * group / 16).  ZL_ERR_UNSUPPORTED when
- * (ceil((total_q * group + 15 * batch) / 16)) * (max_seqlen_k + 64) >= 2^31.
+ * into blocks of R rows (R = 16 for GQA, 32 for MLA) and stream the
+ * sequence's rows once per block, so the key/value bytes read are those of a
+ * decode step times ceil(nq * group / R).  ZL_ERR_UNSUPPORTED when
+ * ceil((total_q * group + (R - 1) * batch) / R) * (max_seqlen_k + C) >= 2^31,
+ * C = 32 (GQA) or 64 (MLA).
  * The workspace is sized by zl_decode_attn_workspace_size(_ex) (GQA) or
  * zl_decode_attn_mla_workspace_size(_ex) (MLA) with the same arguments; the
  * _ex forms take num_workers and phases as above.

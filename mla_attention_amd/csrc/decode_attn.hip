@@ -222,7 +222,7 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
   int NB;  // sequences on the work line
   int T;
   if constexpr (MQ) {
-    vs.init(a.cu_q, cu, B, a.G, a.seg_cost);
+    vs.init(a.cu_q, cu, B, a.G, a.seg_cost, kMqRowsLog2);
     asm volatile("" : "+v"(vs.first.q0), "+v"(vs.first.nq), "+v"(vs.first.k0), "+v"(vs.first.lk));
     NB = vs.V;
     T = vs.T;
@@ -355,9 +355,12 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
         const int j0 = sg.t0 - sg.cs + 32 * j;
         nvalid = min(nvalid, col.lim - j0 + 1);
       }
-      const POperand pop = softmax_update<DT>(s, g, nvalid, a.scale_log2, sm, alpha);
+      bool rescale;
+      const POperand pop = softmax_update<DT>(s, g, nvalid, a.scale_log2, sm, alpha, rescale);
+      if (rescale) {
 #pragma unroll
-      for (int bb = 0; bb < TL::VBLK; ++bb) o[bb] *= alpha;
+        for (int bb = 0; bb < TL::VBLK; ++bb) o[bb] *= alpha;
+      }
       pv_blocks<DT, TL::VBLK, TL::VROWB>(vt, pop, n, g, 0, slot, o);
 
       if (j == ntl - 1) {

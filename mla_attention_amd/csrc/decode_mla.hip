@@ -30,6 +30,13 @@
 //    softmax is computed identically in all waves.
 //  * PV: wave w accumulates output dims [128w, 128w + 128) as O^T = V^T P^T with
 //    V^T read transposed from the tile (ds_read_b64_tr_b16).
+//  * Several new tokens per sequence: a segment's query item holds 32 query
+//    rows (two blocks of 16 MFMA columns), which fill the stage, and the
+//    workgroup has two groups of four waves, one per column block, each
+//    doing the work above for its block on the same tiles (waves 0-3 issue
+//    the loads).  16 heads of two draft tokens thus cost one pass over the
+//    latent rows, and the two waves on each SIMD hide each other's MFMA and
+//    LDS latency: one wave holding both blocks left the tile math exposed.
 //  * Barriers: one per item when it has landed (every wave is then also done
 //    with the previous item, whose stage is refilled right after), and one per
 //    tile when the score halves are in LDS.
@@ -58,9 +65,18 @@ constexpr int kKSteps = kDK / 32;                // 18
 constexpr int kKHalf = kKSteps / 2;              // 9 k-steps per wave
 constexpr int kBlkPerWave = kDV / 16 / kWaves;   // 8 output blocks of 16 dims
 constexpr int kWorkgroupsPerCU = 1;
-constexpr int kXchgB = kWaves * 1024;            // one f32x4 per lane per wave
-constexpr int kLdsBytes = kStages * kTileB + kXchgB;  // 148 KB of the 160 KB
+// Blocks of 16 query columns per tile, one group of kWaves waves each: 16
+// heads of one token, or with several new tokens per sequence 32 query rows
+// (kMlaMqRowsLog2), so that a tile read from HBM serves e.g. 16 heads of two
+// draft tokens at once.
+template <bool MQ>
+constexpr int column_blocks() { return MQ ? 2 : 1; }
+// Score exchange: one f32x4 per lane and wave.
+template <int NCB>
+constexpr int lds_bytes() { return kStages * kTileB + NCB * kWaves * 1024; }  // 148 or 152 KB of 160
 static_assert(kQB <= kTileB, "query rows fit one ring stage");
+static_assert(2 * kQB == kTileB && (16 << (kMlaMqRowsLog2 - 4)) == 32,
+              "32 query rows are exactly one ring stage");
 
 // A 1152-byte row starts half a bank line (8 slots) after the previous one, so
 // row parity separates bank-line halves; XOR inside each group of 8 slots with
@@ -90,7 +106,10 @@ __device__ __forceinline__ QuarterMap quarter_map(int wave, int lane) {
 }
 
 // Rows past nvalid (< 32 only for a segment's last tile or a short run) are
-// clamped to row nvalid - 1: finite data, masked out of the softmax.
+// clamped to row nvalid - 1: finite data, masked out of the softmax.  (The
+// nine loads go out back to back: issued one per k-step of the score product
+// instead, each still holds its wave as long -- the CU's load path, not the
+// issue order, sets that cost.)
 __device__ __forceinline__ void dma_quarter(const uint16_t* rows, int tok0, int nvalid, const QuarterMap& m,
                                             ZL_LDS char* dst, int wave) {
   const char* base = (const char*)rows + (size_t)tok0 * kRowB;
@@ -134,24 +153,25 @@ __device__ __forceinline__ void dma_query_item(const uint16_t* qb, int nh, ZL_LD
 }
 
 // The query item of a virtual sequence (several new tokens per sequence): row
-// r is query row 16 hb + r of the sequence (new token (16 hb + r) / H, head
-// (16 hb + r) % H); rows past the sequence's last repeat it.
+// r (0 .. 31) is query row 32 hb + r of the sequence (new token (32 hb + r) /
+// H, head (32 hb + r) % H); rows past the sequence's last repeat it.  32 rows
+// fill the stage, so every instruction loads distinct data.
 __device__ __forceinline__ void dma_query_item_mq(const uint16_t* q, const VSeqInfo& si, int H, ZL_LDS char* dst,
                                                   int wave, int lane) {
 #pragma unroll
   for (int k = 0; k < kNIw; ++k) {
     const int i = wave * kNIw + k;
-    const int lin = 64 * (i % kNIq) + lane;
+    const int lin = 64 * i + lane;
     const int r = lin / kCPR;
     const int s = lin - r * kCPR;
-    dma16(q + mq_column(si, r, 0, H, H, false).row * kDK + slot(s, r) * 8, dst + i * 1024);
+    dma16(q + mq_column(si, r, 0, H, H, false, kMlaMqRowsLog2).row * kDK + slot(s, r) * 8, dst + i * 1024);
   }
 }
 
 }  // namespace
 
 // Partial scores of one 16-token block over half of the k-steps:
-// lane (g, n) gets tokens 16tb + 4g .. +3 of head n, summed over dims
+// lane (g, n) gets tokens 16tb + 4g .. +3 of column n, summed over dims
 // [288kh, 288kh + 288).  Two accumulators halve the MFMA dependency chain.
 template <int DT>
 __device__ __forceinline__ f32x4 half_scores(const ZL_LDS char* kt, const i16x8 (&qop)[kKHalf], int tb,
@@ -171,17 +191,22 @@ __device__ __forceinline__ f32x4 half_scores(const ZL_LDS char* kt, const i16x8 
 }
 
 template <int DT, bool PAGED, bool MQ>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * kWaves, 64 * kWaves),
-                          amdgpu_waves_per_eu(1, 1))) void
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kWaves * column_blocks<MQ>(),
+                                                      64 * kWaves * column_blocks<MQ>()),
+                          amdgpu_waves_per_eu(column_blocks<MQ>(), column_blocks<MQ>()))) void
 mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __restrict__ block_table) {
   static_assert(!(PAGED && MQ), "several new tokens per sequence: packed caches only");
+  constexpr int NCB = column_blocks<MQ>();
   // One LDS object only (see decode_attn.hip): [4 ring stages][score exchange].
-  __shared__ __attribute__((aligned(1024))) char smem_raw[kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[lds_bytes<NCB>()];
   ZL_LDS char* smem = (ZL_LDS char*)smem_raw;
   ZL_LDS char* xchg = smem + kStages * kTileB;
+  static_assert(16 * NCB <= kMlaSlotCols, "a partial slot holds the item's columns");
 
   const int tid = threadIdx.x;
-  const int wave = readfirstlane(tid >> 6);  // wave-uniform (scalar) index
+  const int wave = readfirstlane((tid >> 6) & (kWaves - 1));  // quarter of the tile (scalar)
+  const int cb = readfirstlane(tid >> 8);                     // column block of the wave group
+  const bool loader = cb == 0;                                // waves that issue the loads
   const int lane = tid & 63;
   const int n = lane & 15;
   const int g = lane >> 4;
@@ -196,7 +221,7 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
 
   // (Empty sequences are written by the merge launch: no run covers them.)
   // The batch: decode sequences, or with several new tokens per sequence the
-  // virtual sequences of 16 query rows.  Sequence boundaries for the lookups
+  // virtual sequences of 32 query rows.  Sequence boundaries for the lookups
   // are loaded here, before any tile load, and waited for, so that no later
   // lookup has to drain the tile loads in flight (B <= 64).
   int window = 0;
@@ -204,7 +229,7 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
   int NB;  // sequences on the work line
   int T;
   if constexpr (MQ) {
-    vs.init(a.cu_q, cu, B, a.G, a.seg_cost);
+    vs.init(a.cu_q, cu, B, a.G, a.seg_cost, kMlaMqRowsLog2);
     asm volatile("" : "+v"(vs.first.q0), "+v"(vs.first.nq), "+v"(vs.first.k0), "+v"(vs.first.lk));
     NB = vs.V;
     T = vs.T;
@@ -253,7 +278,8 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
   auto issue = [&]() {
     ZL_LDS char* dst = smem + (issued % kStages) * kTileB;
     const int ntl = (ds.len + 31) >> 5;
-    if (dj == 0) {
+    if (!loader) {
+    } else if (dj == 0) {
       if constexpr (MQ) {
         dma_query_item_mq(a.q, dsi, a.G, dst, wave, lane);
       } else {
@@ -287,10 +313,11 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
   Segment sg = ds;  // the segment being computed
   int cj = 0;       // its current item
   bool first_seg = true;
-  MqColumn col{};   // several new tokens: this lane's column of sg's row block
+  // Several new tokens: this lane's column 16 cb + n of sg's row block.
+  MqColumn col{};
   if constexpr (MQ) {
     sgi = dsi;
-    col = mq_column(sgi, n, 0, a.G, a.Hq, a.causal != 0);
+    col = mq_column(sgi, 16 * cb + n, 0, a.G, a.Hq, a.causal != 0, kMlaMqRowsLog2);
   }
   for (int s = 0; s < kStages - 1 && dmore; ++s) issue();
 
@@ -312,26 +339,27 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
     const ZL_LDS char* it = smem + (i % kStages) * kTileB;
     const int ntl = (sg.len + 31) >> 5;
     if (cj == 0) {
-      // Query item: this wave's half of the k-steps, B operand layout.
+      // Query item: this wave's half of the k-steps of its column block, B
+      // operand layout (column n is query row 16 cb + n of the item).
+      const int r = 16 * cb + n;
 #pragma unroll
       for (int kb = 0; kb < kKHalf; ++kb) {
         const int c = 4 * (kKHalf * kh_own + kb) + g;
-        qop[kb] = __builtin_bit_cast(i16x8, lds_read_b128(it + n * kRowB + (slot(c, n) << 4)));
+        qop[kb] = __builtin_bit_cast(i16x8, lds_read_b128(it + r * kRowB + (slot(c, r) << 4)));
       }
 #pragma unroll
       for (int bb = 0; bb < kBlkPerWave; ++bb) o[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
       sm = SoftmaxState{-INFINITY, 0.f};
     } else {
       const int j = cj - 1;
-      const f32x4 part = half_scores<DT>(it, qop, tb_own, kh_own, n, g);
-      *(ZL_LDS f32x4*)(xchg + wave * 1024 + lane * 16) = part;
+      ZL_LDS char* xc = xchg + cb * (kWaves * 1024) + lane * 16;  // this group's exchange area
+      *(ZL_LDS f32x4*)(xc + wave * 1024) = half_scores<DT>(it, qop, tb_own, kh_own, n, g);
       barrier_lds();  // all score halves in LDS
-      // Waves 0 and 2 hold the halves of token block 0, waves 1 and 3 block 1.
+      // Waves 0 and 2 of the group hold the halves of token block 0, waves 1
+      // and 3 those of block 1.
       f32x4 s[2];
-      s[0] = *(const ZL_LDS f32x4*)(xchg + 0 * 1024 + lane * 16) +
-             *(const ZL_LDS f32x4*)(xchg + 2 * 1024 + lane * 16);
-      s[1] = *(const ZL_LDS f32x4*)(xchg + 1 * 1024 + lane * 16) +
-             *(const ZL_LDS f32x4*)(xchg + 3 * 1024 + lane * 16);
+      s[0] = *(const ZL_LDS f32x4*)(xc + 0 * 1024) + *(const ZL_LDS f32x4*)(xc + 2 * 1024);
+      s[1] = *(const ZL_LDS f32x4*)(xc + 1 * 1024) + *(const ZL_LDS f32x4*)(xc + 3 * 1024);
       float alpha;
       int nvalid = min(32, sg.len - 32 * j);
       if constexpr (MQ) {
@@ -339,14 +367,18 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
         const int j0 = sg.t0 - sg.cs + 32 * j;
         nvalid = min(nvalid, col.lim - j0 + 1);
       }
-      const POperand pop = softmax_update<DT>(s, g, nvalid, a.scale_log2, sm, alpha);
+      bool rescale;
+      const POperand pop = softmax_update<DT>(s, g, nvalid, a.scale_log2, sm, alpha, rescale);
+      if (rescale) {
 #pragma unroll
-      for (int bb = 0; bb < kBlkPerWave; ++bb) o[bb] *= alpha;
+        for (int bb = 0; bb < kBlkPerWave; ++bb) o[bb] *= alpha;
+      }
       pv_blocks<DT, kBlkPerWave, kRowB>(it, pop, n, g, wave * kBlkPerWave, slot_fn, o);
 
       if (j == ntl - 1) {
-        // ---- segment epilogue: lane (g, n) of wave w holds head n, dims
-        // 128w + 16bb + 4g .. +3.  Stores only; the next items are in flight.
+        // ---- segment epilogue: lane (g, n) of wave w in group cb holds
+        // column 16 cb + n, dims 128w + 16bb + 4g .. +3.  Stores only; the
+        // next items are in flight.  A partial slot holds 16 NCB columns.
         const SeqWorkers sw = seq_workers(line, sg.u, sg.b, sg.cs, sg.ce, per);
         const int h0 = sg.u * kHeadsPerUnit;
         const int nh = min(kHeadsPerUnit, a.G - h0);
@@ -363,10 +395,11 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
             if (a.lse && wave == 0 && g == 0) a.lse[row] = lse_v;
           } else {
             const int sl = 2 * w + (first_seg ? 0 : 1);
-            float* po = a.part_o + ((long long)sl * kHeadsPerUnit + n) * kDV + dim0;
+            const int c = 16 * cb + n;
+            float* po = a.part_o + ((long long)sl * (16 * NCB) + c) * kDV + dim0;
 #pragma unroll
             for (int bb = 0; bb < kBlkPerWave; ++bb) *(f32x4*)(po + 16 * bb) = o[bb] * inv;
-            if (wave == 0 && g == 0) a.part_lse[sl * kLseSlot + n] = lse_v;
+            if (wave == 0 && g == 0) a.part_lse[sl * kLseSlot + c] = lse_v;
           }
         }
       }
@@ -378,7 +411,7 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
       first_seg = false;
       if constexpr (MQ) {
         sgi = vs.info(sg.b);
-        col = mq_column(sgi, n, 0, a.G, a.Hq, a.causal != 0);
+        col = mq_column(sgi, 16 * cb + n, 0, a.G, a.Hq, a.causal != 0, kMlaMqRowsLog2);
       }
     }
   }
@@ -390,7 +423,8 @@ template <int DT>
 static void launch_mla_t(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.P), block(64 * kWaves);
   if (a.cu_q)
-    hipLaunchKernelGGL((mla_decode_kernel<DT, false, true>), grid, block, 0, stream, a, a.cu, a.block_table);
+    hipLaunchKernelGGL((mla_decode_kernel<DT, false, true>), grid, dim3(64 * kWaves * column_blocks<true>()), 0,
+                       stream, a, a.cu, a.block_table);
   else if (a.block_table)
     hipLaunchKernelGGL((mla_decode_kernel<DT, true, false>), grid, block, 0, stream, a, a.cu, a.block_table);
   else

@@ -25,8 +25,9 @@
 namespace zl {
 
 // Several new query tokens per sequence (MQ): one workgroup per (key/value
-// head, virtual sequence), for an upper bound on the number of virtual
-// sequences; the workgroups past the batch's count return at once.
+// head, virtual sequence of 2^rows_log2 query rows), for an upper bound on
+// the number of virtual sequences; the workgroups past the batch's count
+// return at once.  A partial slot holds a.slot_cols columns.
 template <int DT, int DV, bool MQ>
 __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a, const int32_t* __restrict__ cu,
                                                           int heads_per_unit, int wg_per_seq, int seqs) {
@@ -37,7 +38,8 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a, const in
   const int b = ub % seqs;
   const int u = ub / seqs;
   const int kvh = u / a.HB, hb = u - (u / a.HB) * a.HB;
-  const int nh = MQ ? kHeadsPerUnit : min(kHeadsPerUnit, a.G - hb * kHeadsPerUnit);
+  const int nh = MQ ? (1 << a.rows_log2) : min(kHeadsPerUnit, a.G - hb * kHeadsPerUnit);
+  const long long sc = a.slot_cols;
   const int h0 = kvh * a.G + hb * kHeadsPerUnit;
   const int item = part * 256 + (int)threadIdx.x;
   const int h = item / C4;
@@ -47,10 +49,10 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a, const in
   long long row;  // output row of this thread's column
   VirtualSeqs vs;
   if constexpr (MQ) {
-    vs.init(a.cu_q, cu, a.B, a.G, a.seg_cost);
+    vs.init(a.cu_q, cu, a.B, a.G, a.seg_cost, a.rows_log2);
     if (b >= vs.V) return;
     const VSeqInfo si = vs.info(b);
-    const MqColumn col = mq_column(si, h, kvh, a.G, a.Hq, false);
+    const MqColumn col = mq_column(si, h, kvh, a.G, a.Hq, false, a.rows_log2);
     if (!col.valid) return;
     NB = vs.V;
     T = vs.T;
@@ -84,8 +86,8 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a, const in
   const int s0 = 2 * w_first;
   const float ls_a = a.part_lse[s0 * kLseSlot + h];
   const float ls_b = a.part_lse[(s0 + 1) * kLseSlot + h];
-  const f32x4 v_a = *(const f32x4*)(a.part_o + ((long long)s0 * kHeadsPerUnit + h) * DV + 4 * c4);
-  const f32x4 v_b = *(const f32x4*)(a.part_o + ((long long)(s0 + 1) * kHeadsPerUnit + h) * DV + 4 * c4);
+  const f32x4 v_a = *(const f32x4*)(a.part_o + (s0 * sc + h) * DV + 4 * c4);
+  const f32x4 v_b = *(const f32x4*)(a.part_o + ((s0 + 1) * sc + h) * DV + 4 * c4);
 
   const int nparts = w_last - w_first + 1;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a, const in
       const int i = min(i0 + j, nparts - 1);  // tail of the batch re-reads the last one
       const int sl = 2 * (w_first + (i == 0 ? 1 : i));  // slot 0 is chosen below
       ls[j] = i0 + j < nparts ? a.part_lse[sl * kLseSlot + h] : -INFINITY;
-      v[j] = *(const f32x4*)(a.part_o + ((long long)sl * kHeadsPerUnit + h) * DV + 4 * c4);
+      v[j] = *(const f32x4*)(a.part_o + (sl * sc + h) * DV + 4 * c4);
     }
     if (i0 == 0) {
       const bool opened = key_first == seq_key(u, b, NB);
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a, const in
 template <int DT, int DV>
 static hipError_t launch_merge_t(const DecodeArgs& a, int max_vseqs, hipStream_t stream) {
   const bool mq = a.cu_q != nullptr;
-  const int hpu = mq ? kHeadsPerUnit : (a.G < kHeadsPerUnit ? a.G : kHeadsPerUnit);
+  const int hpu = mq ? (1 << a.rows_log2) : (a.G < kHeadsPerUnit ? a.G : kHeadsPerUnit);
   const int wg_per_seq = (hpu * (DV / 4) + 255) / 256;
   const int seqs = mq ? max_vseqs : a.B;
   const long long blocks = (long long)a.Hkv * a.HB * seqs * wg_per_seq;

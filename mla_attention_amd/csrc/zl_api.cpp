@@ -25,14 +25,17 @@ struct WsLayout {
   size_t lse_off, out_off, key_off, total;
 };
 
-// Workspace: [part_lse 2P*32 f32][part_o 2P*16*Dv f32][first_key P i32], each
-// part 256-byte aligned: two fp32 partial slots per worker and the key of
-// each run's first segment (see zl_split.h).
+// Workspace: [part_lse 2P*32 f32][part_o 2P*cols*Dv f32][first_key P i32],
+// each part 256-byte aligned: two fp32 partial slots of `cols` query columns
+// per worker (16; 32 for MLA, whose tiles may serve 32 query rows) and the key
+// of each run's first segment (see zl_split.h).
+int max_slot_cols(int dv) { return dv == 512 ? zl::kMlaSlotCols : zl::kHeadsPerUnit; }
+
 WsLayout ws_layout(int workers, int dv) {
   WsLayout w;
   w.lse_off = 0;
   w.out_off = round_up((size_t)2 * workers * zl::kLseSlot * 4, 256);
-  w.key_off = w.out_off + round_up((size_t)2 * workers * zl::kHeadsPerUnit * dv * 4, 256);
+  w.key_off = w.out_off + round_up((size_t)2 * workers * max_slot_cols(dv) * dv * 4, 256);
   w.total = w.key_off + round_up((size_t)workers * 4, 256);
   return w;
 }
@@ -89,6 +92,11 @@ zl_status_t run_decode(zl::DecodeArgs a, Layout layout, int dv, zl_dtype_t dtype
   a.part_o = reinterpret_cast<float*>(ws + wl.out_off);
   a.first_key = reinterpret_cast<int*>(ws + wl.key_off);
   a.seg_cost = layout == zl::kMla576 ? zl::kSegCostMla : zl::kSegCostGqa;
+  // Slot width the kernels write: 32 columns only for MLA with several new
+  // tokens per sequence (the workspace is sized for the widest).
+  const bool wide = layout == zl::kMla576 && a.cu_q != nullptr;
+  a.slot_cols = wide ? zl::kMlaSlotCols : zl::kHeadsPerUnit;
+  a.rows_log2 = wide ? zl::kMlaMqRowsLog2 : zl::kMqRowsLog2;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (phases & 1) e = zl::launch_decode(a, layout, dtype, st);
@@ -130,19 +138,21 @@ struct Varlen {
   int causal = 0;
 };
 
-// Upper bound on the virtual sequences (blocks of 16 query rows of one
-// sequence) of a call: sum over b of ceil(nq_b * G / 16).
-long long max_virtual_seqs(const Varlen& vl, int batch, int group) {
-  return ((long long)vl.total_q * group + 15LL * batch + 15) / 16;
+// Upper bound on the virtual sequences (blocks of R = 2^rows_log2 query rows
+// of one sequence) of a call: sum over b of ceil(nq_b * G / R).
+long long max_virtual_seqs(const Varlen& vl, int batch, int group, int rows_log2) {
+  const long long R = 1LL << rows_log2;
+  return ((long long)vl.total_q * group + (R - 1) * batch + R - 1) / R;
 }
 
-zl_status_t check_varlen(const Varlen& vl, int batch, int group, int max_seqlen_k, int seg_cost) {
+zl_status_t check_varlen(const Varlen& vl, int batch, int group, int max_seqlen_k, int seg_cost,
+                         int rows_log2) {
   if (!vl.cu_q) return ZL_OK;
   if (!aligned(vl.cu_q, 4) || vl.total_q < 0 || (vl.causal != 0 && vl.causal != 1))
     return ZL_ERR_INVALID_ARGUMENT;
   // Positions of the work line (virtual tokens plus the per-sequence cost)
   // are 32-bit inside the kernels.
-  const long long V = max_virtual_seqs(vl, batch, group);
+  const long long V = max_virtual_seqs(vl, batch, group, rows_log2);
   if (V * ((long long)max_seqlen_k + seg_cost) >= (1LL << 31)) return ZL_ERR_UNSUPPORTED;
   return ZL_OK;
 }
@@ -177,7 +187,8 @@ zl_status_t gqa_impl(const void* q, const void* k_cache, const void* v_cache, co
   int shift = 0;
   const zl_status_t sp = check_paging(pg, max_seqlen_k, shift);
   if (sp != ZL_OK) return sp;
-  const zl_status_t sv = check_varlen(vl, batch, num_q_heads / num_kv_heads, max_seqlen_k, zl::kSegCostGqa);
+  const zl_status_t sv = check_varlen(vl, batch, num_q_heads / num_kv_heads, max_seqlen_k, zl::kSegCostGqa,
+                                       zl::kMqRowsLog2);
   if (sv != ZL_OK) return sv;
   if (batch == 0 || (vl.cu_q && vl.total_q == 0)) return ZL_OK;
   // k_cache / v_cache may be NULL only when every sequence is empty (the
@@ -206,7 +217,7 @@ zl_status_t gqa_impl(const void* q, const void* k_cache, const void* v_cache, co
   a.causal = vl.causal;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   return run_decode(a, layout, head_dim, dtype, phases, workspace, workspace_bytes, stream,
-                    (int)max_virtual_seqs(vl, batch, a.G));
+                    (int)max_virtual_seqs(vl, batch, a.G, zl::kMqRowsLog2));
 }
 
 }  // namespace
@@ -294,7 +305,7 @@ zl_status_t mla_impl(const void* q, const void* kv_cache, const Paging& pg, cons
   int shift = 0;
   const zl_status_t sp = check_paging(pg, max_seqlen_k, shift);
   if (sp != ZL_OK) return sp;
-  const zl_status_t sv = check_varlen(vl, batch, num_q_heads, max_seqlen_k, zl::kSegCostMla);
+  const zl_status_t sv = check_varlen(vl, batch, num_q_heads, max_seqlen_k, zl::kSegCostMla, zl::kMlaMqRowsLog2);
   if (sv != ZL_OK) return sv;
   if (batch == 0 || (vl.cu_q && vl.total_q == 0)) return ZL_OK;
   if (!q || !cu_seqlens || !out) return ZL_ERR_INVALID_ARGUMENT;  // kv_cache: see above
@@ -321,7 +332,7 @@ zl_status_t mla_impl(const void* q, const void* kv_cache, const Paging& pg, cons
   a.causal = vl.causal;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   return run_decode(a, zl::kMla576, kv_lora_rank, dtype, phases, workspace, workspace_bytes, stream,
-                    (int)max_virtual_seqs(vl, batch, num_q_heads));
+                    (int)max_virtual_seqs(vl, batch, num_q_heads, zl::kMlaMqRowsLog2));
 }
 
 }  // namespace

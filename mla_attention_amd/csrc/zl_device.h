@@ -52,9 +52,18 @@ __device__ __forceinline__ uint16_t to16(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
+// Two values rounded to nearest-even and packed (lo in bits 0-15): one
+// v_cvt_pk_{f16,bf16}_f32 on gfx950.
 template <int DT>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return (uint32_t)to16<DT>(lo) | ((uint32_t)to16<DT>(hi) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  if constexpr (DT == kF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Hardware 2^x (v_exp_f32); 2^-inf = 0.

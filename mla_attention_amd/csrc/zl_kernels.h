@@ -13,6 +13,13 @@ constexpr int kHeadsPerUnit = 16;  // query heads packed into one MFMA N dimensi
 // Floats per partial-lse slot: one 128-byte cache line, so no two slots (which
 // different XCDs write and read) ever share a line.
 constexpr int kLseSlot = 32;
+// Rows per virtual sequence with several new tokens per sequence (zl_split.h):
+// 16 for the GQA kernels, 32 for MLA, whose tiles then serve two blocks of 16
+// query columns.  The MLA partial slots hold 32 columns in every mode.
+constexpr int kMqRowsLog2 = 4;
+constexpr int kMlaMqRowsLog2 = 5;
+constexpr int kMlaSlotCols = 32;
+static_assert(kMlaSlotCols <= kLseSlot, "a slot's lse values fit its line");
 
 enum Layout {
   kGqaD64 = 0,   // K, V [T, Hkv, 64]
@@ -28,8 +35,8 @@ struct DecodeArgs {
   const int32_t* cu;    // [B + 1]
   uint16_t* out;        // [B, Hq, Dv]
   float* lse;           // [B, Hq] or nullptr
-  float* part_o;        // [2P, 16, Dv]
-  float* part_lse;      // [2P, kLseSlot] (first 16 used)
+  float* part_o;        // [2P, slot_cols, Dv]
+  float* part_lse;      // [2P, kLseSlot] (first slot_cols used)
   int* first_key;       // [P]: (unit, sequence) of each run's first segment
   // Paged caches (block table): k / v are page pools [pages, 2^page_shift,
   // row]; token i of sequence b lives in page block_table[b*max_pages +
@@ -40,10 +47,12 @@ struct DecodeArgs {
   // Several new query tokens per sequence (cu_q != nullptr): q, out are
   // [cu_q[B], Hq, D] and lse [cu_q[B], Hq]; cu holds the cache bounds; the
   // work units are the key/value heads (HB = 1) and the batch is cut into
-  // virtual sequences of 16 query rows (zl_split.h).  causal: new token i of
+  // virtual sequences of 2^rows_log2 query rows (zl_split.h).  causal: new token i of
   // nq sees cache rows 0 .. lk - nq + i.
   const int32_t* cu_q;
   int causal;
+  int rows_log2;        // rows per virtual sequence: 2^rows_log2 (16 or 32)
+  int slot_cols;        // query columns per partial slot (16, or 32 for MLA)
   int B, Hq, Hkv, G, HB, P;
   int seg_cost;         // phantom positions per sequence (zl_split.h)
   float scale_log2;     // softmax_scale * log2(e)

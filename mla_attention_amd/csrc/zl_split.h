@@ -329,9 +329,11 @@ struct MqColumn {
   int lim;
 };
 
-__device__ __forceinline__ MqColumn mq_column(const VSeqInfo& s, int n, int kvh, int G, int Hq, bool causal) {
+// (Column n counts from the block's first row; blocks hold 2^rows_log2 rows.)
+__device__ __forceinline__ MqColumn mq_column(const VSeqInfo& s, int n, int kvh, int G, int Hq, bool causal,
+                                              int rows_log2 = 4) {
   const int last = s.nq * G - 1;  // the sequence's last query row
-  const int r = 16 * s.hb + n;
+  const int r = (s.hb << rows_log2) + n;
   const int rr = r < last ? r : last;
   const int qi = rr / G;
   MqColumn c;

@@ -58,28 +58,51 @@ struct POperand {
   i16x8 lo;
 };
 
+// Largest rise (log2 units) of a head's running max that the update absorbs
+// without moving its reference max: the probabilities are then at most
+// 2^kLazyMax, well inside the range of both 16-bit formats and of the fp32
+// sums, and most tiles skip the rescale of the accumulators (an exact
+// identity: out = sum 2^(x - m) v / sum 2^(x - m) for any reference m).
+constexpr float kLazyMax = 8.f;
+
 // Online-softmax update with the tile's scores.  Tokens at or past nvalid are
 // masked.  Returns the P^T operand (16-bit probabilities in PV k-slot order)
-// and the factor alpha by which the accumulators must be rescaled.
+// and the factor alpha by which the accumulators must be rescaled; rescale
+// (wave-uniform) is false when alpha is 1 in every lane.
 template <int DT>
 __device__ __forceinline__ POperand softmax_update(const f32x4 (&s)[2], int g, int nvalid,
-                                                   float scale_log2, SoftmaxState& st, float& alpha) {
+                                                   float scale_log2, SoftmaxState& st, float& alpha,
+                                                   bool& rescale) {
   float x[8];
   float tmax = -INFINITY;
+  if (__builtin_amdgcn_ballot_w64(nvalid < 32) == 0) {
+    // Every lane's tile is full: no mask.
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb)
+    for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tok = 16 * tb + 4 * g + r;
-      float xv = s[tb][r] * scale_log2;
-      xv = tok < nvalid ? xv : -INFINITY;
-      x[4 * tb + r] = xv;
-      tmax = fmaxf(tmax, xv);
-    }
+      for (int r = 0; r < 4; ++r) {
+        x[4 * tb + r] = s[tb][r] * scale_log2;
+        tmax = fmaxf(tmax, x[4 * tb + r]);
+      }
+  } else {
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = 16 * tb + 4 * g + r;
+        const float xv = tok < nvalid ? s[tb][r] * scale_log2 : -INFINITY;
+        x[4 * tb + r] = xv;
+        tmax = fmaxf(tmax, xv);
+      }
+  }
   tmax = max_over_groups(tmax);
-  const float m_new = fmaxf(st.m, tmax);
+  // The reference max moves only when the tile's max passes it by more than
+  // kLazyMax (always for the first finite max: -inf + kLazyMax = -inf).
+  const bool grow = tmax > st.m + kLazyMax;
+  const float m_new = grow ? tmax : st.m;
   const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-  alpha = exp2_fast(st.m - m_use);
+  alpha = grow ? exp2_fast(st.m - m_use) : 1.f;
+  rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
   float psum = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -94,14 +117,15 @@ __device__ __forceinline__ POperand softmax_update(const f32x4 (&s)[2], int g, i
   for (int i = 0; i < 4; ++i) pw[i] = pack2<DT>(x[2 * i], x[2 * i + 1]);
   p.hi = __builtin_bit_cast(i16x8, pw);
   if constexpr (DT == kBF16) {
+    // lo = x - hi, exact in fp32; hi read back from the packed pairs.
+    u32x4 pl;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t h = (uint32_t)to16<DT>(x[i]) << 16;  // hi as fp32
-      x[i] -= __builtin_bit_cast(float, h);               // exact residual
+    for (int i = 0; i < 4; ++i) {
+      const float h0 = __builtin_bit_cast(float, pw[i] << 16);
+      const float h1 = __builtin_bit_cast(float, pw[i] & 0xffff0000u);
+      pl[i] = pack2<DT>(x[2 * i] - h0, x[2 * i + 1] - h1);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pw[i] = pack2<DT>(x[2 * i], x[2 * i + 1]);
-    p.lo = __builtin_bit_cast(i16x8, pw);
+    p.lo = __builtin_bit_cast(i16x8, pl);
   } else {
     p.lo = p.hi;  // unused
   }

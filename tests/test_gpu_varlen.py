@@ -113,6 +113,11 @@ MLA_CASES = [
     ([70, 150], [3, 1], 32, torch.bfloat16),
     ([5, 64], [9, 64], 16, torch.bfloat16),      # more new tokens than rows; a whole prompt
     ([(i * 53) % 90 for i in range(70)], [(i * 5) % 3 for i in range(70)], 16, torch.bfloat16),
+    # MLA tiles serve blocks of 32 query rows (two MFMA column blocks):
+    ([300, 45], [3, 5], 16, torch.float16),      # 48 and 80 rows: a half-full last block
+    ([130], [4], 8, torch.bfloat16),             # 4 tokens (4 causal limits) in one block
+    ([90, 200], [2, 2], 128, torch.float16),     # 8 blocks per sequence
+    ([61, 0, 33], [1, 2, 1], 16, torch.float16), # an empty cache with new tokens
 ]
 
 
@@ -121,6 +126,12 @@ def test_mla_varlen(lens, q_lens, H, dt):
     x = workloads.make_inputs(spec_mla(lens, H, dt))
     vq = workloads.make_varlen_query(x, q_lens, seed=len(lens))
     check(x, vq, f"mla varlen {lens[:6]} q {q_lens[:6]} H{H} {dt}")
+
+
+def test_mla_varlen_without_mask():
+    x = workloads.make_inputs(spec_mla([40, 300, 7], 16, torch.bfloat16))
+    vq = workloads.make_varlen_query(x, [3, 20, 9], seed=4)
+    check(x, vq, "mla varlen, no mask", causal=False)
 
 
 @pytest.mark.parametrize("workers", [8, 64, 256, 2048])
