@@ -166,11 +166,21 @@ __device__ __forceinline__ void pf_pv(const ZL_LDS char* vt, const POperand (&po
   }
 }
 
-// Online-softmax update of the wave's four column blocks at once (as
-// softmax_update in zl_tile.h per block).  The four blocks are independent, so
-// every step is written across them: the reductions and exponentials form four
+// The group maxima of the wave's column blocks (one overload per count).
+[[maybe_unused]] __device__ __forceinline__ void max_over_groups_n(float (&x)[2]) { max_over_groups2(x); }
+[[maybe_unused]] __device__ __forceinline__ void max_over_groups_n(float (&x)[4]) { max_over_groups4(x); }
+
+// Online-softmax update of the wave's column blocks at once (as
+// softmax_update in zl_tile.h per block).  The blocks are independent, so
+// every step is written across them: the reductions and exponentials form
 // interleavable chains instead of one long one.  The token mask is compiled
 // in only where a tile needs it.
+//
+// scale_log2 is never negative here (the kernel negates the query operands
+// when the softmax scale is), so the scaled maximum is the raw maximum times
+// the scale and each probability is 2^fma(s, scale, -m): one instruction
+// per score instead of a multiply and a subtract.  Masked scores are zeroed
+// after the exponential (a zero scale would turn -inf into NaN).
 template <int DT, bool MASK>
 __device__ __forceinline__ void pf_softmax4(const f32x4 (&s)[kPfCB][2], int g, const int (&nvalid)[kPfCB],
                                             float scale_log2, SoftmaxState (&st)[kPfCB], float (&alpha)[kPfCB],
@@ -186,25 +196,22 @@ __device__ __forceinline__ void pf_softmax4(const f32x4 (&s)[kPfCB][2], int g, c
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int cb = 0; cb < kPfCB; ++cb) {
-        float xv = s[cb][tb][r] * scale_log2;
+        float xv = s[cb][tb][r];
         if constexpr (MASK) xv = 16 * tb + 4 * g + r < nvalid[cb] ? xv : -INFINITY;
-        x[cb][4 * tb + r] = xv;
-        tmax[cb] = fmaxf(tmax[cb], xv);
+        tmax[cb] = fmaxf(tmax[cb], xv);  // (MFMA results: the compiler forms v_max3)
       }
-  {
-    float t4[4];
+  max_over_groups_n(tmax);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t4[i] = tmax[i % kPfCB];
-    max_over_groups4(t4);
-#pragma unroll
-    for (int cb = 0; cb < kPfCB; ++cb) tmax[cb] = t4[cb];
-  }
+  for (int cb = 0; cb < kPfCB; ++cb) tmax[cb] = tmax[cb] == -INFINITY ? -INFINITY : tmax[cb] * scale_log2;
+  // Lazy rescale (kLazyMax, zl_tile.h): a column's reference max moves only
+  // when the tile's max passes it by more than 2^kLazyMax.
   float m_use[kPfCB], psum[kPfCB];
 #pragma unroll
   for (int cb = 0; cb < kPfCB; ++cb) {
-    const float m_new = fmaxf(st[cb].m, tmax[cb]);
+    const bool grow = tmax[cb] > st[cb].m + kLazyMax;
+    const float m_new = grow ? tmax[cb] : st[cb].m;
     m_use[cb] = (m_new == -INFINITY) ? 0.f : m_new;
-    alpha[cb] = exp2_fast(st[cb].m - m_use[cb]);
+    alpha[cb] = grow ? exp2_fast(st[cb].m - m_use[cb]) : 1.f;
     st[cb].m = m_new;
     psum[cb] = 0.f;
   }
@@ -212,8 +219,10 @@ __device__ __forceinline__ void pf_softmax4(const f32x4 (&s)[kPfCB][2], int g, c
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int cb = 0; cb < kPfCB; ++cb) {
-      x[cb][i] = exp2_fast(x[cb][i] - m_use[cb]);
-      psum[cb] += x[cb][i];
+      float xv = exp2_fast(__builtin_fmaf(s[cb][i >> 2][i & 3], scale_log2, -m_use[cb]));
+      if constexpr (MASK) xv = 16 * (i >> 2) + 4 * g + (i & 3) < nvalid[cb] ? xv : 0.f;
+      x[cb][i] = xv;
+      psum[cb] += xv;
     }
 #pragma unroll
   for (int cb = 0; cb < kPfCB; ++cb) {
@@ -223,11 +232,13 @@ __device__ __forceinline__ void pf_softmax4(const f32x4 (&s)[kPfCB][2], int g, c
     for (int i = 0; i < 4; ++i) pw[i] = pack2<DT>(x[cb][2 * i], x[cb][2 * i + 1]);
     p[cb].hi = __builtin_bit_cast(i16x8, pw);
     if constexpr (DT == kBF16) {
+      // lo = x - hi (exact), hi read back from the packed pairs
+      u32x4 pl;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[cb][i] -= __builtin_bit_cast(float, (uint32_t)to16<DT>(x[cb][i]) << 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pw[i] = pack2<DT>(x[cb][2 * i], x[cb][2 * i + 1]);
-      p[cb].lo = __builtin_bit_cast(i16x8, pw);
+      for (int i = 0; i < 4; ++i)
+        pl[i] = pack2<DT>(x[cb][2 * i] - __builtin_bit_cast(float, pw[i] << 16),
+                          x[cb][2 * i + 1] - __builtin_bit_cast(float, pw[i] & 0xffff0000u));
+      p[cb].lo = __builtin_bit_cast(i16x8, pl);
     } else {
       p[cb].lo = p[cb].hi;
     }
@@ -316,6 +327,16 @@ prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, int nblocks) {
   for (int cb = 0; cb < kPfCB; ++cb)
 #pragma unroll
     for (int kb = 0; kb < GE::KSTEPS; ++kb) touch(qop[cb][kb]);
+  // The softmax takes a non-negative scale: a negative one is moved onto the
+  // query operands (sign flip of every 16-bit value, exact).
+  float scale_log2 = a.scale_log2;
+  if (scale_log2 < 0.f) {
+    scale_log2 = -scale_log2;
+#pragma unroll
+    for (int cb = 0; cb < kPfCB; ++cb)
+#pragma unroll
+      for (int kb = 0; kb < GE::KSTEPS; ++kb) qop[cb][kb] = qop[cb][kb] ^ (short)0x8000;
+  }
 
   const uint32_t row_bytes = (uint32_t)a.Hkv * D * 2;
   const char* kseq = (const char*)(a.k + ((long long)si.k0 * a.Hkv + kvh) * D);
@@ -379,14 +400,14 @@ prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, int nblocks) {
     const bool full = nv == 32 && 32 * i + 31 <= lim_min;
     if (more && full) {
       pf_scores<DT, D>(knext, qop, n, g, slot, s_nxt);
-      pf_softmax4<DT, false>(s_cur, g, nvc, a.scale_log2, sm, alpha, pop);
+      pf_softmax4<DT, false>(s_cur, g, nvc, scale_log2, sm, alpha, pop);
       interleave_scores_softmax<D>();
     } else if (more) {
       pf_scores<DT, D>(knext, qop, n, g, slot, s_nxt);
-      pf_softmax4<DT, true>(s_cur, g, nvc, a.scale_log2, sm, alpha, pop);
+      pf_softmax4<DT, true>(s_cur, g, nvc, scale_log2, sm, alpha, pop);
       interleave_scores_softmax<D>();
     } else {
-      pf_softmax4<DT, true>(s_cur, g, nvc, a.scale_log2, sm, alpha, pop);
+      pf_softmax4<DT, true>(s_cur, g, nvc, scale_log2, sm, alpha, pop);
     }
 #pragma unroll
     for (int cb = 0; cb < kPfCB; ++cb) {

@@ -105,14 +105,23 @@ __device__ __forceinline__ void lane_swap32(uint32_t& a, uint32_t& b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
 
+// v_max_f32 written out: fmaxf on values that come out of inline asm costs
+// two extra canonicalising maxes (IEEE mode quiets signalling NaNs), which
+// the scores and maxima here (finite or -inf) never need.
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 __device__ __forceinline__ float max_over_groups(float x) {
   uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
   lane_swap16(a, b);
-  x = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  x = vmax(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
   a = __builtin_bit_cast(uint32_t, x);
   b = a;
   lane_swap32(a, b);
-  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  return vmax(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 
 // max_over_groups of four independent values at once: the four swaps of each
@@ -129,7 +138,7 @@ __device__ __forceinline__ void max_over_groups4(float (&x)[4]) {
       : "+v"(a[0]), "+v"(b[0]), "+v"(a[1]), "+v"(b[1]), "+v"(a[2]), "+v"(b[2]), "+v"(a[3]), "+v"(b[3]));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    x[i] = fmaxf(__builtin_bit_cast(float, a[i]), __builtin_bit_cast(float, b[i]));
+    x[i] = vmax(__builtin_bit_cast(float, a[i]), __builtin_bit_cast(float, b[i]));
     a[i] = b[i] = __builtin_bit_cast(uint32_t, x[i]);
   }
   asm(
@@ -137,7 +146,25 @@ __device__ __forceinline__ void max_over_groups4(float (&x)[4]) {
       "v_permlane32_swap_b32 %4, %5\n\tv_permlane32_swap_b32 %6, %7"
       : "+v"(a[0]), "+v"(b[0]), "+v"(a[1]), "+v"(b[1]), "+v"(a[2]), "+v"(b[2]), "+v"(a[3]), "+v"(b[3]));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) x[i] = fmaxf(__builtin_bit_cast(float, a[i]), __builtin_bit_cast(float, b[i]));
+  for (int i = 0; i < 4; ++i) x[i] = vmax(__builtin_bit_cast(float, a[i]), __builtin_bit_cast(float, b[i]));
+}
+
+// The same for two values.
+__device__ __forceinline__ void max_over_groups2(float (&x)[2]) {
+  uint32_t a[2], b[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) a[i] = b[i] = __builtin_bit_cast(uint32_t, x[i]);
+  asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_permlane16_swap_b32 %2, %3"
+      : "+v"(a[0]), "+v"(b[0]), "+v"(a[1]), "+v"(b[1]));
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    x[i] = vmax(__builtin_bit_cast(float, a[i]), __builtin_bit_cast(float, b[i]));
+    a[i] = b[i] = __builtin_bit_cast(uint32_t, x[i]);
+  }
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\tv_permlane32_swap_b32 %2, %3"
+      : "+v"(a[0]), "+v"(b[0]), "+v"(a[1]), "+v"(b[1]));
+#pragma unroll
+  for (int i = 0; i < 2; ++i) x[i] = vmax(__builtin_bit_cast(float, a[i]), __builtin_bit_cast(float, b[i]));
 }
 
 __device__ __forceinline__ float sum_over_groups(float x) {

@@ -3,6 +3,7 @@ against the fp64 oracle on identical seeded inputs: whole prompts, chunks of
 prompts, mixed batches, no mask, more new tokens than cache rows, empty
 sequences, G from 1 to 8, both head dims and both 16-bit types; a long
 prompt at full size on sampled rows."""
+import dataclasses
 import math
 
 import numpy as np
@@ -82,6 +83,17 @@ def test_prefill_without_mask():
     out, lse = run(x, vq, causal=False)
     ro, rl = oracle_rows(x, vq, causal=False)
     gate(out, ro, torch.float16, lse, rl, where="prefill, no mask")
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+def test_prefill_negative_and_zero_scale(scale):
+    """A negative softmax scale (the kernel moves its sign onto the query
+    operands) and a zero scale (uniform weights over the visible keys)."""
+    x, vq = make([300, 41], [100, 41], 8, 2, 128, torch.bfloat16)
+    x.spec = dataclasses.replace(x.spec, scale=float(np.float32(scale)))
+    out, lse = run(x, vq)
+    ro, rl = oracle_rows(x, vq)
+    gate(out, ro, torch.bfloat16, lse, rl, where=f"prefill, scale {scale}")
 
 
 def test_prefill_agrees_with_the_several_tokens_path():
