@@ -228,6 +228,20 @@ def main():
     kern_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]))
     merge_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]))
     achieved_gbs = kv_bytes / (kern_ms * 1e-3) / 1e9
+
+    # Per-call spread: K more whole calls, each between two events (the
+    # events add a little to each interval; the headline is the span above).
+    evc = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        evc[i][0].record(stream)
+        step(args.warmup + 2 * K + i)
+        evc[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_call_us = np.array([a.elapsed_time(b) * 1e3 for a, b in evc])
+    spread = {"p10": round(float(np.percentile(per_call_us, 10)), 2),
+              "p50": round(float(np.percentile(per_call_us, 50)), 2),
+              "p90": round(float(np.percentile(per_call_us, 90)), 2)}
     workload = spec.name + (f"+paged{args.paged}" if paged else "") + (f"+q{args.q_len}" if vq else "")
     prof = profile_record(workload)
 
@@ -246,6 +260,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
+        "us_per_call_percentiles": spread,
         "hbm_peak_frac": round(value_gbs / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -424,14 +439,22 @@ def bench_codec(args):
 
 
 def cpu_baseline(x, spec, target_s: float):
-    """The fp64 oracle on all host cores over whole sequences of the same
-    batch, added until about target_s seconds of work; reported in the
-    metric's unit (KV GB/s of the sample)."""
+    """The fp64 oracle over whole sequences of the same batch, on all host
+    cores (about target_s seconds of work), then on one core (a third of
+    that); reported in the metric's unit (KV GB/s of the sample)."""
+    import oracle
+
+    rec = oracle_rate(x, spec, target_s, oracle.max_threads())
+    one = oracle_rate(x, spec, target_s / 3, 1)
+    rec["single_core"] = {"value": one["value"], "unit": one["unit"], "cores": 1, "sample": one["sample"]}
+    return rec
+
+
+def oracle_rate(x, spec, target_s: float, threads: int):
     import numpy as np
 
     import oracle
 
-    threads = oracle.max_threads()
     cu = x.cu_seqlens.numpy()
     dt = oracle.F16 if spec.dtype == "f16" else oracle.BF16
     row_bytes = (spec.head_dim_k * 2 if spec.kind == "mla"
@@ -461,7 +484,8 @@ def cpu_baseline(x, spec, target_s: float):
         "cores": threads,
         "kind": "oracle",
         "sample": f"{nseq} whole sequences of this batch (all {spec.num_q_heads} query heads each, "
-                  f"{done_bytes} KV bytes) through the fp64 C oracle, OpenMP over heads, {elapsed:.1f} s",
+                  f"{done_bytes} KV bytes) through the fp64 C oracle, OpenMP over heads on {threads} "
+                  f"thread{'s' if threads > 1 else ''}, {elapsed:.1f} s",
         "us_per_step_equiv": round(x.kv_bytes() / (done_bytes / elapsed) * 1e6, 1),
     }
 
