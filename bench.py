@@ -111,8 +111,8 @@ def copy_calibration(mib: int, launches: int):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU: the decode kernel is measured on "
-                                   "one GPU's share; multi-GPU scaling is not part of it",
+        print(json.dumps({"error": "bench.py measures one GPU: the decode kernel runs on one GPU's share of "
+                                   "the batch (sharding across GPUs is a design note, not a code path)",
                           "n_gpus_requested": args.gpus}))
         sys.exit(2)
 
@@ -132,7 +132,7 @@ def main():
     import mla_attention_amd as zl
     import workloads
 
-    spec = workloads.CONFIGS[args.config]
+    spec = workloads.WORKLOADS[args.config]
     dev = torch.device("cuda:0")
     x = workloads.make_inputs(spec)
     kv_bytes = x.kv_bytes()
@@ -314,7 +314,7 @@ def bench_prefill(args):
     import mla_attention_amd as zl
     import workloads
 
-    spec0 = workloads.CONFIGS[args.config]
+    spec0 = workloads.WORKLOADS[args.config]
     L, B = args.prefill, args.prefill_batch
     spec = workloads.with_shape(spec0, batch=B, lens=tuple([L] * B))
     dev = torch.device("cuda:0")

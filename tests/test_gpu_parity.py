@@ -79,14 +79,14 @@ def sample_pairs(spec):
 
 # ------------------------------------------------------------ the five configs
 def test_config1_full():
-    x = workloads.make_inputs(workloads.CONFIGS[1])
+    x = workloads.make_inputs(workloads.WORKLOADS[1])
     st = check_full(x, "config 1")
     print("config 1", st)
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_full_size_config_sampled(cfg):
-    spec = workloads.CONFIGS[cfg]
+    spec = workloads.WORKLOADS[cfg]
     print(f"config {cfg}: {spec.name}", flush=True)
     x = workloads.make_inputs(spec)
     out, lse = run_gpu(x)
@@ -152,19 +152,19 @@ def test_mla_edge_shapes(lens, H, dt):
 @pytest.mark.parametrize("workers", [8, 16, 64, 256, 2048])
 def test_any_worker_count_gives_the_same_attention(workers):
     """Invariance to how the batch is cut between workers (split-KV + combine)."""
-    spec = workloads.with_shape(workloads.CONFIGS[2], batch=6, lens=("uniform", 1, 3000))
+    spec = workloads.with_shape(workloads.WORKLOADS[2], batch=6, lens=("uniform", 1, 3000))
     x = workloads.make_inputs(spec, seed=21)
     check_full(x, f"gqa workers={workers}", num_workers=workers)
-    mspec = workloads.with_shape(workloads.CONFIGS[5], batch=3, lens=("uniform", 1, 1500))
+    mspec = workloads.with_shape(workloads.WORKLOADS[5], batch=3, lens=("uniform", 1, 1500))
     xm = workloads.make_inputs(mspec, seed=22)
     check_full(xm, f"mla workers={workers}", num_workers=workers)
 
 
 def test_peaked_scores():
-    spec = workloads.with_shape(workloads.CONFIGS[1], dtype="bf16")
+    spec = workloads.with_shape(workloads.WORKLOADS[1], dtype="bf16")
     x = workloads.make_inputs(spec, q_mult=8.0)
     check_full(x, "peaked gqa")
-    mspec = workloads.with_shape(workloads.CONFIGS[5], batch=2, lens=(40, 300))
+    mspec = workloads.with_shape(workloads.WORKLOADS[5], batch=2, lens=(40, 300))
     xm = workloads.make_inputs(mspec, q_mult=4.0)
     check_full(xm, "peaked mla")
 
@@ -172,7 +172,7 @@ def test_peaked_scores():
 def test_repeated_calls_reuse_workspace_and_are_bitwise_deterministic():
     """Same inputs -> bitwise-identical output on every call; the workspace
     (no initialisation needed) carries nothing between calls."""
-    spec = workloads.with_shape(workloads.CONFIGS[3], batch=8, lens=("uniform", 100, 3000))
+    spec = workloads.with_shape(workloads.WORKLOADS[3], batch=8, lens=("uniform", 100, 3000))
     x = workloads.make_inputs(spec, seed=31)
     B, H, D = x.q.shape
     ws = zl().new_workspace(zl().zl_decode_attn_workspace_size(B, H, 1, D, x.max_seqlen, x.q.dtype), DEV)
@@ -208,7 +208,7 @@ def test_combine_entry_point(S, Dv, dt):
 
 
 def test_combine_of_oracle_partials_equals_unsplit_attention():
-    spec = workloads.with_shape(workloads.CONFIGS[2], batch=4, lens=(100, 257, 64, 1))
+    spec = workloads.with_shape(workloads.WORKLOADS[2], batch=4, lens=(100, 257, 64, 1))
     x = workloads.make_inputs(spec, seed=41)
     S = 3
     B, Hq, D = x.q.shape
@@ -314,7 +314,7 @@ def test_mla_paged(lens, H, dt, ps):
 
 @pytest.mark.parametrize("cfg,ps", [(2, 16), (5, 64)])
 def test_full_size_paged_sampled(cfg, ps):
-    spec = workloads.CONFIGS[cfg]
+    spec = workloads.WORKLOADS[cfg]
     print(f"paged config {cfg} ps{ps}: {spec.name}", flush=True)
     x = workloads.make_inputs(spec)
     p = workloads.make_paged(x, ps, seed=cfg)

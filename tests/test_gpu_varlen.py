@@ -136,11 +136,11 @@ def test_mla_varlen_without_mask():
 
 @pytest.mark.parametrize("workers", [8, 64, 256, 2048])
 def test_any_worker_count_gives_the_same_attention(workers):
-    x = workloads.make_inputs(workloads.with_shape(workloads.CONFIGS[2], batch=5, lens=("uniform", 1, 2000)),
+    x = workloads.make_inputs(workloads.with_shape(workloads.WORKLOADS[2], batch=5, lens=("uniform", 1, 2000)),
                               seed=23)
     vq = workloads.make_varlen_query(x, [1, 4, 16, 2, 7], seed=5)
     check(x, vq, f"gqa varlen workers={workers}", num_workers=workers)
-    xm = workloads.make_inputs(workloads.with_shape(workloads.CONFIGS[5], batch=3, lens=("uniform", 1, 1500)),
+    xm = workloads.make_inputs(workloads.with_shape(workloads.WORKLOADS[5], batch=3, lens=("uniform", 1, 1500)),
                                seed=24)
     vqm = workloads.make_varlen_query(xm, [2, 1, 3], seed=6)
     check(xm, vqm, f"mla varlen workers={workers}", num_workers=workers)
@@ -150,7 +150,7 @@ def test_any_worker_count_gives_the_same_attention(workers):
 def test_one_new_token_gives_the_decode_bits(cfg):
     """With one new token per sequence the virtual sequences are the decode
     batch itself, so the arithmetic, and the bits, are those of decode."""
-    x = workloads.make_inputs(workloads.CONFIGS[cfg])
+    x = workloads.make_inputs(workloads.WORKLOADS[cfg])
     vq = workloads.VarlenQuery(np.ones(x.spec.batch, dtype=np.int64),
                                workloads.cu_from_lens([1] * x.spec.batch), x.q.clone())
     out, lse = run_gpu(x, vq)
@@ -170,7 +170,7 @@ def test_full_size_draft_tokens_sampled(cfg, q_len):
     """Full-size batches with q_len new tokens per sequence (draft-token
     verification), compared on sampled rows: every sequence, its first and
     last new token, and heads spanning every key/value head."""
-    spec = workloads.CONFIGS[cfg]
+    spec = workloads.WORKLOADS[cfg]
     print(f"config {cfg}, {q_len} new tokens per sequence", flush=True)
     x = workloads.make_inputs(spec)
     vq = workloads.make_varlen_query(x, [q_len] * spec.batch, seed=cfg)

@@ -90,7 +90,7 @@ def test_matches_torch_sdpa_float64(dtype, Hq, Hkv, D):
 
 
 def test_config1_matches_torch_sdpa():
-    x = workloads.make_inputs(workloads.CONFIGS[1])
+    x = workloads.make_inputs(workloads.WORKLOADS[1])
     out, lse = run_gqa(x.q, x.k, x.v, x.cu_seqlens, 2, x.spec.scale, torch.float16)
     ro, rl = sdpa_reference(x.q, x.k, x.v, x.cu_seqlens, 2, x.spec.scale)
     np.testing.assert_allclose(out, ro, rtol=1e-12, atol=1e-13)
@@ -432,7 +432,7 @@ def test_gather_paged_hand_example():
 def test_gather_paged_inverts_the_pool_layout():
     """The oracle's gather undoes the shuffled page pool built by the input
     generator (an independent scatter), for several page sizes."""
-    x = workloads.make_inputs(workloads.CONFIGS[1])
+    x = workloads.make_inputs(workloads.WORKLOADS[1])
     for ps in (16, 32, 64):
         p = workloads.make_paged(x, ps, seed=ps)
         k = oracle.gather_paged(p.k_pages.view(torch.int16).numpy().view(np.uint16), p.block_table.numpy(),
@@ -443,7 +443,7 @@ def test_gather_paged_inverts_the_pool_layout():
 def test_paged_decode_equals_packed_decode():
     """Attention over the paged layout is the attention over the same rows
     packed (the layout changes where rows live, not what is computed)."""
-    spec = workloads.with_shape(workloads.CONFIGS[1], lens=(17, 0, 33, 64))
+    spec = workloads.with_shape(workloads.WORKLOADS[1], lens=(17, 0, 33, 64))
     x = workloads.make_inputs(spec)
     p = workloads.make_paged(x, 16, seed=3)
     u16 = lambda t: t.view(torch.int16).numpy().view(np.uint16)

@@ -56,7 +56,7 @@ def _f32(x: float) -> float:
     return float(np.float32(x))
 
 
-CONFIGS = {
+WORKLOADS = {
     1: Spec("tiny-gqa-b4-h8kv2-d64", "gqa", 4, 8, 2, 64, 64, (17, 64, 100, 128), "f16",
             _f32(1.0 / math.sqrt(64)), 1),
     2: Spec("llama3-8b-decode-b32-h32kv8-d128", "gqa", 32, 32, 8, 128, 128, ("uniform", 512, 4096),
