@@ -300,6 +300,49 @@ ZL_API zl_status_t zl_attn_varlen_mla_ex(const void *q, const void *kv_cache, co
                                          zl_stream_t stream);
 
 /*
+ * Several new tokens per sequence over paged caches: the prefix cache the
+ * ZhiLight pages describe keeps key/value rows in blocks (first page,
+ * sections "技术架构" and "功能生态"), and chunked prefill or draft-token
+ * verification then attends over those blocks (same sections).  The
+ * operation, query/output layouts, mask and checks are those of
+ * zl_attn_varlen_gqa / zl_attn_varlen_mla; the caches are page pools as for
+ * zl_decode_attn_gqa_paged / zl_decode_attn_mla_paged: row i of sequence b
+ * (i < cu_seqlens_k[b+1] - cu_seqlens_k[b]) is row i % page_size of page
+ * block_table[b * max_pages_per_seq + i / page_size].  cu_seqlens_k gives
+ * only the lengths here (its values are not row indices into the pools).
+ * Preconditions as for the paged decode calls (every page id names a page
+ * of the pools, max_seqlen_k <= max_pages_per_seq * page_size).
+ */
+ZL_API zl_status_t zl_attn_varlen_gqa_paged(const void *q, const void *k_pages, const void *v_pages,
+                                            const int32_t *block_table, int max_pages_per_seq, int page_size,
+                                            const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int batch,
+                                            int total_q, int num_q_heads, int num_kv_heads, int head_dim,
+                                            int max_seqlen_k, float softmax_scale, int causal, zl_dtype_t dtype,
+                                            void *out, float *lse, void *workspace, size_t workspace_bytes,
+                                            zl_stream_t stream);
+ZL_API zl_status_t zl_attn_varlen_gqa_paged_ex(const void *q, const void *k_pages, const void *v_pages,
+                                               const int32_t *block_table, int max_pages_per_seq, int page_size,
+                                               const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                                               int batch, int total_q, int num_q_heads, int num_kv_heads,
+                                               int head_dim, int max_seqlen_k, float softmax_scale, int causal,
+                                               zl_dtype_t dtype, void *out, float *lse, int num_workers,
+                                               int phases, void *workspace, size_t workspace_bytes,
+                                               zl_stream_t stream);
+ZL_API zl_status_t zl_attn_varlen_mla_paged(const void *q, const void *kv_pages, const int32_t *block_table,
+                                            int max_pages_per_seq, int page_size, const int32_t *cu_seqlens_q,
+                                            const int32_t *cu_seqlens_k, int batch, int total_q, int num_q_heads,
+                                            int kv_lora_rank, int rope_dim, int max_seqlen_k, float softmax_scale,
+                                            int causal, zl_dtype_t dtype, void *out, float *lse, void *workspace,
+                                            size_t workspace_bytes, zl_stream_t stream);
+ZL_API zl_status_t zl_attn_varlen_mla_paged_ex(const void *q, const void *kv_pages, const int32_t *block_table,
+                                               int max_pages_per_seq, int page_size, const int32_t *cu_seqlens_q,
+                                               const int32_t *cu_seqlens_k, int batch, int total_q,
+                                               int num_q_heads, int kv_lora_rank, int rope_dim, int max_seqlen_k,
+                                               float softmax_scale, int causal, zl_dtype_t dtype, void *out,
+                                               float *lse, int num_workers, int phases, void *workspace,
+                                               size_t workspace_bytes, zl_stream_t stream);
+
+/*
  * Long runs of new tokens: prefill and large prefill chunks (the first
  * ZhiLight page lists flash-attention prefill and chunked prefill, sections
  * "技术架构" and "功能生态"; the second page lists them in section "Dual

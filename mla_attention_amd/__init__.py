@@ -70,6 +70,18 @@ SIGNATURES = {
                                     _c_float, _c_int, _c_int, _vp, _vp, _vp, _c_size, _vp]),
     "zl_attn_varlen_mla_ex": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _c_float, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _vp, _c_size, _vp]),
+    "zl_attn_varlen_gqa_paged": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _c_int,
+                                          _c_int, _c_int, _c_int, _c_float, _c_int, _c_int, _vp, _vp, _vp,
+                                          _c_size, _vp]),
+    "zl_attn_varlen_gqa_paged_ex": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int,
+                                             _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _c_int, _vp, _vp,
+                                             _c_int, _c_int, _vp, _c_size, _vp]),
+    "zl_attn_varlen_mla_paged": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _c_int,
+                                          _c_int, _c_int, _c_int, _c_float, _c_int, _c_int, _vp, _vp, _vp,
+                                          _c_size, _vp]),
+    "zl_attn_varlen_mla_paged_ex": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _c_int,
+                                             _c_int, _c_int, _c_int, _c_float, _c_int, _c_int, _vp, _vp, _c_int,
+                                             _c_int, _vp, _c_size, _vp]),
     "zl_attn_combine": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
     "zl_attn_prefill_gqa": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                      _c_float, _c_int, _c_int, _vp, _vp, _vp]),
@@ -415,6 +427,63 @@ def zl_attn_varlen_mla(q, kv_cache, cu_seqlens_q, cu_seqlens_k, max_seqlen_k: in
         int(max_seqlen_k), float(softmax_scale), int(bool(causal)), _DTYPE[q.dtype], _ptr(out), _ptr(lse),
         int(num_workers), int(phases), _ptr(workspace), workspace.numel(), _stream(stream, dev))
     _check(st, "zl_attn_varlen_mla")
+    return (out, lse) if lse is not None else out
+
+
+def zl_attn_varlen_gqa_paged(q, k_pages, v_pages, block_table, cu_seqlens_q, cu_seqlens_k, max_seqlen_k: int,
+                             softmax_scale: float, causal: bool = True, out=None, lse=None, workspace=None,
+                             num_workers: int = 0, stream=None, return_lse: bool = False, phases: int = 3):
+    """zl_attn_varlen_gqa over paged caches k_pages/v_pages [pages, page_size, Hkv, D]
+    with block_table int32 [B, max_pages] (as zl_decode_attn_gqa_paged);
+    cu_seqlens_k gives the cache lengths."""
+    dev, B, out, lse = _varlen_common(q, cu_seqlens_q, cu_seqlens_k, q.shape[2], out, lse, return_lse)
+    _need(k_pages, "k_pages", q.dtype, 4, dev)
+    _need(v_pages, "v_pages", q.dtype, 4, dev)
+    table, max_pages = _paging_args(block_table, dev)
+    Tq, Hq, D = q.shape
+    _, page_size, Hkv, Dk = k_pages.shape
+    if Dk != D or v_pages.shape != k_pages.shape:
+        raise ValueError("k_pages / v_pages must be [pages, page_size, Hkv, head_dim] like q")
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must have batch rows")
+    nbytes = zl_decode_attn_workspace_size(B, Hq, Hkv, D, max_seqlen_k, q.dtype, num_workers)
+    if workspace is None:
+        workspace = new_workspace(nbytes, dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    st = library().zl_attn_varlen_gqa_paged_ex(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), table, max_pages, int(page_size), _ptr(cu_seqlens_q),
+        _ptr(cu_seqlens_k), B, Tq, Hq, Hkv, D, int(max_seqlen_k), float(softmax_scale), int(bool(causal)),
+        _DTYPE[q.dtype], _ptr(out), _ptr(lse), int(num_workers), int(phases), _ptr(workspace), workspace.numel(),
+        _stream(stream, dev))
+    _check(st, "zl_attn_varlen_gqa_paged")
+    return (out, lse) if lse is not None else out
+
+
+def zl_attn_varlen_mla_paged(q, kv_pages, block_table, cu_seqlens_q, cu_seqlens_k, max_seqlen_k: int,
+                             softmax_scale: float, causal: bool = True, kv_lora_rank: int = 512,
+                             rope_dim: int = 64, out=None, lse=None, workspace=None, num_workers: int = 0,
+                             stream=None, return_lse: bool = False, phases: int = 3):
+    """zl_attn_varlen_mla over a paged latent pool kv_pages [pages, page_size, rank+rope]."""
+    dev, B, out, lse = _varlen_common(q, cu_seqlens_q, cu_seqlens_k, kv_lora_rank, out, lse, return_lse)
+    _need(kv_pages, "kv_pages", q.dtype, 3, dev)
+    table, max_pages = _paging_args(block_table, dev)
+    Tq, H, Dk = q.shape
+    _, page_size, Dc = kv_pages.shape
+    if Dk != kv_lora_rank + rope_dim or Dc != Dk:
+        raise ValueError("q and kv_pages rows must be kv_lora_rank + rope_dim wide")
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must have batch rows")
+    nbytes = zl_decode_attn_mla_workspace_size(B, H, kv_lora_rank, rope_dim, max_seqlen_k, q.dtype,
+                                               num_workers)
+    if workspace is None:
+        workspace = new_workspace(nbytes, dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    st = library().zl_attn_varlen_mla_paged_ex(
+        _ptr(q), _ptr(kv_pages), table, max_pages, int(page_size), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, Tq,
+        H, kv_lora_rank, rope_dim, int(max_seqlen_k), float(softmax_scale), int(bool(causal)), _DTYPE[q.dtype],
+        _ptr(out), _ptr(lse), int(num_workers), int(phases), _ptr(workspace), workspace.numel(),
+        _stream(stream, dev))
+    _check(st, "zl_attn_varlen_mla_paged")
     return (out, lse) if lse is not None else out
 
 

@@ -189,7 +189,6 @@ template <int L, int DT, bool PAGED, bool MQ>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, 64),
                           amdgpu_waves_per_eu(1, Geo<L>::MAX_WAVES_PER_SIMD))) void
 decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __restrict__ block_table) {
-  static_assert(!(PAGED && MQ), "several new tokens per sequence: packed caches only");
   using TL = Tile<L>;
   using GE = Geo<L>;
   constexpr int STAGES = GE::STAGES;
@@ -263,7 +262,10 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
     if constexpr (PAGED) {
       if (dmore && dj >= 1) {
         const int k = dj - 1;
-        pf = tile_rows(block_table + (long long)ds.b * a.max_pages, ds.t0 + 32 * k - ds.cs,
+        // (Several new tokens: the pages of the virtual sequence's sequence;
+        // its virtual tokens are that sequence's rows from 0.)
+        const int seq = MQ ? dsi.b : ds.b;
+        pf = tile_rows(block_table + (long long)seq * a.max_pages, ds.t0 + 32 * k - ds.cs,
                        min(32, ds.len - 32 * k), a.page_shift);
       }
     }
@@ -415,7 +417,10 @@ int default_workers(Layout layout) {
 
 template <int L, int DT>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  if (a.cu_q)
+  if (a.cu_q && a.block_table)
+    hipLaunchKernelGGL((decode_kernel<L, DT, true, true>), dim3(a.P), dim3(64), 0, stream, a, a.cu,
+                       a.block_table);
+  else if (a.cu_q)
     hipLaunchKernelGGL((decode_kernel<L, DT, false, true>), dim3(a.P), dim3(64), 0, stream, a, a.cu,
                        a.block_table);
   else if (a.block_table)

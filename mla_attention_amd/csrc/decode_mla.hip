@@ -195,7 +195,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kWaves * column_block
                                                       64 * kWaves * column_blocks<MQ>()),
                           amdgpu_waves_per_eu(column_blocks<MQ>(), column_blocks<MQ>()))) void
 mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __restrict__ block_table) {
-  static_assert(!(PAGED && MQ), "several new tokens per sequence: packed caches only");
   constexpr int NCB = column_blocks<MQ>();
   // One LDS object only (see decode_attn.hip): [4 ring stages][score exchange].
   __shared__ __attribute__((aligned(1024))) char smem_raw[lds_bytes<NCB>()];
@@ -270,7 +269,10 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
     if constexpr (PAGED) {
       if (dmore && dj >= 1) {
         const int k = dj - 1;
-        pf = tile_rows(block_table + (long long)ds.b * a.max_pages, ds.t0 + 32 * k - ds.cs,
+        // (Several new tokens: the pages of the virtual sequence's sequence;
+        // its virtual tokens are that sequence's rows from 0.)
+        const int seq = MQ ? dsi.b : ds.b;
+        pf = tile_rows(block_table + (long long)seq * a.max_pages, ds.t0 + 32 * k - ds.cs,
                        min(32, ds.len - 32 * k), a.page_shift);
       }
     }
@@ -422,7 +424,10 @@ int mla_default_workers() { return 256 * kWorkgroupsPerCU; }
 template <int DT>
 static void launch_mla_t(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.P), block(64 * kWaves);
-  if (a.cu_q)
+  if (a.cu_q && a.block_table)
+    hipLaunchKernelGGL((mla_decode_kernel<DT, true, true>), grid, dim3(64 * kWaves * column_blocks<true>()), 0,
+                       stream, a, a.cu, a.block_table);
+  else if (a.cu_q)
     hipLaunchKernelGGL((mla_decode_kernel<DT, false, true>), grid, dim3(64 * kWaves * column_blocks<true>()), 0,
                        stream, a, a.cu, a.block_table);
   else if (a.block_table)

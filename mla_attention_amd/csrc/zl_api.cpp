@@ -424,6 +424,70 @@ zl_status_t zl_attn_varlen_mla_ex(const void* q, const void* kv_cache, const int
                   stream);
 }
 
+zl_status_t zl_attn_varlen_gqa_paged_ex(const void* q, const void* k_pages, const void* v_pages,
+                                        const int32_t* block_table, int max_pages_per_seq, int page_size,
+                                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
+                                        int total_q, int num_q_heads, int num_kv_heads, int head_dim,
+                                        int max_seqlen_k, float softmax_scale, int causal, zl_dtype_t dtype,
+                                        void* out, float* lse, int num_workers, int phases, void* workspace,
+                                        size_t workspace_bytes, zl_stream_t stream) {
+  if (!cu_seqlens_q || !block_table) return ZL_ERR_INVALID_ARGUMENT;
+  Paging pg;
+  pg.table = block_table;
+  pg.max_pages = max_pages_per_seq;
+  pg.page_size = page_size;
+  Varlen vl;
+  vl.cu_q = cu_seqlens_q;
+  vl.total_q = total_q;
+  vl.causal = causal;
+  return gqa_impl(q, k_pages, v_pages, pg, vl, cu_seqlens_k, batch, num_q_heads, num_kv_heads, head_dim,
+                  max_seqlen_k, softmax_scale, dtype, out, lse, num_workers, phases, workspace, workspace_bytes,
+                  stream);
+}
+
+zl_status_t zl_attn_varlen_gqa_paged(const void* q, const void* k_pages, const void* v_pages,
+                                     const int32_t* block_table, int max_pages_per_seq, int page_size,
+                                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
+                                     int total_q, int num_q_heads, int num_kv_heads, int head_dim, int max_seqlen_k,
+                                     float softmax_scale, int causal, zl_dtype_t dtype, void* out, float* lse,
+                                     void* workspace, size_t workspace_bytes, zl_stream_t stream) {
+  return zl_attn_varlen_gqa_paged_ex(q, k_pages, v_pages, block_table, max_pages_per_seq, page_size, cu_seqlens_q,
+                                     cu_seqlens_k, batch, total_q, num_q_heads, num_kv_heads, head_dim,
+                                     max_seqlen_k, softmax_scale, causal, dtype, out, lse, 0, 3, workspace,
+                                     workspace_bytes, stream);
+}
+
+zl_status_t zl_attn_varlen_mla_paged_ex(const void* q, const void* kv_pages, const int32_t* block_table,
+                                        int max_pages_per_seq, int page_size, const int32_t* cu_seqlens_q,
+                                        const int32_t* cu_seqlens_k, int batch, int total_q, int num_q_heads,
+                                        int kv_lora_rank, int rope_dim, int max_seqlen_k, float softmax_scale,
+                                        int causal, zl_dtype_t dtype, void* out, float* lse, int num_workers,
+                                        int phases, void* workspace, size_t workspace_bytes, zl_stream_t stream) {
+  if (!cu_seqlens_q || !block_table) return ZL_ERR_INVALID_ARGUMENT;
+  Paging pg;
+  pg.table = block_table;
+  pg.max_pages = max_pages_per_seq;
+  pg.page_size = page_size;
+  Varlen vl;
+  vl.cu_q = cu_seqlens_q;
+  vl.total_q = total_q;
+  vl.causal = causal;
+  return mla_impl(q, kv_pages, pg, vl, cu_seqlens_k, batch, num_q_heads, kv_lora_rank, rope_dim, max_seqlen_k,
+                  softmax_scale, dtype, out, lse, num_workers, phases, workspace, workspace_bytes, stream);
+}
+
+zl_status_t zl_attn_varlen_mla_paged(const void* q, const void* kv_pages, const int32_t* block_table,
+                                     int max_pages_per_seq, int page_size, const int32_t* cu_seqlens_q,
+                                     const int32_t* cu_seqlens_k, int batch, int total_q, int num_q_heads,
+                                     int kv_lora_rank, int rope_dim, int max_seqlen_k, float softmax_scale,
+                                     int causal, zl_dtype_t dtype, void* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, zl_stream_t stream) {
+  return zl_attn_varlen_mla_paged_ex(q, kv_pages, block_table, max_pages_per_seq, page_size, cu_seqlens_q,
+                                     cu_seqlens_k, batch, total_q, num_q_heads, kv_lora_rank, rope_dim,
+                                     max_seqlen_k, softmax_scale, causal, dtype, out, lse, 0, 3, workspace,
+                                     workspace_bytes, stream);
+}
+
 zl_status_t zl_attn_varlen_mla(const void* q, const void* kv_cache, const int32_t* cu_seqlens_q,
                                const int32_t* cu_seqlens_k, int batch, int total_q, int num_q_heads,
                                int kv_lora_rank, int rope_dim, int max_seqlen_k, float softmax_scale, int causal,

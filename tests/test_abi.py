@@ -184,6 +184,35 @@ def test_varlen_entry_points_reject_bad_arguments(zl):
     assert mla(Tq=0, q=None, c=None, ck=None, out=None, ws=None) == 0
 
 
+def test_paged_varlen_entry_points_reject_bad_arguments(zl):
+    lib = zl.library()
+
+    def gqa(**kw):
+        a = dict(q=A, k=A, v=A, table=A, maxp=8, ps=16, cq=A, ck=A, B=4, Tq=16, Hq=8, Hkv=2, D=128, maxL=128,
+                 scale=0.125, causal=1, dt=0, out=A, lse=None, workers=0, phases=3, ws=A, wsb=BIG, stream=None)
+        a.update(kw)
+        return lib.zl_attn_varlen_gqa_paged_ex(a["q"], a["k"], a["v"], a["table"], a["maxp"], a["ps"], a["cq"],
+                                               a["ck"], a["B"], a["Tq"], a["Hq"], a["Hkv"], a["D"], a["maxL"],
+                                               a["scale"], a["causal"], a["dt"], a["out"], a["lse"], a["workers"],
+                                               a["phases"], a["ws"], a["wsb"], a["stream"])
+
+    def mla(**kw):
+        a = dict(q=A, c=A, table=A, maxp=4, ps=64, cq=A, ck=A, B=2, Tq=4, H=16, r=512, rope=64, maxL=200,
+                 scale=0.07, causal=1, dt=1, out=A, lse=None, workers=0, phases=3, ws=A, wsb=BIG, stream=None)
+        a.update(kw)
+        return lib.zl_attn_varlen_mla_paged_ex(a["q"], a["c"], a["table"], a["maxp"], a["ps"], a["cq"], a["ck"],
+                                               a["B"], a["Tq"], a["H"], a["r"], a["rope"], a["maxL"], a["scale"],
+                                               a["causal"], a["dt"], a["out"], a["lse"], a["workers"],
+                                               a["phases"], a["ws"], a["wsb"], a["stream"])
+    # both a query prefix and a page table are required
+    assert gqa(cq=None) == 1 and gqa(table=None) == 1 and mla(cq=None) == 1 and mla(table=None) == 1
+    assert gqa(ps=24) == 2 and gqa(maxp=0) == 1 and gqa(maxL=129) == 1 and gqa(causal=3) == 1
+    assert gqa(D=96) == 2 and gqa(wsb=16) == 3 and gqa(table=A + 2) == 1 and gqa(Tq=-1) == 1
+    assert mla(ps=512) == 2 and mla(maxL=257) == 1 and mla(r=256) == 2 and mla(wsb=8) == 3
+    assert gqa(Tq=0, q=None, k=None, v=None, ck=None, out=None, ws=None) == 0
+    assert mla(B=0, Tq=0, q=None, c=None, ck=None, out=None, ws=None) == 0
+
+
 def test_codec_entry_points_reject_bad_arguments(zl):
     lib = zl.library()
     q = lambda **kw: lib.zl_int8_quantize(kw.get("x", A), kw.get("dt", 0), kw.get("n", 1000), kw.get("chunk", 512),

@@ -183,3 +183,84 @@ def test_full_size_draft_tokens_sampled(cfg, q_len):
     tt, th = torch.from_numpy(t).to(DEV), torch.from_numpy(h).to(DEV)
     gate(out[tt, th], ro[t, h], spec.torch_dtype, lse[tt, th], rl[t, h], where=f"config {cfg} q_len {q_len}")
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+
+
+def run_gpu_paged(x, vq, px, causal=True, num_workers=0):
+    s = x.spec
+    q = vq.q.to(DEV)
+    cq, ck, bt = vq.cu_q.to(DEV), x.cu_seqlens.to(DEV), px.block_table.to(DEV)
+    if s.kind == "mla":
+        out, lse = zl().zl_attn_varlen_mla_paged(q, px.kv_pages.to(DEV), bt, cq, ck, x.max_seqlen, s.scale,
+                                                 causal=causal, num_workers=num_workers, return_lse=True)
+    else:
+        out, lse = zl().zl_attn_varlen_gqa_paged(q, px.k_pages.to(DEV), px.v_pages.to(DEV), bt, cq, ck,
+                                                 x.max_seqlen, s.scale, causal=causal, num_workers=num_workers,
+                                                 return_lse=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def check_paged(x, vq, page_size, where, causal=True, num_workers=0):
+    """Paged caches hold the packed caches' rows (the paged layout's
+    definition, checked here on the pools themselves), so the oracle on the
+    packed rows is the reference; the packed call, with the same split, must
+    give the same bits."""
+    print(where, flush=True)
+    px = workloads.make_paged(x, page_size, seed=len(x.lens))
+    cu = x.cu_seqlens.numpy()
+    if x.spec.kind == "mla":
+        assert np.array_equal(oracle.gather_paged(px.kv_pages.view(torch.int16).numpy(), px.block_table.numpy(),
+                                                  cu, page_size), x.latent.view(torch.int16).numpy())
+    else:
+        assert np.array_equal(oracle.gather_paged(px.k_pages.view(torch.int16).numpy(), px.block_table.numpy(),
+                                                  cu, page_size), x.k.view(torch.int16).numpy())
+    out, lse = run_gpu_paged(x, vq, px, causal, num_workers)
+    ro, rl = run_oracle(x, vq, causal)
+    gate(out, ro, x.spec.torch_dtype, lse, rl, where=where)
+    po, pl = run_gpu(x, vq, causal, num_workers)
+    assert torch.equal(out, po) and torch.equal(lse, pl), where
+
+
+PAGED_GQA_CASES = [
+    # (cache lens, new tokens per sequence, Hq, Hkv, D, dtype, page size)
+    ([17, 64, 100, 128], [1, 2, 3, 4], 8, 2, 64, torch.float16, 16),
+    ([100, 1, 300, 64, 33], [100, 1, 37, 0, 33], 8, 2, 128, torch.bfloat16, 16),
+    ([200, 150], [4, 4], 32, 8, 128, torch.float16, 64),
+    ([96, 95, 97], [5, 1, 6], 6, 2, 128, torch.bfloat16, 32),
+    ([0, 50, 0], [2, 3, 0], 8, 2, 128, torch.float16, 16),
+    ([700, 260], [9, 3], 32, 8, 128, torch.bfloat16, 256),
+    ([(i * 37) % 90 for i in range(80)], [(i * 7) % 4 for i in range(80)], 8, 2, 128, torch.bfloat16, 16),
+]
+
+
+@pytest.mark.parametrize("lens,q_lens,Hq,Hkv,D,dt,page", PAGED_GQA_CASES)
+def test_gqa_varlen_paged(lens, q_lens, Hq, Hkv, D, dt, page):
+    x = workloads.make_inputs(spec_gqa(lens, Hq, Hkv, D, dt))
+    vq = workloads.make_varlen_query(x, q_lens, seed=len(lens))
+    check_paged(x, vq, page, f"gqa varlen paged {lens[:6]} q {q_lens[:6]} {Hq}/{Hkv} D{D} {dt} page {page}")
+
+
+PAGED_MLA_CASES = [
+    ([40, 300, 1], [2, 1, 1], 16, torch.bfloat16, 16),
+    ([300, 45], [3, 5], 16, torch.float16, 64),
+    ([5, 64], [9, 64], 16, torch.bfloat16, 16),
+    ([61, 0, 33], [1, 2, 1], 16, torch.float16, 32),
+    ([90, 200], [2, 2], 128, torch.float16, 64),
+    ([(i * 53) % 90 for i in range(70)], [(i * 5) % 3 for i in range(70)], 16, torch.bfloat16, 16),
+]
+
+
+@pytest.mark.parametrize("lens,q_lens,H,dt,page", PAGED_MLA_CASES)
+def test_mla_varlen_paged(lens, q_lens, H, dt, page):
+    x = workloads.make_inputs(spec_mla(lens, H, dt))
+    vq = workloads.make_varlen_query(x, q_lens, seed=len(lens))
+    check_paged(x, vq, page, f"mla varlen paged {lens[:6]} q {q_lens[:6]} H{H} {dt} page {page}")
+
+
+def test_varlen_paged_without_mask_and_split():
+    x = workloads.make_inputs(spec_gqa([40, 300, 7], 8, 2, 128, torch.float16))
+    vq = workloads.make_varlen_query(x, [3, 20, 9], seed=3)
+    check_paged(x, vq, 16, "gqa varlen paged, no mask, 64 workers", causal=False, num_workers=64)
+    xm = workloads.make_inputs(spec_mla([40, 300, 7], 16, torch.bfloat16))
+    vqm = workloads.make_varlen_query(xm, [3, 20, 9], seed=4)
+    check_paged(xm, vqm, 64, "mla varlen paged, no mask, 64 workers", causal=False, num_workers=64)
