@@ -77,17 +77,17 @@ def sample_pairs(spec):
     return [(b, h) for b in range(spec.batch) for h in heads]
 
 
-# ------------------------------------------------------------ the five configs
-def test_config1_full():
+# ------------------------------------------------------------ the five workloads
+def test_small_workload_full():
     x = workloads.make_inputs(workloads.WORKLOADS[1])
-    st = check_full(x, "config 1")
-    print("config 1", st)
+    st = check_full(x, x.spec.name)
+    print(x.spec.name, st)
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
-def test_full_size_config_sampled(cfg):
+def test_full_size_workload_sampled(cfg):
     spec = workloads.WORKLOADS[cfg]
-    print(f"config {cfg}: {spec.name}", flush=True)
+    print(spec.name, flush=True)
     x = workloads.make_inputs(spec)
     out, lse = run_gpu(x)
     pairs = sample_pairs(spec)
@@ -96,14 +96,14 @@ def test_full_size_config_sampled(cfg):
     idx_h = np.array([p[1] for p in pairs])
     tb, th = torch.from_numpy(idx_b).to(DEV), torch.from_numpy(idx_h).to(DEV)
     st = gate(out[tb, th], ro[idx_b, idx_h], spec.torch_dtype, lse[tb, th], rl[idx_b, idx_h],
-              where=f"config {cfg}")
+              where=spec.name)
     # whole output: finite, and every row was written (a row of exact zeros
     # would mean a missed (sequence, head))
     o = out.float()
     assert torch.isfinite(o).all()
     assert (o.abs().amax(dim=-1) > 0).all()
     assert torch.isfinite(lse).all()
-    print(f"config {cfg}", st, flush=True)
+    print(spec.name, st, flush=True)
 
 
 # ------------------------------------------------------------- edge cases
@@ -315,7 +315,7 @@ def test_mla_paged(lens, H, dt, ps):
 @pytest.mark.parametrize("cfg,ps", [(2, 16), (5, 64)])
 def test_full_size_paged_sampled(cfg, ps):
     spec = workloads.WORKLOADS[cfg]
-    print(f"paged config {cfg} ps{ps}: {spec.name}", flush=True)
+    print(f"paged {spec.name}, {ps}-token pages", flush=True)
     x = workloads.make_inputs(spec)
     p = workloads.make_paged(x, ps, seed=cfg)
     out, lse = run_gpu_paged(x, p)
@@ -325,6 +325,6 @@ def test_full_size_paged_sampled(cfg, ps):
     idx_h = np.array([q[1] for q in pairs])
     tb, th = torch.from_numpy(idx_b).to(DEV), torch.from_numpy(idx_h).to(DEV)
     gate(out[tb, th], ro[idx_b, idx_h], spec.torch_dtype, lse[tb, th], rl[idx_b, idx_h],
-         where=f"paged config {cfg}")
+         where=f"paged {spec.name}")
     po, pl = run_gpu(x)
     assert torch.equal(out, po) and torch.equal(lse, pl)

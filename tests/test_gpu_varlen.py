@@ -171,7 +171,7 @@ def test_full_size_draft_tokens_sampled(cfg, q_len):
     verification), compared on sampled rows: every sequence, its first and
     last new token, and heads spanning every key/value head."""
     spec = workloads.WORKLOADS[cfg]
-    print(f"config {cfg}, {q_len} new tokens per sequence", flush=True)
+    print(f"{spec.name}, {q_len} new tokens per sequence", flush=True)
     x = workloads.make_inputs(spec)
     vq = workloads.make_varlen_query(x, [q_len] * spec.batch, seed=cfg)
     out, lse = run_gpu(x, vq)
@@ -181,7 +181,7 @@ def test_full_size_draft_tokens_sampled(cfg, q_len):
     t = np.array([r[0] for r in rows])
     h = np.array([r[1] for r in rows])
     tt, th = torch.from_numpy(t).to(DEV), torch.from_numpy(h).to(DEV)
-    gate(out[tt, th], ro[t, h], spec.torch_dtype, lse[tt, th], rl[t, h], where=f"config {cfg} q_len {q_len}")
+    gate(out[tt, th], ro[t, h], spec.torch_dtype, lse[tt, th], rl[t, h], where=f"{spec.name} q_len {q_len}")
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
 
 
