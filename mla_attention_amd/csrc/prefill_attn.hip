@@ -8,25 +8,27 @@
 // the bottom right) or all lk rows.
 //
 // Unlike decode, every cache row is used by many query rows, so the work is
-// matrix-unit bound.  Structure (one workgroup of four wavefronts per CU):
-//  * A workgroup takes one key/value head and a block of 256 query rows of
+// matrix-unit bound.  Structure (two workgroups of four wavefronts per CU):
+//  * A workgroup takes one key/value head and a block of 128 query rows of
 //    one sequence -- the pairs (new token i, head hh of the head's group),
 //    numbered i*G + hh, so the group's heads share every K/V tile.  Wave w
-//    owns rows 64w .. 64w+63 as four 16-row MFMA column blocks.  Blocks are
+//    owns rows 32w .. 32w+31 as two 16-row MFMA column blocks.  Blocks are
 //    launched longest first (the last blocks of a sequence see the most keys).
 //  * The block streams the keys its last token can see in 32-token tiles
 //    through a four-stage LDS ring; each wave DMAs a quarter of every tile
 //    (global_load_lds, SADDR form) and one barrier per tile both publishes
 //    the tile and frees the stage refilled next.
-//  * Per tile and wave: S^T = K Q^T for 2 token blocks x 4 column blocks
-//    (each K fragment read from LDS once and used for four MFMAs), the causal
-//    mask and online softmax per column, and O^T += V^T P^T (each transposed V
-//    fragment read once, four MFMAs) -- the decode kernels' tile math and
-//    layouts (zl_tile.h), widened to 64 query rows per wave.
+//  * Per tile and wave: S^T = K Q^T for 2 token blocks x 2 column blocks
+//    (each K fragment read from LDS once and used for both), the causal mask
+//    and online softmax per column, and O^T += V^T P^T (each transposed V
+//    fragment read once, used for both) -- the decode kernels' tile math and
+//    layouts (zl_tile.h), widened to 32 query rows per wave.
 #include "zl_device.h"
 #include "zl_kernels.h"
 #include "zl_split.h"
 #include "zl_tile.h"
+
+#include <type_traits>
 
 namespace zl {
 namespace {
@@ -96,21 +98,47 @@ __device__ __forceinline__ void pf_dma_tile(const char* kbase, const char* vbase
   }
 }
 
-// S^T for the tile's 2 token blocks and this wave's column blocks: lane (g, n)
-// gets tokens 16tb + 4g .. +3 of column 16cb + n.
-template <int DT, int D, typename SlotFn>
-__device__ __forceinline__ void pf_scores(const ZL_LDS char* kt, const i16x8 (&qop)[kPfCB][PfGeo<D>::KSTEPS], int n,
-                                          int g, SlotFn slot, f32x4 (&s)[kPfCB][2]) {
+// Per-lane LDS byte offsets of the fragments a lane reads from a stage (the
+// stage's base is OR-ed in once per tile: it lies above every offset bit):
+//  K (scores): row n, slot(4kb + g, n), for k-step kb;
+//  V (PV): row r0 = 4g + n/4, bytes 8(n & 1) into slot(2m + (n & 3)/2, r0),
+//  for group m of 16 output dims.
+// Both swizzles map rows r and r + 16 to the same slots, so one offset serves
+// both 16-row halves of a tile.  In both, the bits that kb (or m) changes are
+// disjoint from the lane's other bits, so every offset is the lane's first
+// one XOR 64 kb (or 32 m): one instruction per offset and tile, two registers.
+template <int D>
+struct PfOffsets {
+  uint32_t k0, v0;
+};
+
+template <int D>
+__device__ __forceinline__ PfOffsets<D> pf_offsets(int n, int g) {
   using GE = PfGeo<D>;
+  const int r0 = 4 * g + (n >> 2);
+  return PfOffsets<D>{(uint32_t)(n * GE::ROWB + (GE::slot(g, n) << 4)),
+                      (uint32_t)(r0 * GE::ROWB + ((n & 1) << 3) + (GE::slot((n & 3) >> 1, r0) << 4))};
+}
+
+// S^T for the tile's 2 token blocks and this wave's column blocks: lane (g, n)
+// gets tokens 16tb + 4g .. +3 of column 16cb + n.  off.k0 includes the
+// stage's base.
+template <int DT, int D>
+__device__ __forceinline__ void pf_scores(const ZL_LDS char* smem, PfOffsets<D> off,
+                                          const i16x8 (&qop)[kPfCB][PfGeo<D>::KSTEPS], f32x4 (&s)[kPfCB][2]) {
+  using GE = PfGeo<D>;
+  // The base offset passes through an empty asm so that the compiler derives
+  // the offsets here (one XOR each, the 16-row step as an immediate) instead
+  // of holding an address per block across the loop.
+  uint32_t k0 = off.k0;
+  asm volatile("" : "+v"(k0));
 #pragma unroll
   for (int cb = 0; cb < kPfCB; ++cb) s[cb][0] = s[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < GE::KSTEPS; ++kb) {
-    const int c = 4 * kb + g;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      const int t = 16 * tb + n;
-      const i16x8 av = __builtin_bit_cast(i16x8, lds_read_b128(kt + t * GE::ROWB + (slot(c, t) << 4)));
+      const i16x8 av = __builtin_bit_cast(i16x8, lds_read_b128(smem + 16 * tb * GE::ROWB + (k0 ^ (64 * kb))));
 #pragma unroll
       for (int cb = 0; cb < kPfCB; ++cb) s[cb][tb] = mfma16x16x32<DT>(av, qop[cb][kb], s[cb][tb]);
     }
@@ -118,25 +146,25 @@ __device__ __forceinline__ void pf_scores(const ZL_LDS char* kt, const i16x8 (&q
 }
 
 // O^T[cb] += V^T P^T[cb] over all D/16 output blocks; every transposed V
-// fragment is read once and used for the four column blocks.  Reads go out in
-// groups of 4 blocks with one group of lookahead (as pv_blocks).
-template <int DT, int D, typename SlotFn>
-__device__ __forceinline__ void pf_pv(const ZL_LDS char* vt, const POperand (&pop)[kPfCB], int n, int g,
-                                      SlotFn slot, f32x4 (&o)[kPfCB][PfGeo<D>::VBLK]) {
+// fragment is read once and used for the column blocks.  Reads go out in
+// groups of 4 blocks with one group of lookahead (as pv_blocks).  off.v0
+// includes the stage's base; the V tile starts VT bytes after it and its rows
+// 16 .. 31 another 16 rows further on (both immediates).
+template <int DT, int D, int VT>
+__device__ __forceinline__ void pf_pv(const ZL_LDS char* smem, PfOffsets<D> off,
+                                      const POperand (&pop)[kPfCB], f32x4 (&o)[kPfCB][PfGeo<D>::VBLK]) {
   using GE = PfGeo<D>;
   constexpr int NG = GE::VBLK / 4;
-  const int r0 = 4 * g + (n >> 2);
-  const int r1 = r0 + 16;
-  const int half = (n & 1) << 3;
-  const int csub = (n & 3) >> 1;
-  const ZL_LDS char* row0 = vt + r0 * GE::ROWB + half;
-  const ZL_LDS char* row1 = vt + r1 * GE::ROWB + half;
+  constexpr int VT1 = VT + 16 * GE::ROWB;
+  static_assert(VT1 <= 65535, "immediate LDS offsets are 16-bit");
+  uint32_t v0 = off.v0;  // (as k0 in pf_scores)
+  asm volatile("" : "+v"(v0));
+  const auto vrow = [&](int m) { return smem + (v0 ^ (32u * m)); };
   i16x4 lo[2][4], hi[2][4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int c = 2 * k + csub;
-    lo[0][k] = lds_read_tr16(row0 + (slot(c, r0) << 4));
-    hi[0][k] = lds_read_tr16(row1 + (slot(c, r1) << 4));
+    lo[0][k] = lds_read_tr16<VT>(vrow(k));
+    hi[0][k] = lds_read_tr16<VT1>(vrow(k));
   }
 #pragma unroll
   for (int grp = 0; grp < NG; ++grp) {
@@ -144,9 +172,8 @@ __device__ __forceinline__ void pf_pv(const ZL_LDS char* vt, const POperand (&po
     if (grp + 1 < NG) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int c = 2 * (4 * (grp + 1) + k) + csub;
-        lo[buf ^ 1][k] = lds_read_tr16(row0 + (slot(c, r0) << 4));
-        hi[buf ^ 1][k] = lds_read_tr16(row1 + (slot(c, r1) << 4));
+        lo[buf ^ 1][k] = lds_read_tr16<VT>(vrow(4 * (grp + 1) + k));
+        hi[buf ^ 1][k] = lds_read_tr16<VT1>(vrow(4 * (grp + 1) + k));
       }
       lds_wait<8>(lo[buf][0], lo[buf][1], lo[buf][2], lo[buf][3], hi[buf][0], hi[buf][1], hi[buf][2],
                   hi[buf][3]);
@@ -245,20 +272,6 @@ __device__ __forceinline__ void pf_softmax4(const f32x4 (&s)[kPfCB][2], int g, c
   }
 }
 
-// Scheduling request for the block above: the K reads first, then each
-// score MFMA followed by a few softmax vector instructions, so the vector unit
-// works while the matrix unit runs (an MFMA occupies it for 16 cycles).
-template <int D>
-__device__ __forceinline__ void interleave_scores_softmax() {
-  constexpr int NMFMA = 2 * kPfCB * PfGeo<D>::KSTEPS;
-  __builtin_amdgcn_sched_group_barrier(0x100, 2 * PfGeo<D>::KSTEPS, 0);  // DS reads
-#pragma unroll
-  for (int k = 0; k < NMFMA; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
-  }
-}
-
 __device__ __forceinline__ int wave_min(int v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v = min(v, __builtin_amdgcn_ds_bpermute((__lane_id() ^ m) << 2, v));
@@ -279,9 +292,8 @@ prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, int nblocks) {
   const int lane = tid & 63;
   const int n = lane & 15;
   const int g = lane >> 4;
-  const auto slot = [](int c, int r) { return PfGeo<D>::slot(c, r); };
 
-  // Workgroup -> (key/value head, block of 256 query rows), longest first.
+  // Workgroup -> (key/value head, block of 128 query rows), longest first.
   const int kvh = (int)blockIdx.x % a.Hkv;
   const int j = (int)blockIdx.x / a.Hkv;
   VirtualSeqs vs;
@@ -290,7 +302,7 @@ prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, int nblocks) {
   const VSeqInfo si = vs.info(vs.V - 1 - j);
   const bool causal = a.causal != 0;
 
-  // This lane's columns: query rows 256 hb + 16 kPfCB wave + 16 cb + n.
+  // This lane's columns: query rows 128 hb + 16 kPfCB wave + 16 cb + n.
   long long orow[kPfCB];
   bool valid[kPfCB];
   int lim[kPfCB];  // last visible cache row, counted from the sequence's first
@@ -376,18 +388,28 @@ prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, int nblocks) {
       wait_vmcnt<0>();
     barrier_lds();
   };
-  f32x4 s_cur[kPfCB][2], s_nxt[kPfCB][2];
+  const PfOffsets<D> off = pf_offsets<D>(n, g);
+  // Lane offsets lie within the first 16 rows; stage bases are multiples of
+  // a power of two at least that large, so OR-ing them in adds them.
+  static_assert((GE::STAGE & (GE::STAGE - 1)) == 0 && GE::STAGE >= 16 * GE::ROWB, "stage bases above offsets");
+  // Scores of tile i live in sb[i & 1]: the loop body is compiled twice, once
+  // per parity, so the buffers are fixed registers and need no copies.
+  f32x4 sb[2][kPfCB][2];
   if (ntiles > 0) {
     wait_tile(0);
-    pf_scores<DT, D>(smem, qop, n, g, slot, s_cur);
+    pf_scores<DT, D>(smem, off, qop, sb[0]);
   }
-  for (int i = 0; i < ntiles; ++i) {
+  int i = 0;
+  auto step = [&](auto parity) __attribute__((always_inline)) {
+    constexpr int CUR = decltype(parity)::value, NXT = CUR ^ 1;
     const bool more = i + 1 < ntiles;
     if (more) {
       wait_tile(i + 1);
       if (issued < ntiles) issue();  // into the stage of tile i-1
     }
-    const ZL_LDS char* knext = smem + ((i + 1) % kPfStages) * GE::STAGE;
+    const uint32_t knext = ((i + 1) % kPfStages) * GE::STAGE;
+    const uint32_t vcur = (i % kPfStages) * GE::STAGE;
+    const PfOffsets<D> offn{off.k0 | knext, off.v0 | vcur};
     const int nv = kend - 32 * i < 32 ? kend - 32 * i : 32;
     POperand pop[kPfCB];
     float alpha[kPfCB];
@@ -399,15 +421,13 @@ prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, int nblocks) {
     }
     const bool full = nv == 32 && 32 * i + 31 <= lim_min;
     if (more && full) {
-      pf_scores<DT, D>(knext, qop, n, g, slot, s_nxt);
-      pf_softmax4<DT, false>(s_cur, g, nvc, scale_log2, sm, alpha, pop);
-      interleave_scores_softmax<D>();
+      pf_scores<DT, D>(smem, offn, qop, sb[NXT]);
+      pf_softmax4<DT, false>(sb[CUR], g, nvc, scale_log2, sm, alpha, pop);
     } else if (more) {
-      pf_scores<DT, D>(knext, qop, n, g, slot, s_nxt);
-      pf_softmax4<DT, true>(s_cur, g, nvc, scale_log2, sm, alpha, pop);
-      interleave_scores_softmax<D>();
+      pf_scores<DT, D>(smem, offn, qop, sb[NXT]);
+      pf_softmax4<DT, true>(sb[CUR], g, nvc, scale_log2, sm, alpha, pop);
     } else {
-      pf_softmax4<DT, true>(s_cur, g, nvc, scale_log2, sm, alpha, pop);
+      pf_softmax4<DT, true>(sb[CUR], g, nvc, scale_log2, sm, alpha, pop);
     }
 #pragma unroll
     for (int cb = 0; cb < kPfCB; ++cb) {
@@ -417,12 +437,13 @@ prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, int nblocks) {
         for (int bb = 0; bb < GE::VBLK; ++bb) o[cb][bb] *= alpha[cb];
       }
     }
-    pf_pv<DT, D>(smem + (i % kPfStages) * GE::STAGE + GE::KBYTES, pop, n, g, slot, o);
-#pragma unroll
-    for (int cb = 0; cb < kPfCB; ++cb) {
-      s_cur[cb][0] = s_nxt[cb][0];
-      s_cur[cb][1] = s_nxt[cb][1];
-    }
+    pf_pv<DT, D, GE::KBYTES>(smem, offn, pop, o);
+  };
+  while (i < ntiles) {
+    step(std::integral_constant<int, 0>{});
+    if (++i == ntiles) break;
+    step(std::integral_constant<int, 1>{});
+    ++i;
   }
 
   // Epilogue: lane (g, n) holds column 16cb + n, dims 16blk + 4g .. +3.
