@@ -210,8 +210,8 @@ __device__ __forceinline__ void pf_pv(const ZL_LDS char* smem, PfOffsets<D> off,
 // after the exponential (a zero scale would turn -inf into NaN).
 template <int DT, bool MASK>
 __device__ __forceinline__ void pf_softmax4(const f32x4 (&s)[kPfCB][2], int g, const int (&nvalid)[kPfCB],
-                                            float scale_log2, SoftmaxState (&st)[kPfCB], float (&alpha)[kPfCB],
-                                            POperand (&p)[kPfCB]) {
+                                            float scale_log2, SoftmaxState (&st)[kPfCB], bool (&grow)[kPfCB],
+                                            float (&dexp)[kPfCB], float (&psum)[kPfCB], POperand (&p)[kPfCB]) {
   static_assert(kPfCB == 2 || kPfCB == 4, "two or four column blocks");
   float x[kPfCB][8];
   float tmax[kPfCB];
@@ -232,13 +232,13 @@ __device__ __forceinline__ void pf_softmax4(const f32x4 (&s)[kPfCB][2], int g, c
   for (int cb = 0; cb < kPfCB; ++cb) tmax[cb] = tmax[cb] == -INFINITY ? -INFINITY : tmax[cb] * scale_log2;
   // Lazy rescale (kLazyMax, zl_tile.h): a column's reference max moves only
   // when the tile's max passes it by more than 2^kLazyMax.
-  float m_use[kPfCB], psum[kPfCB];
+  float m_use[kPfCB];
 #pragma unroll
   for (int cb = 0; cb < kPfCB; ++cb) {
-    const bool grow = tmax[cb] > st[cb].m + kLazyMax;
-    const float m_new = grow ? tmax[cb] : st[cb].m;
+    grow[cb] = tmax[cb] > st[cb].m + kLazyMax;
+    const float m_new = grow[cb] ? tmax[cb] : st[cb].m;
     m_use[cb] = (m_new == -INFINITY) ? 0.f : m_new;
-    alpha[cb] = grow ? exp2_fast(st[cb].m - m_use[cb]) : 1.f;
+    dexp[cb] = st[cb].m - m_use[cb];
     st[cb].m = m_new;
     psum[cb] = 0.f;
   }
@@ -253,7 +253,6 @@ __device__ __forceinline__ void pf_softmax4(const f32x4 (&s)[kPfCB][2], int g, c
     }
 #pragma unroll
   for (int cb = 0; cb < kPfCB; ++cb) {
-    st[cb].l = st[cb].l * alpha[cb] + psum[cb];
     u32x4 pw;
 #pragma unroll
     for (int i = 0; i < 4; ++i) pw[i] = pack2<DT>(x[cb][2 * i], x[cb][2 * i + 1]);
@@ -412,7 +411,8 @@ prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, int nblocks) {
     const PfOffsets<D> offn{off.k0 | knext, off.v0 | vcur};
     const int nv = kend - 32 * i < 32 ? kend - 32 * i : 32;
     POperand pop[kPfCB];
-    float alpha[kPfCB];
+    bool grow[kPfCB];
+    float dexp[kPfCB], psum[kPfCB];
     int nvc[kPfCB];
 #pragma unroll
     for (int cb = 0; cb < kPfCB; ++cb) {
@@ -422,20 +422,23 @@ prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, int nblocks) {
     const bool full = nv == 32 && 32 * i + 31 <= lim_min;
     if (more && full) {
       pf_scores<DT, D>(smem, offn, qop, sb[NXT]);
-      pf_softmax4<DT, false>(sb[CUR], g, nvc, scale_log2, sm, alpha, pop);
+      pf_softmax4<DT, false>(sb[CUR], g, nvc, scale_log2, sm, grow, dexp, psum, pop);
     } else if (more) {
       pf_scores<DT, D>(smem, offn, qop, sb[NXT]);
-      pf_softmax4<DT, true>(sb[CUR], g, nvc, scale_log2, sm, alpha, pop);
+      pf_softmax4<DT, true>(sb[CUR], g, nvc, scale_log2, sm, grow, dexp, psum, pop);
     } else {
-      pf_softmax4<DT, true>(sb[CUR], g, nvc, scale_log2, sm, alpha, pop);
+      pf_softmax4<DT, true>(sb[CUR], g, nvc, scale_log2, sm, grow, dexp, psum, pop);
     }
 #pragma unroll
     for (int cb = 0; cb < kPfCB; ++cb) {
-      // Rescale only when some column's running maximum moved (alpha != 1).
-      if (__ballot(alpha[cb] != 1.f)) {
+      // Rescale only when some column's running maximum moved.
+      if (__ballot(grow[cb])) {
+        const float alpha = grow[cb] ? exp2_fast(dexp[cb]) : 1.f;
+        sm[cb].l *= alpha;
 #pragma unroll
-        for (int bb = 0; bb < GE::VBLK; ++bb) o[cb][bb] *= alpha[cb];
+        for (int bb = 0; bb < GE::VBLK; ++bb) o[cb][bb] *= alpha;
       }
+      sm[cb].l += psum[cb];
     }
     pf_pv<DT, D, GE::KBYTES>(smem, offn, pop, o);
   };
