@@ -139,8 +139,6 @@ def main():
     reps = max(2, math.ceil((1 << 30) / kv_bytes))
     if args.profile_run:
         reps = 1
-    if args.q_len > 1 and args.paged:
-        sys.exit("--q-len and --paged: the several-new-tokens path reads packed caches")
     vq = workloads.make_varlen_query(x, [args.q_len] * spec.batch, seed=args.config) if args.q_len > 1 else None
     cu = x.cu_seqlens.to(dev)
     q = vq.q.to(dev) if vq else x.q.to(dev)
@@ -168,7 +166,14 @@ def main():
 
     def step(i, phases=3):
         c = caches[i % reps]
-        if vq is not None and spec.kind == "mla":
+        if vq is not None and paged and spec.kind == "mla":
+            zl.zl_attn_varlen_mla_paged(q, c[0], table, cu_q, cu, x.max_seqlen, spec.scale, out=out, lse=lse,
+                                        workspace=ws, num_workers=args.workers, stream=stream, phases=phases)
+        elif vq is not None and paged:
+            zl.zl_attn_varlen_gqa_paged(q, c[0], c[1], table, cu_q, cu, x.max_seqlen, spec.scale, out=out,
+                                        lse=lse, workspace=ws, num_workers=args.workers, stream=stream,
+                                        phases=phases)
+        elif vq is not None and spec.kind == "mla":
             zl.zl_attn_varlen_mla(q, c[0], cu_q, cu, x.max_seqlen, spec.scale, out=out, lse=lse, workspace=ws,
                                   num_workers=args.workers, stream=stream, phases=phases)
         elif vq is not None:
