@@ -134,3 +134,54 @@ def test_random_case(i):
         ro, rl = oracle.gqa_varlen(qb, x.bits("k"), x.bits("v"), cqn, ckn, s.num_kv_heads, s.scale, odt,
                                    causal=c["causal"])
     gate(out, ro, c["dt"], lse, rl, where=where)
+
+
+def draw_prefill_case(i: int) -> dict:
+    """Prefill case i: runs of new tokens (whole prompts or chunks after a
+    cached prefix), drawn from a fixed seed."""
+    r = np.random.default_rng(5000 + i)
+    B = int(r.choice([1, 2, 3, 5, 9]))
+    D = int(r.choice([64, 128]))
+    Hkv = int(r.choice([1, 2, 4, 8]))
+    G = int(r.choice([1, 2, 3, 4, 8, 16]))
+    q_lens, lens = [], []
+    for _ in range(B):
+        nq = int(r.integers(0, 400))
+        prefix = int(r.integers(0, 400)) if r.random() < 0.5 else 0
+        q_lens.append(nq)
+        lens.append(nq + prefix)
+    # A few draws with more new tokens than cached rows (leading tokens see none).
+    if r.random() < 0.15:
+        q_lens[0] = lens[0] + int(r.integers(1, 20))
+    work = sum(q * L for q, L in zip(q_lens, lens)) * Hkv * G * 2 * D
+    if work > 1.5e9:
+        f = math.sqrt(1.5e9 / work)
+        q_lens = [int(q * f) for q in q_lens]
+        lens = [max(int(L * f), q) for q, L in zip(q_lens, lens)]
+    dt = torch.float16 if r.random() < 0.5 else torch.bfloat16
+    return dict(B=B, D=D, Hkv=Hkv, H=Hkv * G, lens=lens, q_lens=q_lens, dt=dt, causal=bool(r.random() < 0.8),
+                seed=100 + i)
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_prefill_case(i):
+    import mla_attention_amd as zl
+    c = draw_prefill_case(i)
+    spec = workloads.Spec("random-prefill", "gqa", c["B"], c["H"], c["Hkv"], c["D"], c["D"], tuple(c["lens"]),
+                          "f16" if c["dt"] == torch.float16 else "bf16", float(np.float32(1 / math.sqrt(c["D"]))),
+                          c["seed"])
+    where = (f"prefill case {i}: {c['dt']} H={c['H']}/{c['Hkv']} D={c['D']} lens={c['lens']} q_lens={c['q_lens']} "
+             f"causal={c['causal']}")
+    print(where, flush=True)
+    if sum(c["q_lens"]) == 0:
+        pytest.skip("no new tokens drawn")
+    x = workloads.make_inputs(spec)
+    vq = workloads.make_varlen_query(x, c["q_lens"], seed=c["seed"])
+    out, lse = zl.zl_attn_prefill_gqa(vq.q.to(DEV), x.k.to(DEV), x.v.to(DEV), vq.cu_q.to(DEV), x.cu_seqlens.to(DEV),
+                                      x.max_seqlen, spec.scale, causal=c["causal"], return_lse=True)
+    torch.cuda.synchronize()
+    qb = vq.q.contiguous().view(torch.int16).numpy().view(np.uint16)
+    odt = oracle.F16 if c["dt"] == torch.float16 else oracle.BF16
+    ro, rl = oracle.gqa_varlen(qb, x.bits("k"), x.bits("v"), vq.cu_q.numpy(), x.cu_seqlens.numpy(), c["Hkv"],
+                               spec.scale, odt, causal=c["causal"])
+    gate(out, ro, c["dt"], lse, rl, where=where)
