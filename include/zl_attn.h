@@ -311,7 +311,11 @@ ZL_API zl_status_t zl_attn_varlen_mla_ex(const void *q, const void *kv_cache, co
  * block_table[b * max_pages_per_seq + i / page_size].  cu_seqlens_k gives
  * only the lengths here (its values are not row indices into the pools).
  * Preconditions as for the paged decode calls (every page id names a page
- * of the pools, max_seqlen_k <= max_pages_per_seq * page_size).
+ * of the pools, max_seqlen_k <= max_pages_per_seq * page_size).  A null
+ * cu_seqlens_q or block_table returns ZL_ERR_INVALID_ARGUMENT (the packed or
+ * one-token calls serve those cases); every other check and status is that
+ * of the varlen and paged calls.  Outputs, lse and workspace are owned by the
+ * caller; the call is asynchronous on `stream`.
  */
 ZL_API zl_status_t zl_attn_varlen_gqa_paged(const void *q, const void *k_pages, const void *v_pages,
                                             const int32_t *block_table, int max_pages_per_seq, int page_size,
