@@ -420,6 +420,12 @@ prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, int nblocks) {
       nvc[cb] = nv < lv ? nv : lv;
     }
     const bool full = nv == 32 && 32 * i + 31 <= lim_min;
+    // The next scores and this tile's softmax run at raised wave priority:
+    // when both waves of a SIMD can issue, the one in this mixed matrix and
+    // vector phase goes first, and the other's PV MFMAs fill the matrix
+    // unit behind it (measured 1-3% faster than no priority; raising the
+    // PV phase instead was slower).
+    __builtin_amdgcn_s_setprio(1);
     if (more && full) {
       pf_scores<DT, D>(smem, offn, qop, sb[NXT]);
       pf_softmax4<DT, false>(sb[CUR], g, nvc, scale_log2, sm, grow, dexp, psum, pop);
@@ -429,6 +435,7 @@ prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, int nblocks) {
     } else {
       pf_softmax4<DT, true>(sb[CUR], g, nvc, scale_log2, sm, grow, dexp, psum, pop);
     }
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int cb = 0; cb < kPfCB; ++cb) {
       // Rescale only when some column's running maximum moved.
