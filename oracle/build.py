@@ -10,7 +10,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 def build(verbose: bool = False) -> str:
     """Compile zl_oracle.c with gcc (-O2, OpenMP, strict IEEE) and return the path."""
-    cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC",
+    cmd = ["gcc", "-O3", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC",
            "-shared", "-std=c11", "-Wall", "-Wextra", "-o", LIB + ".tmp", SRC, "-lm"]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)

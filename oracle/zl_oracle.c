@@ -83,12 +83,26 @@ double zo_bf16_to_f64(uint16_t h)
     return sign ? -v : v;
 }
 
-static double dec(uint16_t h, int dtype)
+/* The two decoders above, memoised for all 65,536 patterns when the library
+ * loads (a lookup returns exactly the value the function computes). */
+static double f16_values[65536];
+static double bf16_values[65536];
+
+__attribute__((constructor)) static void zo_fill_decode_tables(void)
 {
-    return dtype == ZO_BF16 ? zo_bf16_to_f64(h) : zo_f16_to_f64(h);
+    for (int i = 0; i < 65536; ++i) {
+        f16_values[i] = zo_f16_to_f64((uint16_t)i);
+        bf16_values[i] = zo_bf16_to_f64((uint16_t)i);
+    }
 }
 
-/* One query row against L key/value rows.  s is scratch of at least L. */
+static double dec(uint16_t h, int dtype)
+{
+    return dtype == ZO_BF16 ? bf16_values[h] : f16_values[h];
+}
+
+/* One query row against L key/value rows.  s is scratch of at least L + dk
+ * doubles (the weights, then the decoded query row). */
 static void attend_one(const uint16_t *q, const uint16_t *k, long k_stride,
                        const uint16_t *v, long v_stride, int L, int dk, int dv,
                        double scale, int dtype, double *out, double *lse,
@@ -100,10 +114,13 @@ static void attend_one(const uint16_t *q, const uint16_t *k, long k_stride,
         *lse = -INFINITY;
         return;
     }
+    double *qd = s + L;
+    for (int d = 0; d < dk; ++d)
+        qd[d] = dec(q[d], dtype);
     for (int i = 0; i < L; ++i) {
         double acc = 0.0;
         for (int d = 0; d < dk; ++d)
-            acc += dec(q[d], dtype) * dec(k[(long)i * k_stride + d], dtype);
+            acc += qd[d] * dec(k[(long)i * k_stride + d], dtype);
         s[i] = scale * acc;
     }
     double m = s[0];
@@ -115,12 +132,17 @@ static void attend_one(const uint16_t *q, const uint16_t *k, long k_stride,
         s[i] = exp(s[i] - m); /* s now holds the weights w_i */
         l += s[i];
     }
-    for (int e = 0; e < dv; ++e) {
-        double acc = 0.0;
-        for (int i = 0; i < L; ++i)
-            acc += s[i] * dec(v[(long)i * v_stride + e], dtype);
-        out[e] = acc / l;
+    /* out[e] = (sum over i, in order, of w_i * V[i][e]) / l; the rows of V
+     * are walked in token order, each adding its term to every out[e]. */
+    for (int e = 0; e < dv; ++e)
+        out[e] = 0.0;
+    for (int i = 0; i < L; ++i) {
+        const uint16_t *vrow = v + (long)i * v_stride;
+        for (int e = 0; e < dv; ++e)
+            out[e] += s[i] * dec(vrow[e], dtype);
     }
+    for (int e = 0; e < dv; ++e)
+        out[e] /= l;
     *lse = m + log(l);
 }
 
@@ -162,7 +184,7 @@ int zo_decode_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     int bad = 0;
 #pragma omp parallel
     {
-        double *s = (double *)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
+        double *s = (double *)malloc(sizeof(double) * ((size_t)max_len + (size_t)dk));
         if (!s) {
 #pragma omp atomic write
             bad = 1;
@@ -232,7 +254,7 @@ int zo_varlen_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     int bad = 0;
 #pragma omp parallel
     {
-        double *s = (double *)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
+        double *s = (double *)malloc(sizeof(double) * ((size_t)max_len + (size_t)dk));
         if (!s) {
 #pragma omp atomic write
             bad = 1;

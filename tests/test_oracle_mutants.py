@@ -20,15 +20,15 @@ from . import test_oracle_pins as pins
 MUTANTS = {
     "drop-scale": ("s[i] = scale * acc;", "s[i] = acc;"),
     "interleaved-head-map": ("int g = h / group;", "int g = h % num_kv_heads;"),
-    "no-normalisation": ("out[e] = acc / l;", "out[e] = acc;"),
+    "no-normalisation": ("out[e] /= l;", "out[e] /= 1.0;"),
     "lse-log2": ("*lse = m + log(l);", "*lse = m + log2(l);"),
     "lse-without-max": ("*lse = m + log(l);", "*lse = log(l);"),
     "weight-sign": ("s[i] = exp(s[i] - m);", "s[i] = exp(m - s[i]);"),
-    "v-dims-reversed": ("acc += s[i] * dec(v[(long)i * v_stride + e], dtype);",
-                        "acc += s[i] * dec(v[(long)i * v_stride + (dv - 1 - e)], dtype);"),
+    "v-dims-reversed": ("out[e] += s[i] * dec(vrow[e], dtype);",
+                        "out[e] += s[i] * dec(vrow[dv - 1 - e], dtype);"),
     "k-stride-ignored": ("dec(k[(long)i * k_stride + d], dtype)", "dec(k[(long)i * dk + d], dtype)"),
-    "last-token-dropped-in-pv": ("for (int i = 0; i < L; ++i)\n            acc += s[i]",
-                                 "for (int i = 0; i < L - 1; ++i)\n            acc += s[i]"),
+    "last-token-dropped-in-pv": ("for (int i = 0; i < L; ++i) {\n        const uint16_t *vrow",
+                                 "for (int i = 0; i < L - 1; ++i) {\n        const uint16_t *vrow"),
     "sequence-base-unscaled": ("k + (long)cu[b] * k_row_stride + (long)g * dk",
                                "k + (long)cu[b] + (long)g * dk"),
     "combine-weight-unshifted": ("double w = exp(part_lse[(long)s * rows + r] - M);",
