@@ -13,6 +13,7 @@ import torch
 
 import oracle
 import workloads
+from tests.guard import CallBuffers
 from tests.parity import gate
 
 pytestmark = pytest.mark.gpu
@@ -94,7 +95,14 @@ def test_random_case(i):
         c["causal"] = True  # decode has no mask switch: one new token sees its whole cache
 
     dq, ck = q.to(DEV), x.cu_seqlens.to(DEV)
-    kw = dict(num_workers=c["workers"], return_lse=True)
+    if s.kind == "mla":
+        ws = zl.zl_decode_attn_mla_workspace_size(s.batch, s.num_q_heads, 512, 64, x.max_seqlen, s.torch_dtype,
+                                                  c["workers"])
+    else:
+        ws = zl.zl_decode_attn_workspace_size(s.batch, s.num_q_heads, s.num_kv_heads, s.head_dim_k, x.max_seqlen,
+                                              s.torch_dtype, c["workers"])
+    bufs = CallBuffers(q.shape[0], s.num_q_heads, s.head_dim_v, s.torch_dtype, DEV, ws)
+    kw = dict(num_workers=c["workers"], **bufs.kwargs())
     px = workloads.make_paged(x, c["paged"], seed=i) if c["paged"] else None
     bt = px.block_table.to(DEV) if px else None
     mla = s.kind == "mla"
@@ -123,6 +131,7 @@ def test_random_case(i):
         else:
             out, lse = zl.zl_decode_attn_gqa(dq, x.k.to(DEV), x.v.to(DEV), ck, x.max_seqlen, s.scale, **kw)
     torch.cuda.synchronize()
+    bufs.check(where)
 
     # The oracle on the packed rows (paged pools hold the same rows).
     qb = q.contiguous().view(torch.int16).numpy().view(np.uint16)
@@ -177,9 +186,11 @@ def test_random_prefill_case(i):
         pytest.skip("no new tokens drawn")
     x = workloads.make_inputs(spec)
     vq = workloads.make_varlen_query(x, c["q_lens"], seed=c["seed"])
+    bufs = CallBuffers(vq.total_q, spec.num_q_heads, spec.head_dim_v, spec.torch_dtype, DEV)
     out, lse = zl.zl_attn_prefill_gqa(vq.q.to(DEV), x.k.to(DEV), x.v.to(DEV), vq.cu_q.to(DEV), x.cu_seqlens.to(DEV),
-                                      x.max_seqlen, spec.scale, causal=c["causal"], return_lse=True)
+                                      x.max_seqlen, spec.scale, causal=c["causal"], **bufs.kwargs())
     torch.cuda.synchronize()
+    bufs.check(where)
     qb = vq.q.contiguous().view(torch.int16).numpy().view(np.uint16)
     odt = oracle.F16 if c["dt"] == torch.float16 else oracle.BF16
     ro, rl = oracle.gqa_varlen(qb, x.bits("k"), x.bits("v"), vq.cu_q.numpy(), x.cu_seqlens.numpy(), c["Hkv"],
