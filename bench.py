@@ -3,23 +3,35 @@
 One step = one call of the fused decode attention for the whole batch: the
 decode kernel (every K/V byte streamed once, split evenly over the workers)
 then the split-merge kernel (log-sum-exp combine of the sequences that several
-workers share), on synthetic inputs already resident in HBM.  The timed region
-is K such calls back to back; a second pass of K calls with an event around
-each kernel gives the decode kernel's own duration for the roofline.  Inputs are replicated
-R = max(2, ceil(1 GiB / bytes)) times and the steps cycle through the
-replicas, so the 256 MB Infinity Cache cannot serve a step from the previous
-one.
+workers share), on synthetic inputs already resident in HBM.  Inputs are
+replicated R = max(2, ceil(1 GiB / bytes)) times and the steps cycle through
+the replicas, so the 256 MB Infinity Cache cannot serve a step from the
+previous one.
+
+The headline workload (--config, default 4: the largest that the workloads
+name) is timed first; then, unless --single, every workload is timed the same
+way in the same process and listed in `per_config`.  Per workload:
+  us_per_step   K whole calls back to back, events only at the two ends
+  kernel_us     K decode-kernel launches back to back (no merge), events at
+                the ends: the kernel's duration plus the launch gap, the
+                figure a kernel trace compares with
+  kernel_us_bracketed  each decode launch between its own events (adds the
+                event overhead), and merge_us_bracketed likewise
+  read_ceiling_us  a plain streaming read of the same bytes at the decode
+                kernel's launch shape and load instruction, with no arithmetic
+                (zl_hbm_read_probe): what a read alone reaches at that size
+Fractions are algorithmic bytes (every K and V element, or every latent row,
+read once) / time / 8 TB/s.
 
 Prints one JSON line:
-  value      KV GB/s = algorithmic bytes (every K and V element, or every
-             latent row, read once) / time per step
-  roofline   the decode kernel against the 8 TB/s HBM peak; achieved = the
-             same bytes / the kernel's average duration, from HIP events
-             recorded around every launch on the launch stream (these include
-             the launch's dispatch, about 2 us more than a kernel trace shows);
-             traffic and mfma_busy come from the committed rocprofv3 counter
-             record when it was taken on the current kernel sources
-  cpu_baseline  the fp64 oracle on the host cores, on a bounded sample
+  value      KV GB/s of the headline workload = algorithmic bytes / us_per_step
+  roofline   the headline's decode kernel against the 8 TB/s HBM peak
+             (achieved = bytes / kernel_us); traffic and mfma_busy come from
+             the committed rocprofv3 counter record when it was taken on the
+             current kernel sources
+  cpu_baseline  the fp64 oracle on the host cores, on a bounded sample of the
+             headline workload
+  per_config every workload, as above
 """
 from __future__ import annotations
 
@@ -68,8 +80,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
-                    help="workload (default 2: batch 32, 32/8 heads, D 128, ragged 512..4096)")
+    ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5],
+                    help="headline workload (default 4, the largest: batch 8, 32/8 heads, D 128, every "
+                         "sequence 32768 tokens, bf16)")
+    ap.add_argument("--single", action="store_true",
+                    help="time the headline workload only (default: also every other workload, in per_config)")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the plain-read ceiling beside each workload")
     ap.add_argument("--workers", type=int, default=0, help="decode workers (0 = library default)")
     ap.add_argument("--q-len", type=int, default=1, metavar="N",
                     help="new query tokens per sequence (N > 1: draft tokens checked in one step, "
@@ -126,147 +143,33 @@ def main():
         bench_prefill(args)
         return
 
-    import numpy as np
-    import torch
-
-    import mla_attention_amd as zl
-    import workloads
-
-    spec = workloads.WORKLOADS[args.config]
-    dev = torch.device("cuda:0")
-    x = workloads.make_inputs(spec)
-    kv_bytes = x.kv_bytes()
-    reps = max(2, math.ceil((1 << 30) / kv_bytes))
     if args.profile_run:
-        reps = 1
-    vq = workloads.make_varlen_query(x, [args.q_len] * spec.batch, seed=args.config) if args.q_len > 1 else None
-    cu = x.cu_seqlens.to(dev)
-    q = vq.q.to(dev) if vq else x.q.to(dev)
-    cu_q = vq.cu_q.to(dev) if vq else None
-    paged = workloads.make_paged(x, args.paged) if args.paged else None
-    table = paged.block_table.to(dev) if paged else None
-    if paged:
-        pools = (paged.kv_pages,) if spec.kind == "mla" else (paged.k_pages, paged.v_pages)
-        caches = [tuple(t.to(dev) for t in pools) for _ in range(reps)]
-    else:
-        caches = [(x.latent.to(dev),) if spec.kind == "mla" else (x.k.to(dev), x.v.to(dev))
-                  for _ in range(reps)]
-    if spec.kind == "mla":
-        ws_bytes = zl.zl_decode_attn_mla_workspace_size(spec.batch, spec.num_q_heads, 512, 64,
-                                                        x.max_seqlen, spec.torch_dtype, args.workers)
-    else:
-        ws_bytes = zl.zl_decode_attn_workspace_size(spec.batch, spec.num_q_heads, spec.num_kv_heads,
-                                                    spec.head_dim_k, x.max_seqlen, spec.torch_dtype,
-                                                    args.workers)
-    ws = zl.new_workspace(ws_bytes, dev)
-    rows = q.shape[0]
-    out = torch.empty(rows, spec.num_q_heads, spec.head_dim_v, dtype=spec.torch_dtype, device=dev)
-    lse = torch.empty(rows, spec.num_q_heads, dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream(dev)
-
-    def step(i, phases=3):
-        c = caches[i % reps]
-        if vq is not None and paged and spec.kind == "mla":
-            zl.zl_attn_varlen_mla_paged(q, c[0], table, cu_q, cu, x.max_seqlen, spec.scale, out=out, lse=lse,
-                                        workspace=ws, num_workers=args.workers, stream=stream, phases=phases)
-        elif vq is not None and paged:
-            zl.zl_attn_varlen_gqa_paged(q, c[0], c[1], table, cu_q, cu, x.max_seqlen, spec.scale, out=out,
-                                        lse=lse, workspace=ws, num_workers=args.workers, stream=stream,
-                                        phases=phases)
-        elif vq is not None and spec.kind == "mla":
-            zl.zl_attn_varlen_mla(q, c[0], cu_q, cu, x.max_seqlen, spec.scale, out=out, lse=lse, workspace=ws,
-                                  num_workers=args.workers, stream=stream, phases=phases)
-        elif vq is not None:
-            zl.zl_attn_varlen_gqa(q, c[0], c[1], cu_q, cu, x.max_seqlen, spec.scale, out=out, lse=lse,
-                                  workspace=ws, num_workers=args.workers, stream=stream, phases=phases)
-        elif paged and spec.kind == "mla":
-            zl.zl_decode_attn_mla_paged(q, c[0], table, cu, x.max_seqlen, spec.scale, out=out, lse=lse,
-                                        workspace=ws, num_workers=args.workers, stream=stream, phases=phases)
-        elif paged:
-            zl.zl_decode_attn_gqa_paged(q, c[0], c[1], table, cu, x.max_seqlen, spec.scale, out=out, lse=lse,
-                                        workspace=ws, num_workers=args.workers, stream=stream, phases=phases)
-        elif spec.kind == "mla":
-            zl.zl_decode_attn_mla(q, c[0], cu, x.max_seqlen, spec.scale, out=out, lse=lse, workspace=ws,
-                                  num_workers=args.workers, stream=stream, phases=phases)
-        else:
-            zl.zl_decode_attn_gqa(q, c[0], c[1], cu, x.max_seqlen, spec.scale, out=out, lse=lse,
-                                  workspace=ws, num_workers=args.workers, stream=stream, phases=phases)
-
-    if args.profile_run:
-        for i in range(max(3, args.steps)):
-            step(i)
-        torch.cuda.synchronize()
-        print(f"profile run: {spec.name}{' paged' if paged else ''}, {max(3, args.steps)} launches", flush=True)
+        decode_profile_run(args)
         return
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # Timed region: K whole calls (decode kernel + merge kernel), back to back
-    # on the launch stream, events only at the two ends.
-    K = args.steps
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(K):
-        step(args.warmup + i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3
-    ms_per_step = ev0.elapsed_time(ev1) / K
-    value_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
-
-    # Per-kernel pass for the roofline: the same K steps with the two phases
-    # of each call enqueued separately and an event around each launch.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    torch.cuda.synchronize()
-    for i in range(K):
-        ev[i][0].record(stream)
-        step(args.warmup + K + i, phases=1)
-        ev[i][1].record(stream)
-        step(args.warmup + K + i, phases=2)
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    kern_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]))
-    merge_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]))
-    achieved_gbs = kv_bytes / (kern_ms * 1e-3) / 1e9
-
-    # Per-call spread: K more whole calls, each between two events (the
-    # events add a little to each interval; the headline is the span above).
-    evc = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
-    torch.cuda.synchronize()
-    for i in range(K):
-        evc[i][0].record(stream)
-        step(args.warmup + 2 * K + i)
-        evc[i][1].record(stream)
-    torch.cuda.synchronize()
-    per_call_us = np.array([a.elapsed_time(b) * 1e3 for a, b in evc])
-    spread = {"p10": round(float(np.percentile(per_call_us, 10)), 2),
-              "p50": round(float(np.percentile(per_call_us, 50)), 2),
-              "p90": round(float(np.percentile(per_call_us, 90)), 2)}
-    workload = spec.name + (f"+paged{args.paged}" if paged else "") + (f"+q{args.q_len}" if vq else "")
-    prof = profile_record(workload)
-
+    head = bench_decode(args.config, args)
+    spec = head["spec"]
     cpu = None
-    if not args.no_cpu and vq is None:  # (the oracle baseline covers one new token per sequence)
-        cpu = cpu_baseline(x, spec, args.cpu_seconds)
-
-    # Useful matrix flops of one step: QK^T and PV, 2 flops per multiply-add.
-    flops = 2.0 * x.total_tokens * spec.num_q_heads * (spec.head_dim_k + spec.head_dim_v) * args.q_len
+    if not args.no_cpu and args.q_len == 1:  # (the oracle baseline covers one new token per sequence)
+        cpu = cpu_baseline(head["inputs"], spec, args.cpu_seconds)
+    per_config = []
+    if not args.single:
+        for c in sorted(WORKLOAD_IDS):
+            per_config.append(head["summary"] if c == args.config else bench_decode(c, args)["summary"])
+    workload = head["summary"]["workload"]
+    prof = profile_record(workload)
+    x = head["inputs"]
     rec = {
         "metric": "decode-attn KV GB/s (algorithmic K+V bytes / step time) and us/step, % of MI355X HBM peak",
-        "value": round(value_gbs, 1),
+        "value": round(head["value_gbs"], 1),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "us_per_step": round(ms_per_step * 1e3, 2),
-        "us_per_call_percentiles": spread,
-        "hbm_peak_frac": round(value_gbs / HBM_PEAK_GBS, 4),
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "us_per_step": round(head["ms_per_step"] * 1e3, 2),
+        "us_per_call_percentiles": head["spread"],
+        "hbm_peak_frac": round(head["value_gbs"] / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -282,29 +185,238 @@ def main():
             "ctx_lens": list(spec.lens) if not isinstance(spec.lens[0], str) else
             f"uniform[{spec.lens[1]},{spec.lens[2]}] seed {spec.seed}",
             "total_tokens": x.total_tokens,
-            "kv_bytes_per_step": kv_bytes,
-            "cold_cache_replicas": reps,
+            "kv_bytes_per_step": x.kv_bytes(),
+            "cold_cache_replicas": head["reps"],
             "workers": args.workers or "default",
-            "kv_layout": f"paged, {args.paged}-token pages in a shuffled pool" if paged else "packed rows",
+            "kv_layout": f"paged, {args.paged}-token pages in a shuffled pool" if args.paged else "packed rows",
             "new_tokens_per_seq": args.q_len,
         },
         "roofline": {
             "bound": "hbm",
             "kernel": "mla_decode_kernel" if spec.kind == "mla" else "decode_kernel",
-            "achieved": round(achieved_gbs, 1),
+            "achieved": round(head["kernel_gbs"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "frac": round(head["kernel_gbs"] / HBM_PEAK_GBS, 4),
             "traffic": prof.get("hbm_bytes_per_launch"),
-            "avg_launch_us": round(kern_ms * 1e3, 2),
-            "merge_launch_us": round(merge_ms * 1e3, 2),
+            "avg_launch_us": round(head["kernel_ms"] * 1e3, 2),
+            "avg_launch_us_bracketed": round(head["kernel_ms_bracketed"] * 1e3, 2),
+            "merge_launch_us": round(head["merge_ms"] * 1e3, 2),
             "mfma_busy": prof.get("mfma_busy_frac"),
-            "math_tflops": round(flops / (kern_ms * 1e-3) / 1e12, 2),
+            "math_tflops": round(head["flops"] / (head["kernel_ms"] * 1e-3) / 1e12, 2),
+            "read_ceiling_us": head["summary"].get("read_ceiling_us"),
         },
         "cpu_baseline": cpu,
-        "wall_ms_timed_region": round(wall_ms, 2),
+        "per_config": per_config,
+        "wall_ms_timed_region": round(head["wall_ms"], 2),
     }
     print(json.dumps(rec), flush=True)
+
+
+WORKLOAD_IDS = (1, 2, 3, 4, 5)
+
+
+class DecodeRig:
+    """Inputs of one workload resident in HBM (R cold-cache replicas of the
+    caches), its output and workspace, and one step = one library call."""
+
+    def __init__(self, cfg, args, reps_override=None):
+        import torch
+
+        import mla_attention_amd as zl
+        import workloads
+
+        self.zl = zl
+        self.args = args
+        spec = self.spec = workloads.WORKLOADS[cfg]
+        dev = self.dev = torch.device("cuda:0")
+        x = self.x = workloads.make_inputs(spec)
+        self.kv_bytes = x.kv_bytes()
+        self.reps = reps_override or max(2, math.ceil((1 << 30) / self.kv_bytes))
+        q_len = args.q_len
+        self.vq = vq = workloads.make_varlen_query(x, [q_len] * spec.batch, seed=cfg) if q_len > 1 else None
+        self.cu = x.cu_seqlens.to(dev)
+        self.q = vq.q.to(dev) if vq else x.q.to(dev)
+        self.cu_q = vq.cu_q.to(dev) if vq else None
+        paged = self.paged = workloads.make_paged(x, args.paged) if args.paged else None
+        self.table = paged.block_table.to(dev) if paged else None
+        if paged:
+            pools = (paged.kv_pages,) if spec.kind == "mla" else (paged.k_pages, paged.v_pages)
+            self.caches = [tuple(t.to(dev) for t in pools) for _ in range(self.reps)]
+        else:
+            self.caches = [(x.latent.to(dev),) if spec.kind == "mla" else (x.k.to(dev), x.v.to(dev))
+                           for _ in range(self.reps)]
+        if spec.kind == "mla":
+            ws_bytes = zl.zl_decode_attn_mla_workspace_size(spec.batch, spec.num_q_heads, 512, 64, x.max_seqlen,
+                                                            spec.torch_dtype, args.workers)
+        else:
+            ws_bytes = zl.zl_decode_attn_workspace_size(spec.batch, spec.num_q_heads, spec.num_kv_heads,
+                                                        spec.head_dim_k, x.max_seqlen, spec.torch_dtype,
+                                                        args.workers)
+        self.ws = zl.new_workspace(ws_bytes, dev)
+        rows = self.q.shape[0]
+        self.out = torch.empty(rows, spec.num_q_heads, spec.head_dim_v, dtype=spec.torch_dtype, device=dev)
+        self.lse = torch.empty(rows, spec.num_q_heads, dtype=torch.float32, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+        self.name = spec.name + (f"+paged{args.paged}" if paged else "") + (f"+q{q_len}" if vq else "")
+
+    def step(self, i, phases=3):
+        zl, spec, x, a = self.zl, self.spec, self.x, self.args
+        c = self.caches[i % self.reps]
+        kw = dict(out=self.out, lse=self.lse, workspace=self.ws, num_workers=a.workers, stream=self.stream,
+                  phases=phases)
+        mla = spec.kind == "mla"
+        if self.vq is not None and self.paged is not None:
+            if mla:
+                zl.zl_attn_varlen_mla_paged(self.q, c[0], self.table, self.cu_q, self.cu, x.max_seqlen, spec.scale,
+                                            **kw)
+            else:
+                zl.zl_attn_varlen_gqa_paged(self.q, c[0], c[1], self.table, self.cu_q, self.cu, x.max_seqlen,
+                                            spec.scale, **kw)
+        elif self.vq is not None:
+            if mla:
+                zl.zl_attn_varlen_mla(self.q, c[0], self.cu_q, self.cu, x.max_seqlen, spec.scale, **kw)
+            else:
+                zl.zl_attn_varlen_gqa(self.q, c[0], c[1], self.cu_q, self.cu, x.max_seqlen, spec.scale, **kw)
+        elif self.paged is not None:
+            if mla:
+                zl.zl_decode_attn_mla_paged(self.q, c[0], self.table, self.cu, x.max_seqlen, spec.scale, **kw)
+            else:
+                zl.zl_decode_attn_gqa_paged(self.q, c[0], c[1], self.table, self.cu, x.max_seqlen, spec.scale, **kw)
+        elif mla:
+            zl.zl_decode_attn_mla(self.q, c[0], self.cu, x.max_seqlen, spec.scale, **kw)
+        else:
+            zl.zl_decode_attn_gqa(self.q, c[0], c[1], self.cu, x.max_seqlen, spec.scale, **kw)
+
+
+def decode_profile_run(args):
+    """A few whole calls only, for rocprofv3 counter passes (no JSON)."""
+    import torch
+
+    rig = DecodeRig(args.config, args, reps_override=1)
+    n = max(3, args.steps)
+    for i in range(n):
+        rig.step(i)
+    torch.cuda.synchronize()
+    print(f"profile run: {rig.name}, {n} launches", flush=True)
+
+
+def timed_span(stream, fn, K):
+    """Milliseconds per call of K back-to-back fn(i) on `stream`, with events
+    only at the two ends."""
+    import torch
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(K):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / K
+
+
+def bench_decode(cfg, args):
+    """Time one workload: whole calls back to back (the headline), the decode
+    kernel alone back to back (its duration for the roofline), each launch
+    between its own events, per-call spread, and the read ceiling."""
+    import numpy as np
+    import torch
+
+    rig = DecodeRig(cfg, args)
+    spec, x, stream = rig.spec, rig.x, rig.stream
+    K, W = args.steps, args.warmup
+    for i in range(W):
+        rig.step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: K whole calls (decode kernel + merge kernel), back to back
+    # on the launch stream, events only at the two ends.
+    t0 = time.perf_counter()
+    ms_per_step = timed_span(stream, lambda i: rig.step(W + i), K)
+    wall_ms = (time.perf_counter() - t0) * 1e3
+
+    # The decode kernel alone: K launches back to back (each leaves its
+    # partials in the workspace; the next overwrites them), events at the
+    # ends: its average duration plus the gap between launches, as close to a
+    # kernel trace as events on the launch stream get.
+    kernel_ms = timed_span(stream, lambda i: rig.step(W + K + i, phases=1), K)
+
+    # Each launch between its own events (these add the event overhead).
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        ev[i][0].record(stream)
+        rig.step(W + 2 * K + i, phases=1)
+        ev[i][1].record(stream)
+        rig.step(W + 2 * K + i, phases=2)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    kern_br = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]))
+    merge_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]))
+
+    # Per-call spread: K more whole calls, each between two events.
+    evc = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        evc[i][0].record(stream)
+        rig.step(W + 3 * K + i)
+        evc[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_call_us = np.array([a.elapsed_time(b) * 1e3 for a, b in evc])
+    spread = {"p10": round(float(np.percentile(per_call_us, 10)), 2),
+              "p50": round(float(np.percentile(per_call_us, 50)), 2),
+              "p90": round(float(np.percentile(per_call_us, 90)), 2)}
+
+    kv = rig.kv_bytes
+    summary = {
+        "config": cfg,
+        "workload": rig.name,
+        "dtype": spec.dtype,
+        "kv_bytes": kv,
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "step_frac": round(kv / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernel_us": round(kernel_ms * 1e3, 2),
+        "kernel_frac": round(kv / (kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernel_us_bracketed": round(kern_br * 1e3, 2),
+        "kernel_frac_bracketed": round(kv / (kern_br * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "merge_us_bracketed": round(merge_ms * 1e3, 2),
+    }
+    if not args.no_read_ceiling and rig.paged is None and rig.vq is None:
+        summary.update(read_ceiling(rig, K, W))
+    del rig.caches
+    torch.cuda.empty_cache()
+    flops = 2.0 * x.total_tokens * spec.num_q_heads * (spec.head_dim_k + spec.head_dim_v) * args.q_len
+    return {"spec": spec, "inputs": x, "reps": rig.reps, "ms_per_step": ms_per_step, "wall_ms": wall_ms,
+            "value_gbs": kv / (ms_per_step * 1e-3) / 1e9, "kernel_ms": kernel_ms, "kernel_ms_bracketed": kern_br,
+            "kernel_gbs": kv / (kernel_ms * 1e-3) / 1e9, "merge_ms": merge_ms, "spread": spread,
+            "flops": flops, "summary": summary}
+
+
+def read_ceiling(rig, K, W):
+    """A plain streaming read of the same byte count at the decode kernel's
+    launch shape (zl_hbm_read_probe: its load instruction and ring, no
+    arithmetic), cold-cache replicas as for the decode steps."""
+    import torch
+
+    zl, spec = rig.zl, rig.spec
+    nbytes = rig.kv_bytes // 1024 * 1024
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=rig.dev) for _ in range(rig.reps)]
+    for b in bufs:
+        b.fill_(1)
+    wg = rig.args.workers or {64: 1536, 128: 768, 576: 256}[spec.head_dim_k]
+    sink = torch.empty(wg, dtype=torch.int32, device=rig.dev)
+
+    def rd(i):
+        zl.zl_hbm_read_probe(bufs[i % rig.reps], spec.head_dim_k, workgroups=rig.args.workers, sink=sink,
+                             stream=rig.stream)
+    for i in range(W):
+        rd(i)
+    ms = timed_span(rig.stream, lambda i: rd(W + i), K)
+    del bufs
+    return {"read_ceiling_us": round(ms * 1e3, 2),
+            "read_ceiling_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "read_ceiling_workgroups": wg}
 
 
 MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16

@@ -88,6 +88,7 @@ SIGNATURES = {
     "zl_int8_quantize": (_c_int, [_vp, _c_int, ctypes.c_longlong, _c_int, _vp, _vp, _vp]),
     "zl_int8_dequantize": (_c_int, [_vp, _vp, ctypes.c_longlong, _c_int, _c_int, _vp, _vp]),
     "zl_int8_reduce_step": (_c_int, [_vp, _vp, _vp, _c_int, ctypes.c_longlong, _c_int, _vp, _vp, _vp, _vp]),
+    "zl_hbm_read_probe": (_c_int, [_vp, _c_size, _c_int, _c_int, _vp, _vp]),
     "zl_status_string": (ctypes.c_char_p, [_c_int]),
 }
 
@@ -584,3 +585,23 @@ def zl_int8_reduce_step(codes_in, scales_in, local, chunk: int = 512, code_out: 
                                        _stream(stream, dev))
     _check(st, "zl_int8_reduce_step")
     return codes_out, scales_out, sum_out
+
+
+# ------------------------------------------------------------- measurement aid
+def zl_hbm_read_probe(src: torch.Tensor, head_dim_k: int, workgroups: int = 0, sink=None, stream=None):
+    """Stream src's bytes (whole 1 KB blocks) through LDS at the launch shape
+    of the decode kernel for head_dim_k (64 / 128: GQA, 576: MLA), with no
+    arithmetic.  sink: uint32-sized int32 tensor of one word per workgroup
+    (allocated here when omitted).  Returns sink."""
+    _need(src, "src")
+    dev = src.device
+    wg = workgroups or {64: 1536, 128: 768, 576: 256}.get(head_dim_k, 8)
+    if sink is None:
+        sink = torch.empty(wg, dtype=torch.int32, device=dev)
+    _need(sink, "sink", torch.int32, 1, dev)
+    if sink.numel() < wg:
+        raise ValueError("sink needs one word per workgroup")
+    st = library().zl_hbm_read_probe(_ptr(src), src.numel() * src.element_size(), int(head_dim_k), int(workgroups),
+                                      _ptr(sink), _stream(stream, dev))
+    _check(st, "zl_hbm_read_probe")
+    return sink

@@ -638,6 +638,19 @@ zl_status_t zl_int8_reduce_step(const int8_t* codes_in, const float* scales_in, 
   return run_codec(a, zl::kCodecReduce, chunk, dtype, stream);
 }
 
+zl_status_t zl_hbm_read_probe(const void* src, size_t bytes, int head_dim_k, int workgroups, uint32_t* sink,
+                              zl_stream_t stream) {
+  if (head_dim_k != 64 && head_dim_k != 128 && head_dim_k != 576) return ZL_ERR_UNSUPPORTED;
+  const int wg = workgroups == 0 ? zl::read_probe_default_workgroups(head_dim_k) : workgroups;
+  if (!workers_ok(wg)) return ZL_ERR_INVALID_ARGUMENT;
+  if (bytes > ((size_t)1 << 46)) return ZL_ERR_INVALID_ARGUMENT;
+  if (bytes < 1024) return ZL_OK;
+  if (!src || !sink || !aligned(src, 16) || !aligned(sink, 4)) return ZL_ERR_INVALID_ARGUMENT;
+  const hipError_t e =
+      zl::launch_read_probe(src, (long long)bytes, head_dim_k, wg, sink, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ZL_OK : ZL_ERR_HIP;
+}
+
 const char* zl_status_string(zl_status_t status) {
   switch (status) {
     case ZL_OK: return "ZL_OK";

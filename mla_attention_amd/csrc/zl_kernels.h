@@ -104,4 +104,11 @@ hipError_t launch_decode(const DecodeArgs& a, Layout layout, int dtype, hipStrea
 hipError_t launch_merge(const DecodeArgs& a, int dv, int dtype, int max_vseqs, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t stream);
 
+// Plain streaming read at a decode kernel's launch shape (hbm_read.hip):
+// head_dim_k 64 / 128 (GQA) or 576 (MLA) picks the shape; workgroups is a
+// multiple of 8; sink holds one word per workgroup.
+int read_probe_default_workgroups(int head_dim_k);
+hipError_t launch_read_probe(const void* src, long long bytes, int head_dim_k, int workgroups, uint32_t* sink,
+                             hipStream_t stream);
+
 }  // namespace zl

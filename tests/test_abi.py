@@ -251,3 +251,16 @@ def test_prefill_entry_point_rejects_bad_arguments(zl):
     assert pf(scale=float("inf")) == 1 and pf(Tq=-1) == 1
     assert pf(Tq=0, q=None, k=None, v=None, cq=None, ck=None, out=None) == 0
     assert pf(Tq=1 << 30, Hq=1024, Hkv=1024) == 2   # 2^22 blocks x 1024 heads
+
+
+def test_read_probe_rejects_bad_arguments(zl):
+    lib = zl.library()
+
+    def rp(**kw):
+        a = dict(src=A, nbytes=1 << 20, D=128, wg=0, sink=A)
+        a.update(kw)
+        return lib.zl_hbm_read_probe(a["src"], a["nbytes"], a["D"], a["wg"], a["sink"], None)
+    assert rp(D=96) == 2 and rp(D=0) == 2
+    assert rp(wg=12) == 1 and rp(wg=-8) == 1 and rp(wg=1 << 17) == 1
+    assert rp(src=None) == 1 and rp(sink=None) == 1 and rp(src=A + 8) == 1 and rp(sink=A + 2) == 1
+    assert rp(nbytes=1000, src=None, sink=None) == 0   # under one block: no-op
