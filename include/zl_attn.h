@@ -114,6 +114,26 @@ ZL_API zl_status_t zl_decode_attn_gqa(const void *q, const void *k_cache, const 
                                void *workspace, size_t workspace_bytes, zl_stream_t stream);
 
 /*
+ * zl_decode_attn_gqa for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same operation, arguments and kernels, with no workspace
+ * argument.  The workspace is a fixed 16 MiB array in device memory that the
+ * library holds on every GPU it runs on until the process ends (the default
+ * worker counts need at most 12.4 MiB, for D = 64 and 128 alike).  A call whose
+ * workspace would exceed it returns ZL_ERR_WORKSPACE_TOO_SMALL; sizes the
+ * plain call rejects get its status.  The first call on a device looks up the
+ * array's device address (one hipGetSymbolAddress); nothing is allocated,
+ * nothing is cleared (the workspace needs no initialisation).  All calls on
+ * one GPU share the array: calls that overlap in time on one GPU race, so
+ * keep them on one stream or order them with events.
+ */
+ZL_API zl_status_t zl_decode_attn_gqa_no_alloc(const void *q, const void *k_cache, const void *v_cache,
+                                               const int32_t *cu_seqlens, int batch, int num_q_heads,
+                                               int num_kv_heads, int head_dim, int max_seqlen_k,
+                                               float softmax_scale, zl_dtype_t dtype, void *out, float *lse,
+                                               zl_stream_t stream);
+
+/*
  * Bytes of device workspace that zl_decode_attn_mla needs (host function,
  * as above).  Returns 0 for invalid sizes.
  */

@@ -89,6 +89,8 @@ SIGNATURES = {
     "zl_int8_dequantize": (_c_int, [_vp, _vp, ctypes.c_longlong, _c_int, _c_int, _vp, _vp]),
     "zl_int8_reduce_step": (_c_int, [_vp, _vp, _vp, _c_int, ctypes.c_longlong, _c_int, _vp, _vp, _vp, _vp]),
     "zl_hbm_read_probe": (_c_int, [_vp, _c_size, _c_int, _c_int, _vp, _vp]),
+    "zl_decode_attn_gqa_no_alloc": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                             _c_float, _c_int, _vp, _vp, _vp]),
     "zl_status_string": (ctypes.c_char_p, [_c_int]),
 }
 
@@ -209,6 +211,40 @@ def zl_decode_attn_gqa(q, k_cache, v_cache, cu_seqlens, max_seqlen_k: int, softm
         float(softmax_scale), _DTYPE[q.dtype], _ptr(out), _ptr(lse), int(num_workers), int(phases),
         _ptr(workspace), workspace.numel(), _stream(stream, dev))
     _check(st, "zl_decode_attn_gqa")
+    return (out, lse) if lse is not None else out
+
+
+def zl_decode_attn_gqa_no_alloc(q, k_cache, v_cache, cu_seqlens, max_seqlen_k: int, softmax_scale: float,
+                                out=None, lse=None, stream=None, return_lse: bool = False):
+    """zl_decode_attn_gqa with the library's fixed device workspace (no
+    workspace argument, nothing allocated by the library; out / lse are
+    allocated here when omitted)."""
+    _need(q, "q", ndim=3)
+    dev = q.device
+    if q.dtype not in _DTYPE:
+        raise ValueError("q must be float16 or bfloat16")
+    _need(k_cache, "k_cache", q.dtype, 3, dev)
+    _need(v_cache, "v_cache", q.dtype, 3, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1, dev)
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    if k_cache.shape[2] != D or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache / v_cache must be [T, Hkv, head_dim] like q")
+    if cu_seqlens.numel() != B + 1:
+        raise ValueError("cu_seqlens must have batch + 1 entries")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, 3, dev)
+    if out.shape != q.shape:
+        raise ValueError("out must be [B, Hq, head_dim]")
+    if lse is None and return_lse:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2, dev)
+    st = library().zl_decode_attn_gqa_no_alloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens), B, Hq, Hkv, D, int(max_seqlen_k),
+        float(softmax_scale), _DTYPE[q.dtype], _ptr(out), _ptr(lse), _stream(stream, dev))
+    _check(st, "zl_decode_attn_gqa_no_alloc")
     return (out, lse) if lse is not None else out
 
 

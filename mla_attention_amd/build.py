@@ -9,7 +9,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libzl_attn.so")
 SOURCES = ["decode_attn.hip", "decode_mla.hip", "split_merge.hip", "attn_combine.hip", "int8_codec.hip", "prefill_attn.hip",
-           "hbm_read.hip", "zl_api.cpp"]
+           "hbm_read.hip", "no_alloc.hip", "zl_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

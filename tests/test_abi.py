@@ -264,3 +264,16 @@ def test_read_probe_rejects_bad_arguments(zl):
     assert rp(wg=12) == 1 and rp(wg=-8) == 1 and rp(wg=1 << 17) == 1
     assert rp(src=None) == 1 and rp(sink=None) == 1 and rp(src=A + 8) == 1 and rp(sink=A + 2) == 1
     assert rp(nbytes=1000, src=None, sink=None) == 0   # under one block: no-op
+
+
+def test_no_alloc_entry_point_rejects_bad_sizes_before_any_hip_call(zl):
+    lib = zl.library()
+
+    def na(**kw):
+        a = dict(q=A, k=A, v=A, cu=A, B=2, Hq=8, Hkv=2, D=128, maxL=100, scale=0.1, dt=0, out=A, lse=None)
+        a.update(kw)
+        return lib.zl_decode_attn_gqa_no_alloc(a["q"], a["k"], a["v"], a["cu"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                                               a["maxL"], a["scale"], a["dt"], a["out"], a["lse"], None)
+    # invalid sizes take the plain call's status, with no HIP call (no GPU here)
+    assert na(D=96) == 2 and na(D=0) == 1 and na(Hq=7) == 1 and na(B=-1) == 1 and na(dt=3) == 1
+    assert na(Hq=40, Hkv=2) == 2   # a group of 20 heads
