@@ -10,12 +10,18 @@
 //  * Work split: every worker streams the same number of (unit, token) rows,
 //    whatever the mix of sequence lengths; see zl_split.h.  Sequences cut
 //    between workers are merged by split_merge.hip, launched right after.
-//  * Data path: 32-token tiles go HBM -> LDS with 16-byte global_load_lds
-//    (no VGPR round trip), each 16-lane group reading contiguous bytes of one
-//    row.  The worker's run is one stream of items through a STAGES-deep LDS
-//    ring (for each segment its query rows, then its tiles), STAGES-1 items
-//    in flight while the oldest is consumed, across segment boundaries.  16-byte slots are XOR-swizzled per row so that both
-//    the MFMA operand reads and the transposing V reads are free of bank
+//  * Data path: a worker's run is one stream of items -- for each segment its
+//    query rows, then its 32-token K/V tiles.  Each item is read with
+//    coalesced 16-byte loads (lane l of load i reads 16-byte chunk 64i + l of
+//    the tile in row-major order, so a load covers whole 128- or 256-byte
+//    rows) into one of two register buffers, two items ahead of the math.
+//    When an item's turn comes its registers are written to LDS in the
+//    swizzled layout the MFMA operand reads need, and the buffer is refilled
+//    with the item two ahead.  (Loads into registers sustain more HBM
+//    bandwidth on gfx950 than the global_load_lds path, which a plain read
+//    of the same bytes and launch shape measures at 71-78% of peak against
+//    78-87% for register loads.)  16-byte slots are XOR-swizzled per row so
+//    that both the operand reads and the transposing V reads are free of bank
 //    conflicts (the LDS bank rules are in zl_tile.h).
 //  * QK^T: v_mfma_f32_16x16x32 with the K tile as A (16 tokens x 32 dims) and
 //    the unit's query heads as B (32 dims x 16 heads, zero-padded when fewer).
@@ -42,7 +48,6 @@ template <>
 struct Geo<kGqaD64> {
   static constexpr int DK = 64, DV = 64;
   static constexpr bool SHARED_KV = false;
-  static constexpr int STAGES = 3;
   static constexpr int WAVES_PER_CU = 6;
   static constexpr int MAX_WAVES_PER_SIMD = 2;
   // 128-byte rows: two rows per 256-byte bank line, so row parity already
@@ -54,7 +59,6 @@ template <>
 struct Geo<kGqaD128> {
   static constexpr int DK = 128, DV = 128;
   static constexpr bool SHARED_KV = false;
-  static constexpr int STAGES = 3;
   static constexpr int WAVES_PER_CU = 3;
   static constexpr int MAX_WAVES_PER_SIMD = 1;
   // 256-byte rows, one bank line each: XOR the 16 slots with the row.
@@ -72,117 +76,52 @@ struct Tile {
   static constexpr int KBYTES = 32 * KROWB;            // one tile of K
   static constexpr int VBYTES = G::SHARED_KV ? 0 : 32 * VROWB;
   static constexpr int STAGE_BYTES = KBYTES + VBYTES;
-  static constexpr int NI_K = KBYTES / 1024;           // 1 KB DMA instructions per tile
+  static constexpr int NI_K = KBYTES / 1024;           // 16-byte loads per lane for a tile of K
   static constexpr int NI_V = VBYTES / 1024;
-  static constexpr int PER_TILE = NI_K + NI_V;
+  static constexpr int NI = NI_K + NI_V;
+  static constexpr int QI = kHeadsPerUnit * KROWB / 1024;  // ... for the 16 query rows
   static constexpr int KSTEPS = DK / 32;
   static constexpr int VBLK = DV / 16;
-  static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "tile must be whole DMA blocks");
+  static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "tile must be whole 1 KB loads");
+  static_assert(QI <= NI_K, "query rows are rows 0-15 of a K tile");
 };
 
-// DMA one tensor's 32-row tile: 1 KB instruction i covers the tile's 16-byte
-// slots 64i .. 64i+63 in row-major order, lane l loading row r = lin / CPR and
-// the global chunk that the swizzle stores in slot lin % CPR (the slot
-// permutation is an involution).  These per-lane byte offsets do not change
-// from tile to tile, so they are computed once: a tile then costs a scalar
-// base (its first row) and one 32-bit offset per instruction.  Rows past
-// nvalid (a segment's last tile) are clamped to row nvalid - 1: finite data,
-// masked out of the softmax.
-template <int L, int NI>
-struct TileMap {
-  uint32_t off[NI];  // r * row_bytes + 16 * chunk
-  int row[NI];       // r
-  uint32_t chunk[NI];
+// Load i of a 32-row tile, lane l: 16-byte chunk lin = 64i + l of the tile in
+// row-major order, i.e. row r = i * RPL + l / CPR (RPL = 64 / CPR rows per
+// load), chunk c = l % CPR, which lands in LDS at row r, slot slot(c, r).
+// The per-lane part is computed once: the global offset grows by RPL rows per
+// load (a wave-uniform step), and the LDS offset is i KB plus one of PERIOD
+// per-lane values (the swizzle depends on r only through bits that repeat
+// every PERIOD loads).  Rows past nvalid (a segment's last tile) are clamped
+// to row nvalid - 1: finite data, masked out of the softmax.
+template <int L, int CPR>
+struct RowLane {
+  static constexpr int RPL = 64 / CPR;
+  // slot(c, r) reads r through bits 0-3 (D = 128: r & 15) or bits 1-3
+  // (D = 64: (r >> 1) & 7); RPL * PERIOD = 16 rows covers both.
+  static constexpr int PERIOD = 16 / RPL;
+  int row0;                // l / CPR
+  uint32_t chunk;          // 16 c
+  uint32_t lpat[PERIOD];   // LDS offset of load k < PERIOD, less k KB
+  __device__ __forceinline__ RowLane(int lane) {
+    row0 = lane / CPR;
+    const int c = lane - row0 * CPR;
+    chunk = 16u * (uint32_t)c;
+#pragma unroll
+    for (int k = 0; k < PERIOD; ++k) {
+      const int r = k * RPL + row0;
+      lpat[k] = (uint32_t)(row0 * CPR + Geo<L>::slot(c, r)) * 16u;
+    }
+  }
+  __device__ __forceinline__ int row(int i) const { return i * RPL + row0; }
+  __device__ __forceinline__ uint32_t loff(int i) const { return (uint32_t)i * 1024u + lpat[i % PERIOD]; }
 };
 
-template <int L, int CPR, int NI>
-__device__ __forceinline__ TileMap<L, NI> tile_map(uint32_t row_bytes, int lane) {
-  TileMap<L, NI> m;
+// N loads' registers into LDS (a whole tensor's tile, or the 16 query rows).
+template <int N, class RL>
+__device__ __forceinline__ void store_rows(ZL_LDS char* st, const RL& m, const u32x4* src) {
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int lin = 64 * i + lane;
-    const int r = lin / CPR;
-    m.row[i] = r;
-    m.chunk[i] = 16u * (uint32_t)Geo<L>::slot(lin - r * CPR, r);
-    m.off[i] = (uint32_t)r * row_bytes + m.chunk[i];
-  }
-  return m;
-}
-
-template <int L, int NI>
-__device__ __forceinline__ void dma_tile(const char* rows, uint32_t row_bytes, const TileMap<L, NI>& m, int nvalid,
-                                         ZL_LDS char* dst) {
-  if (nvalid >= 32) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) dma16_saddr(rows, m.off[i], dst + i * 1024);
-  } else {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int rr = m.row[i] < nvalid ? m.row[i] : nvalid - 1;
-      dma16_saddr(rows, (uint32_t)rr * row_bytes + m.chunk[i], dst + i * 1024);
-    }
-  }
-}
-
-// The same tile from a paged cache: tile rows 0-15 and 16-31 are runs of
-// rows from two scalar bases (one per half of the DMA instructions; the same
-// base unless pages hold 16 tokens).  Rows past nvalid are clamped to row
-// nvalid - 1, which lies in the half whose base the instruction uses.
-template <int L, int NI>
-__device__ __forceinline__ void dma_tile_paged(const char* pool, uint32_t row_bytes, const TileMap<L, NI>& m,
-                                               const TileRows& tr, int nvalid, ZL_LDS char* dst) {
-  static_assert(NI % 2 == 0 && 32 % NI == 0, "each instruction covers 32 / NI whole rows of one 16-row half");
-  const char* b0 = (const char*)((uintptr_t)pool + (uintptr_t)(tr.half0 * row_bytes));
-  const char* b1 = (const char*)((uintptr_t)pool + (uintptr_t)(tr.half1 * row_bytes));
-  if (nvalid >= 32) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) dma16_saddr(i < NI / 2 ? b0 : b1, m.off[i], dst + i * 1024);
-  } else {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int rr = m.row[i] < nvalid ? m.row[i] : nvalid - 1;
-      dma16_saddr(i < NI / 2 ? b0 : b1, (uint32_t)rr * row_bytes + m.chunk[i], dst + i * 1024);
-    }
-  }
-}
-
-// The query item of a segment: rows h0 .. h0+15 (padding rows repeat h0; their
-// results are never stored) in the K-row slot layout, repeated to fill the
-// item's PER_TILE instructions so that every ring item costs the same.
-template <int L>
-__device__ __forceinline__ void dma_query_item(const uint16_t* qb, int nh, ZL_LDS char* dst, int lane) {
-  using TL = Tile<L>;
-  constexpr int QI = kHeadsPerUnit * TL::DK * 2 / 1024;  // 1 KB blocks of query rows
-  static_assert(TL::PER_TILE % QI == 0, "query copies fill the item");
-#pragma unroll
-  for (int i = 0; i < TL::PER_TILE; ++i) {
-    const int lin = 64 * (i % QI) + lane;
-    const int r = lin / TL::KCPR;
-    const int c = Geo<L>::slot(lin - r * TL::KCPR, r);
-    dma16(qb + (long long)(r < nh ? r : 0) * TL::DK + c * 8, dst + i * 1024);
-  }
-}
-
-// The query item of a virtual sequence (several new tokens per sequence): row
-// r of the block is query row 16 hb + r of the sequence (new token (16 hb +
-// r) / G, head kvh*G + (16 hb + r) % G); rows past the sequence's last repeat
-// it.
-template <int L>
-__device__ __forceinline__ void dma_query_item_mq(const uint16_t* q, const VSeqInfo& si, int kvh, int G, int Hq,
-                                                  ZL_LDS char* dst, int lane) {
-  using TL = Tile<L>;
-  constexpr int QI = kHeadsPerUnit * TL::DK * 2 / 1024;
-  static_assert(TL::PER_TILE % QI == 0, "query copies fill the item");
-  const uint16_t* src[QI];
-#pragma unroll
-  for (int i = 0; i < QI; ++i) {
-    const int lin = 64 * i + lane;
-    const int r = lin / TL::KCPR;
-    const int c = Geo<L>::slot(lin - r * TL::KCPR, r);
-    src[i] = q + mq_column(si, r, kvh, G, Hq, false).row * TL::DK + c * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < TL::PER_TILE; ++i) dma16(src[i % QI], dst + i * 1024);
+  for (int i = 0; i < N; ++i) lds_write_b128(st + m.loff(i), src[i]);
 }
 
 template <int L, int DT, bool PAGED, bool MQ>
@@ -191,12 +130,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64),
 decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __restrict__ block_table) {
   using TL = Tile<L>;
   using GE = Geo<L>;
-  constexpr int STAGES = GE::STAGES;
   constexpr int DK = TL::DK, DV = TL::DV;
-  // One LDS object: the ring.  (With a second __shared__ variable the
-  // compiler tracks DMA per object and makes every LDS read wait for all
-  // in-flight DMA.)
-  __shared__ __attribute__((aligned(1024))) char smem_raw[STAGES * TL::STAGE_BYTES];
+  constexpr int NI = TL::NI, NIK = TL::NI_K, QI = TL::QI;
+  // One LDS object: two stages, the item being computed and the next one.
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * TL::STAGE_BYTES];
   ZL_LDS char* smem = (ZL_LDS char*)smem_raw;
 
   const int lane = __lane_id();
@@ -208,27 +145,24 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
   const uint32_t k_row_bytes = (uint32_t)a.Hkv * DK * 2;  // one token's K row (all kv heads)
   const uint32_t v_row_bytes = (uint32_t)a.Hkv * DV * 2;
   const auto slot = [](int c, int r) { return GE::slot(c, r); };
-  const TileMap<L, TL::NI_K> kmap = tile_map<L, TL::KCPR, TL::NI_K>(k_row_bytes, lane);
-  const TileMap<L, TL::NI_V> vmap = tile_map<L, TL::VCPR, TL::NI_V>(v_row_bytes, lane);
+  static_assert(TL::KCPR == TL::VCPR, "K and V rows share the per-lane load map");
+  const RowLane<L, TL::KCPR> rmap(lane);
 
   // (Empty sequences are written by the merge launch: no run covers them.)
   // The batch: decode sequences, or with several new tokens per sequence the
   // virtual sequences of 16 query rows.  Sequence boundaries for the lookups
-  // are loaded here, before any tile load, and waited for, so that no later
-  // lookup has to drain the tile loads in flight (B <= 64).
+  // are loaded here, once, for batches of up to 64 sequences.
   int window = 0;
   VirtualSeqs vs;
   int NB;  // sequences on the work line
   int T;
   if constexpr (MQ) {
     vs.init(a.cu_q, cu, B, a.G, a.seg_cost, kMqRowsLog2);
-    asm volatile("" : "+v"(vs.first.q0), "+v"(vs.first.nq), "+v"(vs.first.k0), "+v"(vs.first.lk));
     NB = vs.V;
     T = vs.T;
   } else {
     T = cu[B];
     window = bounds_window(cu, B, a.seg_cost);
-    asm volatile("" : "+v"(window));
     NB = B;
   }
   const Line line = make_line(T, NB, a.seg_cost);
@@ -236,7 +170,7 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
   const long long per = positions_per_worker(N, a.P);
   const long long p_begin = (long long)w * per;
   const long long p_end = N < p_begin + per ? N : p_begin + per;
-  const auto next_segment = [&](long long p) {
+  const auto next_segment = [&](long long p) __attribute__((always_inline)) {
     if constexpr (MQ)
       return segment_at(p, p_end, line, vs);
     else
@@ -248,17 +182,16 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
   VSeqInfo dsi{}, sgi{};  // several new tokens: the virtual sequences of ds, sg
   if constexpr (MQ) dsi = vs.info(ds.b);
 
-  // The run is one stream of ring items: for every segment (the part of one
+  // The run is one stream of items: for every segment (the part of one
   // sequence of one work unit in the run) its query rows, then its 32-token
-  // K/V tiles.  Loads run STAGES-1 items ahead of the math, across segment
+  // K/V tiles.  Items go to registers two ahead of the math, across segment
   // boundaries, so a new segment does not drain the pipeline.
   int dj = 0;  // next item of segment ds: 0 = query rows, 1 + k = tile k
   bool dmore = true;
-  int issued = 0;
-  // Paged caches: the page ids of the next tile to issue, read one item ahead
+  // Paged caches: the page ids of the next tile to load, read one item ahead
   // so that the scalar loads' latency passes under a tile of math.
   TileRows pf{0, 0};
-  auto prefetch_pages = [&]() {
+  auto prefetch_pages = [&]() __attribute__((always_inline)) {
     if constexpr (PAGED) {
       if (dmore && dj >= 1) {
         const int k = dj - 1;
@@ -270,36 +203,67 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
       }
     }
   };
-  auto issue = [&]() {
-    ZL_LDS char* st = smem + (issued % STAGES) * TL::STAGE_BYTES;
+  // Load the next item into r (returns whether it is a tile).
+  auto issue = [&](u32x4 (&r)[NI]) __attribute__((always_inline)) -> bool {
+    if (!dmore) {
+      // The run has no further item: the same number of loads from the
+      // first query row (always present; the data is never used), so that
+      // every step of the loop below issues NI loads.
+#pragma unroll
+      for (int i = 0; i < NI; ++i) r[i] = load16_stream((const char*)a.q + rmap.chunk);
+      return false;
+    }
     const int ntl = (ds.len + 31) >> 5;
     const int kvh = ds.u / a.HB, hb = ds.u - (ds.u / a.HB) * a.HB;
-    if (dj == 0) {
+    const bool tile = dj > 0;
+    // Tile k = dj - 1 (meaningless for the query item, whose addresses are
+    // the ones used then): its first token's cache row (virtual tokens map
+    // onto the sequence's rows) and its valid rows.
+    const int k = dj - 1;
+    const int last = min(32, ds.len - 32 * k) - 1;
+    const char* kbase = (const char*)(a.k + (long long)kvh * DK);
+    const char* vbase = (const char*)(a.v + (long long)kvh * DV);
+    if constexpr (!PAGED) {
+      const int tok = MQ ? dsi.k0 + (ds.t0 - ds.cs) + 32 * k : ds.t0 + 32 * k;
+      kbase += (long long)tok * k_row_bytes;
+      vbase += (long long)tok * v_row_bytes;
+    }
+    // Address of row-load i of a tile of one tensor.
+    const auto tile_addr = [&](const char* base, uint32_t row_bytes, int i) __attribute__((always_inline)) {
+      const int rr = min(rmap.row(i), last);
+      if constexpr (PAGED) {
+        // Tile row r < 16 is pool row half0 + r, r >= 16 is half1 + r
+        // (zl_split.h, TileRows); a clamped row takes the half it is in.
+        const long long prow = (rr < 16 ? pf.half0 : pf.half1) + rr;
+        return base + (size_t)prow * row_bytes + rmap.chunk;
+      } else {
+        return base + ((uint32_t)rr * row_bytes + rmap.chunk);
+      }
+    };
+    // Query item: the 16 query rows (DK values each, in the layout of K-tile
+    // rows 0-15; rows past the unit's heads repeat its first and are never
+    // stored), loaded NI / QI times over so that every item is NI loads (the
+    // repeats hit the caches) and the compiler's count of loads in flight is
+    // exact.
+    const char* qaddr[QI];
+#pragma unroll
+    for (int i = 0; i < QI; ++i) {
+      const int rr = rmap.row(i);
+      long long qrow;
       if constexpr (MQ) {
-        dma_query_item_mq<L>(a.q, dsi, kvh, a.G, a.Hq, st, lane);
+        qrow = mq_column(dsi, rr, kvh, a.G, a.Hq, false).row;
       } else {
         const int h0 = kvh * a.G + hb * kHeadsPerUnit;
         const int nh = min(kHeadsPerUnit, a.G - hb * kHeadsPerUnit);
-        dma_query_item<L>(a.q + ((long long)ds.b * a.Hq + h0) * DK, nh, st, lane);
+        qrow = (long long)ds.b * a.Hq + h0 + (rr < nh ? rr : 0);
       }
-    } else {
-      const int k = dj - 1;
-      // Cache row of the tile's first token (virtual tokens map onto the
-      // sequence's rows).
-      const int tok = MQ ? dsi.k0 + (ds.t0 - ds.cs) + 32 * k : ds.t0 + 32 * k;
-      const int nv = min(32, ds.len - 32 * k);
-      if constexpr (PAGED) {
-        dma_tile_paged<L, TL::NI_K>((const char*)(a.k + (long long)kvh * DK), k_row_bytes, kmap, pf, nv, st);
-        dma_tile_paged<L, TL::NI_V>((const char*)(a.v + (long long)kvh * DV), v_row_bytes, vmap, pf, nv,
-                                    st + TL::KBYTES);
-      } else {
-        dma_tile<L, TL::NI_K>((const char*)(a.k + (long long)kvh * DK) + (size_t)tok * k_row_bytes, k_row_bytes,
-                              kmap, nv, st);
-        dma_tile<L, TL::NI_V>((const char*)(a.v + (long long)kvh * DV) + (size_t)tok * v_row_bytes, v_row_bytes,
-                              vmap, nv, st + TL::KBYTES);
-      }
+      qaddr[i] = (const char*)(a.q + qrow * DK) + rmap.chunk;
     }
-    ++issued;
+#pragma unroll
+    for (int i = 0; i < NIK; ++i) r[i] = load16_stream(tile ? tile_addr(kbase, k_row_bytes, i) : qaddr[i % QI]);
+#pragma unroll
+    for (int i = 0; i < TL::NI_V; ++i)
+      r[NIK + i] = load16_stream(tile ? tile_addr(vbase, v_row_bytes, i) : qaddr[i % QI]);
     if (++dj > ntl) {
       ds = next_segment(ds.p + ds.len);
       dj = 0;
@@ -308,7 +272,9 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
         if (dmore) dsi = vs.info(ds.b);
     }
     prefetch_pages();
+    return tile;
   };
+
   Segment sg = ds;  // the segment being computed
   int cj = 0;       // its current item
   bool first_seg = true;
@@ -317,24 +283,14 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
     sgi = dsi;
     col = mq_column(sgi, n, sg.u, a.G, a.Hq, a.causal != 0);
   }
-  for (int s = 0; s < STAGES - 1 && dmore; ++s) issue();
 
   f32x4 o[TL::VBLK];
   SoftmaxState sm{-INFINITY, 0.f};
   i16x8 qop[TL::KSTEPS];
 
-  for (int i = 0;; ++i) {
-    // Refill the stage of item i-1 (consumed), then wait for item i: at most
-    // the items issued after it may still be in flight.
-    if (dmore) issue();
-    const int after = issued - i - 1;
-    if (after >= 2)
-      wait_vmcnt<2 * TL::PER_TILE>();
-    else if (after == 1)
-      wait_vmcnt<TL::PER_TILE>();
-    else
-      wait_vmcnt<0>();
-    const ZL_LDS char* st = smem + (i % STAGES) * TL::STAGE_BYTES;
+  // Compute item cj of segment sg from LDS stage st; returns true when the
+  // run is done.
+  auto compute = [&](const ZL_LDS char* st) __attribute__((always_inline)) -> bool {
     const int ntl = (sg.len + 31) >> 5;
     if (cj == 0) {
       // Query item.  B operand: lane (g, n) = head n, dims 32kb + 8g .. +7.
@@ -344,7 +300,6 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
 #pragma unroll
       for (int bb = 0; bb < TL::VBLK; ++bb) o[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
       sm = SoftmaxState{-INFINITY, 0.f};
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // stage free for refill
     } else {
       const int j = cj - 1;
       const ZL_LDS char* vt = GE::SHARED_KV ? st : st + TL::KBYTES;
@@ -396,7 +351,7 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
     }
     if (++cj > ntl) {
       sg = next_segment(sg.p + sg.len);
-      if (sg.len == 0) break;
+      if (sg.len == 0) return true;
       cj = 0;
       first_seg = false;
       if constexpr (MQ) {
@@ -404,6 +359,28 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
         col = mq_column(sgi, n, sg.u, a.G, a.Hq, a.causal != 0);
       }
     }
+    return false;
+  };
+
+  // Items alternate between two register buffers and two LDS stages: the
+  // item in buffer X is written to stage X, X is refilled with the item two
+  // ahead, and the item is computed from stage X.
+  u32x4 ra[NI], rb[NI];
+  bool ta = issue(ra);
+  bool tb = issue(rb);
+  auto step = [&](u32x4 (&r)[NI], bool& is_tile, ZL_LDS char* st) __attribute__((always_inline)) -> bool {
+    if (is_tile) {
+      store_rows<NIK>(st, rmap, r);
+      store_rows<TL::NI_V>(st + TL::KBYTES, rmap, r + NIK);
+    } else {
+      store_rows<QI>(st, rmap, r);
+    }
+    is_tile = issue(r);
+    return compute(st);
+  };
+  for (;;) {
+    if (step(ra, ta, smem)) break;
+    if (step(rb, tb, smem + TL::STAGE_BYTES)) break;
   }
 }
 

@@ -194,6 +194,15 @@ __device__ __forceinline__ void dma16_saddr(const void* base, uint32_t off, ZL_L
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_base) : "memory");
 }
 
+// 16 bytes from global memory into registers, marked non-temporal: key/value
+// rows are streamed once, so their lines need not stay in the caches.
+__device__ __forceinline__ u32x4 load16_stream(const void* p) {
+  return __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+}
+
+// 16 bytes of registers into LDS.
+__device__ __forceinline__ void lds_write_b128(ZL_LDS char* p, u32x4 v) { *(ZL_LDS u32x4*)p = v; }
+
 // Wait until at most N vector-memory operations of this wave are outstanding.
 // (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt/lgkmcnt left at max.)
 template <int N>
