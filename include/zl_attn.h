@@ -418,21 +418,22 @@ ZL_API zl_status_t zl_int8_reduce_step(const int8_t *codes_in, const float *scal
 
 /*
  * Measurement aid, no attention arithmetic: a plain streaming read of `bytes`
- * of `src` (only whole 1 KB blocks; bytes < 1024 is a no-op) through LDS at
- * the launch shape of a decode kernel -- head_dim_k 64 or 128 selects the GQA
- * kernel's shape (one-wave workgroups, 8 or 16 KB ring items, three stages),
- * 576 the MLA kernel's (four-wave workgroups, 36 KB items, four stages); other
- * values give ZL_ERR_UNSUPPORTED -- with that kernel's load instruction, each
- * workgroup reading an equal contiguous share.  Decode attention is bound by
- * its HBM reads (the first ZhiLight page names HBM traffic as the cost its
- * fused kernels cut, section 3 "自研 Fusion Kernel"), so this read of the same
- * bytes with nothing else to do is the ceiling a decode kernel of that shape
- * is measured against.
+ * of `src` (only whole 1 KB blocks; bytes < 1024 is a no-op) at the launch
+ * shape of a decode kernel -- head_dim_k 64 or 128 selects the GQA kernel's
+ * shape (one-wave workgroups, 8 or 16 KB items), 576 the MLA kernel's
+ * (four-wave workgroups, 36 KB items); other values give ZL_ERR_UNSUPPORTED --
+ * with the decode kernels' load path (coalesced 16-byte loads into registers,
+ * two items in flight per wave), each workgroup reading an equal contiguous
+ * share.  Decode attention is bound by its HBM reads (the first ZhiLight page
+ * names HBM traffic as the cost its fused kernels cut, section 3 "自研 Fusion
+ * Kernel"), so this read of the same bytes with nothing else to do is the
+ * ceiling a decode kernel of that shape is measured against.
  *   src         16-byte aligned device buffer of at least `bytes` bytes
  *   workgroups  0 = the decode kernel's default worker count, else a multiple
  *               of 8 in 8 .. 65536
- *   sink        [workgroups] uint32 (device), one word per workgroup written
- *               (its value is meaningless)
+ *   sink        [workgroups] uint32 (device); gives the loads a use: a word
+ *               is written only if a workgroup's checksum of its bytes
+ *               equals a fixed key (its contents are meaningless)
  * Asynchronous on `stream`; allocates nothing.
  */
 ZL_API zl_status_t zl_hbm_read_probe(const void *src, size_t bytes, int head_dim_k, int workgroups,

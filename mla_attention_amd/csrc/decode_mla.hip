@@ -14,14 +14,16 @@
 //    rows; see zl_split.h.  Fewer, larger workers than the GQA kernel keep the
 //    number of 32 KB fp32 partials (one per split point) small; the split
 //    sequences are merged by split_merge.hip.
-//  * A worker's run is one stream of items through a four-stage LDS ring: for
-//    each segment (the part of one sequence in the run) its query rows, then
-//    its 32-token tiles.  A tile is 36 KB of contiguous HBM; the four waves
-//    DMA a quarter each (9 x 1 KB global_load_lds) and the query item is
-//    loaded twice to cost the same.  Three items are in flight while one is
-//    used, across segment boundaries, so a new sequence does not drain the
-//    pipeline.  Slots are XOR-swizzled within groups of 8 (rows are 72 slots
-//    long).
+//  * A worker's run is one stream of items: for each segment (the part of one
+//    sequence in the run) its query rows, then its 32-token tiles.  A tile is
+//    36 KB of contiguous HBM; each wave reads a quarter (9 x 1 KB).  One new
+//    token per sequence (mla_decode_rs_kernel): the quarters go to registers
+//    with coalesced 16-byte loads two items ahead of the math and are written
+//    to LDS when their turn comes (two LDS stages).  Several new tokens per
+//    sequence (mla_decode_kernel): global_load_lds DMA into a four-stage LDS
+//    ring, three items in flight.  Either way items flow across segment
+//    boundaries, so a new sequence does not drain the pipeline.  Slots are
+//    XOR-swizzled within groups of 8 (rows are 72 slots long).
 //  * QK^T is split over the waves: wave w computes the 16 x 16 score block of
 //    tokens 16(w % 2) .. +15 over k-steps 9(w / 2) .. +8 (half of the 576
 //    dims), leaves it in a 4 KB exchange area of LDS, and after a barrier every
@@ -37,9 +39,9 @@
 //    the loads).  16 heads of two draft tokens thus cost one pass over the
 //    latent rows, and the two waves on each SIMD hide each other's MFMA and
 //    LDS latency: one wave holding both blocks left the tile math exposed.
-//  * Barriers: one per item when it has landed (every wave is then also done
-//    with the previous item, whose stage is refilled right after), and one per
-//    tile when the score halves are in LDS.
+//  * Barriers: one per item once it is whole in LDS (every wave is then also
+//    done with the previous item), and one per tile when the score halves are
+//    in LDS.
 #include "zl_device.h"
 #include "zl_kernels.h"
 #include "zl_split.h"
@@ -69,11 +71,10 @@ constexpr int kWorkgroupsPerCU = 1;
 // heads of one token, or with several new tokens per sequence 32 query rows
 // (kMlaMqRowsLog2), so that a tile read from HBM serves e.g. 16 heads of two
 // draft tokens at once.
-template <bool MQ>
-constexpr int column_blocks() { return MQ ? 2 : 1; }
-// Score exchange: one f32x4 per lane and wave.
-template <int NCB>
-constexpr int lds_bytes() { return kStages * kTileB + NCB * kWaves * 1024; }  // 148 or 152 KB of 160
+constexpr int kMqColumnBlocks = 2;
+// The several-new-tokens kernel's LDS: the ring, then a score exchange area
+// of one f32x4 per lane and wave: 152 KB of 160.
+constexpr int kMqLdsBytes = kStages * kTileB + kMqColumnBlocks * kWaves * 1024;
 static_assert(kQB <= kTileB, "query rows fit one ring stage");
 static_assert(2 * kQB == kTileB && (16 << (kMlaMqRowsLog2 - 4)) == 32,
               "32 query rows are exactly one ring stage");
@@ -137,21 +138,6 @@ __device__ __forceinline__ void dma_quarter_paged(const uint16_t* pool, const Ti
   dma_quarter((const uint16_t*)((uintptr_t)pool + (uintptr_t)(half * kRowB)), 0, nvalid, m, dst, wave);
 }
 
-// The query item of a segment: rows h0 .. h0+15 (rows past nh repeat h0) in
-// the tile's slot layout, 18 KB, loaded twice so that it costs the same nine
-// instructions per wave as a tile (the second copy is never read).
-__device__ __forceinline__ void dma_query_item(const uint16_t* qb, int nh, ZL_LDS char* dst, int wave,
-                                               int lane) {
-#pragma unroll
-  for (int k = 0; k < kNIw; ++k) {
-    const int i = wave * kNIw + k;
-    const int lin = 64 * (i % kNIq) + lane;
-    const int r = lin / kCPR;
-    const int s = lin - r * kCPR;
-    dma16(qb + (long long)(r < nh ? r : 0) * kDK + slot(s, r) * 8, dst + i * 1024);
-  }
-}
-
 // The query item of a virtual sequence (several new tokens per sequence): row
 // r (0 .. 31) is query row 32 hb + r of the sequence (new token (32 hb + r) /
 // H, head (32 hb + r) % H); rows past the sequence's last repeat it.  32 rows
@@ -190,14 +176,15 @@ __device__ __forceinline__ f32x4 half_scores(const ZL_LDS char* kt, const i16x8 
   return acc0 + acc1;
 }
 
-template <int DT, bool PAGED, bool MQ>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * kWaves * column_blocks<MQ>(),
-                                                      64 * kWaves * column_blocks<MQ>()),
-                          amdgpu_waves_per_eu(column_blocks<MQ>(), column_blocks<MQ>()))) void
-mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __restrict__ block_table) {
-  constexpr int NCB = column_blocks<MQ>();
+// Several new tokens per sequence (virtual sequences of 32 query rows): two
+// groups of four waves, one per 16-column block, on the same tiles.
+template <int DT, bool PAGED>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kWaves * kMqColumnBlocks, 64 * kWaves * kMqColumnBlocks),
+                          amdgpu_waves_per_eu(kMqColumnBlocks, kMqColumnBlocks))) void
+mla_mq_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __restrict__ block_table) {
+  constexpr int NCB = kMqColumnBlocks;
   // One LDS object only (see decode_attn.hip): [4 ring stages][score exchange].
-  __shared__ __attribute__((aligned(1024))) char smem_raw[lds_bytes<NCB>()];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kMqLdsBytes];
   ZL_LDS char* smem = (ZL_LDS char*)smem_raw;
   ZL_LDS char* xchg = smem + kStages * kTileB;
   static_assert(16 * NCB <= kMlaSlotCols, "a partial slot holds the item's columns");
@@ -219,41 +206,24 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
   const QuarterMap qmap = quarter_map(wave, lane);
 
   // (Empty sequences are written by the merge launch: no run covers them.)
-  // The batch: decode sequences, or with several new tokens per sequence the
-  // virtual sequences of 32 query rows.  Sequence boundaries for the lookups
-  // are loaded here, before any tile load, and waited for, so that no later
-  // lookup has to drain the tile loads in flight (B <= 64).
-  int window = 0;
+  // The batch: the virtual sequences of 32 query rows.  Sequence boundaries
+  // for the lookups are loaded here, before any tile load, and waited for, so
+  // that no later lookup has to drain the tile loads in flight (B <= 64).
   VirtualSeqs vs;
-  int NB;  // sequences on the work line
-  int T;
-  if constexpr (MQ) {
-    vs.init(a.cu_q, cu, B, a.G, a.seg_cost, kMlaMqRowsLog2);
-    asm volatile("" : "+v"(vs.first.q0), "+v"(vs.first.nq), "+v"(vs.first.k0), "+v"(vs.first.lk));
-    NB = vs.V;
-    T = vs.T;
-  } else {
-    T = cu[B];
-    window = bounds_window(cu, B, a.seg_cost);
-    asm volatile("" : "+v"(window));
-    NB = B;
-  }
+  vs.init(a.cu_q, cu, B, a.G, a.seg_cost, kMlaMqRowsLog2);
+  asm volatile("" : "+v"(vs.first.q0), "+v"(vs.first.nq), "+v"(vs.first.k0), "+v"(vs.first.lk));
+  const int NB = vs.V;  // sequences on the work line
+  const int T = vs.T;
   const Line line = make_line(T, NB, a.seg_cost);
   const long long N = (long long)U * line.Tp;
   const long long per = positions_per_worker(N, a.P);
   const long long p_begin = (long long)w * per;
   const long long p_end = N < p_begin + per ? N : p_begin + per;
-  const auto next_segment = [&](long long p) {
-    if constexpr (MQ)
-      return segment_at(p, p_end, line, vs);
-    else
-      return segment_at(p, p_end, line, cu, window);
-  };
+  const auto next_segment = [&](long long p) { return segment_at(p, p_end, line, vs); };
   Segment ds = next_segment(p_begin);
   if (tid == 0) a.first_key[w] = ds.len > 0 ? seq_key(ds.u, ds.b, NB) : -1;
   if (ds.len == 0) return;  // the whole workgroup: w is per workgroup
-  VSeqInfo dsi{}, sgi{};  // several new tokens: the virtual sequences of ds, sg
-  if constexpr (MQ) dsi = vs.info(ds.b);
+  VSeqInfo dsi = vs.info(ds.b), sgi{};  // the virtual sequences of ds, sg
 
   // The run is one stream of ring items: for every segment its query item,
   // then its 32-token tiles.  The issuing side runs up to three items ahead
@@ -269,10 +239,9 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
     if constexpr (PAGED) {
       if (dmore && dj >= 1) {
         const int k = dj - 1;
-        // (Several new tokens: the pages of the virtual sequence's sequence;
-        // its virtual tokens are that sequence's rows from 0.)
-        const int seq = MQ ? dsi.b : ds.b;
-        pf = tile_rows(block_table + (long long)seq * a.max_pages, ds.t0 + 32 * k - ds.cs,
+        // The pages of the virtual sequence's sequence; its virtual tokens
+        // are that sequence's rows from 0.
+        pf = tile_rows(block_table + (long long)dsi.b * a.max_pages, ds.t0 + 32 * k - ds.cs,
                        min(32, ds.len - 32 * k), a.page_shift);
       }
     }
@@ -282,24 +251,16 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
     const int ntl = (ds.len + 31) >> 5;
     if (!loader) {
     } else if (dj == 0) {
-      if constexpr (MQ) {
-        dma_query_item_mq(a.q, dsi, a.G, dst, wave, lane);
-      } else {
-        const int h0 = ds.u * kHeadsPerUnit;
-        dma_query_item(a.q + ((long long)ds.b * a.Hq + h0) * kDK, min(kHeadsPerUnit, a.G - h0), dst, wave,
-                       lane);
-      }
+      dma_query_item_mq(a.q, dsi, a.G, dst, wave, lane);
     } else {
       const int k = dj - 1;
       const int nv = min(32, ds.len - 32 * k);
       if constexpr (PAGED) {
         dma_quarter_paged(a.k, pf, nv, qmap, dst, wave);
-      } else if constexpr (MQ) {
+      } else {
         // Cache row of the tile's first token (virtual tokens map onto the
         // sequence's rows).
         dma_quarter(a.k, dsi.k0 + (ds.t0 - ds.cs) + 32 * k, nv, qmap, dst, wave);
-      } else {
-        dma_quarter(a.k, ds.t0 + 32 * k, nv, qmap, dst, wave);
       }
     }
     ++issued;
@@ -307,20 +268,16 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
       ds = next_segment(ds.p + ds.len);
       dj = 0;
       dmore = ds.len > 0;
-      if constexpr (MQ)
-        if (dmore) dsi = vs.info(ds.b);
+      if (dmore) dsi = vs.info(ds.b);
     }
     prefetch_pages();
   };
   Segment sg = ds;  // the segment being computed
   int cj = 0;       // its current item
   bool first_seg = true;
-  // Several new tokens: this lane's column 16 cb + n of sg's row block.
-  MqColumn col{};
-  if constexpr (MQ) {
-    sgi = dsi;
-    col = mq_column(sgi, 16 * cb + n, 0, a.G, a.Hq, a.causal != 0, kMlaMqRowsLog2);
-  }
+  // This lane's column 16 cb + n of sg's row block.
+  sgi = dsi;
+  MqColumn col = mq_column(sgi, 16 * cb + n, 0, a.G, a.Hq, a.causal != 0, kMlaMqRowsLog2);
   for (int s = 0; s < kStages - 1 && dmore; ++s) issue();
 
   f32x4 o[kBlkPerWave];
@@ -364,7 +321,7 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
       s[1] = *(const ZL_LDS f32x4*)(xc + 1 * 1024) + *(const ZL_LDS f32x4*)(xc + 3 * 1024);
       float alpha;
       int nvalid = min(32, sg.len - 32 * j);
-      if constexpr (MQ) {
+      {
         // Causal limit of this lane's query row: cache rows up to col.lim.
         const int j0 = sg.t0 - sg.cs + 32 * j;
         nvalid = min(nvalid, col.lim - j0 + 1);
@@ -382,13 +339,11 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
         // column 16 cb + n, dims 128w + 16bb + 4g .. +3.  Stores only; the
         // next items are in flight.  A partial slot holds 16 NCB columns.
         const SeqWorkers sw = seq_workers(line, sg.u, sg.b, sg.cs, sg.ce, per);
-        const int h0 = sg.u * kHeadsPerUnit;
-        const int nh = min(kHeadsPerUnit, a.G - h0);
         const float l_tot = sum_over_groups(sm.l);
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         const float lse_v = l_tot > 0.f ? sm.m * kLn2 + __logf(l_tot) : -INFINITY;
-        const bool has_row = MQ ? col.valid : n < nh;
-        const long long row = MQ ? col.row : (long long)sg.b * a.Hq + h0 + n;
+        const bool has_row = col.valid;
+        const long long row = col.row;
         if (has_row) {
           if (sw.first == sw.last) {
             uint16_t* orow = a.out + row * kDV + dim0;
@@ -411,11 +366,247 @@ mla_decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* _
       if (sg.len == 0) break;
       cj = 0;
       first_seg = false;
-      if constexpr (MQ) {
-        sgi = vs.info(sg.b);
-        col = mq_column(sgi, 16 * cb + n, 0, a.G, a.Hq, a.causal != 0, kMlaMqRowsLog2);
+      sgi = vs.info(sg.b);
+      col = mq_column(sgi, 16 * cb + n, 0, a.G, a.Hq, a.causal != 0, kMlaMqRowsLog2);
+    }
+  }
+}
+
+// One new token per sequence: the same tile math, with each wave's quarter
+// of every item read by coalesced 16-byte loads into one of two register
+// buffers (two items ahead of the math) and written to LDS when its turn
+// comes.  Register loads sustain more HBM bandwidth on gfx950 than the
+// global_load_lds path that the several-new-tokens kernel above keeps (its
+// two wave groups share each SIMD and have no registers to spare for the
+// buffers).  Two LDS stages suffice: a wave writes item i into the stage of
+// item i - 2 only after passing the barrier that closes the writes of item
+// i - 1, which every wave reaches only after it has finished computing item
+// i - 2.  The same barrier orders the score exchange area between items.
+namespace {
+
+// This wave's quarter of an item: load k, lane l covers the 16-byte chunk
+// lin = 64 (9 w + k) + l of the tile in row-major order (row r = lin / 72,
+// chunk c = lin % 72).  The global offset from the tile's first row is
+// 16 lin (rows are contiguous), and the chunk lands in LDS at row r, slot
+// slot(c, r) = 16 lin XOR 16 ((r >> 1) & 7) (the swizzle only permutes
+// chunks inside aligned groups of 8, and a row starts on a 128-byte line).
+// Both offsets are kept per load, so a full tile's loads and LDS writes take
+// no address arithmetic.  Wave w's rows are 8w .. 8w + 7, all in one half of
+// the tile.
+struct QuarterLane {
+  uint32_t goff[kNIw];  // 16 lin of load k
+  uint32_t loff[kNIw];  // its LDS offset in a stage
+  int row[kNIw];        // r of load k
+  __device__ __forceinline__ QuarterLane(int wave, int lane) {
+#pragma unroll
+    for (int k = 0; k < kNIw; ++k) {
+      const int lin = 64 * (wave * kNIw + k) + lane;
+      const int r = lin / kCPR;
+      row[k] = r;
+      goff[k] = 16u * (uint32_t)lin;
+      loff[k] = goff[k] ^ (16u * (uint32_t)((r >> 1) & 7));
+    }
+  }
+  // Offset of row rr (in place of this load's row) at this load's chunk.
+  __device__ __forceinline__ uint32_t moved(int k, int rr) const {
+    return goff[k] + (uint32_t)(rr - row[k]) * (uint32_t)kRowB;
+  }
+};
+
+}  // namespace
+
+template <int DT, bool PAGED>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kWaves, 64 * kWaves), amdgpu_waves_per_eu(1, 1))) void
+mla_decode_rs_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __restrict__ block_table) {
+  constexpr int kRsStages = 2;
+  // One LDS object only (see decode_attn.hip): [2 stages][score exchange].
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kRsStages * kTileB + kWaves * 1024];
+  ZL_LDS char* smem = (ZL_LDS char*)smem_raw;
+  ZL_LDS char* xchg = smem + kRsStages * kTileB;
+
+  const int tid = threadIdx.x;
+  const int wave = readfirstlane(tid >> 6);  // quarter of the tile (scalar)
+  const int lane = tid & 63;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int tb_own = wave & 1;   // token block of this wave's score half
+  const int kh_own = wave >> 1;  // k-step half of this wave's score half
+  const int w = worker_id(blockIdx.x, a.P);
+  const int B = a.B;
+  const int U = a.HB;
+  const int dim0 = wave * (kDV / kWaves) + 4 * g;
+  const auto slot_fn = [](int c, int r) { return slot(c, r); };
+  const QuarterLane ql(wave, lane);
+
+  // (Empty sequences are written by the merge launch: no run covers them.)
+  const int T = cu[B];
+  const int window = bounds_window(cu, B, a.seg_cost);
+  const Line line = make_line(T, B, a.seg_cost);
+  const long long N = (long long)U * line.Tp;
+  const long long per = positions_per_worker(N, a.P);
+  const long long p_begin = (long long)w * per;
+  const long long p_end = N < p_begin + per ? N : p_begin + per;
+  const auto next_segment = [&](long long p) __attribute__((always_inline)) {
+    return segment_at(p, p_end, line, cu, window);
+  };
+  Segment ds = next_segment(p_begin);
+  if (tid == 0) a.first_key[w] = ds.len > 0 ? seq_key(ds.u, ds.b, B) : -1;
+  if (ds.len == 0) return;  // the whole workgroup: w is per workgroup
+
+  // The run is one stream of items: for every segment its query rows, then
+  // its 32-token tiles.  Every item is kNIw loads per wave (the 18 KB of
+  // query rows are loaded twice over), so the compiler's count of loads in
+  // flight is exact.
+  int dj = 0;  // next item of segment ds: 0 = query rows, 1 + k = tile k
+  bool dmore = true;
+  TileRows pf{0, 0};  // paged: the page ids of the next tile, one item ahead
+  auto prefetch_pages = [&]() __attribute__((always_inline)) {
+    if constexpr (PAGED) {
+      if (dmore && dj >= 1) {
+        const int k = dj - 1;
+        pf = tile_rows(block_table + (long long)ds.b * a.max_pages, ds.t0 + 32 * k - ds.cs, min(32, ds.len - 32 * k),
+                       a.page_shift);
       }
     }
+  };
+  auto issue = [&](u32x4 (&r)[kNIw]) __attribute__((always_inline)) {
+    // A wave-uniform base and one 32-bit offset per load: a full tile uses
+    // the precomputed offsets; a short tile clamps rows past the last to it
+    // (finite data, masked out of the softmax); the query item reads query
+    // rows 0-15 (rows past the unit's heads repeat its first; tile rows
+    // 16-31 fetch rows 0-15 again, never read); with no further item the
+    // loads re-read the first 1 KB of the queries (never used), so that
+    // every item is kNIw loads and the compiler's count of loads in flight
+    // is exact.
+    const char* base;
+    uint32_t off[kNIw];
+    const int t = dj - 1;  // tile index
+    if (!dmore) {
+      base = (const char*)a.q;
+#pragma unroll
+      for (int k = 0; k < kNIw; ++k) off[k] = ql.goff[k] & 1023u;
+    } else if (dj == 0) {
+      const int h0 = ds.u * kHeadsPerUnit;
+      const int nh = min(kHeadsPerUnit, a.G - h0);
+      base = (const char*)(a.q + ((long long)ds.b * a.Hq + h0) * kDK);
+#pragma unroll
+      for (int k = 0; k < kNIw; ++k) {
+        const int qr = ql.row[k] & 15;
+        off[k] = ql.moved(k, qr < nh ? qr : 0);
+      }
+    } else {
+      const int last = min(32, ds.len - 32 * t) - 1;
+      if constexpr (PAGED)
+        base = (const char*)a.k + (size_t)(wave < 2 ? pf.half0 : pf.half1) * kRowB;
+      else
+        base = (const char*)a.k + (size_t)(ds.t0 + 32 * t) * kRowB;
+      if (last == 31) {
+#pragma unroll
+        for (int k = 0; k < kNIw; ++k) off[k] = ql.goff[k];
+      } else {
+#pragma unroll
+        for (int k = 0; k < kNIw; ++k) off[k] = ql.moved(k, min(ql.row[k], last));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kNIw; ++k) r[k] = load16_stream(base + off[k]);
+    if (dmore) {
+      const int ntl = (ds.len + 31) >> 5;
+      if (++dj > ntl) {
+        ds = next_segment(ds.p + ds.len);
+        dj = 0;
+        dmore = ds.len > 0;
+      }
+      prefetch_pages();
+    }
+  };
+
+  Segment sg = ds;  // the segment being computed
+  int cj = 0;       // its current item
+  bool first_seg = true;
+  f32x4 o[kBlkPerWave];
+  SoftmaxState sm{-INFINITY, 0.f};
+  i16x8 qop[kKHalf];
+
+  // Compute item cj of segment sg from stage `it`; true when the run is done.
+  auto compute = [&](const ZL_LDS char* it) __attribute__((always_inline)) -> bool {
+    const int ntl = (sg.len + 31) >> 5;
+    if (cj == 0) {
+      // Query item: this wave's half of the k-steps, B operand layout.
+#pragma unroll
+      for (int kb = 0; kb < kKHalf; ++kb) {
+        const int c = 4 * (kKHalf * kh_own + kb) + g;
+        qop[kb] = __builtin_bit_cast(i16x8, lds_read_b128(it + n * kRowB + (slot(c, n) << 4)));
+      }
+#pragma unroll
+      for (int bb = 0; bb < kBlkPerWave; ++bb) o[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sm = SoftmaxState{-INFINITY, 0.f};
+    } else {
+      const int j = cj - 1;
+      ZL_LDS char* xc = xchg + lane * 16;
+      *(ZL_LDS f32x4*)(xc + wave * 1024) = half_scores<DT>(it, qop, tb_own, kh_own, n, g);
+      barrier_lds();  // all score halves in LDS
+      f32x4 s[2];
+      s[0] = *(const ZL_LDS f32x4*)(xc + 0 * 1024) + *(const ZL_LDS f32x4*)(xc + 2 * 1024);
+      s[1] = *(const ZL_LDS f32x4*)(xc + 1 * 1024) + *(const ZL_LDS f32x4*)(xc + 3 * 1024);
+      float alpha;
+      bool rescale;
+      const POperand pop = softmax_update<DT>(s, g, min(32, sg.len - 32 * j), a.scale_log2, sm, alpha, rescale);
+      if (rescale) {
+#pragma unroll
+        for (int bb = 0; bb < kBlkPerWave; ++bb) o[bb] *= alpha;
+      }
+      pv_blocks<DT, kBlkPerWave, kRowB>(it, pop, n, g, wave * kBlkPerWave, slot_fn, o);
+
+      if (j == ntl - 1) {
+        // ---- segment epilogue: lane (g, n) of wave w holds head n, dims
+        // 128w + 16bb + 4g .. +3.  Stores only.
+        const SeqWorkers sw = seq_workers(line, sg.u, sg.b, sg.cs, sg.ce, per);
+        const int h0 = sg.u * kHeadsPerUnit;
+        const int nh = min(kHeadsPerUnit, a.G - h0);
+        const float l_tot = sum_over_groups(sm.l);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const float lse_v = l_tot > 0.f ? sm.m * kLn2 + __logf(l_tot) : -INFINITY;
+        const long long row = (long long)sg.b * a.Hq + h0 + n;
+        if (n < nh) {
+          if (sw.first == sw.last) {
+            uint16_t* orow = a.out + row * kDV + dim0;
+#pragma unroll
+            for (int bb = 0; bb < kBlkPerWave; ++bb) store_out4<DT>(orow + 16 * bb, o[bb], inv);
+            if (a.lse && wave == 0 && g == 0) a.lse[row] = lse_v;
+          } else {
+            const int sl = 2 * w + (first_seg ? 0 : 1);
+            float* po = a.part_o + ((long long)sl * kHeadsPerUnit + n) * kDV + dim0;  // 16-column slots
+#pragma unroll
+            for (int bb = 0; bb < kBlkPerWave; ++bb) *(f32x4*)(po + 16 * bb) = o[bb] * inv;
+            if (wave == 0 && g == 0) a.part_lse[sl * kLseSlot + n] = lse_v;
+          }
+        }
+      }
+    }
+    if (++cj > ntl) {
+      sg = next_segment(sg.p + sg.len);
+      if (sg.len == 0) return true;
+      cj = 0;
+      first_seg = false;
+    }
+    return false;
+  };
+
+  // Items alternate between two register buffers and two LDS stages.
+  u32x4 ra[kNIw], rb[kNIw];
+  issue(ra);
+  issue(rb);
+  auto step = [&](u32x4 (&r)[kNIw], ZL_LDS char* st) __attribute__((always_inline)) -> bool {
+#pragma unroll
+    for (int k = 0; k < kNIw; ++k) lds_write_b128(st + ql.loff[k], r[k]);
+    issue(r);
+    barrier_lds();  // the item is whole in LDS
+    return compute(st);
+  };
+  for (;;) {
+    if (step(ra, smem)) break;
+    if (step(rb, smem + kTileB)) break;
   }
 }
 
@@ -423,17 +614,15 @@ int mla_default_workers() { return 256 * kWorkgroupsPerCU; }
 
 template <int DT>
 static void launch_mla_t(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.P), block(64 * kWaves);
+  const dim3 grid(a.P), block(64 * kWaves), mq_block(64 * kWaves * kMqColumnBlocks);
   if (a.cu_q && a.block_table)
-    hipLaunchKernelGGL((mla_decode_kernel<DT, true, true>), grid, dim3(64 * kWaves * column_blocks<true>()), 0,
-                       stream, a, a.cu, a.block_table);
+    hipLaunchKernelGGL((mla_mq_kernel<DT, true>), grid, mq_block, 0, stream, a, a.cu, a.block_table);
   else if (a.cu_q)
-    hipLaunchKernelGGL((mla_decode_kernel<DT, false, true>), grid, dim3(64 * kWaves * column_blocks<true>()), 0,
-                       stream, a, a.cu, a.block_table);
+    hipLaunchKernelGGL((mla_mq_kernel<DT, false>), grid, mq_block, 0, stream, a, a.cu, a.block_table);
   else if (a.block_table)
-    hipLaunchKernelGGL((mla_decode_kernel<DT, true, false>), grid, block, 0, stream, a, a.cu, a.block_table);
+    hipLaunchKernelGGL((mla_decode_rs_kernel<DT, true>), grid, block, 0, stream, a, a.cu, a.block_table);
   else
-    hipLaunchKernelGGL((mla_decode_kernel<DT, false, false>), grid, block, 0, stream, a, a.cu, a.block_table);
+    hipLaunchKernelGGL((mla_decode_rs_kernel<DT, false>), grid, block, 0, stream, a, a.cu, a.block_table);
 }
 
 hipError_t launch_mla(const DecodeArgs& a, int dtype, hipStream_t stream) {
