@@ -36,10 +36,20 @@
  *    workers share, and the merge kernel, which combines those partials and
  *    writes the results of empty sequences.
  *  - Host-checkable arguments are validated before any HIP call; a bad argument
- *    returns an error status and enqueues nothing.  Device contents (the values
- *    in cu_seqlens) are preconditions: cu[0] = 0, non-decreasing, every length
- *    at most max_seqlen_k, cu[batch] = total_tokens of the caches, and
- *    cu[batch] + 64 * batch < 2^31.
+ *    returns an error status and enqueues nothing.
+ *  - Cache lengths are clamped inside the kernels: sequence b attends over
+ *    L_b = clamp(cu[b+1] - cu[b], 0, max_seqlen_k) rows, starting at cache
+ *    row cu[b] (packed caches) or at the first row of its first page (paged
+ *    caches).  A length above max_seqlen_k is cut to its first max_seqlen_k
+ *    rows and a negative one (cu decreasing) counts as empty, so no read
+ *    leaves rows cu[b] .. cu[b] + max_seqlen_k - 1 of a packed cache or the
+ *    first ceil(max_seqlen_k / page_size) entries of a block-table row.  The
+ *    remaining device precondition is that those rows (packed) or the page
+ *    ids in those entries (paged) exist; with cu[0] = 0, cu non-decreasing,
+ *    every length at most max_seqlen_k and cu[batch] = total_tokens the
+ *    clamp changes nothing.  ZL_ERR_UNSUPPORTED when batch * (max_seqlen_k +
+ *    C) >= 2^31 (C = 32 for GQA, 64 for MLA; the work split numbers
+ *    positions in 32 bits).
  *  - 16-bit buffers (q, k, v, latent, out) must be 16-byte aligned.  Rows are
  *    dense: the layouts below have no padding.
  *  - Results are bitwise deterministic for identical inputs, arguments and
@@ -101,7 +111,7 @@ ZL_API size_t zl_decode_attn_workspace_size(int batch, int num_q_heads, int num_
  *   batch >= 0 (0 is a no-op), num_q_heads % num_kv_heads == 0,
  *   num_q_heads / num_kv_heads <= 16 or a multiple of 16,
  *   head_dim in {64, 128} (else ZL_ERR_UNSUPPORTED),
- *   max_seqlen_k (host) >= every sequence length,
+ *   max_seqlen_k (host): the clamp on every sequence length (above),
  *   softmax_scale finite (0 allowed),
  *   out        [batch, num_q_heads, head_dim] dtype, fully overwritten
  *   lse        [batch, num_q_heads] float32, natural log; NULL = not written
@@ -229,7 +239,8 @@ ZL_API zl_status_t zl_decode_attn_mla_ex(const void *q, const void *kv_cache, co
  *   k_pages, v_pages [num_pages, page_size, num_kv_heads, head_dim]  dtype
  *   kv_pages         [num_pages, page_size, kv_lora_rank + rope_dim] dtype
  *   block_table      [batch, max_pages_per_seq] int32 (device), every entry a
- *                    sequence uses is a valid page id (precondition)
+ *                    sequence uses (i / page_size for i < L_b) is a valid
+ *                    page id (precondition)
  *   cu_seqlens       as above: the prefix sums of the sequence lengths (a
  *                    logical numbering; no cache row sits at those indices)
  *   page_size        a power of two, 16 .. 256 (else ZL_ERR_UNSUPPORTED)
@@ -271,7 +282,8 @@ ZL_API zl_status_t zl_decode_attn_mla_paged_ex(const void *q, const void *kv_pag
  * memory model"), and several draft tokens checked in one step.  Sequence b
  * has nq = cu_seqlens_q[b+1] - cu_seqlens_q[b] new query tokens, whose keys
  * and values are already the last nq of its lk = cu_seqlens_k[b+1] -
- * cu_seqlens_k[b] cached rows.  New token i (0 <= i < nq) sits at cache
+ * cu_seqlens_k[b] cached rows (lk clamped to [0, max_seqlen_k] as above;
+ * nq below 0 counts as 0).  New token i (0 <= i < nq) sits at cache
  * position lk - nq + i; with causal = 1 it attends to cache rows
  * 0 .. lk - nq + i (none if that is negative: out 0, lse -inf), with
  * causal = 0 to all lk rows.  Each (token, head) row is the attention in the

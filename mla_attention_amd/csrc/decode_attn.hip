@@ -152,18 +152,19 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
   // The batch: decode sequences, or with several new tokens per sequence the
   // virtual sequences of 16 query rows.  Sequence boundaries for the lookups
   // are loaded here, once, for batches of up to 64 sequences.
-  int window = 0;
   VirtualSeqs vs;
+  PlainSeqs ps;
   int NB;  // sequences on the work line
   int T;
   if constexpr (MQ) {
-    vs.init(a.cu_q, cu, B, a.G, a.seg_cost, kMqRowsLog2);
+    vs.init(a.cu_q, cu, B, a.G, a.seg_cost, a.max_len, kMqRowsLog2);
     NB = vs.V;
     T = vs.T;
   } else {
-    T = cu[B];
-    window = bounds_window(cu, B, a.seg_cost);
+    const BatchBounds bb = batch_bounds(cu, B, a.max_len);
+    ps = PlainSeqs{cu, B, a.seg_cost, a.max_len, bb.first};
     NB = B;
+    T = bb.T;
   }
   const Line line = make_line(T, NB, a.seg_cost);
   const long long N = (long long)U * line.Tp;
@@ -174,7 +175,7 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
     if constexpr (MQ)
       return segment_at(p, p_end, line, vs);
     else
-      return segment_at(p, p_end, line, cu, window);
+      return segment_at(p, p_end, line, ps);
   };
   Segment ds = next_segment(p_begin);
   if (lane == 0) a.first_key[w] = ds.len > 0 ? seq_key(ds.u, ds.b, NB) : -1;
@@ -224,7 +225,7 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
     const char* kbase = (const char*)(a.k + (long long)kvh * DK);
     const char* vbase = (const char*)(a.v + (long long)kvh * DV);
     if constexpr (!PAGED) {
-      const int tok = MQ ? dsi.k0 + (ds.t0 - ds.cs) + 32 * k : ds.t0 + 32 * k;
+      const int tok = (MQ ? dsi.k0 : ds.row0) + (ds.t0 - ds.cs) + 32 * k;
       kbase += (long long)tok * k_row_bytes;
       vbase += (long long)tok * v_row_bytes;
     }

@@ -210,7 +210,7 @@ mla_mq_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
   // for the lookups are loaded here, before any tile load, and waited for, so
   // that no later lookup has to drain the tile loads in flight (B <= 64).
   VirtualSeqs vs;
-  vs.init(a.cu_q, cu, B, a.G, a.seg_cost, kMlaMqRowsLog2);
+  vs.init(a.cu_q, cu, B, a.G, a.seg_cost, a.max_len, kMlaMqRowsLog2);
   asm volatile("" : "+v"(vs.first.q0), "+v"(vs.first.nq), "+v"(vs.first.k0), "+v"(vs.first.lk));
   const int NB = vs.V;  // sequences on the work line
   const int T = vs.T;
@@ -439,15 +439,15 @@ mla_decode_rs_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t
   const QuarterLane ql(wave, lane);
 
   // (Empty sequences are written by the merge launch: no run covers them.)
-  const int T = cu[B];
-  const int window = bounds_window(cu, B, a.seg_cost);
-  const Line line = make_line(T, B, a.seg_cost);
+  const BatchBounds bb = batch_bounds(cu, B, a.max_len);
+  const PlainSeqs ps{cu, B, a.seg_cost, a.max_len, bb.first};
+  const Line line = make_line(bb.T, B, a.seg_cost);
   const long long N = (long long)U * line.Tp;
   const long long per = positions_per_worker(N, a.P);
   const long long p_begin = (long long)w * per;
   const long long p_end = N < p_begin + per ? N : p_begin + per;
   const auto next_segment = [&](long long p) __attribute__((always_inline)) {
-    return segment_at(p, p_end, line, cu, window);
+    return segment_at(p, p_end, line, ps);
   };
   Segment ds = next_segment(p_begin);
   if (tid == 0) a.first_key[w] = ds.len > 0 ? seq_key(ds.u, ds.b, B) : -1;
@@ -499,7 +499,7 @@ mla_decode_rs_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t
       if constexpr (PAGED)
         base = (const char*)a.k + (size_t)(wave < 2 ? pf.half0 : pf.half1) * kRowB;
       else
-        base = (const char*)a.k + (size_t)(ds.t0 + 32 * t) * kRowB;
+        base = (const char*)a.k + (size_t)(ds.row0 + (ds.t0 - ds.cs) + 32 * t) * kRowB;
       if (last == 31) {
 #pragma unroll
         for (int k = 0; k < kNIw; ++k) off[k] = ql.goff[k];

@@ -296,7 +296,7 @@ prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, int nblocks) {
   const int kvh = (int)blockIdx.x % a.Hkv;
   const int j = (int)blockIdx.x / a.Hkv;
   VirtualSeqs vs;
-  vs.init(a.cu_q, cu, a.B, a.G, 0, kPfRowsLog2);
+  vs.init(a.cu_q, cu, a.B, a.G, 0, a.max_len, kPfRowsLog2);
   if (j >= vs.V) return;
   const VSeqInfo si = vs.info(vs.V - 1 - j);
   const bool causal = a.causal != 0;

@@ -44,26 +44,38 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a, const in
   const int item = part * 256 + (int)threadIdx.x;
   const int h = item / C4;
   const int c4 = item - h * C4;
-  if (h >= nh || h >= heads_per_unit) return;
+  // The sequence's bounds come from wave-wide steps (ballots, lane reads and
+  // a prefix sum over the lanes; zl_split.h) that need every lane of the
+  // wave: they run before any thread leaves.  Everything below them is
+  // per-thread.
   int NB, T, cs, ce;
-  long long row;  // output row of this thread's column
   VirtualSeqs vs;
+  VSeqInfo si{};
   if constexpr (MQ) {
-    vs.init(a.cu_q, cu, a.B, a.G, a.seg_cost, a.rows_log2);
-    if (b >= vs.V) return;
-    const VSeqInfo si = vs.info(b);
-    const MqColumn col = mq_column(si, h, kvh, a.G, a.Hq, false, a.rows_log2);
-    if (!col.valid) return;
+    vs.init(a.cu_q, cu, a.B, a.G, a.seg_cost, a.max_len, a.rows_log2);
+    if (b >= vs.V) return;  // workgroup-uniform
+    si = vs.info(b);
     NB = vs.V;
     T = vs.T;
     cs = si.cs;
     ce = si.ce;
+  } else {
+    // Clamped lengths (zl_split.h): sequence b is tokens [ccu[b], ccu[b+1])
+    // of the work line; T = ccu[B].
+    const BatchBounds bb = batch_bounds(cu, a.B, a.max_len);
+    const SeqSpan sb = seq_bounds(cu, a.B, a.max_len, b, bb.first);
+    NB = a.B;
+    T = bb.T;
+    cs = sb.cs;
+    ce = sb.ce;
+  }
+  if (h >= nh || h >= heads_per_unit) return;
+  long long row;  // output row of this thread's column
+  if constexpr (MQ) {
+    const MqColumn col = mq_column(si, h, kvh, a.G, a.Hq, false, a.rows_log2);
+    if (!col.valid) return;
     row = col.row;
   } else {
-    NB = a.B;
-    T = cu[a.B];
-    cs = cu[b];
-    ce = cu[b + 1];
     row = (long long)b * a.Hq + h0 + h;
   }
   if (ce == cs) {

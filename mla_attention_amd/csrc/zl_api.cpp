@@ -145,13 +145,15 @@ long long max_virtual_seqs(const Varlen& vl, int batch, int group, int rows_log2
   return ((long long)vl.total_q * group + (R - 1) * batch + R - 1) / R;
 }
 
+// Positions of the work line (tokens, or virtual tokens, plus the
+// per-sequence cost) are 32-bit inside the kernels.  The kernels clamp every
+// cache length to max_seqlen_k, so the bound holds whatever cu_seqlens holds.
 zl_status_t check_varlen(const Varlen& vl, int batch, int group, int max_seqlen_k, int seg_cost,
                          int rows_log2) {
-  if (!vl.cu_q) return ZL_OK;
+  if (!vl.cu_q)
+    return (long long)batch * ((long long)max_seqlen_k + seg_cost) >= (1LL << 31) ? ZL_ERR_UNSUPPORTED : ZL_OK;
   if (!aligned(vl.cu_q, 4) || vl.total_q < 0 || (vl.causal != 0 && vl.causal != 1))
     return ZL_ERR_INVALID_ARGUMENT;
-  // Positions of the work line (virtual tokens plus the per-sequence cost)
-  // are 32-bit inside the kernels.
   const long long V = max_virtual_seqs(vl, batch, group, rows_log2);
   if (V * ((long long)max_seqlen_k + seg_cost) >= (1LL << 31)) return ZL_ERR_UNSUPPORTED;
   return ZL_OK;
@@ -215,6 +217,7 @@ zl_status_t gqa_impl(const void* q, const void* k_cache, const void* v_cache, co
   a.page_shift = shift;
   a.cu_q = vl.cu_q;
   a.causal = vl.causal;
+  a.max_len = max_seqlen_k;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   return run_decode(a, layout, head_dim, dtype, phases, workspace, workspace_bytes, stream,
                     (int)max_virtual_seqs(vl, batch, a.G, zl::kMqRowsLog2));
@@ -330,6 +333,7 @@ zl_status_t mla_impl(const void* q, const void* kv_cache, const Paging& pg, cons
   a.page_shift = shift;
   a.cu_q = vl.cu_q;
   a.causal = vl.causal;
+  a.max_len = max_seqlen_k;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   return run_decode(a, zl::kMla576, kv_lora_rank, dtype, phases, workspace, workspace_bytes, stream,
                     (int)max_virtual_seqs(vl, batch, num_q_heads, zl::kMlaMqRowsLog2));
@@ -533,6 +537,7 @@ zl_status_t zl_attn_prefill_gqa(const void* q, const void* k_cache, const void* 
   a.Hkv = num_kv_heads;
   a.G = group;
   a.HB = 1;
+  a.max_len = max_seqlen_k;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   const hipError_t e =
       zl::launch_prefill(a, head_dim, dtype, (int)blocks, reinterpret_cast<hipStream_t>(stream));

@@ -55,6 +55,7 @@ struct DecodeArgs {
   int slot_cols;        // query columns per partial slot (16, or 32 for MLA)
   int B, Hq, Hkv, G, HB, P;
   int seg_cost;         // phantom positions per sequence (zl_split.h)
+  int max_len;          // max_seqlen_k: cache lengths are clamped to [0, max_len]
   float scale_log2;     // softmax_scale * log2(e)
 };
 

@@ -4,9 +4,10 @@
 // key/value head, or a block of up to 16 query heads of it) owns positions
 // [u*Tp, (u+1)*Tp) with Tp = T + B*C (T = total tokens, B = batch, C = the
 // segment cost below).  Inside a unit, sequence b owns [cpos(b), cpos(b+1))
-// with cpos(b) = cu[b] + b*C: first C "phantom" positions that carry no token,
-// then one position per token.  Each of the P workers owns an equal run of
-// `per` positions.
+// with cpos(b) = ccu[b] + b*C (ccu: the prefix sums of the clamped sequence
+// lengths, below): first C "phantom" positions that carry no token, then one
+// position per token.  Each of the P workers owns an equal run of `per`
+// positions.
 //
 // The phantom positions stand for the fixed cost of starting a sequence in a
 // run (its query rows, a partly filled last tile, the epilogue stores): a run
@@ -47,52 +48,102 @@ __device__ __forceinline__ long long positions_per_worker(long long N, int P) {
   return per < 64 ? 64 : per;
 }
 
-// Largest b in [0, B) with cpos(b) <= r, for 0 <= r < Tp: the sequence whose
-// stretch holds in-unit position r (an empty sequence owns only its phantom
-// stretch).  Because cpos is non-decreasing with cpos(0) = 0, it equals the
-// number of b in [1, B) with cpos(b) <= r.  The lanes of the wave load cu 64
-// entries at a time and count with a ballot.  Call from wave-uniform control
-// flow with all 64 lanes active.
-__device__ __forceinline__ int seq_at(const int32_t* cu, int B, int C, int r) {
-  const int lane = __lane_id();
-  int count = 0;
-  for (int i0 = 1; i0 < B; i0 += 64) {
-    const int i = i0 + lane;
-    const bool le = i < B && cu[i] + i * C <= r;
-    count += __popcll(__ballot(le));
-  }
-  return __builtin_amdgcn_readfirstlane(count);
+// Sequence lengths are clamped: sequence b has L_b = clamp(cu[b+1] - cu[b],
+// 0, M) tokens (M = max_seqlen_k), its rows start at cache row cu[b], and the
+// work line numbers the batch's tokens by the prefix sums ccu of the clamped
+// lengths (ccu[0] = 0, ccu[b+1] = ccu[b] + L_b).  A sequence longer than M
+// thus attends over its first M rows, and a length below 0 (cu decreasing)
+// counts as 0; with a valid cu (non-decreasing, lengths at most M) ccu = cu.
+//
+// Sequences c0 .. c0+63, one per lane (lanes past the batch hold an empty
+// sequence): the clamped length, the prefix sums ccu around the lane's
+// sequence, and its first cache row.  carry = ccu[c0].  Call from
+// wave-uniform control flow with all 64 lanes active.
+struct SeqChunk {
+  int len;   // L_b
+  int excl;  // ccu[b]
+  int incl;  // ccu[b + 1]
+  int row0;  // cu[b]
+};
+
+__device__ __forceinline__ SeqChunk seq_chunk(const int32_t* cu, int B, int M, int c0, int carry) {
+  const int b = c0 + __lane_id();
+  // Unpredicated loads at clamped indices (a branch here would make the
+  // compiler's wait drain the tile loads in flight).
+  const int s = cu[b < B ? b : B];
+  const int e = cu[b < B ? b + 1 : B];
+  const long long raw = (long long)e - (long long)s;
+  SeqChunk c;
+  c.len = b < B ? (int)(raw < 0 ? 0 : (raw > M ? M : raw)) : 0;
+  c.incl = carry + wave_inclusive_sum(c.len);
+  c.excl = c.incl - c.len;
+  c.row0 = s;
+  return c;
 }
 
-// Lane l holds cpos(1 + l) = cu[1 + l] + (1 + l)*C (INT_MAX past the batch):
-// the boundaries of a batch of up to 64 sequences in one vector load.  Load it
-// once per kernel, before any tile DMA: its use then never has to drain the
-// tile loads in flight.
-__device__ __forceinline__ int bounds_window(const int32_t* cu, int B, int C) {
-  const int i = 1 + __lane_id();
-  const int v = cu[i < B ? i : B];  // unpredicated load (a branch here would
-                                    // make the compiler's wait drain the DMA)
-  return i <= B ? v + i * C : 0x7fffffff;
+// The first chunk (sequences 0 .. 63), and T = ccu[B] for the whole batch.
+struct BatchBounds {
+  SeqChunk first;
+  int T;
+};
+
+__device__ __forceinline__ BatchBounds batch_bounds(const int32_t* cu, int B, int M) {
+  BatchBounds bb;
+  bb.first = seq_chunk(cu, B, M, 0, 0);
+  int T = __builtin_amdgcn_readlane(bb.first.incl, 63);
+  for (int c0 = 64; c0 < B; c0 += 64) T = __builtin_amdgcn_readlane(seq_chunk(cu, B, M, c0, T).incl, 63);
+  bb.T = T;
+  return bb;
 }
 
 struct SeqSpan {
   int b;       // sequence whose stretch holds the position
-  int cs, ce;  // cu[b], cu[b + 1]
+  int cs, ce;  // ccu[b], ccu[b + 1]: its tokens on the work line
+  int row0;    // cu[b]: the cache row of its first token
 };
 
-// The sequence owning in-unit position r and its token bounds: from the window
-// when B <= 64 (a ballot and two lane reads), else by the search above.
-__device__ __forceinline__ SeqSpan find_seq(const int32_t* cu, int B, int C, int r, int window) {
-  SeqSpan s;
-  if (B <= 64) {
-    s.b = __popcll(__ballot(window <= r));
-    s.ce = __builtin_amdgcn_readlane(window, s.b) - (s.b + 1) * C;
-    s.cs = s.b == 0 ? 0 : __builtin_amdgcn_readlane(window, s.b - 1) - s.b * C;
-  } else {
-    s.b = seq_at(cu, B, C, r);
-    s.cs = cu[s.b];
-    s.ce = cu[s.b + 1];
+// The sequence whose stretch holds in-unit position r (0 <= r < Tp; an empty
+// sequence owns only its phantom stretch): the largest b with cpos(b) =
+// ccu[b] + b*C <= r, i.e. the number of boundaries i in [1, B) with
+// cpos(i) <= r (cpos increases with i).  A chunk answers with a ballot and
+// lane reads; the first chunk is the one held in registers, later chunks
+// (batches over 64 sequences) are loaded as the search reaches them.
+__device__ __forceinline__ SeqSpan find_seq(const int32_t* cu, int B, int M, int C, int r, const SeqChunk& first) {
+  SeqChunk ch = first;
+  int c0 = 0;
+  for (;;) {
+    // Lane l holds boundary i = c0 + l + 1: cpos(i) = ch.incl + i*C.
+    const int i = c0 + __lane_id() + 1;
+    const unsigned long long m = __ballot(i < B && ch.incl + i * C <= r);
+    if (m != ~0ull || c0 + 64 >= B) {
+      const int l = __popcll(m);  // sequence c0 + l
+      SeqSpan s;
+      s.b = c0 + l;
+      s.cs = __builtin_amdgcn_readlane(ch.excl, l);
+      s.ce = __builtin_amdgcn_readlane(ch.incl, l);
+      s.row0 = __builtin_amdgcn_readlane(ch.row0, l);
+      return s;
+    }
+    const int carry = __builtin_amdgcn_readlane(ch.incl, 63);
+    c0 += 64;
+    ch = seq_chunk(cu, B, M, c0, carry);
   }
+}
+
+// Sequence b's bounds (for the merge, which knows b): ccu[b], ccu[b + 1].
+__device__ __forceinline__ SeqSpan seq_bounds(const int32_t* cu, int B, int M, int b, const SeqChunk& first) {
+  SeqChunk ch = first;
+  int c0 = 0;
+  while (b >= c0 + 64) {
+    const int carry = __builtin_amdgcn_readlane(ch.incl, 63);
+    c0 += 64;
+    ch = seq_chunk(cu, B, M, c0, carry);
+  }
+  SeqSpan s;
+  s.b = b;
+  s.cs = __builtin_amdgcn_readlane(ch.excl, b - c0);
+  s.ce = __builtin_amdgcn_readlane(ch.incl, b - c0);
+  s.row0 = __builtin_amdgcn_readlane(ch.row0, b - c0);
   return s;
 }
 
@@ -119,6 +170,7 @@ __device__ __forceinline__ long long token_position(const Line& L, int u, int b,
 struct Segment {
   long long p;
   int u, t0, len, b, cs, ce;
+  int row0;  // cache row of the sequence's first token (plain batches)
 };
 
 // Position -> (unit, in-unit position); 32-bit division when it fits.
@@ -155,6 +207,7 @@ __device__ __forceinline__ Segment segment_at(long long p, long long p_end, cons
   s.b = 0;
   s.cs = 0;
   s.ce = 0;
+  s.row0 = 0;
   while (p < p_end) {
     int u, r;
     split_position(p, L.Tp, u, r);
@@ -171,6 +224,7 @@ __device__ __forceinline__ Segment segment_at(long long p, long long p_end, cons
       s.b = q.b;
       s.cs = q.cs;
       s.ce = q.ce;
+      s.row0 = q.row0;
       return s;
     }
     if (p_end - base < q.ce) return s;  // the run ends inside this sequence
@@ -181,18 +235,13 @@ __device__ __forceinline__ Segment segment_at(long long p, long long p_end, cons
 }
 
 // The sequences of a decode batch (one query token each): sequence b is
-// tokens [cu[b], cu[b+1]).
+// tokens [ccu[b], ccu[b+1]) of the work line, rows cu[b] .. of the cache.
 struct PlainSeqs {
   const int32_t* cu;
-  int B, C;
-  int window;  // bounds_window(cu, B, C)
-  __device__ __forceinline__ SeqSpan span(int r) const { return find_seq(cu, B, C, r, window); }
+  int B, C, M;
+  SeqChunk first;  // sequences 0 .. 63 (batch_bounds)
+  __device__ __forceinline__ SeqSpan span(int r) const { return find_seq(cu, B, M, C, r, first); }
 };
-
-__device__ __forceinline__ Segment segment_at(long long p, long long p_end, const Line& L, const int32_t* cu,
-                                              int window) {
-  return segment_at(p, p_end, L, PlainSeqs{cu, L.B, L.C, window});
-}
 
 // Several new query tokens per sequence.  Sequence b has nq = cu_q[b+1] -
 // cu_q[b] new tokens and lk = cu_k[b+1] - cu_k[b] cached key/value rows.  For
@@ -222,18 +271,21 @@ struct VChunk {
   int start, end;  // in-unit positions of its virtual sequences: [start, end)
 };
 
-__device__ __forceinline__ VChunk vchunk(const int32_t* cu_q, const int32_t* cu_k, int B, int G, int C, int c0,
-                                         int vcarry, int kcarry, int shift) {
+// The cache length lk is clamped to [0, M] and nq to at least 0, as for
+// decode batches (lengths clamped in the kernels; see the top of the file).
+__device__ __forceinline__ VChunk vchunk(const int32_t* cu_q, const int32_t* cu_k, int B, int G, int C, int M,
+                                         int c0, int vcarry, int kcarry, int shift) {
   const int b = c0 + __lane_id();
   const int i0 = b < B ? b : B, i1 = b < B ? b + 1 : B;
   // Unpredicated loads (clamped indices): a branch here would make the
   // compiler's wait drain the tile loads in flight.
   const int q0 = cu_q[i0], q1 = cu_q[i1], k0 = cu_k[i0], k1 = cu_k[i1];
+  const long long rawq = (long long)q1 - q0, rawk = (long long)k1 - k0;
   VChunk c;
   c.q0 = q0;
-  c.nq = q1 - q0;
+  c.nq = rawq < 0 ? 0 : (int)rawq;
   c.k0 = k0;
-  c.lk = k1 - k0;
+  c.lk = rawk < 0 ? 0 : (rawk > M ? M : (int)rawk);
   c.nblk = (c.nq * G + (1 << shift) - 1) >> shift;
   const int tok = c.nblk * c.lk;
   c.vbi = vcarry + wave_inclusive_sum(c.nblk);
@@ -248,22 +300,25 @@ struct VirtualSeqs {
   const int32_t* cu_q;
   const int32_t* cu_k;
   int B, G, C;
+  int M;         // max_seqlen_k: cache lengths are clamped to [0, M]
   int shift;     // rows per block: 2^shift
   VChunk first;  // sequences 0 .. 63 (the whole batch when B <= 64)
   int V, T;      // virtual sequences and tokens of the batch
 
-  __device__ __forceinline__ void init(const int32_t* cq, const int32_t* ck, int b, int g, int c, int rows_log2 = 4) {
+  __device__ __forceinline__ void init(const int32_t* cq, const int32_t* ck, int b, int g, int c, int m,
+                                       int rows_log2) {
     cu_q = cq;
     cu_k = ck;
     B = b;
     G = g;
     C = c;
+    M = m;
     shift = rows_log2;
-    first = vchunk(cu_q, cu_k, B, G, C, 0, 0, 0, shift);
+    first = vchunk(cu_q, cu_k, B, G, C, M, 0, 0, 0, shift);
     V = __builtin_amdgcn_readlane(first.vbi, 63);
     T = __builtin_amdgcn_readlane(first.kb + first.nblk * first.lk, 63);
     for (int c0 = 64; c0 < B; c0 += 64) {
-      const VChunk ch = vchunk(cu_q, cu_k, B, G, C, c0, V, T, shift);
+      const VChunk ch = vchunk(cu_q, cu_k, B, G, C, M, c0, V, T, shift);
       V = __builtin_amdgcn_readlane(ch.vbi, 63);
       T = __builtin_amdgcn_readlane(ch.kb + ch.nblk * ch.lk, 63);
     }
@@ -279,7 +334,7 @@ struct VirtualSeqs {
     unsigned long long m = __ballot(before(ch));
     while (m == ~0ull && c0 + 64 < B) {
       c0 += 64;
-      ch = vchunk(cu_q, cu_k, B, G, C, c0, __builtin_amdgcn_readlane(ch.vbi, 63),
+      ch = vchunk(cu_q, cu_k, B, G, C, M, c0, __builtin_amdgcn_readlane(ch.vbi, 63),
                   __builtin_amdgcn_readlane(ch.kb + ch.nblk * ch.lk, 63), shift);
       m = __ballot(before(ch));
     }
@@ -316,7 +371,7 @@ struct VirtualSeqs {
 
   __device__ __forceinline__ SeqSpan span(int r) const {
     const VSeqInfo s = at_position(r);
-    return SeqSpan{s.v, s.cs, s.ce};
+    return SeqSpan{s.v, s.cs, s.ce, s.k0};
   }
 };
 

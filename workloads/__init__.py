@@ -247,3 +247,45 @@ def make_varlen_query(x: Inputs, q_lens, seed: int = 0, q_mult: float = 1.0) -> 
     if q_mult != 1.0:
         q = q * q_mult
     return VarlenQuery(q_lens, cu_q, q.to(x.spec.torch_dtype))
+
+
+@dataclasses.dataclass
+class RawCache:
+    """A cache whose cu_seqlens need not be a valid prefix sum: cu_raw may
+    start above 0, decrease, or give lengths above max_seqlen.  Sequence b
+    owns L_b = clamp(cu_raw[b+1] - cu_raw[b], 0, max_seqlen) rows from row
+    cu_raw[b] of the buffers.  `clamped` holds the same rows gathered into a
+    valid packed batch (lengths L_b, the same Q), the batch that such a call
+    means."""
+    cu_raw: torch.Tensor                  # int32 [B+1]
+    max_seqlen: int
+    k: Optional[torch.Tensor] = None      # [rows, Hkv, D]
+    v: Optional[torch.Tensor] = None
+    latent: Optional[torch.Tensor] = None  # [rows, Dk]
+    clamped: Optional[Inputs] = None
+
+
+def make_raw_cache(spec: Spec, cu_raw: Sequence[int], max_seqlen: int, seed: int) -> RawCache:
+    """Seeded buffers of max(cu_raw) rows (draw order Q, then K and V, or the
+    latent, as make_inputs) addressed by an unchecked cu_raw."""
+    cu = np.asarray(cu_raw, dtype=np.int64)
+    if len(cu) != spec.batch + 1 or cu.min() < 0 or cu.max() > np.iinfo(np.int32).max:
+        raise ValueError("cu_raw must have batch + 1 non-negative int32 entries")
+    lens = np.clip(np.diff(cu), 0, max_seqlen)
+    rows = int(cu.max())
+    gen = torch.Generator("cpu")
+    gen.manual_seed(seed)
+    dt = spec.torch_dtype
+    q = torch.randn(spec.batch, spec.num_q_heads, spec.head_dim_k, generator=gen).to(dt)
+    idx = torch.from_numpy(np.concatenate([np.arange(cu[b], cu[b] + lens[b]) for b in range(spec.batch)]
+                                          + [np.zeros(0, np.int64)]))
+    cspec = with_shape(spec, lens=tuple(int(v) for v in lens))
+    cu_t = torch.from_numpy(cu.astype(np.int32))
+    if spec.kind == "mla":
+        latent = torch.randn(rows, spec.head_dim_k, generator=gen).to(dt)
+        x = Inputs(cspec, lens, cu_from_lens(lens), q, latent=latent[idx])
+        return RawCache(cu_t, max_seqlen, latent=latent, clamped=x)
+    k = torch.randn(rows, spec.num_kv_heads, spec.head_dim_k, generator=gen).to(dt)
+    v = torch.randn(rows, spec.num_kv_heads, spec.head_dim_v, generator=gen).to(dt)
+    x = Inputs(cspec, lens, cu_from_lens(lens), q, k=k[idx], v=v[idx])
+    return RawCache(cu_t, max_seqlen, k=k, v=v, clamped=x)
