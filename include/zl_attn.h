@@ -50,6 +50,10 @@
  *    clamp changes nothing.  ZL_ERR_UNSUPPORTED when batch * (max_seqlen_k +
  *    C) >= 2^31 (C = 32 for GQA, 64 for MLA; the work split numbers
  *    positions in 32 bits).
+ *  - dtype arguments are ints holding a zl_dtype_t value; any other value
+ *    returns ZL_ERR_INVALID_ARGUMENT (an int parameter, so that a value
+ *    outside the enumeration is an error status rather than undefined
+ *    behaviour in the library).  zl_status_string likewise takes any int.
  *  - 16-bit buffers (q, k, v, latent, out) must be 16-byte aligned.  Rows are
  *    dense: the layouts below have no padding.
  *  - Results are bitwise deterministic for identical inputs, arguments and
@@ -97,7 +101,7 @@ typedef struct ihipStream_t *zl_stream_t;
  * initialisation and its contents are meaningless between calls.
  */
 ZL_API size_t zl_decode_attn_workspace_size(int batch, int num_q_heads, int num_kv_heads,
-                                     int head_dim, int max_seqlen_k, zl_dtype_t dtype);
+                                     int head_dim, int max_seqlen_k, int dtype);
 
 /*
  * Grouped-query decode attention over a packed ragged cache (the operation in
@@ -120,7 +124,7 @@ ZL_API size_t zl_decode_attn_workspace_size(int batch, int num_q_heads, int num_
 ZL_API zl_status_t zl_decode_attn_gqa(const void *q, const void *k_cache, const void *v_cache,
                                const int32_t *cu_seqlens, int batch, int num_q_heads,
                                int num_kv_heads, int head_dim, int max_seqlen_k,
-                               float softmax_scale, zl_dtype_t dtype, void *out, float *lse,
+                               float softmax_scale, int dtype, void *out, float *lse,
                                void *workspace, size_t workspace_bytes, zl_stream_t stream);
 
 /*
@@ -140,7 +144,7 @@ ZL_API zl_status_t zl_decode_attn_gqa(const void *q, const void *k_cache, const 
 ZL_API zl_status_t zl_decode_attn_gqa_no_alloc(const void *q, const void *k_cache, const void *v_cache,
                                                const int32_t *cu_seqlens, int batch, int num_q_heads,
                                                int num_kv_heads, int head_dim, int max_seqlen_k,
-                                               float softmax_scale, zl_dtype_t dtype, void *out, float *lse,
+                                               float softmax_scale, int dtype, void *out, float *lse,
                                                zl_stream_t stream);
 
 /*
@@ -148,7 +152,7 @@ ZL_API zl_status_t zl_decode_attn_gqa_no_alloc(const void *q, const void *k_cach
  * as above).  Returns 0 for invalid sizes.
  */
 ZL_API size_t zl_decode_attn_mla_workspace_size(int batch, int num_q_heads, int kv_lora_rank,
-                                         int rope_dim, int max_seqlen_k, zl_dtype_t dtype);
+                                         int rope_dim, int max_seqlen_k, int dtype);
 
 /*
  * Absorbed multi-head latent attention decode (DeepSeek-V2 MLA, which the
@@ -174,7 +178,7 @@ ZL_API size_t zl_decode_attn_mla_workspace_size(int batch, int num_q_heads, int 
  */
 ZL_API zl_status_t zl_decode_attn_mla(const void *q, const void *kv_cache, const int32_t *cu_seqlens,
                                int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
-                               int max_seqlen_k, float softmax_scale, zl_dtype_t dtype,
+                               int max_seqlen_k, float softmax_scale, int dtype,
                                void *out, float *lse, void *workspace, size_t workspace_bytes,
                                zl_stream_t stream);
 
@@ -193,7 +197,7 @@ ZL_API zl_status_t zl_decode_attn_mla(const void *q, const void *kv_cache, const
  * head_dim_v % 4 == 0, partial buffers 16-byte aligned.
  */
 ZL_API zl_status_t zl_attn_combine(const float *partial_out, const float *partial_lse, int num_splits,
-                            int batch, int num_heads, int head_dim_v, zl_dtype_t out_dtype,
+                            int batch, int num_heads, int head_dim_v, int out_dtype,
                             void *out, float *lse, zl_stream_t stream);
 
 /*
@@ -209,20 +213,20 @@ ZL_API zl_status_t zl_attn_combine(const float *partial_out, const float *partia
  * splitting a call lets a caller time or place the two launches separately.
  */
 ZL_API size_t zl_decode_attn_workspace_size_ex(int batch, int num_q_heads, int num_kv_heads,
-                                        int head_dim, int max_seqlen_k, zl_dtype_t dtype,
+                                        int head_dim, int max_seqlen_k, int dtype,
                                         int num_workers);
 ZL_API zl_status_t zl_decode_attn_gqa_ex(const void *q, const void *k_cache, const void *v_cache,
                                   const int32_t *cu_seqlens, int batch, int num_q_heads,
                                   int num_kv_heads, int head_dim, int max_seqlen_k,
-                                  float softmax_scale, zl_dtype_t dtype, void *out, float *lse,
+                                  float softmax_scale, int dtype, void *out, float *lse,
                                   int num_workers, int phases, void *workspace,
                                   size_t workspace_bytes, zl_stream_t stream);
 ZL_API size_t zl_decode_attn_mla_workspace_size_ex(int batch, int num_q_heads, int kv_lora_rank,
-                                            int rope_dim, int max_seqlen_k, zl_dtype_t dtype,
+                                            int rope_dim, int max_seqlen_k, int dtype,
                                             int num_workers);
 ZL_API zl_status_t zl_decode_attn_mla_ex(const void *q, const void *kv_cache, const int32_t *cu_seqlens,
                                   int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
-                                  int max_seqlen_k, float softmax_scale, zl_dtype_t dtype,
+                                  int max_seqlen_k, float softmax_scale, int dtype,
                                   void *out, float *lse, int num_workers, int phases,
                                   void *workspace, size_t workspace_bytes, zl_stream_t stream);
 
@@ -252,25 +256,25 @@ ZL_API zl_status_t zl_decode_attn_gqa_paged(const void *q, const void *k_pages, 
                                             const int32_t *block_table, int max_pages_per_seq, int page_size,
                                             const int32_t *cu_seqlens, int batch, int num_q_heads,
                                             int num_kv_heads, int head_dim, int max_seqlen_k,
-                                            float softmax_scale, zl_dtype_t dtype, void *out, float *lse,
+                                            float softmax_scale, int dtype, void *out, float *lse,
                                             void *workspace, size_t workspace_bytes, zl_stream_t stream);
 ZL_API zl_status_t zl_decode_attn_gqa_paged_ex(const void *q, const void *k_pages, const void *v_pages,
                                                const int32_t *block_table, int max_pages_per_seq,
                                                int page_size, const int32_t *cu_seqlens, int batch,
                                                int num_q_heads, int num_kv_heads, int head_dim,
-                                               int max_seqlen_k, float softmax_scale, zl_dtype_t dtype,
+                                               int max_seqlen_k, float softmax_scale, int dtype,
                                                void *out, float *lse, int num_workers, int phases,
                                                void *workspace, size_t workspace_bytes, zl_stream_t stream);
 ZL_API zl_status_t zl_decode_attn_mla_paged(const void *q, const void *kv_pages, const int32_t *block_table,
                                             int max_pages_per_seq, int page_size, const int32_t *cu_seqlens,
                                             int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
-                                            int max_seqlen_k, float softmax_scale, zl_dtype_t dtype,
+                                            int max_seqlen_k, float softmax_scale, int dtype,
                                             void *out, float *lse, void *workspace, size_t workspace_bytes,
                                             zl_stream_t stream);
 ZL_API zl_status_t zl_decode_attn_mla_paged_ex(const void *q, const void *kv_pages, const int32_t *block_table,
                                                int max_pages_per_seq, int page_size, const int32_t *cu_seqlens,
                                                int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
-                                               int max_seqlen_k, float softmax_scale, zl_dtype_t dtype,
+                                               int max_seqlen_k, float softmax_scale, int dtype,
                                                void *out, float *lse, int num_workers, int phases,
                                                void *workspace, size_t workspace_bytes, zl_stream_t stream);
 
@@ -310,24 +314,24 @@ ZL_API zl_status_t zl_decode_attn_mla_paged_ex(const void *q, const void *kv_pag
 ZL_API zl_status_t zl_attn_varlen_gqa(const void *q, const void *k_cache, const void *v_cache,
                                       const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int batch,
                                       int total_q, int num_q_heads, int num_kv_heads, int head_dim,
-                                      int max_seqlen_k, float softmax_scale, int causal, zl_dtype_t dtype,
+                                      int max_seqlen_k, float softmax_scale, int causal, int dtype,
                                       void *out, float *lse, void *workspace, size_t workspace_bytes,
                                       zl_stream_t stream);
 ZL_API zl_status_t zl_attn_varlen_gqa_ex(const void *q, const void *k_cache, const void *v_cache,
                                          const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int batch,
                                          int total_q, int num_q_heads, int num_kv_heads, int head_dim,
-                                         int max_seqlen_k, float softmax_scale, int causal, zl_dtype_t dtype,
+                                         int max_seqlen_k, float softmax_scale, int causal, int dtype,
                                          void *out, float *lse, int num_workers, int phases, void *workspace,
                                          size_t workspace_bytes, zl_stream_t stream);
 ZL_API zl_status_t zl_attn_varlen_mla(const void *q, const void *kv_cache, const int32_t *cu_seqlens_q,
                                       const int32_t *cu_seqlens_k, int batch, int total_q, int num_q_heads,
                                       int kv_lora_rank, int rope_dim, int max_seqlen_k, float softmax_scale,
-                                      int causal, zl_dtype_t dtype, void *out, float *lse, void *workspace,
+                                      int causal, int dtype, void *out, float *lse, void *workspace,
                                       size_t workspace_bytes, zl_stream_t stream);
 ZL_API zl_status_t zl_attn_varlen_mla_ex(const void *q, const void *kv_cache, const int32_t *cu_seqlens_q,
                                          const int32_t *cu_seqlens_k, int batch, int total_q, int num_q_heads,
                                          int kv_lora_rank, int rope_dim, int max_seqlen_k, float softmax_scale,
-                                         int causal, zl_dtype_t dtype, void *out, float *lse, int num_workers,
+                                         int causal, int dtype, void *out, float *lse, int num_workers,
                                          int phases, void *workspace, size_t workspace_bytes,
                                          zl_stream_t stream);
 
@@ -353,7 +357,7 @@ ZL_API zl_status_t zl_attn_varlen_gqa_paged(const void *q, const void *k_pages, 
                                             const int32_t *block_table, int max_pages_per_seq, int page_size,
                                             const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int batch,
                                             int total_q, int num_q_heads, int num_kv_heads, int head_dim,
-                                            int max_seqlen_k, float softmax_scale, int causal, zl_dtype_t dtype,
+                                            int max_seqlen_k, float softmax_scale, int causal, int dtype,
                                             void *out, float *lse, void *workspace, size_t workspace_bytes,
                                             zl_stream_t stream);
 ZL_API zl_status_t zl_attn_varlen_gqa_paged_ex(const void *q, const void *k_pages, const void *v_pages,
@@ -361,20 +365,20 @@ ZL_API zl_status_t zl_attn_varlen_gqa_paged_ex(const void *q, const void *k_page
                                                const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
                                                int batch, int total_q, int num_q_heads, int num_kv_heads,
                                                int head_dim, int max_seqlen_k, float softmax_scale, int causal,
-                                               zl_dtype_t dtype, void *out, float *lse, int num_workers,
+                                               int dtype, void *out, float *lse, int num_workers,
                                                int phases, void *workspace, size_t workspace_bytes,
                                                zl_stream_t stream);
 ZL_API zl_status_t zl_attn_varlen_mla_paged(const void *q, const void *kv_pages, const int32_t *block_table,
                                             int max_pages_per_seq, int page_size, const int32_t *cu_seqlens_q,
                                             const int32_t *cu_seqlens_k, int batch, int total_q, int num_q_heads,
                                             int kv_lora_rank, int rope_dim, int max_seqlen_k, float softmax_scale,
-                                            int causal, zl_dtype_t dtype, void *out, float *lse, void *workspace,
+                                            int causal, int dtype, void *out, float *lse, void *workspace,
                                             size_t workspace_bytes, zl_stream_t stream);
 ZL_API zl_status_t zl_attn_varlen_mla_paged_ex(const void *q, const void *kv_pages, const int32_t *block_table,
                                                int max_pages_per_seq, int page_size, const int32_t *cu_seqlens_q,
                                                const int32_t *cu_seqlens_k, int batch, int total_q,
                                                int num_q_heads, int kv_lora_rank, int rope_dim, int max_seqlen_k,
-                                               float softmax_scale, int causal, zl_dtype_t dtype, void *out,
+                                               float softmax_scale, int causal, int dtype, void *out,
                                                float *lse, int num_workers, int phases, void *workspace,
                                                size_t workspace_bytes, zl_stream_t stream);
 
@@ -394,7 +398,7 @@ ZL_API zl_status_t zl_attn_varlen_mla_paged_ex(const void *q, const void *kv_pag
 ZL_API zl_status_t zl_attn_prefill_gqa(const void *q, const void *k_cache, const void *v_cache,
                                        const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int batch,
                                        int total_q, int num_q_heads, int num_kv_heads, int head_dim,
-                                       int max_seqlen_k, float softmax_scale, int causal, zl_dtype_t dtype,
+                                       int max_seqlen_k, float softmax_scale, int causal, int dtype,
                                        void *out, float *lse, zl_stream_t stream);
 
 /*
@@ -420,12 +424,12 @@ ZL_API zl_status_t zl_attn_prefill_gqa(const void *q, const void *k_cache, const
  *     neither given), sum_out = y rounded to dtype (optional; at least one of
  *     codes_out and sum_out).
  */
-ZL_API zl_status_t zl_int8_quantize(const void *x, zl_dtype_t dtype, long long n, int chunk, int8_t *codes,
+ZL_API zl_status_t zl_int8_quantize(const void *x, int dtype, long long n, int chunk, int8_t *codes,
                                     float *scales, zl_stream_t stream);
 ZL_API zl_status_t zl_int8_dequantize(const int8_t *codes, const float *scales, long long n, int chunk,
-                                      zl_dtype_t dtype, void *out, zl_stream_t stream);
+                                      int dtype, void *out, zl_stream_t stream);
 ZL_API zl_status_t zl_int8_reduce_step(const int8_t *codes_in, const float *scales_in, const void *local,
-                                       zl_dtype_t dtype, long long n, int chunk, int8_t *codes_out,
+                                       int dtype, long long n, int chunk, int8_t *codes_out,
                                        float *scales_out, void *sum_out, zl_stream_t stream);
 
 /*
@@ -451,8 +455,10 @@ ZL_API zl_status_t zl_int8_reduce_step(const int8_t *codes_in, const float *scal
 ZL_API zl_status_t zl_hbm_read_probe(const void *src, size_t bytes, int head_dim_k, int workgroups,
                                      uint32_t *sink, zl_stream_t stream);
 
-/* Static, human-readable name of a status code (host). */
-ZL_API const char *zl_status_string(zl_status_t status);
+/* Static, human-readable name of a status code (host).  Takes any int (a
+ * zl_status_t value converts to it); values that name no status give
+ * "unknown zl_status_t". */
+ZL_API const char *zl_status_string(int status);
 
 #ifdef __cplusplus
 }

@@ -24,7 +24,9 @@ from typing import Optional
 import torch  # loads the HIP runtime first; the library reuses it (same soname)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libzl_attn.so")
+# ZL_ATTN_LIBRARY names another build of the same library (a host-side
+# sanitizer build, for instance); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("ZL_ATTN_LIBRARY") or os.path.join(_HERE, "libzl_attn.so")
 _lib = None
 _lock = threading.Lock()
 

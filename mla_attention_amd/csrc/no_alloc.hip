@@ -48,7 +48,7 @@ extern "C" {
 
 zl_status_t zl_decode_attn_gqa_no_alloc(const void* q, const void* k_cache, const void* v_cache,
                                         const int32_t* cu_seqlens, int batch, int num_q_heads, int num_kv_heads,
-                                        int head_dim, int max_seqlen_k, float softmax_scale, zl_dtype_t dtype,
+                                        int head_dim, int max_seqlen_k, float softmax_scale, int dtype,
                                         void* out, float* lse, zl_stream_t stream) {
   const size_t need =
       zl_decode_attn_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_seqlen_k, dtype);

@@ -54,7 +54,7 @@ bool workers_ok(int w) { return w >= 8 && w <= kMaxWorkers && w % 8 == 0; }
 
 // Shared shape checks; returns ZL_OK or the status to report.
 zl_status_t check_common(int batch, int num_q_heads, int num_kv_heads, int max_seqlen_k,
-                         zl_dtype_t dtype, int workers) {
+                         int dtype, int workers) {
   if (batch < 0 || batch > kMaxBatch) return ZL_ERR_INVALID_ARGUMENT;
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads > kMaxHeads) return ZL_ERR_INVALID_ARGUMENT;
   if (num_q_heads % num_kv_heads != 0) return ZL_ERR_INVALID_ARGUMENT;
@@ -66,7 +66,7 @@ zl_status_t check_common(int batch, int num_q_heads, int num_kv_heads, int max_s
 }
 
 size_t gqa_ws_size(int batch, int num_q_heads, int num_kv_heads, int head_dim, int max_seqlen_k,
-                   zl_dtype_t dtype, int num_workers) {
+                   int dtype, int num_workers) {
   if (head_dim != 64 && head_dim != 128) return 0;
   const Layout layout = head_dim == 128 ? zl::kGqaD128 : zl::kGqaD64;
   const int P = pick_workers(num_workers, layout);
@@ -75,14 +75,14 @@ size_t gqa_ws_size(int batch, int num_q_heads, int num_kv_heads, int head_dim, i
 }
 
 size_t mla_ws_size(int batch, int num_q_heads, int kv_lora_rank, int rope_dim, int max_seqlen_k,
-                   zl_dtype_t dtype, int num_workers) {
+                   int dtype, int num_workers) {
   if (kv_lora_rank != 512 || rope_dim != 64) return 0;
   const int P = pick_workers(num_workers, zl::kMla576);
   if (check_common(batch, num_q_heads, 1, max_seqlen_k, dtype, P) != ZL_OK) return 0;
   return ws_layout(P, kv_lora_rank).total;
 }
 
-zl_status_t run_decode(zl::DecodeArgs a, Layout layout, int dv, zl_dtype_t dtype, int phases,
+zl_status_t run_decode(zl::DecodeArgs a, Layout layout, int dv, int dtype, int phases,
                        void* workspace, size_t workspace_bytes, zl_stream_t stream, int max_vseqs = 0) {
   const WsLayout wl = ws_layout(a.P, dv);
   if (workspace == nullptr || !aligned(workspace, 256)) return ZL_ERR_INVALID_ARGUMENT;
@@ -109,12 +109,12 @@ zl_status_t run_decode(zl::DecodeArgs a, Layout layout, int dv, zl_dtype_t dtype
 extern "C" {
 
 size_t zl_decode_attn_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
-                                     int max_seqlen_k, zl_dtype_t dtype) {
+                                     int max_seqlen_k, int dtype) {
   return gqa_ws_size(batch, num_q_heads, num_kv_heads, head_dim, max_seqlen_k, dtype, 0);
 }
 
 size_t zl_decode_attn_workspace_size_ex(int batch, int num_q_heads, int num_kv_heads, int head_dim,
-                                        int max_seqlen_k, zl_dtype_t dtype, int num_workers) {
+                                        int max_seqlen_k, int dtype, int num_workers) {
   if (num_workers < 0) return 0;
   return gqa_ws_size(batch, num_q_heads, num_kv_heads, head_dim, max_seqlen_k, dtype, num_workers);
 }
@@ -173,7 +173,7 @@ zl_status_t check_paging(const Paging& pg, int max_seqlen_k, int& shift) {
 
 zl_status_t gqa_impl(const void* q, const void* k_cache, const void* v_cache, const Paging& pg, const Varlen& vl,
                      const int32_t* cu_seqlens, int batch, int num_q_heads, int num_kv_heads, int head_dim,
-                     int max_seqlen_k, float softmax_scale, zl_dtype_t dtype, void* out, float* lse,
+                     int max_seqlen_k, float softmax_scale, int dtype, void* out, float* lse,
                      int num_workers, int phases, void* workspace, size_t workspace_bytes,
                      zl_stream_t stream) {
   if (num_workers < 0 || phases < 1 || phases > 3) return ZL_ERR_INVALID_ARGUMENT;
@@ -230,7 +230,7 @@ extern "C" {
 zl_status_t zl_decode_attn_gqa_ex(const void* q, const void* k_cache, const void* v_cache,
                                   const int32_t* cu_seqlens, int batch, int num_q_heads,
                                   int num_kv_heads, int head_dim, int max_seqlen_k,
-                                  float softmax_scale, zl_dtype_t dtype, void* out, float* lse,
+                                  float softmax_scale, int dtype, void* out, float* lse,
                                   int num_workers, int phases, void* workspace,
                                   size_t workspace_bytes, zl_stream_t stream) {
   return gqa_impl(q, k_cache, v_cache, Paging{}, Varlen{}, cu_seqlens, batch, num_q_heads, num_kv_heads, head_dim,
@@ -242,7 +242,7 @@ zl_status_t zl_decode_attn_gqa_paged_ex(const void* q, const void* k_pages, cons
                                         const int32_t* block_table, int max_pages_per_seq, int page_size,
                                         const int32_t* cu_seqlens, int batch, int num_q_heads,
                                         int num_kv_heads, int head_dim, int max_seqlen_k,
-                                        float softmax_scale, zl_dtype_t dtype, void* out, float* lse,
+                                        float softmax_scale, int dtype, void* out, float* lse,
                                         int num_workers, int phases, void* workspace,
                                         size_t workspace_bytes, zl_stream_t stream) {
   if (!block_table) return ZL_ERR_INVALID_ARGUMENT;
@@ -259,7 +259,7 @@ zl_status_t zl_decode_attn_gqa_paged(const void* q, const void* k_pages, const v
                                      const int32_t* block_table, int max_pages_per_seq, int page_size,
                                      const int32_t* cu_seqlens, int batch, int num_q_heads,
                                      int num_kv_heads, int head_dim, int max_seqlen_k, float softmax_scale,
-                                     zl_dtype_t dtype, void* out, float* lse, void* workspace,
+                                     int dtype, void* out, float* lse, void* workspace,
                                      size_t workspace_bytes, zl_stream_t stream) {
   return zl_decode_attn_gqa_paged_ex(q, k_pages, v_pages, block_table, max_pages_per_seq, page_size,
                                      cu_seqlens, batch, num_q_heads, num_kv_heads, head_dim, max_seqlen_k,
@@ -270,7 +270,7 @@ zl_status_t zl_decode_attn_gqa_paged(const void* q, const void* k_pages, const v
 zl_status_t zl_decode_attn_gqa(const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* cu_seqlens, int batch, int num_q_heads,
                                int num_kv_heads, int head_dim, int max_seqlen_k,
-                               float softmax_scale, zl_dtype_t dtype, void* out, float* lse,
+                               float softmax_scale, int dtype, void* out, float* lse,
                                void* workspace, size_t workspace_bytes, zl_stream_t stream) {
   return zl_decode_attn_gqa_ex(q, k_cache, v_cache, cu_seqlens, batch, num_q_heads, num_kv_heads,
                                head_dim, max_seqlen_k, softmax_scale, dtype, out, lse, 0, 3,
@@ -278,12 +278,12 @@ zl_status_t zl_decode_attn_gqa(const void* q, const void* k_cache, const void* v
 }
 
 size_t zl_decode_attn_mla_workspace_size(int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
-                                         int max_seqlen_k, zl_dtype_t dtype) {
+                                         int max_seqlen_k, int dtype) {
   return mla_ws_size(batch, num_q_heads, kv_lora_rank, rope_dim, max_seqlen_k, dtype, 0);
 }
 
 size_t zl_decode_attn_mla_workspace_size_ex(int batch, int num_q_heads, int kv_lora_rank,
-                                            int rope_dim, int max_seqlen_k, zl_dtype_t dtype,
+                                            int rope_dim, int max_seqlen_k, int dtype,
                                             int num_workers) {
   if (num_workers < 0) return 0;
   return mla_ws_size(batch, num_q_heads, kv_lora_rank, rope_dim, max_seqlen_k, dtype, num_workers);
@@ -296,7 +296,7 @@ namespace {
 zl_status_t mla_impl(const void* q, const void* kv_cache, const Paging& pg, const Varlen& vl,
                      const int32_t* cu_seqlens, int batch,
                      int num_q_heads, int kv_lora_rank, int rope_dim, int max_seqlen_k, float softmax_scale,
-                     zl_dtype_t dtype, void* out, float* lse, int num_workers, int phases, void* workspace,
+                     int dtype, void* out, float* lse, int num_workers, int phases, void* workspace,
                      size_t workspace_bytes, zl_stream_t stream) {
   if (num_workers < 0 || phases < 1 || phases > 3) return ZL_ERR_INVALID_ARGUMENT;
   if (kv_lora_rank <= 0 || rope_dim < 0) return ZL_ERR_INVALID_ARGUMENT;
@@ -345,7 +345,7 @@ extern "C" {
 
 zl_status_t zl_decode_attn_mla_ex(const void* q, const void* kv_cache, const int32_t* cu_seqlens,
                                   int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
-                                  int max_seqlen_k, float softmax_scale, zl_dtype_t dtype,
+                                  int max_seqlen_k, float softmax_scale, int dtype,
                                   void* out, float* lse, int num_workers, int phases,
                                   void* workspace, size_t workspace_bytes, zl_stream_t stream) {
   return mla_impl(q, kv_cache, Paging{}, Varlen{}, cu_seqlens, batch, num_q_heads, kv_lora_rank, rope_dim, max_seqlen_k,
@@ -355,7 +355,7 @@ zl_status_t zl_decode_attn_mla_ex(const void* q, const void* kv_cache, const int
 zl_status_t zl_decode_attn_mla_paged_ex(const void* q, const void* kv_pages, const int32_t* block_table,
                                         int max_pages_per_seq, int page_size, const int32_t* cu_seqlens,
                                         int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
-                                        int max_seqlen_k, float softmax_scale, zl_dtype_t dtype, void* out,
+                                        int max_seqlen_k, float softmax_scale, int dtype, void* out,
                                         float* lse, int num_workers, int phases, void* workspace,
                                         size_t workspace_bytes, zl_stream_t stream) {
   if (!block_table) return ZL_ERR_INVALID_ARGUMENT;
@@ -370,7 +370,7 @@ zl_status_t zl_decode_attn_mla_paged_ex(const void* q, const void* kv_pages, con
 zl_status_t zl_decode_attn_mla_paged(const void* q, const void* kv_pages, const int32_t* block_table,
                                      int max_pages_per_seq, int page_size, const int32_t* cu_seqlens,
                                      int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
-                                     int max_seqlen_k, float softmax_scale, zl_dtype_t dtype, void* out,
+                                     int max_seqlen_k, float softmax_scale, int dtype, void* out,
                                      float* lse, void* workspace, size_t workspace_bytes, zl_stream_t stream) {
   return zl_decode_attn_mla_paged_ex(q, kv_pages, block_table, max_pages_per_seq, page_size, cu_seqlens, batch,
                                      num_q_heads, kv_lora_rank, rope_dim, max_seqlen_k, softmax_scale, dtype, out,
@@ -379,7 +379,7 @@ zl_status_t zl_decode_attn_mla_paged(const void* q, const void* kv_pages, const 
 
 zl_status_t zl_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* cu_seqlens,
                                int batch, int num_q_heads, int kv_lora_rank, int rope_dim,
-                               int max_seqlen_k, float softmax_scale, zl_dtype_t dtype, void* out,
+                               int max_seqlen_k, float softmax_scale, int dtype, void* out,
                                float* lse, void* workspace, size_t workspace_bytes,
                                zl_stream_t stream) {
   return zl_decode_attn_mla_ex(q, kv_cache, cu_seqlens, batch, num_q_heads, kv_lora_rank, rope_dim,
@@ -390,7 +390,7 @@ zl_status_t zl_decode_attn_mla(const void* q, const void* kv_cache, const int32_
 zl_status_t zl_attn_varlen_gqa_ex(const void* q, const void* k_cache, const void* v_cache,
                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch, int total_q,
                                   int num_q_heads, int num_kv_heads, int head_dim, int max_seqlen_k,
-                                  float softmax_scale, int causal, zl_dtype_t dtype, void* out, float* lse,
+                                  float softmax_scale, int causal, int dtype, void* out, float* lse,
                                   int num_workers, int phases, void* workspace, size_t workspace_bytes,
                                   zl_stream_t stream) {
   if (!cu_seqlens_q) return ZL_ERR_INVALID_ARGUMENT;
@@ -406,7 +406,7 @@ zl_status_t zl_attn_varlen_gqa_ex(const void* q, const void* k_cache, const void
 zl_status_t zl_attn_varlen_gqa(const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch, int total_q,
                                int num_q_heads, int num_kv_heads, int head_dim, int max_seqlen_k,
-                               float softmax_scale, int causal, zl_dtype_t dtype, void* out, float* lse,
+                               float softmax_scale, int causal, int dtype, void* out, float* lse,
                                void* workspace, size_t workspace_bytes, zl_stream_t stream) {
   return zl_attn_varlen_gqa_ex(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, batch, total_q, num_q_heads,
                                num_kv_heads, head_dim, max_seqlen_k, softmax_scale, causal, dtype, out, lse, 0, 3,
@@ -416,7 +416,7 @@ zl_status_t zl_attn_varlen_gqa(const void* q, const void* k_cache, const void* v
 zl_status_t zl_attn_varlen_mla_ex(const void* q, const void* kv_cache, const int32_t* cu_seqlens_q,
                                   const int32_t* cu_seqlens_k, int batch, int total_q, int num_q_heads,
                                   int kv_lora_rank, int rope_dim, int max_seqlen_k, float softmax_scale, int causal,
-                                  zl_dtype_t dtype, void* out, float* lse, int num_workers, int phases,
+                                  int dtype, void* out, float* lse, int num_workers, int phases,
                                   void* workspace, size_t workspace_bytes, zl_stream_t stream) {
   if (!cu_seqlens_q) return ZL_ERR_INVALID_ARGUMENT;
   Varlen vl;
@@ -432,7 +432,7 @@ zl_status_t zl_attn_varlen_gqa_paged_ex(const void* q, const void* k_pages, cons
                                         const int32_t* block_table, int max_pages_per_seq, int page_size,
                                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
                                         int total_q, int num_q_heads, int num_kv_heads, int head_dim,
-                                        int max_seqlen_k, float softmax_scale, int causal, zl_dtype_t dtype,
+                                        int max_seqlen_k, float softmax_scale, int causal, int dtype,
                                         void* out, float* lse, int num_workers, int phases, void* workspace,
                                         size_t workspace_bytes, zl_stream_t stream) {
   if (!cu_seqlens_q || !block_table) return ZL_ERR_INVALID_ARGUMENT;
@@ -453,7 +453,7 @@ zl_status_t zl_attn_varlen_gqa_paged(const void* q, const void* k_pages, const v
                                      const int32_t* block_table, int max_pages_per_seq, int page_size,
                                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
                                      int total_q, int num_q_heads, int num_kv_heads, int head_dim, int max_seqlen_k,
-                                     float softmax_scale, int causal, zl_dtype_t dtype, void* out, float* lse,
+                                     float softmax_scale, int causal, int dtype, void* out, float* lse,
                                      void* workspace, size_t workspace_bytes, zl_stream_t stream) {
   return zl_attn_varlen_gqa_paged_ex(q, k_pages, v_pages, block_table, max_pages_per_seq, page_size, cu_seqlens_q,
                                      cu_seqlens_k, batch, total_q, num_q_heads, num_kv_heads, head_dim,
@@ -465,7 +465,7 @@ zl_status_t zl_attn_varlen_mla_paged_ex(const void* q, const void* kv_pages, con
                                         int max_pages_per_seq, int page_size, const int32_t* cu_seqlens_q,
                                         const int32_t* cu_seqlens_k, int batch, int total_q, int num_q_heads,
                                         int kv_lora_rank, int rope_dim, int max_seqlen_k, float softmax_scale,
-                                        int causal, zl_dtype_t dtype, void* out, float* lse, int num_workers,
+                                        int causal, int dtype, void* out, float* lse, int num_workers,
                                         int phases, void* workspace, size_t workspace_bytes, zl_stream_t stream) {
   if (!cu_seqlens_q || !block_table) return ZL_ERR_INVALID_ARGUMENT;
   Paging pg;
@@ -484,7 +484,7 @@ zl_status_t zl_attn_varlen_mla_paged(const void* q, const void* kv_pages, const 
                                      int max_pages_per_seq, int page_size, const int32_t* cu_seqlens_q,
                                      const int32_t* cu_seqlens_k, int batch, int total_q, int num_q_heads,
                                      int kv_lora_rank, int rope_dim, int max_seqlen_k, float softmax_scale,
-                                     int causal, zl_dtype_t dtype, void* out, float* lse, void* workspace,
+                                     int causal, int dtype, void* out, float* lse, void* workspace,
                                      size_t workspace_bytes, zl_stream_t stream) {
   return zl_attn_varlen_mla_paged_ex(q, kv_pages, block_table, max_pages_per_seq, page_size, cu_seqlens_q,
                                      cu_seqlens_k, batch, total_q, num_q_heads, kv_lora_rank, rope_dim,
@@ -495,7 +495,7 @@ zl_status_t zl_attn_varlen_mla_paged(const void* q, const void* kv_pages, const 
 zl_status_t zl_attn_varlen_mla(const void* q, const void* kv_cache, const int32_t* cu_seqlens_q,
                                const int32_t* cu_seqlens_k, int batch, int total_q, int num_q_heads,
                                int kv_lora_rank, int rope_dim, int max_seqlen_k, float softmax_scale, int causal,
-                               zl_dtype_t dtype, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                               int dtype, void* out, float* lse, void* workspace, size_t workspace_bytes,
                                zl_stream_t stream) {
   return zl_attn_varlen_mla_ex(q, kv_cache, cu_seqlens_q, cu_seqlens_k, batch, total_q, num_q_heads, kv_lora_rank,
                                rope_dim, max_seqlen_k, softmax_scale, causal, dtype, out, lse, 0, 3, workspace,
@@ -504,7 +504,7 @@ zl_status_t zl_attn_varlen_mla(const void* q, const void* kv_cache, const int32_
 
 zl_status_t zl_attn_prefill_gqa(const void* q, const void* k_cache, const void* v_cache, const int32_t* cu_seqlens_q,
                                 const int32_t* cu_seqlens_k, int batch, int total_q, int num_q_heads, int num_kv_heads,
-                                int head_dim, int max_seqlen_k, float softmax_scale, int causal, zl_dtype_t dtype,
+                                int head_dim, int max_seqlen_k, float softmax_scale, int causal, int dtype,
                                 void* out, float* lse, zl_stream_t stream) {
   if (batch < 0 || batch > kMaxBatch || total_q < 0 || max_seqlen_k < 0) return ZL_ERR_INVALID_ARGUMENT;
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads > kMaxHeads || num_q_heads % num_kv_heads != 0)
@@ -545,7 +545,7 @@ zl_status_t zl_attn_prefill_gqa(const void* q, const void* k_cache, const void* 
 }
 
 zl_status_t zl_attn_combine(const float* partial_out, const float* partial_lse, int num_splits,
-                            int batch, int num_heads, int head_dim_v, zl_dtype_t out_dtype,
+                            int batch, int num_heads, int head_dim_v, int out_dtype,
                             void* out, float* lse, zl_stream_t stream) {
   if (num_splits < 1 || num_splits > 1024) return ZL_ERR_INVALID_ARGUMENT;
   if (batch < 0 || batch > kMaxBatch || num_heads <= 0 || num_heads > kMaxHeads)
@@ -578,7 +578,7 @@ constexpr long long kMaxCodecElems = 1LL << 40;
 
 bool codec_chunk_ok(int chunk) { return chunk == 256 || chunk == 512 || chunk == 1024; }
 
-zl_status_t run_codec(const zl::CodecArgs& a, int op, int chunk, zl_dtype_t dtype, zl_stream_t stream) {
+zl_status_t run_codec(const zl::CodecArgs& a, int op, int chunk, int dtype, zl_stream_t stream) {
   const hipError_t e = zl::launch_codec(a, op, chunk, dtype, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ZL_OK : ZL_ERR_HIP;
 }
@@ -587,7 +587,7 @@ zl_status_t run_codec(const zl::CodecArgs& a, int op, int chunk, zl_dtype_t dtyp
 
 extern "C" {
 
-zl_status_t zl_int8_quantize(const void* x, zl_dtype_t dtype, long long n, int chunk, int8_t* codes,
+zl_status_t zl_int8_quantize(const void* x, int dtype, long long n, int chunk, int8_t* codes,
                              float* scales, zl_stream_t stream) {
   if (dtype != ZL_DTYPE_F16 && dtype != ZL_DTYPE_BF16) return ZL_ERR_INVALID_ARGUMENT;
   if (n < 0 || n > kMaxCodecElems) return ZL_ERR_INVALID_ARGUMENT;
@@ -603,7 +603,7 @@ zl_status_t zl_int8_quantize(const void* x, zl_dtype_t dtype, long long n, int c
   return run_codec(a, zl::kCodecQuantize, chunk, dtype, stream);
 }
 
-zl_status_t zl_int8_dequantize(const int8_t* codes, const float* scales, long long n, int chunk, zl_dtype_t dtype,
+zl_status_t zl_int8_dequantize(const int8_t* codes, const float* scales, long long n, int chunk, int dtype,
                                void* out, zl_stream_t stream) {
   if (dtype != ZL_DTYPE_F16 && dtype != ZL_DTYPE_BF16) return ZL_ERR_INVALID_ARGUMENT;
   if (n < 0 || n > kMaxCodecElems) return ZL_ERR_INVALID_ARGUMENT;
@@ -619,7 +619,7 @@ zl_status_t zl_int8_dequantize(const int8_t* codes, const float* scales, long lo
   return run_codec(a, zl::kCodecDequantize, chunk, dtype, stream);
 }
 
-zl_status_t zl_int8_reduce_step(const int8_t* codes_in, const float* scales_in, const void* local, zl_dtype_t dtype,
+zl_status_t zl_int8_reduce_step(const int8_t* codes_in, const float* scales_in, const void* local, int dtype,
                                 long long n, int chunk, int8_t* codes_out, float* scales_out, void* sum_out,
                                 zl_stream_t stream) {
   if (dtype != ZL_DTYPE_F16 && dtype != ZL_DTYPE_BF16) return ZL_ERR_INVALID_ARGUMENT;
@@ -656,7 +656,7 @@ zl_status_t zl_hbm_read_probe(const void* src, size_t bytes, int head_dim_k, int
   return e == hipSuccess ? ZL_OK : ZL_ERR_HIP;
 }
 
-const char* zl_status_string(zl_status_t status) {
+const char* zl_status_string(int status) {
   switch (status) {
     case ZL_OK: return "ZL_OK";
     case ZL_ERR_INVALID_ARGUMENT: return "ZL_ERR_INVALID_ARGUMENT";

@@ -32,9 +32,12 @@ def _load():
     with _lock:
         if _lib is not None:
             return _lib
-        if not os.path.exists(_build.LIB):
-            _build.build()
-        _lib = load_library(_build.LIB)
+        path = os.environ.get("ZL_ORACLE_LIBRARY")  # another build (a sanitizer build, say)
+        if not path:
+            path = _build.LIB
+            if not os.path.exists(path):
+                _build.build()
+        _lib = load_library(path)
         return _lib
 
 
