@@ -178,7 +178,6 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
       return segment_at(p, p_end, line, ps);
   };
   Segment ds = next_segment(p_begin);
-  if (lane == 0) a.first_key[w] = ds.len > 0 ? seq_key(ds.u, ds.b, NB) : -1;
   if (ds.len == 0) return;
   VSeqInfo dsi{}, sgi{};  // several new tokens: the virtual sequences of ds, sg
   if constexpr (MQ) dsi = vs.info(ds.b);
@@ -278,7 +277,6 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
 
   Segment sg = ds;  // the segment being computed
   int cj = 0;       // its current item
-  bool first_seg = true;
   MqColumn col{};   // several new tokens: this lane's column of sg's row block
   if constexpr (MQ) {
     sgi = dsi;
@@ -341,7 +339,7 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
             for (int blk = 0; blk < TL::VBLK; ++blk) store_out4<DT>(orow + 16 * blk, o[blk], inv);
             if (a.lse && g == 0) a.lse[row] = lse_v;
           } else {
-            const int sl = 2 * w + (first_seg ? 0 : 1);
+            const int sl = own_slot(w, sg.t0, sg.cs);
             float* po = a.part_o + ((long long)sl * kHeadsPerUnit + n) * DV + 4 * g;
 #pragma unroll
             for (int blk = 0; blk < TL::VBLK; ++blk) *(f32x4*)(po + 16 * blk) = o[blk] * inv;
@@ -354,7 +352,6 @@ decode_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
       sg = next_segment(sg.p + sg.len);
       if (sg.len == 0) return true;
       cj = 0;
-      first_seg = false;
       if constexpr (MQ) {
         sgi = vs.info(sg.b);
         col = mq_column(sgi, n, sg.u, a.G, a.Hq, a.causal != 0);

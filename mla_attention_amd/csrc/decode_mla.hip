@@ -221,7 +221,6 @@ mla_mq_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
   const long long p_end = N < p_begin + per ? N : p_begin + per;
   const auto next_segment = [&](long long p) { return segment_at(p, p_end, line, vs); };
   Segment ds = next_segment(p_begin);
-  if (tid == 0) a.first_key[w] = ds.len > 0 ? seq_key(ds.u, ds.b, NB) : -1;
   if (ds.len == 0) return;  // the whole workgroup: w is per workgroup
   VSeqInfo dsi = vs.info(ds.b), sgi{};  // the virtual sequences of ds, sg
 
@@ -274,7 +273,6 @@ mla_mq_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
   };
   Segment sg = ds;  // the segment being computed
   int cj = 0;       // its current item
-  bool first_seg = true;
   // This lane's column 16 cb + n of sg's row block.
   sgi = dsi;
   MqColumn col = mq_column(sgi, 16 * cb + n, 0, a.G, a.Hq, a.causal != 0, kMlaMqRowsLog2);
@@ -351,7 +349,7 @@ mla_mq_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
             for (int bb = 0; bb < kBlkPerWave; ++bb) store_out4<DT>(orow + 16 * bb, o[bb], inv);
             if (a.lse && wave == 0 && g == 0) a.lse[row] = lse_v;
           } else {
-            const int sl = 2 * w + (first_seg ? 0 : 1);
+            const int sl = own_slot(w, sg.t0, sg.cs);
             const int c = 16 * cb + n;
             float* po = a.part_o + ((long long)sl * (16 * NCB) + c) * kDV + dim0;
 #pragma unroll
@@ -365,7 +363,6 @@ mla_mq_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __res
       sg = next_segment(sg.p + sg.len);
       if (sg.len == 0) break;
       cj = 0;
-      first_seg = false;
       sgi = vs.info(sg.b);
       col = mq_column(sgi, 16 * cb + n, 0, a.G, a.Hq, a.causal != 0, kMlaMqRowsLog2);
     }
@@ -450,7 +447,6 @@ mla_decode_rs_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t
     return segment_at(p, p_end, line, ps);
   };
   Segment ds = next_segment(p_begin);
-  if (tid == 0) a.first_key[w] = ds.len > 0 ? seq_key(ds.u, ds.b, B) : -1;
   if (ds.len == 0) return;  // the whole workgroup: w is per workgroup
 
   // The run is one stream of items: for every segment its query rows, then
@@ -523,7 +519,6 @@ mla_decode_rs_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t
 
   Segment sg = ds;  // the segment being computed
   int cj = 0;       // its current item
-  bool first_seg = true;
   f32x4 o[kBlkPerWave];
   SoftmaxState sm{-INFINITY, 0.f};
   i16x8 qop[kKHalf];
@@ -575,7 +570,7 @@ mla_decode_rs_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t
             for (int bb = 0; bb < kBlkPerWave; ++bb) store_out4<DT>(orow + 16 * bb, o[bb], inv);
             if (a.lse && wave == 0 && g == 0) a.lse[row] = lse_v;
           } else {
-            const int sl = 2 * w + (first_seg ? 0 : 1);
+            const int sl = own_slot(w, sg.t0, sg.cs);
             float* po = a.part_o + ((long long)sl * kHeadsPerUnit + n) * kDV + dim0;  // 16-column slots
 #pragma unroll
             for (int bb = 0; bb < kBlkPerWave; ++bb) *(f32x4*)(po + 16 * bb) = o[bb] * inv;
@@ -588,7 +583,6 @@ mla_decode_rs_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t
       sg = next_segment(sg.p + sg.len);
       if (sg.len == 0) return true;
       cj = 0;
-      first_seg = false;
     }
     return false;
   };

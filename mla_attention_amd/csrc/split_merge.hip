@@ -90,17 +90,6 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a, const in
   const SeqWorkers sw = seq_workers(line, u, b, cs, ce, per);
   const int w_first = sw.first, w_last = sw.last;
   if (w_first == w_last) return;
-  // Worker w_first used slot 2w if this sequence opened its run, else 2w+1;
-  // every later worker's run opens with this sequence (slot 2w).  Both
-  // candidates of the first worker are loaded together with its key and the
-  // other partials, so the choice adds no memory round trip.
-  const int key_first = a.first_key[w_first];
-  const int s0 = 2 * w_first;
-  const float ls_a = a.part_lse[s0 * kLseSlot + h];
-  const float ls_b = a.part_lse[(s0 + 1) * kLseSlot + h];
-  const f32x4 v_a = *(const f32x4*)(a.part_o + (s0 * sc + h) * DV + 4 * c4);
-  const f32x4 v_b = *(const f32x4*)(a.part_o + ((s0 + 1) * sc + h) * DV + 4 * c4);
-
   const int nparts = w_last - w_first + 1;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float M = -INFINITY, wsum = 0.f;
@@ -111,14 +100,9 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a, const in
 #pragma unroll
     for (int j = 0; j < BATCH; ++j) {
       const int i = min(i0 + j, nparts - 1);  // tail of the batch re-reads the last one
-      const int sl = 2 * (w_first + (i == 0 ? 1 : i));  // slot 0 is chosen below
+      const long long sl = part_slot(w_first, i);
       ls[j] = i0 + j < nparts ? a.part_lse[sl * kLseSlot + h] : -INFINITY;
       v[j] = *(const f32x4*)(a.part_o + (sl * sc + h) * DV + 4 * c4);
-    }
-    if (i0 == 0) {
-      const bool opened = key_first == seq_key(u, b, NB);
-      ls[0] = opened ? ls_a : ls_b;
-      v[0] = opened ? v_a : v_b;
     }
     float bm = ls[0];
 #pragma unroll

@@ -22,21 +22,20 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t lse_off, out_off, key_off, total;
+  size_t lse_off, out_off, total;
 };
 
-// Workspace: [part_lse 2P*32 f32][part_o 2P*cols*Dv f32][first_key P i32],
-// each part 256-byte aligned: two fp32 partial slots of `cols` query columns
-// per worker (16; 32 for MLA, whose tiles may serve 32 query rows) and the key
-// of each run's first segment (see zl_split.h).
+// Workspace: [part_lse 2P*32 f32][part_o 2P*cols*Dv f32], each part 256-byte
+// aligned: two fp32 partial slots of `cols` query columns per worker (16; 32
+// for MLA, whose tiles may serve 32 query rows; see zl_split.h for which run
+// writes which slot).
 int max_slot_cols(int dv) { return dv == 512 ? zl::kMlaSlotCols : zl::kHeadsPerUnit; }
 
 WsLayout ws_layout(int workers, int dv) {
   WsLayout w;
   w.lse_off = 0;
   w.out_off = round_up((size_t)2 * workers * zl::kLseSlot * 4, 256);
-  w.key_off = w.out_off + round_up((size_t)2 * workers * max_slot_cols(dv) * dv * 4, 256);
-  w.total = w.key_off + round_up((size_t)workers * 4, 256);
+  w.total = w.out_off + round_up((size_t)2 * workers * max_slot_cols(dv) * dv * 4, 256);
   return w;
 }
 
@@ -90,7 +89,6 @@ zl_status_t run_decode(zl::DecodeArgs a, Layout layout, int dv, int dtype, int p
   char* ws = static_cast<char*>(workspace);
   a.part_lse = reinterpret_cast<float*>(ws + wl.lse_off);
   a.part_o = reinterpret_cast<float*>(ws + wl.out_off);
-  a.first_key = reinterpret_cast<int*>(ws + wl.key_off);
   a.seg_cost = layout == zl::kMla576 ? zl::kSegCostMla : zl::kSegCostGqa;
   // Slot width the kernels write: 32 columns only for MLA with several new
   // tokens per sequence (the workspace is sized for the widest).

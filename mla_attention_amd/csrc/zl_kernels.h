@@ -37,7 +37,6 @@ struct DecodeArgs {
   float* lse;           // [B, Hq] or nullptr
   float* part_o;        // [2P, slot_cols, Dv]
   float* part_lse;      // [2P, kLseSlot] (first slot_cols used)
-  int* first_key;       // [P]: (unit, sequence) of each run's first segment
   // Paged caches (block table): k / v are page pools [pages, 2^page_shift,
   // row]; token i of sequence b lives in page block_table[b*max_pages +
   // (i >> page_shift)], row i & (2^page_shift - 1).  block_table == nullptr:

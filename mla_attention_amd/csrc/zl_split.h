@@ -28,10 +28,13 @@
 // A run that covers a whole sequence writes that sequence's output directly;
 // a sequence cut between runs gets one fp32 partial (O / l, lse) per run,
 // merged by the split-merge kernel (split_merge.hip) launched right after.
-// Partial slots: worker w writes slot 2w for the first segment of its run and
-// 2w+1 for its last (a run has at most these two cut segments), and records in
-// first_key[w] which (unit, sequence) its first segment belongs to, so that
-// the merge knows which slot the first worker of a sequence used.
+// Partial slots: run w writes slot 2w for a segment cut at its start (the
+// sequence began in an earlier run) and slot 2w + 1 for a segment cut only at
+// its end (it began in this run).  A run holds at most one of each: only its
+// first segment can be cut at its start, only its last at its end, and a
+// segment cut at both ends is the run's only one.  So part k of a sequence
+// whose first run is wf is in slot 2wf + 1 for k = 0 and 2(wf + k) for k >= 1
+// (part_slot), which the merge computes with no lookup.
 #pragma once
 
 #include <stdint.h>
@@ -432,8 +435,12 @@ __device__ __forceinline__ TileRows tile_rows(const int32_t* table_row, int l0, 
   return t;
 }
 
-// Key of (unit u, sequence b) in first_key.
-__device__ __forceinline__ int seq_key(int u, int b, int B) { return u * B + b; }
+// Slot of part k of a sequence whose first run is wf (see the top of the file).
+__device__ __forceinline__ int part_slot(int wf, int k) { return k == 0 ? 2 * wf + 1 : 2 * (wf + k); }
+
+// Slot that run w writes for its cut segment starting at token t0 of a
+// sequence whose first token is cs.
+__device__ __forceinline__ int own_slot(int w, int t0, int cs) { return t0 > cs ? 2 * w : 2 * w + 1; }
 
 // Worker id from the block id: consecutive worker ids are placed on the same
 // XCD (blocks are dealt round-robin over the 8 XCDs).
