@@ -98,6 +98,8 @@ def parse():
                     help="instead: time the prefill kernel on --prefill-batch whole prompts of LEN tokens "
                          "(heads, head dim and dtype of --config), causal")
     ap.add_argument("--prefill-batch", type=int, default=4)
+    ap.add_argument("--prefill-lens", type=str, default="", metavar="L1,L2,...",
+                    help="instead of --prefill / --prefill-batch: whole prompts of these lengths (a ragged batch)")
     ap.add_argument("--codec-chunk", type=int, default=512)
     ap.add_argument("--paged", type=int, default=0, metavar="PAGE_SIZE",
                     help="read the caches from a shuffled page pool through a block table "
@@ -139,7 +141,7 @@ def main():
     if args.codec:
         bench_codec(args)
         return
-    if args.prefill:
+    if args.prefill or args.prefill_lens:
         bench_prefill(args)
         return
 
@@ -432,16 +434,18 @@ def bench_prefill(args):
     import workloads
 
     spec0 = workloads.WORKLOADS[args.config]
-    L, B = args.prefill, args.prefill_batch
-    spec = workloads.with_shape(spec0, batch=B, lens=tuple([L] * B))
+    lens = [int(t) for t in args.prefill_lens.split(",")] if args.prefill_lens else [args.prefill] * args.prefill_batch
+    B, L = len(lens), max(lens)
+    spec = workloads.with_shape(spec0, batch=B, lens=tuple(lens))
     dev = torch.device("cuda:0")
     x = workloads.make_inputs(spec)
-    vq = workloads.make_varlen_query(x, [L] * B, seed=args.config)
+    vq = workloads.make_varlen_query(x, lens, seed=args.config)
     q, k, v = vq.q.to(dev), x.k.to(dev), x.v.to(dev)
     cq, ck = vq.cu_q.to(dev), x.cu_seqlens.to(dev)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream(dev)
-    flops = 4.0 * spec.num_q_heads * spec.head_dim_k * B * L * (L + 1) / 2
+    flops = sum(4.0 * spec.num_q_heads * spec.head_dim_k * n * (n + 1) / 2 for n in lens)
+    ragged = len(set(lens)) > 1
 
     def step(i):
         zl.zl_attn_prefill_gqa(q, k, v, cq, ck, L, spec.scale, out=out, stream=stream)
@@ -473,8 +477,9 @@ def bench_prefill(args):
         "value": round(tf, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16" if spec.dtype == "f16" else "bf16", "data": "synthetic (seeded N(0,1) Q/K/V)",
-        "config": {"workload": f"prefill-b{B}-L{L}-h{spec.num_q_heads}kv{spec.num_kv_heads}-d{spec.head_dim_k}",
-                   "batch": B, "prompt_len": L, "num_q_heads": spec.num_q_heads,
+        "config": {"workload": (f"prefill-ragged-b{B}-Lmax{L}" if ragged else f"prefill-b{B}-L{L}") +
+                   f"-h{spec.num_q_heads}kv{spec.num_kv_heads}-d{spec.head_dim_k}",
+                   "batch": B, "prompt_len": lens if ragged else L, "num_q_heads": spec.num_q_heads,
                    "num_kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim_k, "causal": True},
         "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tf, 1),
                      "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_TFLOPS, 4),
