@@ -440,15 +440,23 @@ def bench_prefill(args):
     dev = torch.device("cuda:0")
     x = workloads.make_inputs(spec)
     vq = workloads.make_varlen_query(x, lens, seed=args.config)
-    q, k, v = vq.q.to(dev), x.k.to(dev), x.v.to(dev)
+    q = vq.q.to(dev)
     cq, ck = vq.cu_q.to(dev), x.cu_seqlens.to(dev)
+    if args.paged:
+        px = workloads.make_paged(x, args.paged)
+        k, v, table = px.k_pages.to(dev), px.v_pages.to(dev), px.block_table.to(dev)
+    else:
+        k, v = x.k.to(dev), x.v.to(dev)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream(dev)
     flops = sum(4.0 * spec.num_q_heads * spec.head_dim_k * n * (n + 1) / 2 for n in lens)
     ragged = len(set(lens)) > 1
 
     def step(i):
-        zl.zl_attn_prefill_gqa(q, k, v, cq, ck, L, spec.scale, out=out, stream=stream)
+        if args.paged:
+            zl.zl_attn_prefill_gqa_paged(q, k, v, table, cq, ck, L, spec.scale, out=out, stream=stream)
+        else:
+            zl.zl_attn_prefill_gqa(q, k, v, cq, ck, L, spec.scale, out=out, stream=stream)
 
     if args.profile_run:
         for i in range(max(3, args.steps)):
@@ -478,7 +486,8 @@ def bench_prefill(args):
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16" if spec.dtype == "f16" else "bf16", "data": "synthetic (seeded N(0,1) Q/K/V)",
         "config": {"workload": (f"prefill-ragged-b{B}-Lmax{L}" if ragged else f"prefill-b{B}-L{L}") +
-                   f"-h{spec.num_q_heads}kv{spec.num_kv_heads}-d{spec.head_dim_k}",
+                   f"-h{spec.num_q_heads}kv{spec.num_kv_heads}-d{spec.head_dim_k}" +
+                   (f"+paged{args.paged}" if args.paged else ""),
                    "batch": B, "prompt_len": lens if ragged else L, "num_q_heads": spec.num_q_heads,
                    "num_kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim_k, "causal": True},
         "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tf, 1),

@@ -402,6 +402,31 @@ ZL_API zl_status_t zl_attn_prefill_gqa(const void *q, const void *k_cache, const
                                        void *out, float *lse, zl_stream_t stream);
 
 /*
+ * zl_attn_prefill_gqa over page pools: long prompt chunks attending over a
+ * prefix cache kept in fixed-size blocks (the first ZhiLight page lists
+ * Prefix Cache and chunked prefill among the engine's features, sections
+ * "技术架构" and "功能生态"; the second page lists chunked prefill with the
+ * paged memory model, section "Dual streams, host all-reduce and the memory
+ * model").  Operation, query / output layouts, mask and checks are those of
+ * zl_attn_prefill_gqa; the caches are the pools of zl_decode_attn_gqa_paged:
+ *   k_pages, v_pages [num_pages, page_size, num_kv_heads, head_dim] dtype;
+ *   row i of sequence b (i < its clamped length) is row i % page_size of
+ *   page block_table[b * max_pages_per_seq + i / page_size];
+ *   cu_seqlens_k gives the cache lengths only (no row indices).
+ * page_size a power of two, 16 .. 256 (else ZL_ERR_UNSUPPORTED);
+ * max_seqlen_k <= max_pages_per_seq * page_size and a null or unaligned
+ * block_table give ZL_ERR_INVALID_ARGUMENT.  Precondition: every table entry
+ * a sequence uses names a page of the pools.  No workspace; asynchronous on
+ * `stream`.
+ */
+ZL_API zl_status_t zl_attn_prefill_gqa_paged(const void *q, const void *k_pages, const void *v_pages,
+                                             const int32_t *block_table, int max_pages_per_seq, int page_size,
+                                             const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int batch,
+                                             int total_q, int num_q_heads, int num_kv_heads, int head_dim,
+                                             int max_seqlen_k, float softmax_scale, int causal, int dtype,
+                                             void *out, float *lse, zl_stream_t stream);
+
+/*
  * INT8 coding of an all-reduce payload: the single-GPU half of the INT8
  * all-reduce (the first ZhiLight page, section 1: the all-reduce of tensor
  * parallelism can move INT8 data to cut the bytes between GPUs; the second

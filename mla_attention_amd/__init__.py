@@ -10,6 +10,10 @@ Entry points (same names as the C ABI):
   zl_decode_attn_mla      absorbed multi-head latent attention decode
   zl_decode_attn_gqa_paged / zl_decode_attn_mla_paged
                           the same over paged caches (block table)
+  zl_attn_varlen_gqa / zl_attn_varlen_mla (+ _paged)
+                          several new query tokens per sequence (draft tokens, chunks)
+  zl_attn_prefill_gqa / zl_attn_prefill_gqa_paged
+                          long runs of new tokens (prefill, large chunks)
   zl_attn_combine         log-sum-exp combine of split partial results
   zl_decode_attn_workspace_size / zl_decode_attn_mla_workspace_size
   zl_status_string
@@ -87,6 +91,8 @@ SIGNATURES = {
     "zl_attn_combine": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
     "zl_attn_prefill_gqa": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                      _c_float, _c_int, _c_int, _vp, _vp, _vp]),
+    "zl_attn_prefill_gqa_paged": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _c_int,
+                                           _c_int, _c_int, _c_int, _c_float, _c_int, _c_int, _vp, _vp, _vp]),
     "zl_int8_quantize": (_c_int, [_vp, _c_int, ctypes.c_longlong, _c_int, _vp, _vp, _vp]),
     "zl_int8_dequantize": (_c_int, [_vp, _vp, ctypes.c_longlong, _c_int, _c_int, _vp, _vp]),
     "zl_int8_reduce_step": (_c_int, [_vp, _vp, _vp, _c_int, ctypes.c_longlong, _c_int, _vp, _vp, _vp, _vp]),
@@ -442,6 +448,30 @@ def zl_attn_prefill_gqa(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, max_seq
         int(max_seqlen_k), float(softmax_scale), int(bool(causal)), _DTYPE[q.dtype], _ptr(out), _ptr(lse),
         _stream(stream, dev))
     _check(st, "zl_attn_prefill_gqa")
+    return (out, lse) if lse is not None else out
+
+
+def zl_attn_prefill_gqa_paged(q, k_pages, v_pages, block_table, cu_seqlens_q, cu_seqlens_k, max_seqlen_k: int,
+                              softmax_scale: float, causal: bool = True, out=None, lse=None, stream=None,
+                              return_lse: bool = False):
+    """zl_attn_prefill_gqa over page pools k_pages/v_pages [pages, page_size, Hkv, D]
+    with block_table int32 [B, max_pages] (as zl_decode_attn_gqa_paged);
+    cu_seqlens_k gives the cache lengths."""
+    dev, B, out, lse = _varlen_common(q, cu_seqlens_q, cu_seqlens_k, q.shape[2], out, lse, return_lse)
+    _need(k_pages, "k_pages", q.dtype, 4, dev)
+    _need(v_pages, "v_pages", q.dtype, 4, dev)
+    table, max_pages = _paging_args(block_table, dev)
+    Tq, Hq, D = q.shape
+    _, page_size, Hkv, Dk = k_pages.shape
+    if Dk != D or v_pages.shape != k_pages.shape:
+        raise ValueError("k_pages / v_pages must be [pages, page_size, Hkv, head_dim] like q")
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must have batch rows")
+    st = library().zl_attn_prefill_gqa_paged(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), table, max_pages, int(page_size), _ptr(cu_seqlens_q),
+        _ptr(cu_seqlens_k), B, Tq, Hq, Hkv, D, int(max_seqlen_k), float(softmax_scale), int(bool(causal)),
+        _DTYPE[q.dtype], _ptr(out), _ptr(lse), _stream(stream, dev))
+    _check(st, "zl_attn_prefill_gqa_paged")
     return (out, lse) if lse is not None else out
 
 

@@ -279,10 +279,10 @@ __device__ __forceinline__ int wave_min(int v) {
 
 }  // namespace
 
-template <int D, int DT>
+template <int D, int DT, bool PAGED>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kPfWaves, 64 * kPfWaves),
                           amdgpu_waves_per_eu(2, 2))) void
-prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, int nblocks) {
+prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __restrict__ block_table, int nblocks) {
   using GE = PfGeo<D>;
   __shared__ __attribute__((aligned(1024))) char smem_raw[kPfStages * GE::STAGE];
   ZL_LDS char* smem = (ZL_LDS char*)smem_raw;
@@ -350,15 +350,30 @@ prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, int nblocks) {
   }
 
   const uint32_t row_bytes = (uint32_t)a.Hkv * D * 2;
-  const char* kseq = (const char*)(a.k + ((long long)si.k0 * a.Hkv + kvh) * D);
-  const char* vseq = (const char*)(a.v + ((long long)si.k0 * a.Hkv + kvh) * D);
+  // Packed caches: the sequence's rows from cache row k0.  Paged caches: the
+  // pools' rows [page, row in page] through the sequence's block-table row;
+  // a tile starts on a multiple of 32 tokens, so its rows 0-15 lie in one
+  // page and rows 16-31 in that page or (16-token pages) the next
+  // (tile_rows), and each wave's DMA covers rows of one half only: waves 0
+  // and 2 rows 0-15 (of K and of V), waves 1 and 3 rows 16-31.
+  const long long seq_row0 = PAGED ? 0 : si.k0;
+  const char* kseq = (const char*)(a.k + (seq_row0 * a.Hkv + kvh) * D);
+  const char* vseq = (const char*)(a.v + (seq_row0 * a.Hkv + kvh) * D);
+  const int32_t* table_row = PAGED ? block_table + (long long)si.b * a.max_pages : nullptr;
   const PfMap<D> map = pf_map<D>(wave, lane);
   int issued = 0;
   auto issue = [&]() {
     const int t0 = 32 * issued;
     const int nv = kend - t0 < 32 ? kend - t0 : 32;
-    pf_dma_tile<D>(kseq + (size_t)t0 * row_bytes, vseq + (size_t)t0 * row_bytes, row_bytes, map, nv,
-                   smem + (issued % kPfStages) * GE::STAGE, wave);
+    size_t tile_off;  // bytes from kseq / vseq to this wave's rows of the tile, less 32-row steps
+    if constexpr (PAGED) {
+      const TileRows tr = tile_rows(table_row, t0, nv, a.page_shift);
+      tile_off = (size_t)((wave & 1) ? tr.half1 : tr.half0) * row_bytes;
+    } else {
+      tile_off = (size_t)t0 * row_bytes;
+    }
+    pf_dma_tile<D>(kseq + tile_off, vseq + tile_off, row_bytes, map, nv, smem + (issued % kPfStages) * GE::STAGE,
+                   wave);
     ++issued;
   };
   for (int s = 0; s < kPfStages - 1 && issued < ntiles; ++s) issue();
@@ -473,8 +488,11 @@ prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, int nblocks) {
 
 template <int D, int DT>
 static void launch_prefill_t(const DecodeArgs& a, int nblocks, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_kernel<D, DT>), dim3((unsigned)(a.Hkv * nblocks)), dim3(64 * kPfWaves), 0, stream, a,
-                     a.cu, nblocks);
+  const dim3 grid((unsigned)(a.Hkv * nblocks)), block(64 * kPfWaves);
+  if (a.block_table)
+    hipLaunchKernelGGL((prefill_kernel<D, DT, true>), grid, block, 0, stream, a, a.cu, a.block_table, nblocks);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, DT, false>), grid, block, 0, stream, a, a.cu, a.block_table, nblocks);
 }
 
 hipError_t launch_prefill(const DecodeArgs& a, int head_dim, int dtype, int max_blocks, hipStream_t stream) {

@@ -337,6 +337,55 @@ zl_status_t mla_impl(const void* q, const void* kv_cache, const Paging& pg, cons
                     (int)max_virtual_seqs(vl, batch, num_q_heads, zl::kMlaMqRowsLog2));
 }
 
+// The prefill calls, packed (pg.table == nullptr) or paged.
+zl_status_t prefill_impl(const void* q, const void* k_cache, const void* v_cache, const Paging& pg,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch, int total_q,
+                         int num_q_heads, int num_kv_heads, int head_dim, int max_seqlen_k, float softmax_scale,
+                         int causal, int dtype, void* out, float* lse, zl_stream_t stream) {
+  if (batch < 0 || batch > kMaxBatch || total_q < 0 || max_seqlen_k < 0) return ZL_ERR_INVALID_ARGUMENT;
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads > kMaxHeads || num_q_heads % num_kv_heads != 0)
+    return ZL_ERR_INVALID_ARGUMENT;
+  if (dtype != ZL_DTYPE_F16 && dtype != ZL_DTYPE_BF16) return ZL_ERR_INVALID_ARGUMENT;
+  if (causal != 0 && causal != 1) return ZL_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(softmax_scale)) return ZL_ERR_INVALID_ARGUMENT;
+  if (head_dim != 64 && head_dim != 128) return head_dim <= 0 ? ZL_ERR_INVALID_ARGUMENT : ZL_ERR_UNSUPPORTED;
+  int shift = 0;
+  const zl_status_t sp = check_paging(pg, max_seqlen_k, shift);
+  if (sp != ZL_OK) return sp;
+  const int group = num_q_heads / num_kv_heads;
+  // Blocks of R = 2^kPrefillRowsLog2 query rows: sum over b of ceil(nq_b * G / R).
+  const long long R = 1LL << zl::kPrefillRowsLog2;
+  const long long blocks = ((long long)total_q * group + (R - 1) * batch + R - 1) / R;
+  if (blocks * num_kv_heads >= (1LL << 31)) return ZL_ERR_UNSUPPORTED;
+  if (batch == 0 || total_q == 0) return ZL_OK;
+  if (!q || !cu_seqlens_q || !cu_seqlens_k || !out) return ZL_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4) || !aligned(lse, 4))
+    return ZL_ERR_INVALID_ARGUMENT;
+  zl::DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_cache);
+  a.v = static_cast<const uint16_t*>(v_cache);
+  a.cu = cu_seqlens_k;
+  a.cu_q = cu_seqlens_q;
+  a.causal = causal;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.B = batch;
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.G = group;
+  a.HB = 1;
+  a.max_len = max_seqlen_k;
+  a.block_table = pg.table;
+  a.max_pages = pg.max_pages;
+  a.page_shift = shift;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  const hipError_t e =
+      zl::launch_prefill(a, head_dim, dtype, (int)blocks, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ZL_OK : ZL_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -504,42 +553,20 @@ zl_status_t zl_attn_prefill_gqa(const void* q, const void* k_cache, const void* 
                                 const int32_t* cu_seqlens_k, int batch, int total_q, int num_q_heads, int num_kv_heads,
                                 int head_dim, int max_seqlen_k, float softmax_scale, int causal, int dtype,
                                 void* out, float* lse, zl_stream_t stream) {
-  if (batch < 0 || batch > kMaxBatch || total_q < 0 || max_seqlen_k < 0) return ZL_ERR_INVALID_ARGUMENT;
-  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads > kMaxHeads || num_q_heads % num_kv_heads != 0)
-    return ZL_ERR_INVALID_ARGUMENT;
-  if (dtype != ZL_DTYPE_F16 && dtype != ZL_DTYPE_BF16) return ZL_ERR_INVALID_ARGUMENT;
-  if (causal != 0 && causal != 1) return ZL_ERR_INVALID_ARGUMENT;
-  if (!std::isfinite(softmax_scale)) return ZL_ERR_INVALID_ARGUMENT;
-  if (head_dim != 64 && head_dim != 128) return head_dim <= 0 ? ZL_ERR_INVALID_ARGUMENT : ZL_ERR_UNSUPPORTED;
-  const int group = num_q_heads / num_kv_heads;
-  // Blocks of R = 2^kPrefillRowsLog2 query rows: sum over b of ceil(nq_b * G / R).
-  const long long R = 1LL << zl::kPrefillRowsLog2;
-  const long long blocks = ((long long)total_q * group + (R - 1) * batch + R - 1) / R;
-  if (blocks * num_kv_heads >= (1LL << 31)) return ZL_ERR_UNSUPPORTED;
-  if (batch == 0 || total_q == 0) return ZL_OK;
-  if (!q || !cu_seqlens_q || !cu_seqlens_k || !out) return ZL_ERR_INVALID_ARGUMENT;
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
-      !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4) || !aligned(lse, 4))
-    return ZL_ERR_INVALID_ARGUMENT;
-  zl::DecodeArgs a{};
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k_cache);
-  a.v = static_cast<const uint16_t*>(v_cache);
-  a.cu = cu_seqlens_k;
-  a.cu_q = cu_seqlens_q;
-  a.causal = causal;
-  a.out = static_cast<uint16_t*>(out);
-  a.lse = lse;
-  a.B = batch;
-  a.Hq = num_q_heads;
-  a.Hkv = num_kv_heads;
-  a.G = group;
-  a.HB = 1;
-  a.max_len = max_seqlen_k;
-  a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  const hipError_t e =
-      zl::launch_prefill(a, head_dim, dtype, (int)blocks, reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ZL_OK : ZL_ERR_HIP;
+  return prefill_impl(q, k_cache, v_cache, Paging{}, cu_seqlens_q, cu_seqlens_k, batch, total_q, num_q_heads,
+                      num_kv_heads, head_dim, max_seqlen_k, softmax_scale, causal, dtype, out, lse, stream);
+}
+
+zl_status_t zl_attn_prefill_gqa_paged(const void* q, const void* k_pages, const void* v_pages,
+                                      const int32_t* block_table, int max_pages_per_seq, int page_size,
+                                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
+                                      int total_q, int num_q_heads, int num_kv_heads, int head_dim, int max_seqlen_k,
+                                      float softmax_scale, int causal, int dtype, void* out, float* lse,
+                                      zl_stream_t stream) {
+  if (!block_table) return ZL_ERR_INVALID_ARGUMENT;  // (the packed call serves that case)
+  return prefill_impl(q, k_pages, v_pages, Paging{block_table, max_pages_per_seq, page_size}, cu_seqlens_q,
+                      cu_seqlens_k, batch, total_q, num_q_heads, num_kv_heads, head_dim, max_seqlen_k, softmax_scale,
+                      causal, dtype, out, lse, stream);
 }
 
 zl_status_t zl_attn_combine(const float* partial_out, const float* partial_lse, int num_splits,

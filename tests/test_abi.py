@@ -253,6 +253,23 @@ def test_prefill_entry_point_rejects_bad_arguments(zl):
     assert pf(Tq=1 << 30, Hq=1024, Hkv=1024) == 2   # 2^22 blocks x 1024 heads
 
 
+def test_paged_prefill_entry_point_rejects_bad_arguments(zl):
+    lib = zl.library()
+
+    def pp(**kw):
+        a = dict(q=A, k=A, v=A, bt=A, mp=8, ps=64, cq=A, ck=A, B=2, Tq=300, Hq=8, Hkv=2, D=128, maxL=300, scale=0.1,
+                 causal=1, dt=1, out=A, lse=None, stream=None)
+        a.update(kw)
+        return lib.zl_attn_prefill_gqa_paged(a["q"], a["k"], a["v"], a["bt"], a["mp"], a["ps"], a["cq"], a["ck"],
+                                             a["B"], a["Tq"], a["Hq"], a["Hkv"], a["D"], a["maxL"], a["scale"],
+                                             a["causal"], a["dt"], a["out"], a["lse"], a["stream"])
+    assert pp(bt=None) == 1 and pp(bt=A + 2) == 1 and pp(mp=0) == 1 and pp(maxL=513) == 1   # 513 > 8 x 64
+    assert pp(ps=8) == 2 and pp(ps=48) == 2 and pp(ps=512) == 2
+    # every check of the packed prefill call holds here too
+    assert pp(cq=None) == 1 and pp(q=None) == 1 and pp(D=96) == 2 and pp(causal=3) == 1 and pp(dt=4) == 1
+    assert pp(Tq=0, q=None, k=None, v=None, cq=None, ck=None, out=None) == 0
+
+
 def test_read_probe_rejects_bad_arguments(zl):
     lib = zl.library()
 
