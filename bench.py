@@ -23,12 +23,18 @@ way in the same process and listed in `per_config`.  Per workload:
 Fractions are algorithmic bytes (every K and V element, or every latent row,
 read once) / time / 8 TB/s.
 
+Warm-up: at least --warmup calls and at least 0.25 s of them (the clocks
+settle only after a fraction of a second of work); `warmup` reports the
+calls made.
+
 Prints one JSON line:
   value      KV GB/s of the headline workload = algorithmic bytes / us_per_step
   roofline   the headline's decode kernel against the 8 TB/s HBM peak
-             (achieved = bytes / kernel_us); traffic and mfma_busy come from
-             the committed rocprofv3 counter record when it was taken on the
-             current kernel sources
+             (achieved = bytes / kernel_us); traffic (L2-to-fabric bytes per
+             launch, read + written, from request counts) and mfma_busy come
+             from the committed rocprofv3 counter record
+             (profiles/traffic_<workload>.json) when it was taken on the
+             current kernel sources, else null
   cpu_baseline  the fp64 oracle on the host cores, on a bounded sample of the
              headline workload
   per_config every workload, as above
@@ -49,19 +55,25 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["zl_device.h", "zl_split.h", "zl_tile.h", "zl_kernels.h", "decode_attn.hip",
-                  "decode_mla.hip", "split_merge.hip"]
+# The sources of each mode's kernels: a counter record is used only when it
+# was taken on these exact sources.
+KERNEL_SOURCES = {
+    "decode": ["zl_device.h", "zl_split.h", "zl_tile.h", "zl_kernels.h", "decode_attn.hip", "decode_mla.hip",
+               "split_merge.hip"],
+    "prefill": ["zl_device.h", "zl_split.h", "zl_tile.h", "zl_kernels.h", "prefill_attn.hip"],
+    "codec": ["zl_device.h", "zl_kernels.h", "int8_codec.hip"],
+}
 
 
-def kernel_source_sha() -> str:
+def kernel_source_sha(kind: str = "decode") -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, "mla_attention_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def profile_record(workload: str) -> dict:
+def profile_record(workload: str, kind: str = "decode") -> dict:
     """The committed rocprofv3 counter record for this workload (HBM bytes per
     launch, matrix-core busy share), if it was taken on the current kernel
     sources; else an empty dict."""
@@ -70,7 +82,7 @@ def profile_record(workload: str) -> dict:
         return {}
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha") != kernel_source_sha():
+    if rec.get("kernel_source_sha") != kernel_source_sha(kind):
         return {}
     return rec
 
@@ -167,7 +179,7 @@ def main():
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": head["summary"]["warmup_calls"],
         "ms_per_step": round(head["ms_per_step"], 5),
         "us_per_step": round(head["ms_per_step"] * 1e3, 2),
         "us_per_call_percentiles": head["spread"],
@@ -303,6 +315,28 @@ def decode_profile_run(args):
     print(f"profile run: {rig.name}, {n} launches", flush=True)
 
 
+# The clocks reach their sustained level only after a fraction of a second of
+# work (the prefill measurements below show it for the matrix units; decode
+# steps measured right after a few warm-up calls read up to 8% slow).
+MIN_WARMUP_S = 0.25
+
+
+def warm_up(step, W):
+    """Run step(i) at least W times and for at least MIN_WARMUP_S seconds;
+    returns the number of warm-up calls made."""
+    import torch
+
+    t0 = time.perf_counter()
+    i = 0
+    while i < W or time.perf_counter() - t0 < MIN_WARMUP_S:
+        step(i)
+        i += 1
+        if i >= W and i % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return i
+
+
 def timed_span(stream, fn, K):
     """Milliseconds per call of K back-to-back fn(i) on `stream`, with events
     only at the two ends."""
@@ -327,10 +361,8 @@ def bench_decode(cfg, args):
 
     rig = DecodeRig(cfg, args)
     spec, x, stream = rig.spec, rig.x, rig.stream
-    K, W = args.steps, args.warmup
-    for i in range(W):
-        rig.step(i)
-    torch.cuda.synchronize()
+    K = args.steps
+    W = warm_up(rig.step, args.warmup)
 
     # Timed region: K whole calls (decode kernel + merge kernel), back to back
     # on the launch stream, events only at the two ends.
@@ -383,6 +415,7 @@ def bench_decode(cfg, args):
         "kernel_us_bracketed": round(kern_br * 1e3, 2),
         "kernel_frac_bracketed": round(kv / (kern_br * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "merge_us_bracketed": round(merge_ms * 1e3, 2),
+        "warmup_calls": W,
     }
     if not args.no_read_ceiling and rig.paged is None and rig.vq is None:
         summary.update(read_ceiling(rig, K, W))
@@ -480,19 +513,21 @@ def bench_prefill(args):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / K
     tf = flops / (ms * 1e-3) / 1e12
+    workload = ((f"prefill-ragged-b{B}-Lmax{L}" if ragged else f"prefill-b{B}-L{L}") +
+                f"-h{spec.num_q_heads}kv{spec.num_kv_heads}-d{spec.head_dim_k}-{spec.dtype}" +
+                (f"+paged{args.paged}" if args.paged else ""))
+    prof = profile_record(workload, "prefill")
     print(json.dumps({
         "metric": "prefill attention TFLOP/s (useful causal QK^T + PV flops / step time)",
         "value": round(tf, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16" if spec.dtype == "f16" else "bf16", "data": "synthetic (seeded N(0,1) Q/K/V)",
-        "config": {"workload": (f"prefill-ragged-b{B}-Lmax{L}" if ragged else f"prefill-b{B}-L{L}") +
-                   f"-h{spec.num_q_heads}kv{spec.num_kv_heads}-d{spec.head_dim_k}" +
-                   (f"+paged{args.paged}" if args.paged else ""),
+        "config": {"workload": workload,
                    "batch": B, "prompt_len": lens if ragged else L, "num_q_heads": spec.num_q_heads,
                    "num_kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim_k, "causal": True},
         "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tf, 1),
                      "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": prof.get("hbm_bytes_per_launch"), "mfma_busy": prof.get("mfma_busy_frac")},
         "cpu_baseline": None}), flush=True)
 
 
@@ -560,15 +595,18 @@ def bench_codec(args):
     kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     gbs = per_call / (ms * 1e-3) / 1e9
     kgbs = per_call / (kern_ms * 1e-3) / 1e9
+    workload = f"codec-{args.codec}-{args.codec_mib}MiB-fp16-chunk{C}"
+    prof = profile_record(workload, "codec")
     print(json.dumps({
         "metric": f"INT8 all-reduce payload codec ({args.codec}) GB/s of algorithmic bytes",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16->i8", "data": "synthetic (seeded N(0,1) fp16 payload)",
-        "config": {"workload": f"codec-{args.codec}-{args.codec_mib}MiB-fp16-chunk{C}", "elements": n,
+        "config": {"workload": workload, "elements": n,
                    "bytes_per_call": per_call, "cold_cache_replicas": reps},
         "roofline": {"bound": "hbm", "kernel": "codec_kernel", "achieved": round(kgbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
+                     "traffic": prof.get("hbm_bytes_per_launch"),
                      "avg_launch_us": round(kern_ms * 1e3, 2)},
         "cpu_baseline": None}), flush=True)
 
