@@ -46,6 +46,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -65,11 +66,25 @@ KERNEL_SOURCES = {
 }
 
 
-def kernel_source_sha(kind: str = "decode") -> str:
+def code_only(text: str) -> str:
+    """C++ source without its comments and with runs of whitespace collapsed,
+    so that the hash below names the code that was measured, not its prose.
+    (String literals in these sources hold no comment markers.)"""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_source_sha(kind: str = "decode", read=None) -> str:
+    """Hash of the code of one mode's kernel sources.  read(name) -> text
+    (default: the files in mla_attention_amd/csrc)."""
+    if read is None:
+        def read(name):
+            with open(os.path.join(ROOT, "mla_attention_amd", "csrc", name)) as f:
+                return f.read()
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, "mla_attention_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        h.update(code_only(read(name)).encode())
     return h.hexdigest()[:16]
 
 

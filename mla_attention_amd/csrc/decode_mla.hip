@@ -20,7 +20,7 @@
 //    token per sequence (mla_decode_rs_kernel): the quarters go to registers
 //    with coalesced 16-byte loads two items ahead of the math and are written
 //    to LDS when their turn comes (two LDS stages).  Several new tokens per
-//    sequence (mla_decode_kernel): global_load_lds DMA into a four-stage LDS
+//    sequence (mla_mq_kernel): global_load_lds DMA into a four-stage LDS
 //    ring, three items in flight.  Either way items flow across segment
 //    boundaries, so a new sequence does not drain the pipeline.  Slots are
 //    XOR-swizzled within groups of 8 (rows are 72 slots long).
