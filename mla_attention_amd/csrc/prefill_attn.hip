@@ -9,13 +9,19 @@
 //
 // Unlike decode, every cache row is used by many query rows, so the work is
 // matrix-unit bound.  Structure (two workgroups of four wavefronts per CU):
-//  * A workgroup takes one key/value head and a block of 128 query rows of
-//    one sequence -- the pairs (new token i, head hh of the head's group),
-//    numbered i*G + hh, so the group's heads share every K/V tile.  Wave w
-//    owns rows 32w .. 32w+31 as two 16-row MFMA column blocks.  Blocks are
-//    launched longest first (the last blocks of a sequence see the most keys).
-//  * The block streams the keys its last token can see in 32-token tiles
-//    through a four-stage LDS ring; each wave DMAs a quarter of every tile
+//  * A block is one key/value head and 128 query rows of one sequence -- the
+//    pairs (new token i, head hh of the head's group), numbered i*G + hh, so
+//    the group's heads share every K/V tile.  Wave w owns rows 32w .. 32w+31
+//    as two 16-row MFMA column blocks.  Blocks are ordered longest first
+//    (the last blocks of a sequence see the most keys).
+//  * The workgroups are persistent (two per CU): each takes one block per
+//    round, walking the order forwards and backwards in turn, so that equal
+//    prompts give every workgroup the same number of tiles.  A block's start
+//    (its query operands, the first tiles' latency) used to cost as much as
+//    several tiles when every block was a workgroup of its own.
+//  * A workgroup streams the keys each block's last token can see in
+//    32-token tiles through a four-stage LDS ring that runs on from one
+//    block into the next; each wave DMAs a quarter of every tile
 //    (global_load_lds, SADDR form) and one barrier per tile both publishes
 //    the tile and frees the stage refilled next.
 //  * Per tile and wave: S^T = K Q^T for 2 token blocks x 2 column blocks
@@ -277,13 +283,85 @@ __device__ __forceinline__ int wave_min(int v) {
   return v;
 }
 
+// One block: 128 query rows of one sequence for one key/value head, and the
+// keys its last row sees.
+struct PfBlock {
+  int kvh;
+  VSeqInfo si;
+  int kend;    // keys seen by the block's last row
+  int ntiles;  // 32-token tiles holding them
+};
+
+// Block p of the order: key/value head p mod Hkv, and per head the blocks
+// longest first (a sequence's last block first, sequences in reverse batch
+// order).
+__device__ __forceinline__ PfBlock pf_block(const VirtualSeqs& vs, const DecodeArgs& a, int p) {
+  PfBlock bk;
+  bk.kvh = p % a.Hkv;
+  bk.si = vs.info(vs.V - 1 - p / a.Hkv);
+  const int last_row = bk.si.nq * a.G - 1;
+  const int blk_last = ((bk.si.hb + 1) << kPfRowsLog2) - 1;
+  const int last_tok = (blk_last < last_row ? blk_last : last_row) / a.G;
+  const int kend = a.causal ? bk.si.lk - bk.si.nq + last_tok + 1 : bk.si.lk;
+  bk.kend = kend < bk.si.lk ? kend : bk.si.lk;
+  bk.ntiles = bk.kend > 0 ? (bk.kend + 31) >> 5 : 0;
+  return bk;
+}
+
+// The position in that order that workgroup w of P takes in round r: rounds
+// walk the order P positions at a time, alternately forwards and backwards,
+// so over two rounds a workgroup gets one block from each end of a stretch
+// of decreasing lengths (equal-length prompts balance exactly).
+__device__ __forceinline__ long long pf_position(int r, int w, int P) {
+  return (long long)r * P + ((r & 1) ? P - 1 - w : w);
+}
+
+// This lane's columns of a block: query rows 128 hb + 16 kPfCB wave + 16 cb + n.
+struct PfRows {
+  long long orow[kPfCB];  // output row (clamped to the block's last valid one)
+  bool valid[kPfCB];
+  int lim[kPfCB];         // last visible cache row, counted from the sequence's first
+  int lim_min;            // the wave's smallest lim: tiles below it need no mask
+};
+
+__device__ __forceinline__ PfRows pf_rows(const PfBlock& bk, const DecodeArgs& a, int wave, int n) {
+  PfRows rw;
+  const int last_row = bk.si.nq * a.G - 1;
+  int lim_lane = 0x7fffffff;
+#pragma unroll
+  for (int cb = 0; cb < kPfCB; ++cb) {
+    const int r = (bk.si.hb << kPfRowsLog2) + 16 * kPfCB * wave + 16 * cb + n;
+    const int rr = r < last_row ? r : last_row;
+    const int qi = rr / a.G;
+    rw.orow[cb] = (long long)(bk.si.q0 + qi) * a.Hq + bk.kvh * a.G + (rr - qi * a.G);
+    rw.valid[cb] = r <= last_row;
+    rw.lim[cb] = a.causal ? bk.si.lk - bk.si.nq + qi : bk.si.lk - 1;
+    lim_lane = min(lim_lane, rw.lim[cb]);
+  }
+  rw.lim_min = readfirstlane(wave_min(lim_lane));
+  return rw;
+}
+
+// The stream's next tile to load: tile t of round r's block, and what its
+// loads need of that block.
+struct PfCursor {
+  int r, t;
+  int kvh, row0;  // row0: the sequence's first cache row (packed) or its block-table row (paged)
+  int kend, ntiles;
+  bool live;
+};
+
 }  // namespace
 
+// Persistent: a workgroup takes the blocks of its rounds one after another,
+// and its tile ring runs on across their boundaries, so the first tiles of
+// the next block are in flight while the current one ends.
 template <int D, int DT, bool PAGED>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kPfWaves, 64 * kPfWaves),
                           amdgpu_waves_per_eu(2, 2))) void
-prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __restrict__ block_table, int nblocks) {
+prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __restrict__ block_table) {
   using GE = PfGeo<D>;
+  static_assert((kPfStages & (kPfStages - 1)) == 0, "ring stage of a tile by masking");
   __shared__ __attribute__((aligned(1024))) char smem_raw[kPfStages * GE::STAGE];
   ZL_LDS char* smem = (ZL_LDS char*)smem_raw;
   const int tid = threadIdx.x;
@@ -291,107 +369,105 @@ prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __re
   const int lane = tid & 63;
   const int n = lane & 15;
   const int g = lane >> 4;
+  const int P = (int)gridDim.x;
+  const int w = (int)blockIdx.x;
 
-  // Workgroup -> (key/value head, block of 128 query rows), longest first.
-  const int kvh = (int)blockIdx.x % a.Hkv;
-  const int j = (int)blockIdx.x / a.Hkv;
   VirtualSeqs vs;
   vs.init(a.cu_q, cu, a.B, a.G, 0, a.max_len, kPfRowsLog2);
-  if (j >= vs.V) return;
-  const VSeqInfo si = vs.info(vs.V - 1 - j);
-  const bool causal = a.causal != 0;
+  const int N = a.Hkv * vs.V;  // blocks of the batch (the host bounds this below 2^31)
+  if (pf_position(0, w, P) >= N) return;  // workgroup-uniform, before any barrier
 
-  // This lane's columns: query rows 128 hb + 16 kPfCB wave + 16 cb + n.
-  long long orow[kPfCB];
-  bool valid[kPfCB];
-  int lim[kPfCB];  // last visible cache row, counted from the sequence's first
-  const int last_row = si.nq * a.G - 1;
-#pragma unroll
-  for (int cb = 0; cb < kPfCB; ++cb) {
-    const int r = (si.hb << kPfRowsLog2) + 16 * kPfCB * wave + 16 * cb + n;
-    const int rr = r < last_row ? r : last_row;
-    const int qi = rr / a.G;
-    orow[cb] = (long long)(si.q0 + qi) * a.Hq + kvh * a.G + (rr - qi * a.G);
-    valid[cb] = r <= last_row;
-    lim[cb] = causal ? si.lk - si.nq + qi : si.lk - 1;
-  }
-  // Tiles below every column's limit need no mask (wave-uniform).
-  int lim_lane = lim[0];
-#pragma unroll
-  for (int cb = 1; cb < kPfCB; ++cb) lim_lane = min(lim_lane, lim[cb]);
-  const int lim_min = readfirstlane(wave_min(lim_lane));
-  // Keys the block's last row can see.
-  const int blk_last = ((si.hb + 1) << kPfRowsLog2) - 1;
-  const int last_tok = (blk_last < last_row ? blk_last : last_row) / a.G;
-  int kend = causal ? si.lk - si.nq + last_tok + 1 : si.lk;
-  kend = kend < si.lk ? kend : si.lk;
-  const int ntiles = kend > 0 ? (kend + 31) >> 5 : 0;
-
-  // Query operands straight from global memory (waited for before any DMA).
-  i16x8 qop[kPfCB][GE::KSTEPS];
-#pragma unroll
-  for (int cb = 0; cb < kPfCB; ++cb)
-#pragma unroll
-    for (int kb = 0; kb < GE::KSTEPS; ++kb)
-      qop[cb][kb] = *(const i16x8*)(a.q + orow[cb] * D + 32 * kb + 8 * g);
-#pragma unroll
-  for (int cb = 0; cb < kPfCB; ++cb)
-#pragma unroll
-    for (int kb = 0; kb < GE::KSTEPS; ++kb) touch(qop[cb][kb]);
   // The softmax takes a non-negative scale: a negative one is moved onto the
   // query operands (sign flip of every 16-bit value, exact).
-  float scale_log2 = a.scale_log2;
-  if (scale_log2 < 0.f) {
-    scale_log2 = -scale_log2;
+  const bool flip = a.scale_log2 < 0.f;
+  const float scale_log2 = flip ? -a.scale_log2 : a.scale_log2;
+  i16x8 qop[kPfCB][GE::KSTEPS];
+  auto load_q = [&](const long long (&orow)[kPfCB]) {
 #pragma unroll
     for (int cb = 0; cb < kPfCB; ++cb)
 #pragma unroll
-      for (int kb = 0; kb < GE::KSTEPS; ++kb) qop[cb][kb] = qop[cb][kb] ^ (short)0x8000;
+      for (int kb = 0; kb < GE::KSTEPS; ++kb)
+        qop[cb][kb] = *(const i16x8*)(a.q + orow[cb] * D + 32 * kb + 8 * g);
+  };
+  auto flip_q = [&]() {
+    if (flip) {
+#pragma unroll
+      for (int cb = 0; cb < kPfCB; ++cb)
+#pragma unroll
+        for (int kb = 0; kb < GE::KSTEPS; ++kb) qop[cb][kb] = qop[cb][kb] ^ (short)0x8000;
+    }
+  };
+
+  int r = 0;
+  PfBlock bk = pf_block(vs, a, (int)pf_position(0, w, P));
+  PfRows rw = pf_rows(bk, a, wave, n);
+  // The first block's query operands, waited for before any DMA.
+  if (bk.ntiles > 0) {
+    load_q(rw.orow);
+#pragma unroll
+    for (int cb = 0; cb < kPfCB; ++cb)
+#pragma unroll
+      for (int kb = 0; kb < GE::KSTEPS; ++kb) touch(qop[cb][kb]);
   }
 
+  // Tile loads.  Packed caches: the sequence's rows from cache row k0.
+  // Paged caches: the pools' rows [page, row in page] through the sequence's
+  // block-table row; a tile starts on a multiple of 32 tokens, so its rows
+  // 0-15 lie in one page and rows 16-31 in that page or (16-token pages) the
+  // next (tile_rows), and each wave's DMA covers rows of one half only:
+  // waves 0 and 2 rows 0-15 (of K and of V), waves 1 and 3 rows 16-31.
   const uint32_t row_bytes = (uint32_t)a.Hkv * D * 2;
-  // Packed caches: the sequence's rows from cache row k0.  Paged caches: the
-  // pools' rows [page, row in page] through the sequence's block-table row;
-  // a tile starts on a multiple of 32 tokens, so its rows 0-15 lie in one
-  // page and rows 16-31 in that page or (16-token pages) the next
-  // (tile_rows), and each wave's DMA covers rows of one half only: waves 0
-  // and 2 rows 0-15 (of K and of V), waves 1 and 3 rows 16-31.
-  const long long seq_row0 = PAGED ? 0 : si.k0;
-  const char* kseq = (const char*)(a.k + (seq_row0 * a.Hkv + kvh) * D);
-  const char* vseq = (const char*)(a.v + (seq_row0 * a.Hkv + kvh) * D);
-  const int32_t* table_row = PAGED ? block_table + (long long)si.b * a.max_pages : nullptr;
   const PfMap<D> map = pf_map<D>(wave, lane);
-  int issued = 0;
+  // The cursor's first block with tiles at or after round r0 (live = false
+  // past the last).
+  auto seek = [&](int r0) {
+    PfCursor c;
+    c.live = false;
+    c.t = 0;
+    for (int rr = r0;; ++rr) {
+      const long long p = pf_position(rr, w, P);
+      if (p >= N) break;
+      const PfBlock bb = pf_block(vs, a, (int)p);
+      if (bb.ntiles > 0) {
+        c.r = rr;
+        c.kvh = bb.kvh;
+        c.row0 = PAGED ? bb.si.b : bb.si.k0;
+        c.kend = bb.kend;
+        c.ntiles = bb.ntiles;
+        c.live = true;
+        break;
+      }
+    }
+    return c;
+  };
+  PfCursor cur = seek(0);
+  int issued = 0;  // tiles of the stream issued so far
   auto issue = [&]() {
-    const int t0 = 32 * issued;
-    const int nv = kend - t0 < 32 ? kend - t0 : 32;
+    const int t0 = 32 * cur.t;
+    const int nv = cur.kend - t0 < 32 ? cur.kend - t0 : 32;
+    const long long seq_row0 = PAGED ? 0 : cur.row0;
+    const char* kseq = (const char*)(a.k + (seq_row0 * a.Hkv + cur.kvh) * D);
+    const char* vseq = (const char*)(a.v + (seq_row0 * a.Hkv + cur.kvh) * D);
     size_t tile_off;  // bytes from kseq / vseq to this wave's rows of the tile, less 32-row steps
     if constexpr (PAGED) {
-      const TileRows tr = tile_rows(table_row, t0, nv, a.page_shift);
+      const TileRows tr = tile_rows(block_table + (long long)cur.row0 * a.max_pages, t0, nv, a.page_shift);
       tile_off = (size_t)((wave & 1) ? tr.half1 : tr.half0) * row_bytes;
     } else {
       tile_off = (size_t)t0 * row_bytes;
     }
-    pf_dma_tile<D>(kseq + tile_off, vseq + tile_off, row_bytes, map, nv, smem + (issued % kPfStages) * GE::STAGE,
-                   wave);
+    pf_dma_tile<D>(kseq + tile_off, vseq + tile_off, row_bytes, map, nv,
+                   smem + (issued & (kPfStages - 1)) * GE::STAGE, wave);
     ++issued;
+    if (++cur.t == cur.ntiles) cur = seek(cur.r + 1);
   };
-  for (int s = 0; s < kPfStages - 1 && issued < ntiles; ++s) issue();
+  for (int s = 0; s < kPfStages - 1 && cur.live; ++s) issue();
 
-  f32x4 o[kPfCB][GE::VBLK];
-  SoftmaxState sm[kPfCB];
-#pragma unroll
-  for (int cb = 0; cb < kPfCB; ++cb) {
-    sm[cb] = SoftmaxState{-INFINITY, 0.f};
-#pragma unroll
-    for (int bb = 0; bb < GE::VBLK; ++bb) o[cb][bb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // Software pipeline: the scores of tile i+1 (matrix units) are computed in
-  // the same basic block as the softmax of tile i (vector unit), so the two
-  // overlap; then tile i's PV.  Ring: tile i+1 must have landed before its
-  // scores; the stage of tile i-1 (whose PV every wave has finished at the
-  // barrier) takes tile i+3.
+  // Ring: a tile must have landed before its scores; the stage of tile c-1
+  // (whose PV every wave has finished at the barrier) takes tile c+3.  The
+  // waits count only the ring's loads; query loads and output stores issued
+  // in between are older or newer memory operations of the same in-order
+  // counter, so a wait may cover some of them too but never too few.
+  int waited = 0;  // tiles of the stream known to be in LDS for every wave
   auto wait_tile = [&](int t) {
     const int after = issued - t - 1;  // tiles issued after t may be in flight
     if (after >= 2)
@@ -401,98 +477,140 @@ prefill_kernel(DecodeArgs a, const int32_t* __restrict__ cu, const int32_t* __re
     else
       wait_vmcnt<0>();
     barrier_lds();
+    waited = t + 1;
   };
   const PfOffsets<D> off = pf_offsets<D>(n, g);
   // Lane offsets lie within the first 16 rows; stage bases are multiples of
   // a power of two at least that large, so OR-ing them in adds them.
   static_assert((GE::STAGE & (GE::STAGE - 1)) == 0 && GE::STAGE >= 16 * GE::ROWB, "stage bases above offsets");
-  // Scores of tile i live in sb[i & 1]: the loop body is compiled twice, once
-  // per parity, so the buffers are fixed registers and need no copies.
+  auto stage = [](int t) { return (uint32_t)(t & (kPfStages - 1)) * GE::STAGE; };
+
+  f32x4 o[kPfCB][GE::VBLK];
+  SoftmaxState sm[kPfCB];
+  // Scores of a block's tile i live in sb[i & 1]: the loop body is compiled
+  // twice, once per parity, so the buffers are fixed registers and need no
+  // copies.
   f32x4 sb[2][kPfCB][2];
-  if (ntiles > 0) {
+  int c0 = 0;  // the block's first tile in the stream
+  if (bk.ntiles > 0) {
     wait_tile(0);
-    pf_scores<DT, D>(smem, off, qop, sb[0]);
-  }
-  int i = 0;
-  auto step = [&](auto parity) __attribute__((always_inline)) {
-    constexpr int CUR = decltype(parity)::value, NXT = CUR ^ 1;
-    const bool more = i + 1 < ntiles;
-    if (more) {
-      wait_tile(i + 1);
-      if (issued < ntiles) issue();  // into the stage of tile i-1
-    }
-    const uint32_t knext = ((i + 1) % kPfStages) * GE::STAGE;
-    const uint32_t vcur = (i % kPfStages) * GE::STAGE;
-    const PfOffsets<D> offn{off.k0 | knext, off.v0 | vcur};
-    const int nv = kend - 32 * i < 32 ? kend - 32 * i : 32;
-    POperand pop[kPfCB];
-    bool grow[kPfCB];
-    float dexp[kPfCB], psum[kPfCB];
-    int nvc[kPfCB];
-#pragma unroll
-    for (int cb = 0; cb < kPfCB; ++cb) {
-      const int lv = lim[cb] - 32 * i + 1;
-      nvc[cb] = nv < lv ? nv : lv;
-    }
-    const bool full = nv == 32 && 32 * i + 31 <= lim_min;
-    // The next scores and this tile's softmax run at raised wave priority:
-    // when both waves of a SIMD can issue, the one in this mixed matrix and
-    // vector phase goes first, and the other's PV MFMAs fill the matrix
-    // unit behind it (measured 1-3% faster than no priority; raising the
-    // PV phase instead was slower).
-    __builtin_amdgcn_s_setprio(1);
-    if (more && full) {
-      pf_scores<DT, D>(smem, offn, qop, sb[NXT]);
-      pf_softmax4<DT, false>(sb[CUR], g, nvc, scale_log2, sm, grow, dexp, psum, pop);
-    } else if (more) {
-      pf_scores<DT, D>(smem, offn, qop, sb[NXT]);
-      pf_softmax4<DT, true>(sb[CUR], g, nvc, scale_log2, sm, grow, dexp, psum, pop);
-    } else {
-      pf_softmax4<DT, true>(sb[CUR], g, nvc, scale_log2, sm, grow, dexp, psum, pop);
-    }
-    __builtin_amdgcn_s_setprio(0);
-#pragma unroll
-    for (int cb = 0; cb < kPfCB; ++cb) {
-      // Rescale only when some column's running maximum moved.
-      if (__ballot(grow[cb])) {
-        const float alpha = grow[cb] ? exp2_fast(dexp[cb]) : 1.f;
-        sm[cb].l *= alpha;
-#pragma unroll
-        for (int bb = 0; bb < GE::VBLK; ++bb) o[cb][bb] *= alpha;
-      }
-      sm[cb].l += psum[cb];
-    }
-    pf_pv<DT, D, GE::KBYTES>(smem, offn, pop, o);
-  };
-  while (i < ntiles) {
-    step(std::integral_constant<int, 0>{});
-    if (++i == ntiles) break;
-    step(std::integral_constant<int, 1>{});
-    ++i;
+    flip_q();
+    pf_scores<DT, D>(smem, PfOffsets<D>{off.k0 | stage(0), off.v0}, qop, sb[0]);
   }
 
-  // Epilogue: lane (g, n) holds column 16cb + n, dims 16blk + 4g .. +3.
+  for (;;) {
 #pragma unroll
-  for (int cb = 0; cb < kPfCB; ++cb) {
-    const float l_tot = sum_over_groups(sm[cb].l);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const float lse_v = l_tot > 0.f ? sm[cb].m * kLn2 + __logf(l_tot) : -INFINITY;
-    if (valid[cb]) {
-      uint16_t* dst = a.out + orow[cb] * D + 4 * g;
+    for (int cb = 0; cb < kPfCB; ++cb) {
+      sm[cb] = SoftmaxState{-INFINITY, 0.f};
 #pragma unroll
-      for (int bb = 0; bb < GE::VBLK; ++bb) store_out4<DT>(dst + 16 * bb, o[cb][bb], inv);
-      if (a.lse && g == 0) a.lse[orow[cb]] = lse_v;
+      for (int bb = 0; bb < GE::VBLK; ++bb) o[cb][bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const long long pn = pf_position(r + 1, w, P);  // this workgroup's next block
+    const bool has_next = pn < N;
+
+    // Software pipeline: the scores of tile i+1 (matrix units) are computed
+    // in the same basic block as the softmax of tile i (vector unit), so the
+    // two overlap; then tile i's PV.
+    int i = 0;
+    auto step = [&](auto parity) __attribute__((always_inline)) {
+      constexpr int CUR = decltype(parity)::value, NXT = CUR ^ 1;
+      const int c = c0 + i;
+      if (c + 1 < issued) {
+        wait_tile(c + 1);
+        if (cur.live) issue();  // into the stage of tile c-1
+      }
+      const bool more = i + 1 < bk.ntiles;
+      const PfOffsets<D> offn{off.k0 | stage(c + 1), off.v0 | stage(c)};
+      const int nv = bk.kend - 32 * i < 32 ? bk.kend - 32 * i : 32;
+      POperand pop[kPfCB];
+      bool grow[kPfCB];
+      float dexp[kPfCB], psum[kPfCB];
+      int nvc[kPfCB];
+#pragma unroll
+      for (int cb = 0; cb < kPfCB; ++cb) {
+        const int lv = rw.lim[cb] - 32 * i + 1;
+        nvc[cb] = nv < lv ? nv : lv;
+      }
+      const bool full = nv == 32 && 32 * i + 31 <= rw.lim_min;
+      // The next scores and this tile's softmax run at raised wave priority:
+      // when both waves of a SIMD can issue, the one in this mixed matrix and
+      // vector phase goes first, and the other's PV MFMAs fill the matrix
+      // unit behind it (measured 1-3% faster than no priority; raising the
+      // PV phase instead was slower).
+      __builtin_amdgcn_s_setprio(1);
+      if (more && full) {
+        pf_scores<DT, D>(smem, offn, qop, sb[NXT]);
+        pf_softmax4<DT, false>(sb[CUR], g, nvc, scale_log2, sm, grow, dexp, psum, pop);
+      } else if (more) {
+        pf_scores<DT, D>(smem, offn, qop, sb[NXT]);
+        pf_softmax4<DT, true>(sb[CUR], g, nvc, scale_log2, sm, grow, dexp, psum, pop);
+      } else {
+        pf_softmax4<DT, true>(sb[CUR], g, nvc, scale_log2, sm, grow, dexp, psum, pop);
+      }
+      __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+      for (int cb = 0; cb < kPfCB; ++cb) {
+        // Rescale only when some column's running maximum moved.
+        if (__ballot(grow[cb])) {
+          const float alpha = grow[cb] ? exp2_fast(dexp[cb]) : 1.f;
+          sm[cb].l *= alpha;
+#pragma unroll
+          for (int bb = 0; bb < GE::VBLK; ++bb) o[cb][bb] *= alpha;
+        }
+        sm[cb].l += psum[cb];
+      }
+      pf_pv<DT, D, GE::KBYTES>(smem, offn, pop, o);
+    };
+    while (i < bk.ntiles) {
+      step(std::integral_constant<int, 0>{});
+      if (++i == bk.ntiles) break;
+      step(std::integral_constant<int, 1>{});
+      ++i;
+    }
+
+    // Epilogue: lane (g, n) holds column 16cb + n, dims 16blk + 4g .. +3.
+#pragma unroll
+    for (int cb = 0; cb < kPfCB; ++cb) {
+      const float l_tot = sum_over_groups(sm[cb].l);
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const float lse_v = l_tot > 0.f ? sm[cb].m * kLn2 + __logf(l_tot) : -INFINITY;
+      if (rw.valid[cb]) {
+        uint16_t* dst = a.out + rw.orow[cb] * D + 4 * g;
+#pragma unroll
+        for (int bb = 0; bb < GE::VBLK; ++bb) store_out4<DT>(dst + 16 * bb, o[cb][bb], inv);
+        if (a.lse && g == 0) a.lse[rw.orow[cb]] = lse_v;
+      }
+    }
+    if (!has_next) break;
+    c0 += bk.ntiles;
+    ++r;
+    bk = pf_block(vs, a, (int)pn);
+    rw = pf_rows(bk, a, wave, n);
+    if (bk.ntiles > 0) {
+      // The query operands are loaded here, at the block's start, and
+      // waited for before its first scores, outside the tile loop: loaded
+      // inside it (during the previous block's last tile), they made the
+      // compiler wait for them before every tile's scores, and with them for
+      // every tile load in flight.
+      load_q(rw.orow);
+      if (waited <= c0) wait_tile(c0);
+      flip_q();
+      pf_scores<DT, D>(smem, PfOffsets<D>{off.k0 | stage(c0), off.v0}, qop, sb[0]);
     }
   }
 }
 
+// Two workgroups per CU (their LDS and registers), persistent over the blocks.
+constexpr int kPfResident = 2 * 256;
+
 template <int D, int DT>
 static void launch_prefill_t(const DecodeArgs& a, int nblocks, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.Hkv * nblocks)), block(64 * kPfWaves);
+  const long long total = (long long)a.Hkv * nblocks;
+  const dim3 grid((unsigned)(total < kPfResident ? total : kPfResident)), block(64 * kPfWaves);
   if (a.block_table)
-    hipLaunchKernelGGL((prefill_kernel<D, DT, true>), grid, block, 0, stream, a, a.cu, a.block_table, nblocks);
+    hipLaunchKernelGGL((prefill_kernel<D, DT, true>), grid, block, 0, stream, a, a.cu, a.block_table);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, DT, false>), grid, block, 0, stream, a, a.cu, a.block_table, nblocks);
+    hipLaunchKernelGGL((prefill_kernel<D, DT, false>), grid, block, 0, stream, a, a.cu, a.block_table);
 }
 
 hipError_t launch_prefill(const DecodeArgs& a, int head_dim, int dtype, int max_blocks, hipStream_t stream) {

@@ -72,9 +72,9 @@ struct CombineArgs {
   int S, rows, Dv;
 };
 
-// Long runs of new tokens (prefill_attn.hip): one workgroup per (key/value
-// head, block of 2^kPrefillRowsLog2 query rows); max_blocks bounds the blocks
-// of the batch.
+// Long runs of new tokens (prefill_attn.hip): blocks of (key/value head,
+// 2^kPrefillRowsLog2 query rows), taken in rounds by at most two persistent
+// workgroups per CU; max_blocks bounds the blocks of the batch per head.
 constexpr int kPrefillRowsLog2 = 7;
 hipError_t launch_prefill(const DecodeArgs& a, int head_dim, int dtype, int max_blocks, hipStream_t stream);
 
