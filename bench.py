@@ -532,6 +532,7 @@ def bench_prefill(args):
                 f"-h{spec.num_q_heads}kv{spec.num_kv_heads}-d{spec.head_dim_k}-{spec.dtype}" +
                 (f"+paged{args.paged}" if args.paged else ""))
     prof = profile_record(workload, "prefill")
+    cpu = None if args.no_cpu else cpu_baseline_prefill(x, vq, spec, flops, args.cpu_seconds)
     print(json.dumps({
         "metric": "prefill attention TFLOP/s (useful causal QK^T + PV flops / step time)",
         "value": round(tf, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": W,
@@ -543,7 +544,7 @@ def bench_prefill(args):
         "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tf, 1),
                      "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_TFLOPS, 4),
                      "traffic": prof.get("hbm_bytes_per_launch"), "mfma_busy": prof.get("mfma_busy_frac")},
-        "cpu_baseline": None}), flush=True)
+        "cpu_baseline": cpu}), flush=True)
 
 
 def bench_codec(args):
@@ -612,6 +613,7 @@ def bench_codec(args):
     kgbs = per_call / (kern_ms * 1e-3) / 1e9
     workload = f"codec-{args.codec}-{args.codec_mib}MiB-fp16-chunk{C}"
     prof = profile_record(workload, "codec")
+    cpu = None if args.no_cpu else cpu_baseline_codec(args.codec, base, C, per_call / n, args.cpu_seconds)
     print(json.dumps({
         "metric": f"INT8 all-reduce payload codec ({args.codec}) GB/s of algorithmic bytes",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -623,7 +625,7 @@ def bench_codec(args):
                      "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
                      "traffic": prof.get("hbm_bytes_per_launch"),
                      "avg_launch_us": round(kern_ms * 1e3, 2)},
-        "cpu_baseline": None}), flush=True)
+        "cpu_baseline": cpu}), flush=True)
 
 
 def cpu_baseline(x, spec, target_s: float):
@@ -675,6 +677,82 @@ def oracle_rate(x, spec, target_s: float, threads: int):
                   f"{done_bytes} KV bytes) through the fp64 C oracle, OpenMP over heads on {threads} "
                   f"thread{'s' if threads > 1 else ''}, {elapsed:.1f} s",
         "us_per_step_equiv": round(x.kv_bytes() / (done_bytes / elapsed) * 1e6, 1),
+    }
+
+
+def cpu_baseline_prefill(x, vq, spec, flops_per_step: float, target_s: float):
+    """The fp64 oracle on a bounded sample of the prefill's query rows: every
+    (new token, head) pair of a strided grid (about 256 tokens by 8 heads),
+    repeated for about target_s seconds on all host cores; reported in the
+    metric's unit (useful causal flops of the sample per second)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    threads = oracle.max_threads()
+    dt = oracle.F16 if spec.dtype == "f16" else oracle.BF16
+    cq, ck = vq.cu_q.numpy(), x.cu_seqlens.numpy()
+    Tq, Hq, D = vq.total_q, spec.num_q_heads, spec.head_dim_k
+    rows = [(t, h) for t in range(0, Tq, max(1, Tq // 256)) for h in range(0, Hq, max(1, Hq // 8))]
+    seq = np.searchsorted(cq, np.arange(Tq), side="right") - 1
+    flops = 0.0
+    for t, _ in rows:  # keys seen by new token i of nq over a cache of lk rows: lk - nq + i + 1
+        b = seq[t]
+        nq, lk = int(cq[b + 1] - cq[b]), int(ck[b + 1] - ck[b])
+        flops += 4.0 * D * max(0, lk - nq + (t - int(cq[b])) + 1)
+    qb = vq.q.contiguous().view(torch.int16).numpy().view(np.uint16)
+    kb, vb = x.bits("k"), x.bits("v")
+    elapsed, calls = 0.0, 0
+    while elapsed < target_s or calls == 0:
+        t0 = time.perf_counter()
+        oracle.gqa_varlen(qb, kb, vb, cq, ck, spec.num_kv_heads, spec.scale, dt, causal=True, rows=rows,
+                          threads=threads)
+        elapsed += time.perf_counter() - t0
+        calls += 1
+    rate = flops * calls / elapsed
+    return {
+        "value": round(rate / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{len(rows)} (new token, head) rows of this prefill on a strided grid, {flops:.4g} useful "
+                  f"flops, through the fp64 C oracle {calls} times on {threads} threads, {elapsed:.1f} s",
+        "us_per_step_equiv": round(flops_per_step / rate * 1e6, 1),
+    }
+
+
+def cpu_baseline_codec(mode: str, base, chunk: int, bytes_per_elem: float, target_s: float):
+    """The numpy codec oracle (one core) on the first 4 Mi elements of the same
+    payload, repeated for about target_s seconds; reported in the metric's
+    unit (algorithmic bytes per second)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from oracle import codec
+
+    n = min(base.numel(), 1 << 22)
+    n -= n % chunk
+    bits = base[:n].contiguous().view(torch.int16).numpy().view(np.uint16)
+    codes, scales = codec.quantize(bits, oracle.F16, chunk)
+    elapsed, calls = 0.0, 0
+    while elapsed < target_s or calls == 0:
+        t0 = time.perf_counter()
+        if mode == "quantize":
+            codec.quantize(bits, oracle.F16, chunk)
+        elif mode == "dequantize":
+            codec.dequantize(codes, scales, chunk, oracle.F16)
+        else:
+            codec.reduce_step(codes, scales, bits, oracle.F16, chunk)
+        elapsed += time.perf_counter() - t0
+        calls += 1
+    return {
+        "value": round(bytes_per_elem * n * calls / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"the codec oracle (numpy) on the payload's first {n} fp16 values, {calls} calls, {elapsed:.1f} s",
     }
 
 
