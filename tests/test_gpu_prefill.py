@@ -184,3 +184,23 @@ def test_paged_long_prompt_every_row(ps):
     gate(out, ro, torch.bfloat16, lse, rl, where=where)
     po, _ = run(x, vq)
     assert torch.equal(out, po)
+
+
+@pytest.mark.parametrize("ps", [0, 16])
+def test_many_sequences_many_rounds(ps):
+    """80 ragged sequences, 32 query / 8 key-value heads: about 3,000 blocks,
+    so every one of the 512 resident workgroups takes several, over the
+    batch's second chunk of 64 sequences too; some sequences have more new
+    tokens than cache rows (their first blocks see no key) and some none.
+    Every row against the oracle, packed and over 16-token pages."""
+    lens = [(i * 53) % 400 + 1 for i in range(80)]
+    q_lens = [0 if i % 17 == 5 else min(lens[i] + (i % 3) * 40, (i * 29) % 300 + 1) for i in range(80)]
+    x, vq = make(lens, q_lens, 32, 8, 128, torch.bfloat16, seed=23)
+    where = f"80 sequences, pages {ps}"
+    print(where, flush=True)
+    if ps:
+        out, lse = run_paged(x, vq, workloads.make_paged(x, ps), where=where)
+    else:
+        out, lse = run(x, vq, where=where)
+    ro, rl = oracle_rows(x, vq)
+    gate(out, ro, torch.bfloat16, lse, rl, where=where)
