@@ -180,3 +180,31 @@ def test_duplicated_rows_add_ln2(kind, dt, paged):
     shifted = lse.cpu().numpy().astype(np.float64)[fin] - math.log(2.0)
     assert np.all(np.abs(shifted - rl[fin]) <= LSE_ABS + LSE_REL * np.abs(rl[fin])), where
     assert np.all(np.isneginf(lse.cpu().numpy()[~fin]))
+
+
+def permuted(x, seed=7):
+    """Every sequence's rows in a seeded random order (the same order for K
+    and V, or for the latent rows): the attention does not depend on it."""
+    s = x.spec
+    cu = x.cu_seqlens.numpy()
+    rng = np.random.default_rng(seed)
+    order = np.concatenate([int(cu[b]) + rng.permutation(int(cu[b + 1] - cu[b])) for b in range(s.batch)])
+    idx = torch.from_numpy(order.astype(np.int64))
+    if s.kind == "mla":
+        return workloads.Inputs(s, np.asarray(x.lens), x.cu_seqlens, x.q, latent=x.latent[idx].contiguous())
+    return workloads.Inputs(s, np.asarray(x.lens), x.cu_seqlens, x.q, k=x.k[idx].contiguous(),
+                            v=x.v[idx].contiguous())
+
+
+@pytest.mark.parametrize("kind,dt,paged", PARAMS, ids=IDS)
+def test_token_permutation(kind, dt, paged):
+    """Rows of every sequence shuffled: the kernel's result on the shuffled
+    caches meets the gate against the oracle on the original order (the
+    split points and tile boundaries now fall on other rows)."""
+    x0 = base_inputs(kind, dt)
+    x = permuted(x0)
+    where = f"permuted rows {kind} {dt} {'paged' if paged else 'packed'}"
+    print(where, flush=True)
+    out, lse = run(x, paged, where)
+    ro, rl = run_oracle(x0)
+    gate(out, ro, dt, lse, rl, where=where + " (against the original order)")
