@@ -186,24 +186,34 @@ def test_paged_long_prompt_every_row(ps):
     assert torch.equal(out, po)
 
 
-@pytest.mark.parametrize("ps", [0, 16])
-def test_many_sequences_many_rounds(ps):
-    """80 ragged sequences, 32 query / 8 key-value heads: about 3,000 blocks,
-    so every one of the 512 resident workgroups takes several, over the
-    batch's second chunk of 64 sequences too; some sequences have more new
-    tokens than cache rows (their first blocks see no key) and some none.
-    Every row against the oracle, packed and over 16-token pages."""
+MANY = [
+    # (query heads, key/value heads, head dim, dtype, causal, page size)
+    (32, 8, 128, torch.bfloat16, True, 0),
+    (32, 8, 128, torch.bfloat16, True, 16),
+    (8, 8, 64, torch.float16, True, 0),       # G = 1, D = 64
+    (16, 2, 64, torch.bfloat16, False, 64),   # no mask, D = 64, 64-token pages
+    (24, 3, 128, torch.float16, True, 0),     # G = 8
+]
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,dt,causal,ps", MANY)
+def test_many_sequences_many_rounds(Hq, Hkv, D, dt, causal, ps):
+    """80 ragged sequences: hundreds to thousands of blocks, so the 512
+    resident workgroups take several each, over the batch's second chunk of
+    64 sequences too; some sequences have more new tokens than cache rows
+    (their first blocks see no key) and some none.  Every row against the
+    oracle, packed or over pages."""
     lens = [(i * 53) % 400 + 1 for i in range(80)]
     q_lens = [0 if i % 17 == 5 else min(lens[i] + (i % 3) * 40, (i * 29) % 300 + 1) for i in range(80)]
-    x, vq = make(lens, q_lens, 32, 8, 128, torch.bfloat16, seed=23)
-    where = f"80 sequences, pages {ps}"
+    x, vq = make(lens, q_lens, Hq, Hkv, D, dt, seed=23)
+    where = f"80 sequences, {Hq}/{Hkv} heads, D {D}, causal {causal}, pages {ps}"
     print(where, flush=True)
     if ps:
-        out, lse = run_paged(x, vq, workloads.make_paged(x, ps), where=where)
+        out, lse = run_paged(x, vq, workloads.make_paged(x, ps), causal=causal, where=where)
     else:
-        out, lse = run(x, vq, where=where)
-    ro, rl = oracle_rows(x, vq)
-    gate(out, ro, torch.bfloat16, lse, rl, where=where)
+        out, lse = run(x, vq, causal=causal, where=where)
+    ro, rl = oracle_rows(x, vq, causal=causal)
+    gate(out, ro, dt, lse, rl, where=where)
 
 
 def test_repeated_calls_are_bitwise_identical():
