@@ -19,7 +19,8 @@ from tests.parity import gate
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-N_CASES = 48
+N_CASES = 200
+N_PREFILL_CASES = 100
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -172,7 +173,7 @@ def draw_prefill_case(i: int) -> dict:
                 seed=100 + i)
 
 
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", range(N_PREFILL_CASES))
 def test_random_prefill_case(i):
     import mla_attention_amd as zl
     c = draw_prefill_case(i)
