@@ -438,7 +438,9 @@ ZL_API zl_status_t zl_attn_prefill_gqa_paged(const void *q, const void *k_pages,
  *   amax = max |x| over the chunk,  code = rint(x * (127 / amax)) (ties to
  *   even; 0 when amax = 0),  scale = amax / 127,  value = code * scale
  * in fp32 with every product, sum and quotient rounded on its own (a short
- * last chunk is coded on its own).  All pointers are device pointers; the
+ * last chunk is coded on its own).  The payload values are finite (a NaN or
+ * an infinity leaves its chunk's codes and scale unspecified; nothing is
+ * read or written out of bounds).  All pointers are device pointers; the
  * 16-bit arrays and the codes must be 16-byte aligned, the scales 4-byte
  * aligned; n == 0 is a no-op.  The collective itself (moving the codes
  * between GPUs) is not part of this library.
