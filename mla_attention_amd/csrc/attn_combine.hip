@@ -38,13 +38,25 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   for (int off = 1; off < 64; off <<= 1) wsum += shfl_xor(wsum, off);
   const float winv = 1.f / wsum;
 
+  // Partials are loaded kBatch at a time (past the last split the loads
+  // repeat it and carry no weight) and added in split order.
+  constexpr int kBatch = 8;
   for (int c4 = lane; c4 * 4 < a.Dv; c4 += 64) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < a.S; ++s) {
-      const float ls = a.part_lse[s * rows + row];
-      if (ls == -INFINITY) continue;  // an empty split carries no weight
-      const float wt = exp2_fast((ls - M) * kLog2e);
-      acc += wt * *(const f32x4*)(a.part_o + ((long long)s * rows + row) * a.Dv + 4 * c4);
+    for (int s0 = 0; s0 < a.S; s0 += kBatch) {
+      float ls[kBatch];
+      f32x4 v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int s = min(s0 + j, a.S - 1);
+        ls[j] = s0 + j < a.S ? a.part_lse[s * rows + row] : -INFINITY;
+        v[j] = *(const f32x4*)(a.part_o + ((long long)s * rows + row) * a.Dv + 4 * c4);
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (ls[j] == -INFINITY) continue;  // an empty split carries no weight
+        acc += exp2_fast((ls[j] - M) * kLog2e) * v[j];
+      }
     }
     u32x2 w;
     w[0] = pack2<DT>(acc[0] * winv, acc[1] * winv);
