@@ -1,16 +1,16 @@
 // no_alloc.hip -- grouped-query decode attention for callers that cannot
 // allocate device memory (code under HIP graph capture, tight serving loops,
 // harnesses that forbid hipMalloc): zl_decode_attn_gqa with its workspace (the
-// fp32 partials of split sequences and the per-worker keys) taken from a
-// fixed array in device memory instead of a caller buffer.
+// fp32 partials of split sequences) taken from a fixed array in device memory
+// instead of a caller buffer.
 //
 // `scratch` is a file-scope device array; every GPU the library runs on holds
 // its own copy, at its own address, until the process ends.  In host code its
 // name is only a stand-in, so its device address is looked up once per device
 // with hipGetSymbolAddress (with that device current) and only that address
 // is ever passed on.  The workspace needs no initialisation (every worker
-// writes its key and its partial slots before the merge reads them), so
-// nothing is cleared between calls.  Calls that overlap in time on one GPU
+// writes its partial slots before the merge reads them, and the merge finds
+// them by rule), so nothing is cleared between calls.  Calls that overlap in time on one GPU
 // share the array and race; calls on one stream are ordered.
 #include <hip/hip_runtime.h>
 
