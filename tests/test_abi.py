@@ -1,7 +1,6 @@
 """The C ABI on the CPU: the library loads without a GPU, exports exactly what
 include/zl_attn.h declares, sizes workspaces, and rejects every bad argument
 with the documented status before making any HIP call."""
-import ctypes
 import os
 import re
 

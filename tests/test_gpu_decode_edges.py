@@ -13,7 +13,7 @@ import torch
 
 import workloads
 from tests.parity import LSE_ABS, LSE_REL, gate
-from tests.test_gpu_parity import DEV, run_gpu, run_gpu_paged, run_oracle, run_oracle_paged
+from tests.test_gpu_parity import run_gpu, run_gpu_paged, run_oracle, run_oracle_paged
 
 pytestmark = pytest.mark.gpu
 
