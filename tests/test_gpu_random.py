@@ -3,9 +3,11 @@ several new tokens, packed or paged caches, GQA or MLA, f16 or bf16, causal
 or not, library-chosen or forced worker counts) against the fp64 oracle on
 identical inputs.  The cases are drawn from a fixed seed, so a failure names
 a reproducible case; they complement the hand-picked edge cases with shapes
-nobody chose.
+nobody chose.  ZL_RANDOM_CASES and ZL_RANDOM_PREFILL_CASES widen the sweep
+(case i is the same draw whatever the count).
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -19,8 +21,8 @@ from tests.parity import gate
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-N_CASES = 200
-N_PREFILL_CASES = 100
+N_CASES = int(os.environ.get("ZL_RANDOM_CASES", "200"))
+N_PREFILL_CASES = int(os.environ.get("ZL_RANDOM_PREFILL_CASES", "100"))
 
 
 @pytest.fixture(scope="module", autouse=True)
