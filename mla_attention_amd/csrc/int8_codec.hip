@@ -125,12 +125,13 @@ __device__ __forceinline__ void store_codes(int8_t* p, int valid, const int8_t (
 }
 
 // Chunks a wave loads before coding any of them (memory-level parallelism),
-// measured per operation on a cold 256 MiB payload: decoding gains from four
-// (73 against 86 us), the hop, which moves four arrays, runs best with one
-// (146 against 174 us with four), coding is indifferent.
+// measured per operation on a cold 256 MiB payload with the non-temporal
+// accesses: decoding gains from four (71 against 75-85 us with fewer), the
+// hop, which moves four arrays, runs best with two (130 against 139 us with
+// one and 145 with four), coding is indifferent.
 template <int OP>
 constexpr int chunks_per_wave() {
-  return OP == kCodecDequantize ? 4 : (OP == kCodecReduce ? 1 : 2);
+  return OP == kCodecDequantize ? 4 : 2;
 }
 
 // Most workgroups per launch (the waves stride over the groups beyond), also
